@@ -1,0 +1,173 @@
+"""fp64 CPU oracle for the Gated DeltaNet token mixer.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the CPU-baseline leg
+of the benchmark are the only callers. The product path never imports this
+package, and this package imports nothing from the product package.
+
+The arithmetic lives in ``gdn_oracle.c`` (a plain token-by-token fp64
+recurrence; see its header for the definition and the reading of the pages it
+follows). This module only builds/loads that library and walks it over
+(sequence, value-head) chains with a thread pool. ctypes drops the GIL for
+the duration of each call, so the chains run in parallel on the host cores.
+
+Layouts (the same as the HIP library's):
+  q, k  [tokens, Hk, Dk]   v  [tokens, Hv, Dv]   alpha, beta [tokens, Hv]
+  states [chains, Hv, Dv, Dk]   (S in R^{Dv x Dk}, row-major)
+bf16 tensors are passed as numpy uint16 arrays holding the bit patterns.
+Value head h reads q/k head h // (Hv // Hk).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+F32, BF16 = 0, 1
+
+
+def build(force: bool = True) -> str:
+    """Compile gdn_oracle.c into liboracle.so with gcc (host code only)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O3", "-march=x86-64-v3", "-fno-fast-math", "-fPIC",
+               "-shared", "-std=c11", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        f = lib.gdn_oracle_chain
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                      ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                      ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                      ctypes.c_void_p, ctypes.c_void_p]
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    env = os.environ.get("GDN_ORACLE_THREADS")
+    if env:
+        return max(1, int(env))
+    return max(1, min(os.cpu_count() or 1, 16))
+
+
+def _dtype_code(arr: np.ndarray) -> int:
+    if arr.dtype == np.uint16:
+        return BF16
+    if arr.dtype == np.float32:
+        return F32
+    raise TypeError(f"q/k/v must be float32 or uint16 (bf16 bits), got {arr.dtype}")
+
+
+def chain(q, k, v, alpha, beta, t0: int, t1: int, h: int, S0=None, scale: float = 1.0,
+          want_o: bool = True):
+    """Run the recurrence for value head ``h`` over packed tokens [t0, t1).
+
+    Returns (o [t1-t0, Dv] fp64 or None, S [Dv, Dk] fp64)."""
+    lib = _load()
+    for a in (q, k, v, alpha, beta):
+        if not a.flags.c_contiguous:
+            raise ValueError("oracle inputs must be C-contiguous")
+    dt = _dtype_code(q)
+    if _dtype_code(k) != dt or _dtype_code(v) != dt:
+        raise TypeError("q, k, v must share one dtype")
+    if alpha.dtype != np.float32 or beta.dtype != np.float32:
+        raise TypeError("alpha, beta must be float32")
+    _, Hk, Dk = q.shape
+    _, Hv, Dv = v.shape
+    g = h // (Hv // Hk)
+    T = t1 - t0
+    S = np.zeros((Dv, Dk), np.float64) if S0 is None else np.array(S0, np.float64, order="C")
+    o = np.empty((max(T, 0), Dv), np.float64) if want_o else None
+    isz = q.itemsize
+    rc = lib.gdn_oracle_chain(
+        q.ctypes.data + ((t0 * Hk + g) * Dk) * isz,
+        k.ctypes.data + ((t0 * Hk + g) * Dk) * isz,
+        v.ctypes.data + ((t0 * Hv + h) * Dv) * isz,
+        dt,
+        alpha.ctypes.data + (t0 * Hv + h) * 4,
+        beta.ctypes.data + (t0 * Hv + h) * 4,
+        T, Hk * Dk, Hv * Dv, Hv, Dk, Dv, float(scale),
+        S.ctypes.data, o.ctypes.data if o is not None else None)
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return o, S
+
+
+def _flatten_batch(x):
+    return x.reshape((-1,) + x.shape[2:])
+
+
+def prefill(q, k, v, alpha, beta, initial_state=None, scale=1.0, chains=None,
+            threads=None):
+    """Dense-batch prefill: q,k [B,T,Hk,Dk]; v [B,T,Hv,Dv]; alpha,beta [B,T,Hv].
+
+    ``chains`` optionally lists the (b, h) pairs to compute (default: all).
+    Returns (o, S): o [B,T,Hv,Dv] fp64 and S [B,Hv,Dv,Dk] fp64; entries of
+    chains not computed are NaN."""
+    B, T = q.shape[0], q.shape[1]
+    Hv, Dv = v.shape[2], v.shape[3]
+    Dk = q.shape[3]
+    cu = np.arange(B + 1, dtype=np.int64) * T
+    o, S = varlen(_flatten_batch(q), _flatten_batch(k), _flatten_batch(v),
+                  _flatten_batch(alpha), _flatten_batch(beta), cu, initial_state,
+                  scale, chains, threads)
+    return o.reshape(B, T, Hv, Dv), S.reshape(B, Hv, Dv, Dk)
+
+
+def varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None, scale=1.0,
+           chains=None, threads=None):
+    """Packed prefill: q,k [total,Hk,Dk]; v [total,Hv,Dv]; alpha,beta [total,Hv];
+    sequence n spans tokens cu_seqlens[n] .. cu_seqlens[n+1]-1.
+
+    Returns (o [total,Hv,Dv] fp64, S [N,Hv,Dv,Dk] fp64); entries of chains not
+    listed in ``chains`` are NaN."""
+    cu = [int(x) for x in np.asarray(cu_seqlens)]
+    N = len(cu) - 1
+    total, Hv, Dv = v.shape
+    Dk = q.shape[2]
+    if chains is None:
+        chains = [(n, h) for n in range(N) for h in range(Hv)]
+    o = np.full((total, Hv, Dv), np.nan)
+    S = np.full((N, Hv, Dv, Dk), np.nan)
+
+    def work(nh):
+        n, h = nh
+        s0 = None if initial_state is None else initial_state[n, h]
+        oc, sc = chain(q, k, v, alpha, beta, cu[n], cu[n + 1], h, s0, scale)
+        o[cu[n]:cu[n + 1], h, :] = oc
+        S[n, h] = sc
+
+    nthreads = threads or default_threads()
+    if nthreads == 1 or len(chains) == 1:
+        for nh in chains:
+            work(nh)
+    else:
+        with ThreadPoolExecutor(nthreads) as ex:
+            list(ex.map(work, chains))
+    return o, S
+
+
+def decode(q, k, v, alpha, beta, state, scale=1.0, threads=None):
+    """One token per sequence: q,k [B,Hk,Dk]; v [B,Hv,Dv]; alpha,beta [B,Hv];
+    state [B,Hv,Dv,Dk] fp32 (not modified). Returns (o [B,Hv,Dv], S') in fp64."""
+    B = q.shape[0]
+    cu = np.arange(B + 1, dtype=np.int64)
+    return varlen(q, k, v, alpha, beta, cu, state, scale, None, threads)

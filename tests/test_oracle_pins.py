@@ -1,0 +1,299 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle.
+
+Each test fixes the oracle to something independent of its own code: a
+hand-worked example, a closed form of the recurrence for special inputs, an
+algebraic invariant, or the literal matrix form of the rule on tiny inputs.
+The rule is the gated delta rule used by the Gated DeltaNet layers named in
+"The Hybrid Attention in Qwen3.8-27B" (section "Why 27B parameters can carry
+262K tokens"): S_t = a_t S_{t-1}(I - b_t k_t k_t^T) + b_t v_t k_t^T and
+o_t = S_t q_t, with value head h reading q/k head h // (Hv / Hk).
+
+Which planted mistake each pin catches:
+  hand-worked  : any wrong term, sign or order on a 2x2 case
+  decay-only   : alpha taken from the wrong token/head, initial state ignored
+  single-token : o from S_{t-1} instead of S_t, S vs S^T, beta dropped, scale
+  overwrite    : alpha applied after the write, alpha missing from the erase,
+                 a wrong sign in the erase term
+  literal form : the rank-1 rewrite of the matrix product
+  memory/repeat: overwrite semantics of the delta rule
+  linearity    : a hidden non-linearity in (S0, V)
+  split        : state hand-over between calls
+  chunk mirror : the chunked algebra the GPU evaluates
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from gdn_synth import bf16_bits, bf16_to_f32, small_prefill
+from tests.chunk_mirror import chunk_chain
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_inputs(rng, T, Hk, Hv, dk, dv, unit_k=True):
+    q = rng.standard_normal((T, Hk, dk)).astype(np.float32)
+    k = rng.standard_normal((T, Hk, dk)).astype(np.float32)
+    if unit_k:
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+        q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, Hv, dv)).astype(np.float32)
+    alpha = rng.uniform(0.05, 1.0, (T, Hv)).astype(np.float32)
+    beta = rng.uniform(0.0, 1.0, (T, Hv)).astype(np.float32)
+    return q, k, v, alpha, beta
+
+
+def _f64(x):
+    return np.asarray(x, np.float64)
+
+
+# ------------------------------------------------------------ hand-worked
+def test_hand_worked_two_tokens():
+    g = json.load(open(os.path.join(GOLDEN, "hand_worked_two_tokens.json")))
+    inp = g["inputs"]
+    q = np.array(inp["q"], np.float32)[:, None, :]
+    k = np.array(inp["k"], np.float32)[:, None, :]
+    v = np.array(inp["v"], np.float32)[:, None, :]
+    a = np.array(inp["alpha"], np.float32)[:, None]
+    b = np.array(inp["beta"], np.float32)[:, None]
+    o, S = oracle.chain(q, k, v, a, b, 0, 2, 0)
+    np.testing.assert_array_equal(o, np.array(g["expected"]["o"]))
+    np.testing.assert_array_equal(S, np.array(g["expected"]["S_final"]))
+    o2, S2 = oracle.chain(q, k, v, a, b, 0, 2, 0, scale=2.0)
+    np.testing.assert_array_equal(o2, 2.0 * np.array(g["expected"]["o"]))
+    np.testing.assert_array_equal(S2, S)
+
+
+# ------------------------------------------------------------ closed forms
+def test_decay_only_beta_zero():
+    """beta = 0: S_T = (prod a) S0 and o_t = (prod_{s<=t} a_s) S0 q_t."""
+    rng = np.random.default_rng(1)
+    T, Hk, Hv, d = 37, 2, 6, 16
+    q, k, v, alpha, _ = _rand_inputs(rng, T, Hk, Hv, d, d)
+    beta = np.zeros((T, Hv), np.float32)
+    S0 = rng.standard_normal((1, Hv, d, d)).astype(np.float32)
+    o, S = oracle.prefill(q[None], k[None], v[None], alpha[None], beta[None], S0)
+    for h in range(Hv):
+        g = h // (Hv // Hk)
+        cp = np.cumprod(_f64(alpha[:, h]))
+        exp_o = cp[:, None] * (_f64(q[:, g]) @ _f64(S0[0, h]).T)
+        np.testing.assert_allclose(o[0, :, h], exp_o, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(S[0, h], cp[-1] * _f64(S0[0, h]), rtol=1e-12, atol=1e-300)
+
+
+def test_single_token_from_zero():
+    """T = 1, S0 = 0: S_1 = b v k^T and o = scale * b (k.q) v (q != k)."""
+    rng = np.random.default_rng(2)
+    Hk, Hv, dk, dv = 3, 6, 8, 12
+    q, k, v, alpha, beta = _rand_inputs(rng, 1, Hk, Hv, dk, dv)
+    o, S = oracle.prefill(q[None], k[None], v[None], alpha[None], beta[None], None, scale=0.75)
+    for h in range(Hv):
+        g = h // (Hv // Hk)
+        kq = float(_f64(k[0, g]) @ _f64(q[0, g]))
+        np.testing.assert_allclose(o[0, 0, h], 0.75 * float(beta[0, h]) * kq * _f64(v[0, h]),
+                                   rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(S[0, h], float(beta[0, h]) * np.outer(_f64(v[0, h]), _f64(k[0, g])),
+                                   rtol=1e-12, atol=1e-14)
+
+
+def _exact_unit_keys(rng, T, H, d, nnz):
+    """Keys with nnz entries of +-1/sqrt(nnz) (nnz a power of 4): norm exactly 1."""
+    k = np.zeros((T, H, d), np.float32)
+    val = np.float32(1.0 / np.sqrt(nnz))
+    for t in range(T):
+        for h in range(H):
+            idx = rng.choice(d, nnz, replace=False)
+            k[t, h, idx] = val * rng.choice([-1.0, 1.0], nnz)
+    return k
+
+
+def test_exact_overwrite_beta_one():
+    """beta = 1 and unit k: after the write S_t k_t = v_t, for any alpha and S."""
+    rng = np.random.default_rng(3)
+    T, Hk, Hv, d = 25, 2, 4, 64
+    q, _, v, alpha, _ = _rand_inputs(rng, T, Hk, Hv, d, d)
+    k = _exact_unit_keys(rng, T, Hk, d, 16)
+    beta = np.ones((T, Hv), np.float32)
+    S0 = rng.standard_normal((1, Hv, d, d)).astype(np.float32)
+    for t1 in range(1, T + 1):
+        _, S = oracle.prefill(q[None, :t1], k[None, :t1], v[None, :t1], alpha[None, :t1],
+                              beta[None, :t1], S0)
+        for h in range(Hv):
+            g = h // (Hv // Hk)
+            np.testing.assert_allclose(S[0, h] @ _f64(k[t1 - 1, g]), _f64(v[t1 - 1, h]),
+                                       rtol=0, atol=1e-12)
+
+
+def test_literal_matrix_form():
+    """Tiny inputs: the rank-1 token loop equals the literal
+    a S (I - b k k^T) + b v k^T evaluated with explicit d x d matrices."""
+    rng = np.random.default_rng(4)
+    for (T, dk, dv) in [(1, 1, 1), (3, 2, 5), (8, 8, 8), (7, 5, 3)]:
+        q, k, v, alpha, beta = _rand_inputs(rng, T, 1, 1, dk, dv, unit_k=False)
+        S0 = rng.standard_normal((1, 1, dv, dk)).astype(np.float32)
+        o, S = oracle.prefill(q[None], k[None], v[None], alpha[None], beta[None], S0, scale=1.5)
+        Sx = _f64(S0[0, 0])
+        for t in range(T):
+            kt, qt, vt = _f64(k[t, 0]), _f64(q[t, 0]), _f64(v[t, 0])
+            a, b = float(alpha[t, 0]), float(beta[t, 0])
+            Sx = a * Sx @ (np.eye(dk) - b * np.outer(kt, kt)) + b * np.outer(vt, kt)
+            np.testing.assert_allclose(o[0, t, 0], 1.5 * Sx @ qt, rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(S[0, 0], Sx, rtol=1e-13, atol=1e-13)
+
+
+def _hadamard(n):
+    H = np.array([[1.0]])
+    while H.shape[0] < n:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+def test_delta_rule_memory_orthonormal_keys():
+    """a = b = 1, orthonormal keys, S0 = 0: S_m = sum v_j k_j^T, and a query
+    equal to an earlier key returns that key's value."""
+    rng = np.random.default_rng(5)
+    d, m = 64, 40
+    Hrows = (_hadamard(d) / np.sqrt(d)).astype(np.float32)  # entries +-1/8: exact
+    order = rng.permutation(d)[:m]
+    k = Hrows[order][:, None, :]
+    q = k[rng.integers(0, m, m)]  # query: some key (possibly a later one)
+    v = rng.standard_normal((m, 1, d)).astype(np.float32)
+    ones = np.ones((m, 1), np.float32)
+    o, S = oracle.chain(q, k, v, ones, ones, 0, m, 0)
+    np.testing.assert_allclose(S, sum(np.outer(_f64(v[j, 0]), _f64(k[j, 0])) for j in range(m)),
+                               atol=1e-12)
+    for t in range(m):
+        j = int(np.where((k[:, 0] == q[t, 0]).all(axis=1))[0][0])
+        expect = _f64(v[j, 0]) if j <= t else np.zeros(d)
+        np.testing.assert_allclose(o[t], expect, atol=1e-12)
+
+
+def test_repeated_key_keeps_latest_value():
+    rng = np.random.default_rng(6)
+    d = 16
+    k1 = _exact_unit_keys(rng, 1, 1, d, 4)[0, 0]
+    k = np.stack([k1, k1])[:, None, :]
+    v = rng.standard_normal((2, 1, d)).astype(np.float32)
+    ones = np.ones((2, 1), np.float32)
+    _, S = oracle.chain(k, k, v, ones, ones, 0, 2, 0)
+    np.testing.assert_allclose(S @ _f64(k1), _f64(v[1, 0]), atol=1e-13)
+
+
+# ------------------------------------------------------------ invariants
+def test_linearity_in_state_and_values():
+    rng = np.random.default_rng(7)
+    T, Hk, Hv, d = 20, 1, 2, 16
+    q, k, _, alpha, beta = _rand_inputs(rng, T, Hk, Hv, d, d)
+    v1 = (rng.integers(-64, 64, (T, Hv, d)) / 16).astype(np.float32)
+    v2 = (rng.integers(-64, 64, (T, Hv, d)) / 16).astype(np.float32)
+    s1 = (rng.integers(-64, 64, (1, Hv, d, d)) / 64).astype(np.float32)
+    s2 = (rng.integers(-64, 64, (1, Hv, d, d)) / 64).astype(np.float32)
+    oa, Sa = oracle.prefill(q[None], k[None], v1[None], alpha[None], beta[None], s1)
+    ob, Sb = oracle.prefill(q[None], k[None], v2[None], alpha[None], beta[None], s2)
+    oc, Sc = oracle.prefill(q[None], k[None], (v1 + v2)[None], alpha[None], beta[None], s1 + s2)
+    np.testing.assert_allclose(oc, oa + ob, rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(Sc, Sa + Sb, rtol=1e-11, atol=1e-11)
+    oz, Sz = oracle.prefill(q[None], k[None], np.zeros_like(v1)[None], alpha[None], beta[None],
+                            None)
+    assert not oz.any() and not Sz.any()
+
+
+@pytest.mark.parametrize("T1", [0, 1, 63, 64, 65, 100])
+def test_split_invariance(T1):
+    d = small_prefill(1, 130, 2, 4, 32, "bf16", seed=8, init_state=True)
+    args = [d[n] for n in ("q", "k", "v", "alpha", "beta")]
+    o, S = oracle.prefill(*args, d["S0"])
+    oa, Sa = oracle.prefill(*[x[:, :T1] for x in args], d["S0"])
+    ob, Sb = oracle.prefill(*[x[:, T1:] for x in args], Sa)
+    np.testing.assert_array_equal(np.concatenate([oa, ob], axis=1), o)
+    np.testing.assert_array_equal(Sb, S)
+
+
+def test_zero_length_returns_initial_state():
+    d = small_prefill(1, 0, 1, 2, 8, "f32", seed=9, init_state=True)
+    o, S = oracle.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"])
+    assert o.shape == (1, 0, 2, 8)
+    np.testing.assert_array_equal(S, d["S0"].astype(np.float64))
+
+
+def test_bf16_inputs_widen_exactly():
+    d = small_prefill(1, 50, 2, 4, 16, "bf16", seed=10, init_state=True)
+    o1, S1 = oracle.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"])
+    f = {n: bf16_to_f32(d[n]) for n in ("q", "k", "v")}
+    o2, S2 = oracle.prefill(f["q"], f["k"], f["v"], d["alpha"], d["beta"], d["S0"])
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(S1, S2)
+
+
+def test_varlen_equals_per_sequence_and_decode_equals_T1():
+    rng = np.random.default_rng(11)
+    lengths = [5, 1, 17, 0, 9]
+    from gdn_synth import generate_packed
+    d = generate_packed(2, 4, 16, "bf16", 12, lengths, init_state=True)
+    o, S = oracle.varlen(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["cu_seqlens"], d["S0"])
+    cu = d["cu_seqlens"]
+    for n, L in enumerate(lengths):
+        sl = slice(cu[n], cu[n + 1])
+        on, Sn = oracle.prefill(d["q"][None, sl], d["k"][None, sl], d["v"][None, sl],
+                                d["alpha"][None, sl], d["beta"][None, sl], d["S0"][n:n + 1])
+        np.testing.assert_array_equal(o[sl], on[0])
+        np.testing.assert_array_equal(S[n], Sn[0])
+    # decode: one token per sequence == prefill with T = 1
+    q, k, v = d["q"][:3], d["k"][:3], d["v"][:3]
+    a, b = d["alpha"][:3], d["beta"][:3]
+    S0 = np.ascontiguousarray(np.concatenate([d["S0"], d["S0"][:1]])[:3])
+    od, Sd = oracle.decode(q, k, v, a, b, S0)
+    for i in range(3):
+        op, Sp = oracle.prefill(q[None, i:i + 1], k[None, i:i + 1], v[None, i:i + 1],
+                                a[None, i:i + 1], b[None, i:i + 1], S0[i:i + 1])
+        np.testing.assert_array_equal(od[i], op[0, 0])
+        np.testing.assert_array_equal(Sd[i], Sp[0])
+    del rng
+
+
+# ------------------------------------------------------------ chunk algebra
+@pytest.mark.parametrize("C", [1, 4, 16, 64])
+def test_chunk_mirror_matches_oracle(C):
+    d = small_prefill(1, 203, 2, 6, 32, "bf16", seed=13, init_state=True)
+    o, S = oracle.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], scale=0.5)
+    for h in range(6):
+        g = h // 3
+        om, Sm = chunk_chain(d["q"][0, :, g], d["k"][0, :, g], d["v"][0, :, h],
+                             d["alpha"][0, :, h], d["beta"][0, :, h], d["S0"][0, h], C=C,
+                             scale=0.5)
+        np.testing.assert_allclose(om, o[0, :, h], rtol=1e-10, atol=1e-11)
+        np.testing.assert_allclose(Sm, S[0, h], rtol=1e-10, atol=1e-11)
+
+
+def test_chunk_mirror_slow_decay():
+    d = small_prefill(1, 300, 1, 1, 32, "bf16", seed=14, alpha_shift=-5.0, beta_shift=-2.0,
+                      init_state=True)
+    o, S = oracle.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"])
+    om, Sm = chunk_chain(d["q"][0, :, 0], d["k"][0, :, 0], d["v"][0, :, 0],
+                         d["alpha"][0, :, 0], d["beta"][0, :, 0], d["S0"][0, 0], C=64)
+    np.testing.assert_allclose(om, o[0, :, 0], rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(Sm, S[0, 0], rtol=1e-10, atol=1e-11)
+
+
+# ------------------------------------------------------------ page facts
+def test_state_size_matches_page():
+    """48 GDN layers x 48 value heads x 128 x 128 fp32 is the page's ~150 MiB;
+    bf16 or fp64 states would be 72 or 288 MiB."""
+    g = json.load(open(os.path.join(GOLDEN, "qwen_gdn_layer.json")))["facts"]
+    n = g["gdn_layers"]["value"] * g["gdn_v_heads"]["value"] * g["gdn_head_dim"]["value"] ** 2
+    approx = g["gdn_state_total_mib_approx"]["value"]
+    assert g["gdn_layers"]["value"] * 4 == g["layers_total"]["value"] * 3
+    assert abs(n * 4 / 2**20 - approx) / approx < 0.05
+    assert abs(n * 2 / 2**20 - approx) / approx > 0.4
+    assert abs(n * 8 / 2**20 - approx) / approx > 0.4
+    assert g["gdn_v_heads"]["value"] % g["gdn_qk_heads"]["value"] == 0
+
+
+def test_generator_rounding_is_rne():
+    x = np.array([1.0, 1.00390625, 1.005859375, -2.5, 3.0e-3], np.float32)
+    # 1 + 2^-8 is halfway between two bf16 values -> ties to even (1.0)
+    np.testing.assert_array_equal(bf16_to_f32(bf16_bits(x))[:2], [1.0, 1.0])
+    assert bf16_to_f32(bf16_bits(x))[2] == np.float32(1.0078125)
+    assert bf16_to_f32(bf16_bits(x))[3] == np.float32(-2.5)
