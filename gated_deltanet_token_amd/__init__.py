@@ -1,0 +1,188 @@
+"""Python binding of libgdn.so, the MI355X Gated DeltaNet token mixer.
+
+Argument marshalling only: each function checks dtypes, devices, shapes and
+contiguity of torch tensors, allocates the outputs it is not given, and
+calls the C entry point of the same name with raw device pointers and the
+current HIP stream. Every step of the computation runs in the library's HIP
+kernels; there is no fallback path. If libgdn.so is missing or cannot be
+loaded, the first call raises.
+
+The recurrence, per sequence and value head h (q/k head h // (Hv // Hk)):
+    S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+    o_t = scale * S_t q_t
+States are fp32 [.., Hv, Dv, Dk] (S in R^{Dv x Dk}, row-major).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_F32, GDN_BF16 = 0, 1
+_STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL_POINTER", 2: "GDN_ERR_BAD_SHAPE",
+           3: "GDN_ERR_UNSUPPORTED", 4: "GDN_ERR_MISALIGNED", 5: "GDN_ERR_ALIAS",
+           6: "GDN_ERR_HIP"}
+EXPORTS = ("gdn_prefill_chunked", "gdn_decode_step", "gdn_varlen_prefill",
+           "gdn_status_string", "gdn_version")
+
+_lib = None
+
+
+class GDNError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{_STATUS.get(status, status)}: {detail}")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libgdn.so (after torch, so that both share torch's HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m gated_deltanet_token_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    lib.gdn_prefill_chunked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                        i32, ctypes.c_int, f32, vp]
+    lib.gdn_prefill_chunked.restype = ctypes.c_int
+    lib.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                    ctypes.c_int, f32, vp]
+    lib.gdn_decode_step.restype = ctypes.c_int
+    lib.gdn_varlen_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, i32, i32,
+                                       i32, i32, ctypes.c_int, f32, vp]
+    lib.gdn_varlen_prefill.restype = ctypes.c_int
+    lib.gdn_status_string.argtypes = [ctypes.c_int]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_version.argtypes = []
+    lib.gdn_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise GDNError(status, _lib.gdn_status_string(status).decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError(f"q, k, v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, name, dtype=None, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(device, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return s.cuda_stream
+
+
+def gdn_prefill_chunked(q, k, v, alpha, beta, initial_state=None, *, out=None,
+                        final_state=None, scale: float = 1.0, want_final_state: bool = True,
+                        stream=None):
+    """Chunked prefill. q,k [B,T,Hk,D]; v [B,T,Hv,D]; alpha,beta [B,T,Hv] fp32;
+    initial_state [B,Hv,D,D] fp32 or None. Returns (out, final_state)."""
+    lib = load_library()
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    dev = q.device
+    _need(q, "q", device=dev)
+    _need(k, "k", q.dtype, q.shape, dev)
+    _need(v, "v", q.dtype, (B, T, Hv, Dv), dev)
+    _need(alpha, "alpha", torch.float32, (B, T, Hv), dev)
+    _need(beta, "beta", torch.float32, (B, T, Hv), dev)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (B, Hv, Dv, Dk), dev)
+    if out is None:
+        out = torch.empty((B, T, Hv, Dv), dtype=q.dtype, device=dev)
+    _need(out, "out", q.dtype, (B, T, Hv, Dv), dev)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((B, Hv, Dv, Dk), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, (B, Hv, Dv, Dk), dev)
+    _check(lib.gdn_prefill_chunked(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state), _ptr(out),
+        _ptr(final_state), B, T, Hk, Hv, Dk, Dv, _dtype_code(q), float(scale),
+        _stream_handle(dev, stream)))
+    return out, final_state
+
+
+def gdn_varlen_prefill(q, k, v, alpha, beta, cu_seqlens, initial_state=None, *, out=None,
+                       final_state=None, scale: float = 1.0, want_final_state: bool = True,
+                       stream=None):
+    """Packed prefill. q,k [total,Hk,D]; v [total,Hv,D]; alpha,beta [total,Hv];
+    cu_seqlens int32 [N+1] on the device. Returns (out, final_state [N,Hv,D,D])."""
+    lib = load_library()
+    total, Hk, Dk = q.shape
+    Hv, Dv = v.shape[1], v.shape[2]
+    dev = q.device
+    _need(cu_seqlens, "cu_seqlens", torch.int32, device=dev)
+    N = cu_seqlens.shape[0] - 1
+    _need(q, "q", device=dev)
+    _need(k, "k", q.dtype, q.shape, dev)
+    _need(v, "v", q.dtype, (total, Hv, Dv), dev)
+    _need(alpha, "alpha", torch.float32, (total, Hv), dev)
+    _need(beta, "beta", torch.float32, (total, Hv), dev)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (N, Hv, Dv, Dk), dev)
+    if out is None:
+        out = torch.empty((total, Hv, Dv), dtype=q.dtype, device=dev)
+    _need(out, "out", q.dtype, (total, Hv, Dv), dev)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((N, Hv, Dv, Dk), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, (N, Hv, Dv, Dk), dev)
+    _check(lib.gdn_varlen_prefill(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(cu_seqlens), N, total,
+        _ptr(initial_state), _ptr(out), _ptr(final_state), Hk, Hv, Dk, Dv, _dtype_code(q),
+        float(scale), _stream_handle(dev, stream)))
+    return out, final_state
+
+
+def gdn_decode_step(q, k, v, alpha, beta, state, *, out=None, scale: float = 1.0, stream=None):
+    """One token per sequence; `state` [B,Hv,D,D] fp32 is updated in place.
+    q,k [B,Hk,D]; v [B,Hv,D]; alpha,beta [B,Hv]. Returns out [B,Hv,D]."""
+    lib = load_library()
+    B, Hk, Dk = q.shape
+    Hv, Dv = v.shape[1], v.shape[2]
+    dev = q.device
+    _need(q, "q", device=dev)
+    _need(k, "k", q.dtype, q.shape, dev)
+    _need(v, "v", q.dtype, (B, Hv, Dv), dev)
+    _need(alpha, "alpha", torch.float32, (B, Hv), dev)
+    _need(beta, "beta", torch.float32, (B, Hv), dev)
+    _need(state, "state", torch.float32, (B, Hv, Dv, Dk), dev)
+    if out is None:
+        out = torch.empty((B, Hv, Dv), dtype=q.dtype, device=dev)
+    _need(out, "out", q.dtype, (B, Hv, Dv), dev)
+    _check(lib.gdn_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state), _ptr(out), B, Hk, Hv,
+        Dk, Dv, _dtype_code(q), float(scale), _stream_handle(dev, stream)))
+    return out
+
+
+def gdn_version() -> int:
+    return load_library().gdn_version()

@@ -1,0 +1,204 @@
+// gdn_api.hip -- the C ABI (include/gdn.h): argument validation and launch.
+//
+// Every entry point checks its arguments on the host before touching the HIP
+// runtime, so a rejected call has no side effects and costs no device work.
+// Accepted calls enqueue their kernels on the caller's stream and return.
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/gdn.h"
+#include "gdn_launch.hpp"
+
+namespace {
+
+thread_local char g_detail[256];
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi); empty when lo == hi
+};
+
+Range range_of(const void *p, int64_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, bytes > 0 && p ? a + (uintptr_t)bytes : a};
+}
+
+bool overlap(const Range &a, const Range &b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// a*b*c*... as int64 with overflow detection (all factors >= 0)
+bool mul_ok(int64_t &acc, int64_t f) {
+    if (f < 0) return false;
+    if (f != 0 && acc > INT64_MAX / f) return false;
+    acc *= f;
+    return true;
+}
+
+gdn_status_t check_heads(int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv) {
+    if (Hk < 1 || Hv < 1 || Dk < 1 || Dv < 1) return GDN_ERR_BAD_SHAPE;
+    if (Hv % Hk != 0) return GDN_ERR_BAD_SHAPE;
+    if (Dk != Dv || (Dk != 64 && Dk != 128)) return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+gdn_status_t hip_fail(hipError_t e, const char *where) {
+    snprintf(g_detail, sizeof g_detail, "HIP error in %s: %s (%d)", where, hipGetErrorString(e),
+             (int)e);
+    return GDN_ERR_HIP;
+}
+
+gdn_status_t device_cus(int *cus) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    return GDN_OK;
+}
+
+// Shared checks of the two prefill entry points. `tokens` is B*T or total_T,
+// `nstates` is B or N.
+gdn_status_t check_prefill(const void *q, const void *k, const void *v, const float *alpha,
+                           const float *beta, const float *s0, const void *out, const float *sf,
+                           const int32_t *cu, int64_t cu_count, int64_t tokens, int64_t nstates,
+                           int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv, gdn_dtype_t dtype) {
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    const int64_t es = dtype == GDN_BF16 ? 2 : 4;
+    int64_t nqk = tokens, nv = tokens, nab = tokens, nst = nstates;
+    if (!mul_ok(nqk, Hk) || !mul_ok(nqk, Dk) || !mul_ok(nqk, es)) return GDN_ERR_BAD_SHAPE;
+    if (!mul_ok(nv, Hv) || !mul_ok(nv, Dv) || !mul_ok(nv, es)) return GDN_ERR_BAD_SHAPE;
+    if (!mul_ok(nab, Hv) || !mul_ok(nab, 4)) return GDN_ERR_BAD_SHAPE;
+    if (!mul_ok(nst, Hv) || !mul_ok(nst, Dv) || !mul_ok(nst, Dk) || !mul_ok(nst, 4))
+        return GDN_ERR_BAD_SHAPE;
+    if (nstates * Hv > 0x7FFFFFFF / 8) return GDN_ERR_BAD_SHAPE;  // grid size
+
+    if (tokens > 0 && (!q || !k || !v || !alpha || !beta || !out)) return GDN_ERR_NULL_POINTER;
+    if (cu_count > 0 && !cu) return GDN_ERR_NULL_POINTER;
+    const void *ptrs[] = {q, k, v, alpha, beta, s0, out, sf, cu};
+    for (const void *ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return GDN_ERR_MISALIGNED;
+
+    const Range rq = range_of(q, nqk), rk = range_of(k, nqk), rv = range_of(v, nv);
+    const Range ra = range_of(alpha, nab), rb = range_of(beta, nab);
+    const Range rs0 = range_of(s0, nst), ro = range_of(out, nv), rsf = range_of(sf, nst);
+    const Range rcu = range_of(cu, cu_count * 4);
+    const Range inputs[] = {rq, rk, rv, ra, rb, rs0, rcu};
+    for (const Range &r : inputs)
+        if (overlap(ro, r) || overlap(ro, rsf)) return GDN_ERR_ALIAS;
+    if (sf && sf != s0) {
+        for (const Range &r : inputs)
+            if (overlap(rsf, r)) return GDN_ERR_ALIAS;
+    }
+    if (sf && sf == s0) {
+        const Range others[] = {rq, rk, rv, ra, rb, rcu};
+        for (const Range &r : others)
+            if (overlap(rsf, r)) return GDN_ERR_ALIAS;
+    }
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gdn_status_string(gdn_status_t s) {
+    switch (s) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case GDN_ERR_BAD_SHAPE: return "a size is out of range or inconsistent";
+    case GDN_ERR_UNSUPPORTED: return "unsupported dtype or head dimension (Dk == Dv in {64, 128})";
+    case GDN_ERR_MISALIGNED: return "a pointer is not 16-byte aligned";
+    case GDN_ERR_ALIAS: return "forbidden overlap between buffers";
+    case GDN_ERR_HIP: return g_detail[0] ? g_detail : "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int32_t gdn_version(void) { return 100; }
+
+gdn_status_t gdn_prefill_chunked(const void *q, const void *k, const void *v, const float *alpha,
+                                 const float *beta, const float *initial_state, void *out,
+                                 float *final_state, int32_t B, int64_t T, int32_t Hk, int32_t Hv,
+                                 int32_t Dk, int32_t Dv, gdn_dtype_t dtype, float scale,
+                                 hipStream_t stream) {
+    gdn_status_t st = check_heads(Hk, Hv, Dk, Dv);
+    if (st != GDN_OK) return st;
+    if (B < 1 || T < 0) return GDN_ERR_BAD_SHAPE;
+    int64_t tokens = B;
+    if (!mul_ok(tokens, T)) return GDN_ERR_BAD_SHAPE;
+    st = check_prefill(q, k, v, alpha, beta, initial_state, out, final_state, nullptr, 0, tokens,
+                       B, Hk, Hv, Dk, Dv, dtype);
+    if (st != GDN_OK) return st;
+    if (tokens == 0 && !final_state) return GDN_OK;  // nothing to write
+    int cus = 0;
+    if ((st = device_cus(&cus)) != GDN_OK) return st;
+    gdn::PrefillParams p{q, k, v, alpha, beta, initial_state, out, final_state, nullptr, T, B,
+                         Hk, Hv, scale};
+    const hipError_t e = gdn::launch_prefill(p, dtype == GDN_BF16 ? 1 : 0, Dk, cus, stream);
+    if (e != hipSuccess) return hip_fail(e, "gdn_prefill_chunked launch");
+    return GDN_OK;
+}
+
+gdn_status_t gdn_varlen_prefill(const void *q, const void *k, const void *v, const float *alpha,
+                                const float *beta, const int32_t *cu_seqlens, int32_t N,
+                                int64_t total_T, const float *initial_state, void *out,
+                                float *final_state, int32_t Hk, int32_t Hv, int32_t Dk,
+                                int32_t Dv, gdn_dtype_t dtype, float scale, hipStream_t stream) {
+    gdn_status_t st = check_heads(Hk, Hv, Dk, Dv);
+    if (st != GDN_OK) return st;
+    if (N < 1 || total_T < 0 || total_T > 0x7FFFFFFF) return GDN_ERR_BAD_SHAPE;
+    if (!cu_seqlens) return GDN_ERR_NULL_POINTER;
+    st = check_prefill(q, k, v, alpha, beta, initial_state, out, final_state, cu_seqlens,
+                       (int64_t)N + 1, total_T, N, Hk, Hv, Dk, Dv, dtype);
+    if (st != GDN_OK) return st;
+    if (total_T == 0 && !final_state) return GDN_OK;
+    int cus = 0;
+    if ((st = device_cus(&cus)) != GDN_OK) return st;
+    gdn::PrefillParams p{q, k, v, alpha, beta, initial_state, out, final_state, cu_seqlens, 0, N,
+                         Hk, Hv, scale};
+    const hipError_t e = gdn::launch_prefill(p, dtype == GDN_BF16 ? 1 : 0, Dk, cus, stream);
+    if (e != hipSuccess) return hip_fail(e, "gdn_varlen_prefill launch");
+    return GDN_OK;
+}
+
+gdn_status_t gdn_decode_step(const void *q, const void *k, const void *v, const float *alpha,
+                             const float *beta, float *state, void *out, int32_t B, int32_t Hk,
+                             int32_t Hv, int32_t Dk, int32_t Dv, gdn_dtype_t dtype, float scale,
+                             hipStream_t stream) {
+    gdn_status_t st = check_heads(Hk, Hv, Dk, Dv);
+    if (st != GDN_OK) return st;
+    if (B < 1) return GDN_ERR_BAD_SHAPE;
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !alpha || !beta || !state || !out) return GDN_ERR_NULL_POINTER;
+    const int64_t es = dtype == GDN_BF16 ? 2 : 4;
+    int64_t nqk = B, nv = B, nab = B, nst = B;
+    if (!mul_ok(nqk, Hk) || !mul_ok(nqk, Dk) || !mul_ok(nqk, es)) return GDN_ERR_BAD_SHAPE;
+    if (!mul_ok(nv, Hv) || !mul_ok(nv, Dv) || !mul_ok(nv, es)) return GDN_ERR_BAD_SHAPE;
+    if (!mul_ok(nab, Hv) || !mul_ok(nab, 4)) return GDN_ERR_BAD_SHAPE;
+    if (!mul_ok(nst, Hv) || !mul_ok(nst, Dv) || !mul_ok(nst, Dk) || !mul_ok(nst, 4))
+        return GDN_ERR_BAD_SHAPE;
+    if ((int64_t)B * Hv > 0x7FFFFFFF) return GDN_ERR_BAD_SHAPE;
+    const void *ptrs[] = {q, k, v, alpha, beta, state, out};
+    for (const void *ptr : ptrs)
+        if (!aligned16(ptr)) return GDN_ERR_MISALIGNED;
+    const Range rq = range_of(q, nqk), rk = range_of(k, nqk), rv = range_of(v, nv);
+    const Range ra = range_of(alpha, nab), rb = range_of(beta, nab);
+    const Range rs = range_of(state, nst), ro = range_of(out, nv);
+    const Range inputs[] = {rq, rk, rv, ra, rb};
+    for (const Range &r : inputs)
+        if (overlap(ro, r) || overlap(rs, r)) return GDN_ERR_ALIAS;
+    if (overlap(ro, rs)) return GDN_ERR_ALIAS;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    gdn::DecodeParams p{q, k, v, alpha, beta, state, out, B, Hk, Hv, scale};
+    e = gdn::launch_decode(p, dtype == GDN_BF16 ? 1 : 0, Dk, stream);
+    if (e != hipSuccess) return hip_fail(e, "gdn_decode_step launch");
+    return GDN_OK;
+}
+
+}  // extern "C"

@@ -221,3 +221,22 @@ def small_prefill(B, T, Hk, Hv, D, dtype="bf16", seed=0, alpha_shift=2.0, init_s
     for name in ("q", "k", "v", "alpha", "beta"):
         d[name] = d[name].reshape((B, T) + d[name].shape[1:])
     return d
+
+
+def to_torch(arr: np.ndarray, device):
+    """numpy -> torch on `device`; uint16 arrays are bf16 bit patterns."""
+    import torch
+    if arr is None:
+        return None
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
+
+
+def from_torch(t) -> np.ndarray:
+    """torch -> numpy on the host; bf16 comes back as uint16 bit patterns."""
+    import torch
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()

@@ -1,0 +1,146 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet token mixer.
+ *
+ * The layer: the Gated DeltaNet blocks that fill 48 of the 64 layers of the
+ * hybrid stack in "The Hybrid Attention in Qwen3.8-27B" (section "Why 27B
+ * parameters can carry 262K tokens": layout 16 x (3 x (Gated DeltaNet ->
+ * FFN) -> 1 x (Gated Attention -> FFN)); section "Grouped-query attention
+ * multiplies on top of that": 16 query/key heads, 48 value heads, head
+ * dimension 128). Each value head keeps one fixed-size state whatever the
+ * context length ("The economics of hybrid attention", TL;DR: the 48 blocks
+ * hold a fixed ~150 MiB, i.e. 48 x 48 x 128 x 128 fp32).
+ *
+ * The pages name the layer but do not print its recurrence; this library
+ * computes the published gated delta rule, for each sequence and value head
+ * h (S in R^{Dv x Dk}, row-major; q/k head g = h / (Hv / Hk)):
+ *
+ *     S_t = alpha_t * S_{t-1} * (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = scale * S_t q_t
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers, contiguous, in the layouts
+ *    stated per call, and 16-byte aligned. q, k, v and out have the element
+ *    type `dtype` (GDN_BF16 or GDN_F32); alpha, beta and states are fp32.
+ *  - Ownership: the caller owns every buffer. The library allocates and
+ *    frees nothing, keeps no pointer after the call returns and holds no
+ *    global mutable state; calls are re-entrant and thread-safe.
+ *  - Asynchrony: each call validates its arguments on the host, enqueues
+ *    kernels on `stream` and returns without synchronising. Results are
+ *    ready when the stream reaches that point.
+ *  - Validation happens before any HIP call; a call that fails validation
+ *    has no side effects. GDN_ERR_HIP reports a failure of the HIP runtime
+ *    (no device, launch error); gdn_status_string() then gives the detail
+ *    for the calling thread.
+ *  - Values are not validated: NaN or Inf inputs propagate. alpha and beta
+ *    are meant to lie in [0, 1]; alpha is clamped to >= FLT_MIN before its
+ *    logarithm is taken.
+ *  - `out` must not overlap any input. `final_state` must either be the same
+ *    pointer as `initial_state` (in-place update) or not overlap it, and it
+ *    must not overlap any other argument.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
+    GDN_ERR_BAD_SHAPE = 2,    /* a size is out of range or inconsistent */
+    GDN_ERR_UNSUPPORTED = 3,  /* a valid shape this build has no kernel for */
+    GDN_ERR_MISALIGNED = 4,   /* a pointer is not 16-byte aligned */
+    GDN_ERR_ALIAS = 5,        /* forbidden overlap between buffers */
+    GDN_ERR_HIP = 6           /* HIP runtime error; see gdn_status_string */
+} gdn_status_t;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype_t; /* type of q, k, v, out */
+
+/*
+ * gdn_prefill_chunked -- chunked prefill of B equal-length sequences.
+ *
+ *   q, k          [B, T, Hk, Dk]  dtype
+ *   v             [B, T, Hv, Dv]  dtype
+ *   alpha, beta   [B, T, Hv]      fp32   per-token decay and write strength
+ *   initial_state [B, Hv, Dv, Dk] fp32   S_0 per (sequence, value head);
+ *                                        NULL means a zero state
+ *   out           [B, T, Hv, Dv]  dtype  o_t (fp32 -> bf16 rounds to nearest even)
+ *   final_state   [B, Hv, Dv, Dk] fp32   S_T; NULL means not written;
+ *                                        may equal initial_state
+ *
+ * Sizes: B >= 1, T >= 0, Hk >= 1, Hv a multiple of Hk, Dk == Dv in {64, 128}.
+ * T == 0 writes the initial state (or zeros) to final_state.
+ * The sequence is processed in chunks of 64 tokens; the result equals the
+ * token recurrence up to rounding (the chunked form is an exact rewrite).
+ */
+gdn_status_t gdn_prefill_chunked(const void *q, const void *k, const void *v,
+                                 const float *alpha, const float *beta,
+                                 const float *initial_state, void *out,
+                                 float *final_state, int32_t B, int64_t T,
+                                 int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
+                                 gdn_dtype_t dtype, float scale,
+                                 hipStream_t stream);
+
+/*
+ * gdn_decode_step -- one new token per sequence, state updated in place.
+ *
+ *   q, k         [B, Hk, Dk]     dtype
+ *   v            [B, Hv, Dv]     dtype
+ *   alpha, beta  [B, Hv]         fp32
+ *   state        [B, Hv, Dv, Dk] fp32   read as S_{t-1}, overwritten with S_t
+ *   out          [B, Hv, Dv]     dtype  o_t = scale * S_t q_t
+ *
+ * Sizes: B >= 1, Hk >= 1, Hv a multiple of Hk, Dk == Dv in {64, 128}.
+ * This is the fixed-cost step the pages point to when they note that decode
+ * speed stays flat as the context grows ("The economics of hybrid
+ * attention", section "Where the constraint moved").
+ */
+gdn_status_t gdn_decode_step(const void *q, const void *k, const void *v,
+                             const float *alpha, const float *beta, float *state,
+                             void *out, int32_t B, int32_t Hk, int32_t Hv,
+                             int32_t Dk, int32_t Dv, gdn_dtype_t dtype,
+                             float scale, hipStream_t stream);
+
+/*
+ * gdn_varlen_prefill -- chunked prefill of N packed sequences.
+ *
+ *   q, k          [total_T, Hk, Dk] dtype
+ *   v, out        [total_T, Hv, Dv] dtype
+ *   alpha, beta   [total_T, Hv]     fp32
+ *   cu_seqlens    [N + 1] int32, DEVICE memory: sequence n spans tokens
+ *                 cu_seqlens[n] .. cu_seqlens[n+1]-1; cu_seqlens[0] = 0,
+ *                 non-decreasing, cu_seqlens[N] = total_T. Its contents are
+ *                 not checked (malformed offsets are undefined behaviour).
+ *   initial_state [N, Hv, Dv, Dk] fp32 or NULL (zero states)
+ *   final_state   [N, Hv, Dv, Dk] fp32 or NULL; may equal initial_state
+ *
+ * Sizes: N >= 1, 0 <= total_T < 2^31, Hv a multiple of Hk, Dk == Dv in
+ * {64, 128}. Chunks restart at every sequence boundary.
+ */
+gdn_status_t gdn_varlen_prefill(const void *q, const void *k, const void *v,
+                                const float *alpha, const float *beta,
+                                const int32_t *cu_seqlens, int32_t N,
+                                int64_t total_T, const float *initial_state,
+                                void *out, float *final_state, int32_t Hk,
+                                int32_t Hv, int32_t Dk, int32_t Dv,
+                                gdn_dtype_t dtype, float scale,
+                                hipStream_t stream);
+
+/* Static description of a status; for GDN_ERR_HIP, the calling thread's
+ * last HIP error detail. The pointer stays valid until the thread's next
+ * call into the library. */
+const char *gdn_status_string(gdn_status_t s);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

@@ -1,0 +1,284 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Every case draws seeded synthetic inputs, runs the library on cuda:0 and
+compares with the oracle on the same bits. Metric (per (sequence, value
+head) slice, max |x - r| / max |r|) and tolerances (2e-2 for bf16 inputs,
+1e-4 for fp32) are in tests/parity.py. Full-size workloads that the oracle
+cannot redo whole (the 262,144-token prefill and the 64-sequence varlen
+batch) are checked on sampled (sequence, head) chains, each run by the oracle
+over its full length.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from gdn_synth import (WORKLOADS, from_torch, generate, generate_packed, lengths_for,
+                       small_prefill, to_torch)
+from tests.parity import TOL, max_error, slice_error
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    import gated_deltanet_token_amd as g
+    g.load_library()
+    return g
+
+
+def _t(d, names):
+    return [to_torch(d[n], DEV) for n in names]
+
+
+def gpu_prefill(gdn, d, use_init=True, scale=1.0, stream=None):
+    q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
+    s0 = to_torch(d["S0"], DEV) if use_init and d.get("S0") is not None else None
+    out, sf = gdn.gdn_prefill_chunked(q, k, v, a, b, s0, scale=scale, stream=stream)
+    torch.cuda.synchronize()
+    return from_torch(out), from_torch(sf)
+
+
+def oracle_prefill(d, use_init=True, scale=1.0):
+    s0 = d["S0"] if use_init else None
+    return oracle.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], s0, scale)
+
+
+def check(o, S, o_ref, S_ref, dtype, label, o_axes=(0, 2), s_axes=(0, 1)):
+    eo = max_error(o, o_ref, o_axes) if np.asarray(o_ref).size else 0.0
+    es = max_error(S, S_ref, s_axes)
+    print(f"[parity] {label}: out {eo:.3e}  state {es:.3e}  (tol {TOL[dtype]:.0e})", flush=True)
+    assert eo <= TOL[dtype], f"{label}: output error {eo}"
+    assert es <= TOL[dtype], f"{label}: state error {es}"
+    return eo, es
+
+
+# ----------------------------------------------------------------- small shapes
+SMALL = [
+    # B, T, Hk, Hv, D, dtype, init
+    (1, 1, 1, 1, 64, "bf16", False),
+    (1, 63, 1, 2, 64, "bf16", True),
+    (2, 64, 2, 4, 64, "bf16", True),
+    (1, 65, 2, 6, 128, "bf16", False),
+    (1, 127, 2, 6, 128, "bf16", True),
+    (2, 200, 4, 12, 128, "bf16", True),
+    (1, 200, 2, 2, 128, "bf16", True),    # Hk == Hv
+    (1, 129, 1, 3, 64, "f32", True),
+    (1, 100, 2, 4, 128, "f32", True),
+]
+
+
+@pytest.mark.parametrize("B,T,Hk,Hv,D,dtype,init", SMALL)
+@pytest.mark.parametrize("nsplit", ["auto", "1", "2", "4", "8"])
+def test_prefill_small(gdn, monkeypatch, B, T, Hk, Hv, D, dtype, init, nsplit):
+    if nsplit != "auto":
+        monkeypatch.setenv("GDN_PREFILL_NSPLIT", nsplit)
+    d = small_prefill(B, T, Hk, Hv, D, dtype, seed=100 + T + D + Hv, init_state=init)
+    o, S = gpu_prefill(gdn, d, scale=0.5)
+    o_ref, S_ref = oracle_prefill(d, scale=0.5)
+    check(o, S, o_ref, S_ref, dtype, f"prefill B{B} T{T} Hk{Hk} Hv{Hv} D{D} {dtype} ns={nsplit}")
+
+
+def test_tiny_f32_workload(gdn):
+    w = WORKLOADS["tiny_f32"]
+    d = generate(w)
+    o, S = gpu_prefill(gdn, d)
+    o_ref, S_ref = oracle_prefill(d)
+    check(o, S, o_ref, S_ref, "f32", w.name)
+
+
+def test_layer_prefill_4k_workload(gdn):
+    w = WORKLOADS["layer_prefill_4k"]
+    d = generate(w)
+    o, S = gpu_prefill(gdn, d)
+    o_ref, S_ref = oracle_prefill(d)
+    check(o, S, o_ref, S_ref, "bf16", w.name)
+
+
+def test_prefill_zero_length_copies_state(gdn):
+    d = small_prefill(2, 0, 2, 4, 128, "bf16", seed=5, init_state=True)
+    o, S = gpu_prefill(gdn, d)
+    assert o.shape == (2, 0, 4, 128)
+    np.testing.assert_array_equal(S, d["S0"])
+    o, S = gpu_prefill(gdn, d, use_init=False)
+    assert not S.any()
+
+
+def test_prefill_in_place_state(gdn):
+    d = small_prefill(1, 150, 2, 4, 128, "bf16", seed=6, init_state=True)
+    q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
+    s = to_torch(d["S0"], DEV)
+    out, sf = gdn.gdn_prefill_chunked(q, k, v, a, b, s, final_state=s)
+    torch.cuda.synchronize()
+    assert sf.data_ptr() == s.data_ptr()
+    o_ref, S_ref = oracle_prefill(d)
+    check(from_torch(out), from_torch(s), o_ref, S_ref, "bf16", "in-place state")
+
+
+def test_prefill_split_invariance(gdn):
+    """run(T) == run(T1) then run(T - T1) from its final state (T1 not a
+    multiple of 64)."""
+    d = small_prefill(1, 300, 2, 6, 128, "bf16", seed=7, init_state=True)
+    o, S = gpu_prefill(gdn, d)
+    T1 = 101
+    d1 = {n: d[n][:, :T1] for n in ("q", "k", "v", "alpha", "beta")}
+    d1["S0"] = d["S0"]
+    o1, S1 = gpu_prefill(gdn, d1)
+    d2 = {n: np.ascontiguousarray(d[n][:, T1:]) for n in ("q", "k", "v", "alpha", "beta")}
+    d2["S0"] = S1
+    o2, S2 = gpu_prefill(gdn, d2)
+    o_ref, S_ref = oracle_prefill(d)
+    check(np.concatenate([o1, o2], axis=1), S2, o_ref, S_ref, "bf16", "split at 101")
+    check(o, S, o_ref, S_ref, "bf16", "unsplit")
+
+
+def test_prefill_deterministic(gdn):
+    d = small_prefill(1, 333, 2, 6, 128, "bf16", seed=8, init_state=True)
+    o1, S1 = gpu_prefill(gdn, d)
+    o2, S2 = gpu_prefill(gdn, d)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(S1, S2)
+
+
+def test_prefill_nondefault_stream(gdn):
+    d = small_prefill(1, 190, 2, 4, 64, "bf16", seed=9, init_state=True)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, S = gpu_prefill(gdn, d, stream=s)
+    o_ref, S_ref = oracle_prefill(d)
+    check(o, S, o_ref, S_ref, "bf16", "side stream")
+
+
+# ----------------------------------------------------------------- decode
+def gpu_decode(gdn, d, scale=1.0):
+    q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
+    state = to_torch(d["S0"], DEV)
+    out = gdn.gdn_decode_step(q, k, v, a, b, state, scale=scale)
+    torch.cuda.synchronize()
+    return from_torch(out), from_torch(state)
+
+
+@pytest.mark.parametrize("D,dtype", [(128, "bf16"), (64, "bf16"), (128, "f32"), (64, "f32")])
+def test_decode_small(gdn, D, dtype):
+    d = generate_packed(2, 6, D, dtype, 20 + D, [1] * 5, init_state=True)
+    o, S = gpu_decode(gdn, d, scale=0.7)
+    o_ref, S_ref = oracle.decode(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], 0.7)
+    check(o, S, o_ref, S_ref, dtype, f"decode D{D} {dtype}", o_axes=(0, 1), s_axes=(0, 1))
+
+
+def test_decode_b256_workload(gdn):
+    w = WORKLOADS["decode_b256"]
+    d = generate(w)
+    o, S = gpu_decode(gdn, d)
+    o_ref, S_ref = oracle.decode(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"])
+    check(o, S, o_ref, S_ref, "bf16", w.name, o_axes=(0, 1), s_axes=(0, 1))
+
+
+def test_decode_matches_prefill_T1(gdn):
+    d = generate_packed(2, 6, 128, "bf16", 31, [1] * 3, init_state=True)
+    o, S = gpu_decode(gdn, d)
+    dp = {n: d[n][:, None] for n in ("q", "k", "v", "alpha", "beta")}
+    dp["S0"] = d["S0"]
+    op, Sp = gpu_prefill(gdn, dp)
+    assert max_error(o, op[:, 0], (0, 1)) <= TOL["bf16"]
+    assert max_error(S, Sp, (0, 1)) <= TOL["bf16"]  # prefill rounds S to bf16 as an operand
+
+
+# ----------------------------------------------------------------- varlen
+def gpu_varlen(gdn, d, use_init=True):
+    q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
+    cu = to_torch(d["cu_seqlens"], DEV)
+    s0 = to_torch(d["S0"], DEV) if use_init and d["S0"] is not None else None
+    out, sf = gdn.gdn_varlen_prefill(q, k, v, a, b, cu, s0)
+    torch.cuda.synchronize()
+    return out, sf
+
+
+@pytest.mark.parametrize("D,dtype", [(128, "bf16"), (64, "bf16"), (64, "f32")])
+def test_varlen_small(gdn, D, dtype):
+    lengths = [5, 1, 70, 0, 129, 64, 200]
+    d = generate_packed(2, 6, D, dtype, 40 + D, lengths, init_state=True)
+    out, sf = gpu_varlen(gdn, d)
+    o_ref, S_ref = oracle.varlen(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["cu_seqlens"],
+                                 d["S0"])
+    o = from_torch(out)
+    cu = d["cu_seqlens"]
+    for n in range(len(lengths)):
+        if lengths[n] == 0:
+            continue
+        e = max_error(o[cu[n]:cu[n + 1]][None], o_ref[cu[n]:cu[n + 1]][None], (0, 2))
+        assert e <= TOL[dtype], (n, e)
+    check(o[:0], from_torch(sf), o_ref[:0], S_ref, dtype, f"varlen D{D} {dtype} states")
+
+
+def test_varlen_matches_per_sequence_prefill(gdn):
+    lengths = [77, 300, 64]
+    d = generate_packed(2, 6, 128, "bf16", 50, lengths, init_state=True)
+    out, sf = gpu_varlen(gdn, d)
+    o = from_torch(out)
+    S = from_torch(sf)
+    cu = d["cu_seqlens"]
+    for n in range(len(lengths)):
+        dn = {x: np.ascontiguousarray(d[x][cu[n]:cu[n + 1]][None])
+              for x in ("q", "k", "v", "alpha", "beta")}
+        dn["S0"] = d["S0"][n:n + 1]
+        op, Sp = gpu_prefill(gdn, dn)
+        np.testing.assert_array_equal(o[cu[n]:cu[n + 1]], op[0])
+        np.testing.assert_array_equal(S[n], Sp[0])
+
+
+# ----------------------------------------------------------------- full-size, sampled
+def _chains_check(d, out_t, sf_t, chains, cu, label):
+    worst_o = worst_s = 0.0
+    for (n, h) in chains:
+        s0 = d["S0"][n, h] if d.get("S0") is not None else None
+        o_ref, S_ref = oracle.chain(d["q"], d["k"], d["v"], d["alpha"], d["beta"], int(cu[n]),
+                                    int(cu[n + 1]), h, s0)
+        o = from_torch(out_t[int(cu[n]):int(cu[n + 1]), h])
+        S = from_torch(sf_t[n, h])
+        worst_o = max(worst_o, slice_error(o, o_ref))
+        worst_s = max(worst_s, slice_error(S, S_ref))
+    print(f"[parity] {label}: {len(chains)} sampled chains: out {worst_o:.3e} "
+          f"state {worst_s:.3e}", flush=True)
+    assert worst_o <= TOL["bf16"] and worst_s <= TOL["bf16"]
+
+
+@pytest.mark.slow
+def test_long_prefill_256k_workload_sampled(gdn):
+    w = WORKLOADS["long_prefill_256k"]
+    d = generate(w)
+    flat = {n: d[n].reshape((-1,) + d[n].shape[2:]) for n in ("q", "k", "v", "alpha", "beta")}
+    flat["S0"] = None
+    q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
+    out, sf = gdn.gdn_prefill_chunked(q, k, v, a, b, None)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    out = out.reshape(-1, w.Hv, w.D)
+    cu = np.array([0, w.T])
+    _chains_check(flat, out, sf, [(0, 0), (0, 25), (0, 47)], cu, w.name)
+
+
+@pytest.mark.slow
+def test_varlen_64seq_workload_sampled(gdn):
+    w = WORKLOADS["varlen_64seq"]
+    d = generate(w)
+    out, sf = gpu_varlen(gdn, d)
+    assert torch.isfinite(out.float()).all()
+    L = lengths_for(w)
+    order = np.argsort(L)
+    chains = [(int(order[-1]), 0), (int(order[0]), 47), (int(order[len(L) // 2]), 17),
+              (5, 30)]
+    _chains_check(d, out, sf, chains, d["cu_seqlens"], w.name)
+
+
+def test_slow_decay_stress_diagnostic(gdn):
+    """Slow decay (alpha ~ 0.99, small beta) exercises the carried state across
+    many chunks, which the workloads' fast decay hides. Diagnostic bound."""
+    d = small_prefill(1, 4096, 2, 6, 128, "bf16", seed=60, alpha_shift=-5.0, beta_shift=-2.0,
+                      init_state=True)
+    o, S = gpu_prefill(gdn, d)
+    o_ref, S_ref = oracle_prefill(d)
+    check(o, S, o_ref, S_ref, "bf16", "slow-decay stress T=4096")
