@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gated DeltaNet token mixer on one MI355X.
+
+One step = one pass of the whole hot path on synthetic inputs already
+resident in HBM:
+  * prefill of the layer workload (B=1, T=4096, 16 q/k heads, 48 value
+    heads, d=128, bf16 q/k/v, fp32 alpha/beta/state, zero initial state), and
+  * one decode step of the batched workload (B=256, same heads, fp32 states
+    updated in place).
+Shapes follow "The Hybrid Attention in Qwen3.8-27B" (section "Grouped-query
+attention multiplies on top of that").
+
+Reported: prefill tokens/s (value) with its fraction of the bf16 MFMA peak,
+decode state-update GB/s with its fraction of HBM bandwidth, both from HIP
+events on the stream the kernels run on; and the fp64 oracle timed on the
+host cores as a CPU baseline.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN prefill tokens/s (% bf16 MFMA peak); decode state-update GB/s (% HBM)"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+CHUNK = 64
+
+
+def prefill_flops_per_token(Hk, Hv, dk, dv, C=CHUNK):
+    """Algorithmic flops per token of the chunk-64 method (triangular
+    products counted as triangular, Gram products once per q/k head):
+    Hk*2*C*dk + Hv*(6*dk*dv + (C+1)*(2*dv + dk) + C^2/3)."""
+    return Hk * 2 * C * dk + Hv * (6 * dk * dv + (C + 1) * (2 * dv + dk) + C * C / 3.0)
+
+
+def prefill_bytes_per_token(Hk, Hv, dk, dv, es=2):
+    """Required HBM bytes per token: q, k, v in, o out, alpha and beta (fp32)."""
+    return 2 * Hk * dk * es + 2 * Hv * dv * es + 2 * Hv * 4
+
+
+def decode_bytes_per_step(B, Hk, Hv, dk, dv, es=2):
+    """Required HBM bytes of one decode step: each fp32 state read and written
+    once, q, k, v read, o written, alpha and beta read."""
+    return B * (Hv * dv * dk * 4 * 2 + 2 * Hk * dk * es + 2 * Hv * dv * es + 2 * Hv * 4)
+
+
+def _src_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "gated_deltanet_token_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key, digest):
+    """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE +
+    WRITE_SIZE, scaled by a copy-kernel calibration), if recorded for the
+    current kernel source; None otherwise."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_digest") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(d, w, budget_s=20.0):
+    """Time the fp64 oracle on the prefill workload on the host cores: whole
+    passes over all 48 value heads until about budget_s seconds are spent
+    (at least one pass)."""
+    import oracle
+    threads = oracle.default_threads()
+    tokens = 0
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        oracle.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], None, threads=threads)
+        passes += 1
+        tokens += w.B * w.T
+        el = time.perf_counter() - t0
+        if el >= budget_s or el * (passes + 1) / passes > 1.5 * budget_s:
+            break
+    return {"value": tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{passes} full pass(es) of the fp64 token-by-token oracle over "
+                      f"{w.name} (B={w.B}, T={w.T}, {w.Hv} value heads), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--prefill-workload", default="layer_prefill_4k",
+                    help="prefill workload name from gdn_synth.WORKLOADS")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the token mixer is sharded by sequence or by "
+              "q/k head group with no exchange, so throughput at N GPUs is N x this figure; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_deltanet_token_amd as gdn
+    from gdn_synth import WORKLOADS, generate, to_torch
+
+    gdn.load_library()
+    dev = torch.device("cuda:0")
+    wp = WORKLOADS[args.prefill_workload]
+    wd = WORKLOADS["decode_b256"]
+    dp = generate(wp)
+    dd = generate(wd)
+
+    pt = {n: to_torch(dp[n], dev) for n in ("q", "k", "v", "alpha", "beta")}
+    p_s0 = to_torch(dp["S0"], dev) if dp["S0"] is not None else None
+    p_out = torch.empty(pt["v"].shape, dtype=pt["q"].dtype, device=dev)
+    p_sf = torch.empty((wp.B, wp.Hv, wp.D, wp.D), dtype=torch.float32, device=dev)
+    varlen = wp.kind == "varlen"
+    p_cu = to_torch(dp["cu_seqlens"], dev) if varlen else None
+    dt = {n: to_torch(dd[n], dev) for n in ("q", "k", "v", "alpha", "beta")}
+    d_state = to_torch(dd["S0"], dev)
+    d_out = torch.empty((wd.B, wd.Hv, wd.D), dtype=dt["q"].dtype, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step_prefill():
+        if varlen:
+            gdn.gdn_varlen_prefill(pt["q"], pt["k"], pt["v"], pt["alpha"], pt["beta"], p_cu,
+                                   p_s0, out=p_out, final_state=p_sf, stream=stream)
+        else:
+            gdn.gdn_prefill_chunked(pt["q"], pt["k"], pt["v"], pt["alpha"], pt["beta"], p_s0,
+                                    out=p_out, final_state=p_sf, stream=stream)
+
+    def step_decode():
+        gdn.gdn_decode_step(dt["q"], dt["k"], dt["v"], dt["alpha"], dt["beta"], d_state,
+                            out=d_out, stream=stream)
+
+    for _ in range(args.warmup):
+        step_prefill()
+        step_decode()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        step_prefill()
+        ev[i][1].record(stream)
+        step_decode()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
+    dec_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
+    pre_avg = float(np.mean(pre_ms))
+    dec_avg = float(np.mean(dec_ms))
+
+    tokens = int(pt["v"].shape[0] * (1 if varlen else pt["v"].shape[1]))
+    f_tok = prefill_flops_per_token(wp.Hk, wp.Hv, wp.D, wp.D)
+    pre_tflops = tokens * f_tok / (pre_avg * 1e-3) / 1e12
+    pre_tok_s = tokens / (pre_avg * 1e-3)
+    pre_gbs = tokens * prefill_bytes_per_token(wp.Hk, wp.Hv, wp.D, wp.D) / (pre_avg * 1e-3) / 1e9
+    dec_bytes = decode_bytes_per_step(wd.B, wd.Hk, wd.Hv, wd.D, wd.D)
+    dec_gbs = dec_bytes / (dec_avg * 1e-3) / 1e9
+
+    pdig = _src_digest("gdn_prefill.hip", "gdn_device.hpp")
+    ddig = _src_digest("gdn_decode.hip", "gdn_device.hpp")
+    res = {
+        "metric": METRIC,
+        "value": round(pre_tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wp.name} prefill + {wd.name} decode step",
+            "prefill": {"B": wp.B, "T": wp.T if not varlen else None, "tokens": tokens,
+                        "Hk": wp.Hk, "Hv": wp.Hv, "d": wp.D,
+                        "chunk": CHUNK, "io": "bf16 q/k/v/o, fp32 alpha/beta/state"},
+            "decode": {"B": wd.B, "Hk": wd.Hk, "Hv": wd.Hv, "d": wd.D,
+                       "state": "fp32, updated in place"},
+        },
+        "prefill": {"tokens_per_s": round(pre_tok_s, 1), "ms": round(pre_avg, 5),
+                    "ms_min": round(float(np.min(pre_ms)), 5),
+                    "algorithmic_tflops": round(pre_tflops, 2),
+                    "frac_mfma_peak": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
+                    "required_io_GBps": round(pre_gbs, 1)},
+        "decode": {"GB_per_s": round(dec_gbs, 1), "ms": round(dec_avg, 5),
+                   "ms_min": round(float(np.min(dec_ms)), 5),
+                   "frac_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4),
+                   "tokens_per_s": round(wd.B / (dec_avg * 1e-3), 1)},
+        "roofline": {"kernel": "prefill_kernel", "bound": "mfma",
+                     "achieved": round(pre_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": _traffic("prefill_" + wp.name, pdig)},
+        "roofline_decode": {"kernel": "decode_kernel", "bound": "hbm",
+                            "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
+                            "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                            "traffic": _traffic("decode_" + wd.name, ddig)},
+    }
+    if not args.no_cpu_baseline and not varlen:
+        res["cpu_baseline"] = cpu_baseline(dp, wp)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
