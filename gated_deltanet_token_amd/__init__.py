@@ -27,7 +27,7 @@ _STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL_POINTER", 2: "GDN_ERR_BAD_SHAPE",
            3: "GDN_ERR_UNSUPPORTED", 4: "GDN_ERR_MISALIGNED", 5: "GDN_ERR_ALIAS",
            6: "GDN_ERR_HIP"}
 EXPORTS = ("gdn_prefill_chunked", "gdn_decode_step", "gdn_varlen_prefill",
-           "gdn_status_string", "gdn_version")
+           "gdn_prefill_workspace_size", "gdn_status_string", "gdn_version")
 
 _lib = None
 
@@ -48,15 +48,18 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                           "`python -m gated_deltanet_token_amd.build`")
     lib = ctypes.CDLL(path)
     vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    sz = ctypes.c_size_t
     lib.gdn_prefill_chunked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
-                                        i32, ctypes.c_int, f32, vp]
+                                        i32, ctypes.c_int, f32, vp, sz, vp]
     lib.gdn_prefill_chunked.restype = ctypes.c_int
     lib.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                     ctypes.c_int, f32, vp]
     lib.gdn_decode_step.restype = ctypes.c_int
     lib.gdn_varlen_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, i32, i32,
-                                       i32, i32, ctypes.c_int, f32, vp]
+                                       i32, i32, ctypes.c_int, f32, vp, sz, vp]
     lib.gdn_varlen_prefill.restype = ctypes.c_int
+    lib.gdn_prefill_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, ctypes.c_int, i32]
+    lib.gdn_prefill_workspace_size.restype = sz
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_version.argtypes = []
@@ -95,16 +98,42 @@ def _need(t, name, dtype=None, shape=None, device=None):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _stream_handle(device, stream):
-    s = stream if stream is not None else torch.cuda.current_stream(device)
-    return s.cuda_stream
+def _stream(device, stream):
+    return stream if stream is not None else torch.cuda.current_stream(device)
+
+
+def gdn_prefill_workspace_size(num_seqs, tokens, Hk, Hv, Dk, Dv, dtype, packed) -> int:
+    """Workspace bytes the prefill calls can use (0: they would not use one)."""
+    code = _dtype_code(torch.empty(0, dtype=dtype)) if isinstance(dtype, torch.dtype) else dtype
+    return int(load_library().gdn_prefill_workspace_size(num_seqs, tokens, Hk, Hv, Dk, Dv, code,
+                                                         int(bool(packed))))
+
+
+def _workspace(workspace, num_seqs, tokens, Hk, Hv, Dk, Dv, dtype_code, packed, dev, stream):
+    """(pointer, bytes, keep-alive) of the workspace argument: None = no
+    workspace; "auto" = allocate what the library asks for; a uint8 tensor."""
+    if workspace is None:
+        return None, 0, None
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be None, 'auto' or a tensor")
+        n = _lib.gdn_prefill_workspace_size(num_seqs, tokens, Hk, Hv, Dk, Dv, dtype_code,
+                                            int(packed))
+        if n == 0:
+            return None, 0, None
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", device=dev)
+    workspace.record_stream(stream)
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size(), workspace
 
 
 def gdn_prefill_chunked(q, k, v, alpha, beta, initial_state=None, *, out=None,
                         final_state=None, scale: float = 1.0, want_final_state: bool = True,
-                        stream=None):
+                        workspace="auto", stream=None):
     """Chunked prefill. q,k [B,T,Hk,D]; v [B,T,Hv,D]; alpha,beta [B,T,Hv] fp32;
-    initial_state [B,Hv,D,D] fp32 or None. Returns (out, final_state)."""
+    initial_state [B,Hv,D,D] fp32 or None. Returns (out, final_state).
+    workspace: "auto" (allocate what the library asks for), None, or a
+    device uint8 tensor."""
     lib = load_library()
     B, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
@@ -123,16 +152,18 @@ def gdn_prefill_chunked(q, k, v, alpha, beta, initial_state=None, *, out=None,
         final_state = torch.empty((B, Hv, Dv, Dk), dtype=torch.float32, device=dev)
     if final_state is not None:
         _need(final_state, "final_state", torch.float32, (B, Hv, Dv, Dk), dev)
+    st = _stream(dev, stream)
+    wp, wb, _keep = _workspace(workspace, B, T, Hk, Hv, Dk, Dv, _dtype_code(q), False, dev, st)
     _check(lib.gdn_prefill_chunked(
         _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state), _ptr(out),
-        _ptr(final_state), B, T, Hk, Hv, Dk, Dv, _dtype_code(q), float(scale),
-        _stream_handle(dev, stream)))
+        _ptr(final_state), B, T, Hk, Hv, Dk, Dv, _dtype_code(q), float(scale), wp, wb,
+        st.cuda_stream))
     return out, final_state
 
 
 def gdn_varlen_prefill(q, k, v, alpha, beta, cu_seqlens, initial_state=None, *, out=None,
                        final_state=None, scale: float = 1.0, want_final_state: bool = True,
-                       stream=None):
+                       workspace="auto", stream=None):
     """Packed prefill. q,k [total,Hk,D]; v [total,Hv,D]; alpha,beta [total,Hv];
     cu_seqlens int32 [N+1] on the device. Returns (out, final_state [N,Hv,D,D])."""
     lib = load_library()
@@ -155,10 +186,12 @@ def gdn_varlen_prefill(q, k, v, alpha, beta, cu_seqlens, initial_state=None, *, 
         final_state = torch.empty((N, Hv, Dv, Dk), dtype=torch.float32, device=dev)
     if final_state is not None:
         _need(final_state, "final_state", torch.float32, (N, Hv, Dv, Dk), dev)
+    st = _stream(dev, stream)
+    wp, wb, _keep = _workspace(workspace, N, total, Hk, Hv, Dk, Dv, _dtype_code(q), True, dev, st)
     _check(lib.gdn_varlen_prefill(
         _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(cu_seqlens), N, total,
         _ptr(initial_state), _ptr(out), _ptr(final_state), Hk, Hv, Dk, Dv, _dtype_code(q),
-        float(scale), _stream_handle(dev, stream)))
+        float(scale), wp, wb, st.cuda_stream))
     return out, final_state
 
 
@@ -180,7 +213,7 @@ def gdn_decode_step(q, k, v, alpha, beta, state, *, out=None, scale: float = 1.0
     _need(out, "out", q.dtype, (B, Hv, Dv), dev)
     _check(lib.gdn_decode_step(
         _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state), _ptr(out), B, Hk, Hv,
-        Dk, Dv, _dtype_code(q), float(scale), _stream_handle(dev, stream)))
+        Dk, Dv, _dtype_code(q), float(scale), _stream(dev, stream).cuda_stream))
     return out
 
 

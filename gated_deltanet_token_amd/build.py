@@ -25,6 +25,10 @@ def build(verbose: bool = False) -> str:
            "-Wall", "-Wno-unused-function",
            # no packed fp32 instructions (v_pk_*_f32) anywhere in device code
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # MFMA results in ordinary VGPRs: the elementwise steps between
+           # contractions then read them directly instead of copying each
+           # value out of (and back into) the accumulator registers
+           "-mllvm", "-amdgpu-mfma-vgpr-form=1",
            "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature for this target"

@@ -65,7 +65,8 @@ gdn_status_t device_cus(int *cus) {
 gdn_status_t check_prefill(const void *q, const void *k, const void *v, const float *alpha,
                            const float *beta, const float *s0, const void *out, const float *sf,
                            const int32_t *cu, int64_t cu_count, int64_t tokens, int64_t nstates,
-                           int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv, gdn_dtype_t dtype) {
+                           int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv, gdn_dtype_t dtype,
+                           const void *ws, size_t ws_bytes) {
     if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
     const int64_t es = dtype == GDN_BF16 ? 2 : 4;
     int64_t nqk = tokens, nv = tokens, nab = tokens, nst = nstates;
@@ -78,9 +79,10 @@ gdn_status_t check_prefill(const void *q, const void *k, const void *v, const fl
 
     if (tokens > 0 && (!q || !k || !v || !alpha || !beta || !out)) return GDN_ERR_NULL_POINTER;
     if (cu_count > 0 && !cu) return GDN_ERR_NULL_POINTER;
-    const void *ptrs[] = {q, k, v, alpha, beta, s0, out, sf, cu};
+    const void *ptrs[] = {q, k, v, alpha, beta, s0, out, sf, cu, ws};
     for (const void *ptr : ptrs)
         if (ptr && !aligned16(ptr)) return GDN_ERR_MISALIGNED;
+    if (ws_bytes > (size_t)INT64_MAX) return GDN_ERR_BAD_SHAPE;
 
     const Range rq = range_of(q, nqk), rk = range_of(k, nqk), rv = range_of(v, nv);
     const Range ra = range_of(alpha, nab), rb = range_of(beta, nab);
@@ -98,6 +100,10 @@ gdn_status_t check_prefill(const void *q, const void *k, const void *v, const fl
         for (const Range &r : others)
             if (overlap(rsf, r)) return GDN_ERR_ALIAS;
     }
+    const Range rws = range_of(ws, (int64_t)ws_bytes);
+    const Range all[] = {rq, rk, rv, ra, rb, rs0, ro, rsf, rcu};
+    for (const Range &r : all)
+        if (overlap(rws, r)) return GDN_ERR_ALIAS;
     return GDN_OK;
 }
 
@@ -118,27 +124,44 @@ const char *gdn_status_string(gdn_status_t s) {
     return "unknown status";
 }
 
-int32_t gdn_version(void) { return 100; }
+int32_t gdn_version(void) { return 200; }
+
+size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t tokens, int32_t Hk, int32_t Hv,
+                                  int32_t Dk, int32_t Dv, gdn_dtype_t dtype, int32_t packed) {
+    if (check_heads(Hk, Hv, Dk, Dv) != GDN_OK) return 0;
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return 0;
+    if (num_seqs < 1 || tokens < 0 || (packed && tokens > 0x7FFFFFFF)) return 0;
+    int64_t total = packed ? tokens : (int64_t)num_seqs;
+    if (!packed && !mul_ok(total, tokens)) return 0;
+    if (total == 0) return 0;
+    int cus = 0;
+    if (device_cus(&cus) != GDN_OK) return 0;
+    if (!gdn::prefill_wants_workspace((int64_t)num_seqs * Hv, cus)) return 0;
+    const int64_t slots = gdn::prefill_ws_slots(num_seqs, total, packed ? 0 : tokens, packed != 0);
+    return gdn::prefill_ws_bytes(slots, Hv, dtype == GDN_BF16 ? 1 : 0);
+}
 
 gdn_status_t gdn_prefill_chunked(const void *q, const void *k, const void *v, const float *alpha,
                                  const float *beta, const float *initial_state, void *out,
                                  float *final_state, int32_t B, int64_t T, int32_t Hk, int32_t Hv,
                                  int32_t Dk, int32_t Dv, gdn_dtype_t dtype, float scale,
-                                 hipStream_t stream) {
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream) {
     gdn_status_t st = check_heads(Hk, Hv, Dk, Dv);
     if (st != GDN_OK) return st;
     if (B < 1 || T < 0) return GDN_ERR_BAD_SHAPE;
     int64_t tokens = B;
     if (!mul_ok(tokens, T)) return GDN_ERR_BAD_SHAPE;
     st = check_prefill(q, k, v, alpha, beta, initial_state, out, final_state, nullptr, 0, tokens,
-                       B, Hk, Hv, Dk, Dv, dtype);
+                       B, Hk, Hv, Dk, Dv, dtype, workspace, workspace_bytes);
     if (st != GDN_OK) return st;
     if (tokens == 0 && !final_state) return GDN_OK;  // nothing to write
     int cus = 0;
     if ((st = device_cus(&cus)) != GDN_OK) return st;
     gdn::PrefillParams p{q, k, v, alpha, beta, initial_state, out, final_state, nullptr, T, B,
                          Hk, Hv, scale};
-    const hipError_t e = gdn::launch_prefill(p, dtype == GDN_BF16 ? 1 : 0, Dk, cus, stream);
+    const int64_t slots = gdn::prefill_ws_slots(B, tokens, T, false);
+    const hipError_t e = gdn::launch_prefill(p, dtype == GDN_BF16 ? 1 : 0, Dk, cus, workspace,
+                                             workspace_bytes, slots, stream);
     if (e != hipSuccess) return hip_fail(e, "gdn_prefill_chunked launch");
     return GDN_OK;
 }
@@ -147,20 +170,24 @@ gdn_status_t gdn_varlen_prefill(const void *q, const void *k, const void *v, con
                                 const float *beta, const int32_t *cu_seqlens, int32_t N,
                                 int64_t total_T, const float *initial_state, void *out,
                                 float *final_state, int32_t Hk, int32_t Hv, int32_t Dk,
-                                int32_t Dv, gdn_dtype_t dtype, float scale, hipStream_t stream) {
+                                int32_t Dv, gdn_dtype_t dtype, float scale, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
     gdn_status_t st = check_heads(Hk, Hv, Dk, Dv);
     if (st != GDN_OK) return st;
     if (N < 1 || total_T < 0 || total_T > 0x7FFFFFFF) return GDN_ERR_BAD_SHAPE;
     if (!cu_seqlens) return GDN_ERR_NULL_POINTER;
     st = check_prefill(q, k, v, alpha, beta, initial_state, out, final_state, cu_seqlens,
-                       (int64_t)N + 1, total_T, N, Hk, Hv, Dk, Dv, dtype);
+                       (int64_t)N + 1, total_T, N, Hk, Hv, Dk, Dv, dtype, workspace,
+                       workspace_bytes);
     if (st != GDN_OK) return st;
     if (total_T == 0 && !final_state) return GDN_OK;
     int cus = 0;
     if ((st = device_cus(&cus)) != GDN_OK) return st;
     gdn::PrefillParams p{q, k, v, alpha, beta, initial_state, out, final_state, cu_seqlens, 0, N,
                          Hk, Hv, scale};
-    const hipError_t e = gdn::launch_prefill(p, dtype == GDN_BF16 ? 1 : 0, Dk, cus, stream);
+    const int64_t slots = gdn::prefill_ws_slots(N, total_T, 0, true);
+    const hipError_t e = gdn::launch_prefill(p, dtype == GDN_BF16 ? 1 : 0, Dk, cus, workspace,
+                                             workspace_bytes, slots, stream);
     if (e != hipSuccess) return hip_fail(e, "gdn_varlen_prefill launch");
     return GDN_OK;
 }

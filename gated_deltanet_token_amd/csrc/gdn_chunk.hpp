@@ -1,0 +1,449 @@
+// gdn_chunk.hpp -- pieces of the chunk-64 gated delta rule shared by the
+// prefill kernels: LDS layout constants, staging helpers, the solve of
+// T = (I + A)^{-1}, and the state chain of one chunk.
+//
+// Notation (per chunk of 64 tokens, start state S in R^{Dv x Dk}):
+//   g_t = sum_{s<=t} ln a_s (chunk-local), gamma_t = e^{g_t},
+//   dec_t = e^{g_63 - g_t},
+//   A_ts = b_t e^{g_t - g_s} (k_t . k_s) for s < t,  T = (I + A)^{-1},
+//   P_ts = e^{g_t - g_s} (q_t . k_s)     for s <= t,
+//   R    = diag(b) (V - diag(gamma) K S^T),  U = T R,
+//   O^T  = S Q^T diag(gamma) + U^T P^T,
+//   S'   = gamma_63 S + U^T diag(dec) K.
+// This is an exact rewrite of the token recurrence
+//   S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,  o_t = S_t q_t:
+// by induction S_t = gamma_t S + sum_{j<=t} e^{g_t - g_j} u_j k_j^T with
+// u_t = b_t (v_t - a_t S_{t-1} k_t), and substituting gives (I + A) U = R.
+#pragma once
+#include <float.h>
+
+#include "gdn_device.hpp"
+
+namespace gdn {
+
+constexpr int kC = 64;  // chunk length
+
+// LDS pitches (elements) of the chunk matrices.
+template <typename DT, int D> struct ChunkPitch {
+    static constexpr bool BF = sizeof(DT) == 2;
+    static constexpr int PK = D + (BF ? 8 : 4);  // K, Q rows
+    static constexpr int PT = kC + 4;            // T, P, K^T, V^T rows
+    static constexpr int PA = kC + 4;            // fp32 A / E rows
+};
+
+// Task -> (row pair, piece). A task is one 16-byte piece of two consecutive
+// rows. Within 64 consecutive tasks the row pair varies fastest over 16 (or
+// 32) values, so the transposed LDS writes of a wave spread over all banks
+// while each wave still reads whole 64-byte row segments from global memory.
+template <int PPR>
+__device__ __forceinline__ void task_coords(int task, int &rp, int &pc) {
+    constexpr int PCB = PPR < 4 ? PPR : 4;  // pieces per 64-task group
+    constexpr int RPB = 64 / PCB;           // row pairs per 64-task group
+    constexpr int NRB = 32 / RPB;           // row-pair blocks
+    const int li = task & 63, grp = task >> 6;
+    rp = (li % RPB) + RPB * (grp % NRB);
+    pc = (li / RPB) + PCB * (grp / NRB);
+}
+
+// Two rows (l = row r, h = row r+1) of 8 bf16 each, written transposed:
+// column j of the pair goes to dst[j * PT .. +1] as one 32-bit word.
+template <int PT>
+__device__ __forceinline__ void store_pair_transposed(__bf16 *dst, const u32x4 &l, const u32x4 &h) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        *reinterpret_cast<uint32_t *>(dst + (2 * w) * PT) = (l[w] & 0xFFFFu) | (h[w] << 16);
+        *reinterpret_cast<uint32_t *>(dst + (2 * w + 1) * PT) = (l[w] >> 16) | (h[w] & 0xFFFF0000u);
+    }
+}
+template <int PT>
+__device__ __forceinline__ void store_pair_transposed(float *, const u32x4 &, const u32x4 &) {}
+
+// Lower 16x16 tile pairs (ti, tj), tj <= ti, of a 64x64 chunk matrix.
+__device__ __forceinline__ constexpr int pair_i(int pr) {
+    return pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3;
+}
+__device__ __forceinline__ constexpr int pair_j(int pr) {
+    return pr - pair_i(pr) * (pair_i(pr) + 1) / 2;
+}
+
+// Chunk-local decay vectors from this lane's token (wave-wide, 64 lanes):
+// inclusive scan of ln(alpha) with DPP (rows of 16, then across rows).
+__device__ __forceinline__ float wave_inclusive_scan(float x) {
+    // within each row of 16 lanes: shifts 1, 2, 4, 8 (lanes shifted in read 0)
+#define GDN_SHR(v, n)                                                                       \
+    __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (v)),  \
+                                                          0x110 + (n), 0xF, 0xF, false))
+    x += GDN_SHR(x, 1);
+    x += GDN_SHR(x, 2);
+    x += GDN_SHR(x, 4);
+    x += GDN_SHR(x, 8);
+#undef GDN_SHR
+    // row r (r = 1, 3) adds the last lane of row r-1; rows 2, 3 add lane 31
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142,
+                                                               0xA, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x143,
+                                                               0xC, 0xF, false));
+    return x;
+}
+
+// Gram products of one lower tile pair (ti, tj), transposed so that the
+// accumulator holds X[s][t] (s in tile tj, t in tile ti):
+//   gk = k_s . k_t,   gq = k_s . q_t.
+template <typename DT, int D, int PK>
+__device__ __forceinline__ void gram_pair(const DT *sK, const DT *sQ, int ti, int tj, int g4,
+                                          int c16, f32x4 &gk, f32x4 &gq) {
+    using F = Frag<DT>;
+    constexpr int KS = D / 32;
+    F fks[KS], fkt[KS], fqt[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        ld_nat(sK + (16 * tj + c16) * PK + 32 * kk + 8 * g4, fks[kk]);
+        ld_nat(sK + (16 * ti + c16) * PK + 32 * kk + 8 * g4, fkt[kk]);
+        ld_nat(sQ + (16 * ti + c16) * PK + 32 * kk + 8 * g4, fqt[kk]);
+    }
+    gk = zero4();
+    gq = zero4();
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        gk = mma(fks[kk], fkt[kk], gk);
+        gq = mma(fks[kk], fqt[kk], gq);
+    }
+}
+
+// Apply the decay masks to a transposed Gram pair and write rows of A
+// (fp32, pitch PA) and P (operand type, pitch PT): row t gets columns
+// s = 16 tj + 4 g4 .. +3 from this lane.
+template <typename DT, int PA, int PT>
+__device__ __forceinline__ void mask_pair(const f32x4 &gk, const f32x4 &gq, int ti, int tj, int g4,
+                                          int c16, const float *sG, const float *sBeta, float *sA,
+                                          DT *sP) {
+    const int t = 16 * ti + c16;
+    const float gt = sG[t];
+    const float bt = sBeta[t];
+    const f32x4 gs = *reinterpret_cast<const f32x4 *>(sG + 16 * tj + 4 * g4);
+    f32x4 av;
+    float pv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int s = 16 * tj + 4 * g4 + r;
+        // for s > t (diagonal tiles only) the product is discarded below
+        const float dec = __expf(gt - gs[r]);
+        const float a = bt * dec * gk[r];
+        const float pp = dec * gq[r];
+        if (ti == tj) {
+            av[r] = s < t ? a : 0.f;
+            pv[r] = s <= t ? pp : 0.f;
+        } else {
+            av[r] = a;
+            pv[r] = pp;
+        }
+    }
+    *reinterpret_cast<f32x4 *>(sA + t * PA + 16 * tj + 4 * g4) = av;
+    if constexpr (sizeof(DT) == 2) {
+        bf16x4 pb;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pb[r] = (__bf16)pv[r];
+        *reinterpret_cast<bf16x4 *>(sP + t * PT + 16 * tj + 4 * g4) = pb;
+    } else {
+        *reinterpret_cast<f32x4 *>(sP + t * PT + 16 * tj + 4 * g4) = f32x4{pv[0], pv[1], pv[2], pv[3]};
+    }
+}
+
+// T = (I + A)^{-1} for one wave. A: fp32 rows (pitch PA), strictly lower.
+// E: fp32 scratch for the diagonal-block inverses (may be A itself: each
+// diagonal block is read in full before it is overwritten). Writes T to
+// sT (operand type, pitch PT); blocks above the diagonal are not written.
+//   diagonal blocks E_b = (I + A_bb)^{-1}: lane = 16 b + column, forward
+//   substitution four rows at a time (a batch's rows are read first);
+//   block rows 1..3: T_ij = -E_i sum_{m=j}^{i-1} A_im T_mj on MFMA, with the
+//   finished off-diagonal blocks kept in registers.
+template <typename DT, int PA, int PT>
+__device__ __forceinline__ void solve_unit_lower(const float *sA, float *sE, DT *sT, int g4, int c16) {
+    {
+        const int blk = g4, col = c16;
+        const float *ab = sA + (16 * blk) * PA + 16 * blk;
+        float x[16];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            f32x4 arow[4][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int m4 = 0; m4 <= rb; ++m4)
+                    arow[i][m4] = *reinterpret_cast<const f32x4 *>(ab + (4 * rb + i) * PA + 4 * m4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * rb + i;
+                float acc = r == col ? 1.f : 0.f;
+#pragma unroll
+                for (int m = 0; m < r; ++m) acc -= arow[i][m >> 2][m & 3] * x[m];
+                x[r] = acc;
+            }
+        }
+        float *eb = sE + (16 * blk) * PA + 16 * blk + col;
+        DT *tb = sT + (16 * blk) * PT + 16 * blk + col;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            eb[r * PA] = x[r];
+            tb[r * PT] = from_f32<DT>(x[r]);
+        }
+    }
+    f32x4 Toff[4][4];
+    float ecol[3][4];  // columns of E_0..E_2 as B operands (k = 4 g4 + e)
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ecol[m][e] = sE[(16 * m + 4 * g4 + e) * PA + 16 * m + c16];
+#pragma unroll
+    for (int ti = 1; ti < 4; ++ti) {
+        f32x4 aim[3];
+#pragma unroll
+        for (int m = 0; m < ti; ++m)
+            aim[m] = *reinterpret_cast<const f32x4 *>(sA + (16 * ti + c16) * PA + 16 * m + 4 * g4);
+        const f32x4 ev = *reinterpret_cast<const f32x4 *>(sE + (16 * ti + c16) * PA + 16 * ti + 4 * g4);
+#pragma unroll
+        for (int tj = 0; tj < ti; ++tj) {
+            f32x4 X = zero4();
+#pragma unroll
+            for (int m = tj; m < ti; ++m) {
+                float a4[4], b4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    a4[e] = aim[m][e];
+                    b4[e] = m == tj ? ecol[m][e] : Toff[m][tj][e];
+                }
+                X = mma_k16(a4, b4, X, DT{});
+            }
+            float a4[4], b4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a4[e] = ev[e];
+                b4[e] = X[e];
+            }
+            const f32x4 Y = mma_k16(a4, b4, zero4(), DT{});
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Toff[ti][tj][r] = -Y[r];
+            DT *tb = sT + (16 * ti + 4 * g4) * PT + 16 * tj + c16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tb[r * PT] = from_f32<DT>(-Y[r]);
+        }
+    }
+}
+
+// LDS views the state chain reads for one chunk.
+template <typename DT> struct ChainSmem {
+    const DT *K, *Q;    // row-major [64][PK]
+    const DT *KT;       // bf16: K^T [D][PT]; fp32: unused (K read by column)
+    const DT *V;        // bf16: V^T [DVS][PT] (slice-local columns); fp32: V [64][PV]
+    const DT *T, *P;    // row-major [64][PT]
+    const float *gam, *dec, *beta;  // [64]
+};
+
+// State-only half of the chain for one wave: R_raw = K S^T (C[t][dv]) and
+// O^T = S Q^T (C[dv][t]) for this wave's NB value tiles. The k steps are the
+// outer loop so that 8 * NB independent accumulators interleave (no MFMA
+// waits on the previous one), and the fragments of step kk + 1 are read
+// while step kk computes.
+// PIPE = false reads each step's fragments just before use (fewer live
+// registers, for kernels that run two waves per SIMD).
+template <typename DT, int D, int NB, int PK, bool PIPE = true>
+__device__ __forceinline__ void chain_state_half(const ChainSmem<DT> &m, const f32x4 (&st)[D / 16][NB],
+                                                 Frag<DT> (&sf)[D / 32][NB], f32x4 (&racc)[4][NB],
+                                                 f32x4 (&oT)[4][NB], int g4, int c16) {
+    using F = Frag<DT>;
+    constexpr int KS = D / 32;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) c_to_frag(st[2 * kk][b], st[2 * kk + 1][b], sf[kk][b]);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            racc[mt][b] = zero4();
+            oT[mt][b] = zero4();
+        }
+    const DT *kp = m.K + c16 * PK + 4 * g4;
+    const DT *qp = m.Q + c16 * PK + 4 * g4;
+    F fk[2][4], fq[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        ld_chain(kp + 16 * mt * PK, fk[0][mt]);
+        ld_chain(qp + 16 * mt * PK, fq[0][mt]);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        if (!PIPE && kk > 0) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                ld_chain(kp + 16 * mt * PK + 32 * kk, fk[kk & 1][mt]);
+                ld_chain(qp + 16 * mt * PK + 32 * kk, fq[kk & 1][mt]);
+            }
+        }
+        if (PIPE && kk + 1 < KS) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                ld_chain(kp + 16 * mt * PK + 32 * (kk + 1), fk[(kk + 1) & 1][mt]);
+                ld_chain(qp + 16 * mt * PK + 32 * (kk + 1), fq[(kk + 1) & 1][mt]);
+            }
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                racc[mt][b] = mma(fk[kk & 1][mt], sf[kk][b], racc[mt][b]);
+                oT[mt][b] = mma(sf[kk][b], fq[kk & 1][mt], oT[mt][b]);
+            }
+    }
+}
+
+// Rest of the chain for one wave, given T: R, U = T R, O^T += U^T P^T and its
+// store (rows t < lenc; `oc` points at token 0 of the chunk, this wave's
+// first column), then the state update.
+template <typename DT, int D, int NB, int PK, int PT, int PV>
+__device__ __forceinline__ void chain_finish(const ChainSmem<DT> &m, f32x4 (&st)[D / 16][NB],
+                                             f32x4 (&racc)[4][NB], f32x4 (&oT)[4][NB], int wdv,
+                                             DT *oc, int64_t sVO, int lenc, float scale, int g4,
+                                             int c16) {
+    using F = Frag<DT>;
+    constexpr int NKT = D / 16;
+    constexpr bool BF = sizeof(DT) == 2;
+    // R = beta (V - gamma K S^T)           (C layout [t][dv])
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        const int tb = 16 * mt + 4 * g4;
+        const f32x4 bet = *reinterpret_cast<const f32x4 *>(m.beta + tb);
+        const f32x4 gam = *reinterpret_cast<const f32x4 *>(m.gam + tb);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int dvl = wdv + 16 * b + c16;
+            float vv[4];
+            if constexpr (BF) {
+                const bf16x4 v4 = *reinterpret_cast<const bf16x4 *>(m.V + dvl * PT + tb);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) vv[r] = (float)v4[r];
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) vv[r] = to_f32(m.V[(tb + r) * PV + dvl]);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) racc[mt][b][r] = bet[r] * (vv[r] - gam[r] * racc[mt][b][r]);
+        }
+    }
+    // U = T R (T lower triangular: block row mt needs k steps 0..mt/2)
+    F fr[2][NB];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) c_to_frag(racc[2 * k2][b], racc[2 * k2 + 1][b], fr[k2][b]);
+    // T fragments (block rows 0, 1 need one k step, rows 2, 3 two), read first
+    F ft[6];
+    ld_chain(m.T + c16 * PT + 4 * g4, ft[0]);
+    ld_chain(m.T + (16 + c16) * PT + 4 * g4, ft[1]);
+    ld_chain(m.T + (32 + c16) * PT + 4 * g4, ft[2]);
+    ld_chain(m.T + (32 + c16) * PT + 32 + 4 * g4, ft[3]);
+    ld_chain(m.T + (48 + c16) * PT + 4 * g4, ft[4]);
+    ld_chain(m.T + (48 + c16) * PT + 32 + 4 * g4, ft[5]);
+    f32x4 u[4][NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        u[0][b] = mma(ft[0], fr[0][b], zero4());
+        u[1][b] = mma(ft[1], fr[0][b], zero4());
+        u[2][b] = mma(ft[2], fr[0][b], zero4());
+        u[3][b] = mma(ft[4], fr[0][b], zero4());
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        u[2][b] = mma(ft[3], fr[1][b], u[2][b]);
+        u[3][b] = mma(ft[5], fr[1][b], u[3][b]);
+    }
+    // O^T = (S Q^T) diag(gamma) + U^T P^T, stored for valid rows
+    F fp[6];
+    ld_chain(m.P + c16 * PT + 4 * g4, fp[0]);
+    ld_chain(m.P + (16 + c16) * PT + 4 * g4, fp[1]);
+    ld_chain(m.P + (32 + c16) * PT + 4 * g4, fp[2]);
+    ld_chain(m.P + (32 + c16) * PT + 32 + 4 * g4, fp[3]);
+    ld_chain(m.P + (48 + c16) * PT + 4 * g4, fp[4]);
+    ld_chain(m.P + (48 + c16) * PT + 32 + 4 * g4, fp[5]);
+    F fu[2][NB];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) c_to_frag(u[2 * k2][b], u[2 * k2 + 1][b], fu[k2][b]);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        const float gam = m.gam[16 * mt + c16];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) oT[mt][b] *= gam;
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        oT[0][b] = mma(fu[0][b], fp[0], oT[0][b]);
+        oT[1][b] = mma(fu[0][b], fp[1], oT[1][b]);
+        oT[2][b] = mma(fu[0][b], fp[2], oT[2][b]);
+        oT[3][b] = mma(fu[0][b], fp[4], oT[3][b]);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        oT[2][b] = mma(fu[1][b], fp[3], oT[2][b]);
+        oT[3][b] = mma(fu[1][b], fp[5], oT[3][b]);
+    }
+    {
+        DT *o0 = oc + (int64_t)c16 * sVO + 4 * g4;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            if (16 * mt + c16 < lenc) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    DT *dst = o0 + (int64_t)(16 * mt) * sVO + 16 * b;
+                    if constexpr (BF) {
+                        bf16x4 ob;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) ob[r] = (__bf16)(scale * oT[mt][b][r]);
+                        *reinterpret_cast<bf16x4 *>(dst) = ob;
+                    } else {
+                        *reinterpret_cast<f32x4 *>(dst) = scale * oT[mt][b];
+                    }
+                }
+            }
+        }
+    }
+    // S^T <- gamma_C S^T + K^T diag(dec) U
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        const f32x4 dec = *reinterpret_cast<const f32x4 *>(m.dec + 16 * mt + 4 * g4);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) u[mt][b][r] *= dec[r];
+    }
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) c_to_frag(u[2 * k2][b], u[2 * k2 + 1][b], fu[k2][b]);
+    const float gC = m.gam[kC - 1];
+#pragma unroll
+    for (int a0 = 0; a0 < NKT; a0 += 4) {
+        F fkt[4][2];
+#pragma unroll
+        for (int a = a0; a < a0 + 4 && a < NKT; ++a)
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                if constexpr (BF)
+                    ld_chain(m.KT + (16 * a + c16) * PT + 32 * k2 + 4 * g4, fkt[a - a0][k2]);
+                else
+                    ld_chain_col<DT>(m.K + (32 * k2 + 4 * g4) * PK + 16 * a + c16, PK, fkt[a - a0][k2]);
+            }
+#pragma unroll
+        for (int a = a0; a < a0 + 4 && a < NKT; ++a) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) st[a][b] *= gC;
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+                for (int b = 0; b < NB; ++b) st[a][b] = mma(fkt[a - a0][k2], fu[k2][b], st[a][b]);
+        }
+    }
+}
+
+}  // namespace gdn

@@ -27,9 +27,17 @@ struct DecodeParams {
     float scale;
 };
 
-// dtype: 0 = fp32, 1 = bf16. D: 64 or 128. Returns a hipError_t.
-hipError_t launch_prefill(const PrefillParams &p, int dtype, int D, int num_cus,
-                          hipStream_t stream);
+// dtype: 0 = fp32, 1 = bf16. D: 64 or 128. Returns a hipError_t. With a
+// workspace of at least prefill_ws_bytes(nslots, ...) bytes (and when
+// prefill_wants_workspace agrees) the two-pass path runs; otherwise the
+// fused kernel.
+hipError_t launch_prefill(const PrefillParams &p, int dtype, int D, int num_cus, void *ws,
+                          size_t ws_bytes, int64_t nslots, hipStream_t stream);
+// Chunk records the two-pass workspace holds: B * ceil(T/64) for dense
+// batches, ceil(total/64) + N for packed ones.
+int64_t prefill_ws_slots(int64_t nseq, int64_t total_tokens, int64_t seq_len, bool packed);
+size_t prefill_ws_bytes(int64_t slots, int Hv, int dtype);
+bool prefill_wants_workspace(int64_t chains, int num_cus);
 hipError_t launch_decode(const DecodeParams &p, int dtype, int D, hipStream_t stream);
 
 }  // namespace gdn

@@ -2,66 +2,189 @@
 //
 // The token recurrence (S in R^{Dv x Dk}; q/k head g = h / (Hv/Hk))
 //     S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,   o_t = S_t q_t
-// is evaluated 64 tokens at a time through an exact rewrite. Inside a chunk
-// with start state S let g_t = sum_{s<=t} ln a_s (chunk-local, so every
-// exponent below is g_t - g_s with t >= s and no factor exceeds 1),
-// gamma_t = e^{g_t}, and
-//     A_ts = b_t e^{g_t - g_s} (k_t . k_s)   for s < t,   T = (I + A)^{-1}
-//     P_ts = e^{g_t - g_s} (q_t . k_s)       for s <= t
-// Then, with R = diag(b) (V - diag(gamma) K S^T),
-//     U     = T R                 (row t of U is b_t (v_t - a_t S_{t-1} k_t))
-//     O^T   = S Q^T diag(gamma) + U^T P^T
-//     S_end = gamma_C S + U^T diag(e^{g_C - g}) K
+// is evaluated 64 tokens at a time through the exact rewrite documented in
+// gdn_chunk.hpp. Two ways to run it:
 //
-// Work decomposition. One workgroup owns one (sequence, value head, slice of
-// DVS value columns) and walks that sequence's chunks in order; the rows of S
-// it owns evolve independently of the other rows, so slices never talk to
-// each other. Wave w owns DVW value columns and keeps S^T for them in MFMA
-// accumulators (fp32) for the whole call. The state-free part of a chunk
-// (Gram products, decay, T, P) is computed cooperatively and shared through
-// LDS.
+// Fused (no workspace). One workgroup owns one (sequence, value head, slice
+// of DVS value columns) and walks that sequence's chunks in order; wave w
+// owns DVW value columns and keeps S^T for them in MFMA accumulators for the
+// whole call. Per chunk (barriers marked |):
+//   | stage  registers -> LDS (K, Q row-major; K^T, V^T for bf16), wave 0
+//            turns its alpha/beta registers into the chunk-local decay; the
+//            next chunk's global loads are then issued into registers so
+//            their latency overlaps this chunk. Rows past the end of the
+//            sequence are staged as k = q = v = 0, alpha = 1, beta = 0, which
+//            leaves the recurrence unchanged.
+//   | gram   transposed Gram tiles on MFMA, decay masks, rows of A and P.
+//   | solve  wave 0: T = (I + A)^{-1}; the other waves form K S^T, S Q^T.
+//   | chain  R, U = T R, O, state update on MFMA.
+// The rows of S a workgroup owns evolve independently of the other rows, so
+// slices never talk to each other; they only repeat the state-free work.
 //
-// Per chunk (barriers marked |):
-//   | stage   registers -> LDS: K, Q row-major, K^T and V^T (bf16) or V
-//             (fp32). Wave 0 turns its alpha/beta registers into the
-//             chunk-local log decay. The next chunk's global loads are then
-//             issued into registers so their latency overlaps this chunk.
-//             Rows past the end of the sequence are staged as k = q = v = 0,
-//             alpha = 1, beta = 0, which leaves the recurrence unchanged.
-//   | gram    (K K^T)^T and (Q K^T)^T lower 16x16 tiles on MFMA; the decay
-//             masks are applied in registers and A (fp32) / P rows written.
-//   | solve   wave 0: T = (I + A)^{-1} (forward substitution on the four
-//             16x16 diagonal blocks, one lane per column; block rows 1..3 on
-//             MFMA with the finished blocks kept in registers). The other
-//             waves meanwhile form K S^T and S Q^T for their columns.
-//   | chain   R, U = T R, O^T += U^T P^T, store O, state update, all on MFMA
-//             with fp32 accumulation.
+// Two-pass (caller-provided workspace). The state-free work of every chunk
+// (Gram products, decay, the solve) has no dependence on the state, so
+// prep_kernel does it for all (chunk, value head) pairs at once and writes
+// T, P and the decay vectors to the workspace; chain_kernel then walks the
+// chunks in order doing only the MFMA state chain. This moves the solve's
+// latency off the sequential path, which is what limits small batches.
 #include <float.h>
+#include <stdlib.h>
 
-#include "gdn_device.hpp"
+#include "gdn_chunk.hpp"
 #include "gdn_launch.hpp"
 
 namespace gdn {
 
-constexpr int kC = 64;  // chunk length
+// ----------------------------------------------------------------------------
+// shared per-workgroup bookkeeping
 
-template <typename DT, int D, int NW, int DVW> struct PrefillCfg {
+// Sequence bounds of sequence n.
+__device__ __forceinline__ void seq_bounds(const PrefillParams &p, int n, int64_t &tok0,
+                                           int64_t &len) {
+    if (p.cu_seqlens) {
+        tok0 = p.cu_seqlens[n];
+        len = (int64_t)p.cu_seqlens[n + 1] - tok0;
+    } else {
+        tok0 = (int64_t)n * p.seq_len;
+        len = p.seq_len;
+    }
+}
+
+// Workspace slot of chunk 0 of sequence n. Dense batches: n * ceil(T/64).
+// Packed batches: floor(cu[n] / 64) + n, which is injective over all
+// (sequence, chunk) pairs and below ceil(total/64) + N.
+__device__ __forceinline__ int64_t slot_base(const PrefillParams &p, int n) {
+    if (p.cu_seqlens) return (int64_t)(p.cu_seqlens[n] >> 6) + n;
+    return (int64_t)n * ((p.seq_len + kC - 1) / kC);
+}
+
+// Logical workgroup id: workgroups are dispatched to the 8 XCDs round-robin;
+// give each XCD a contiguous range of logical ids so that workgroups sharing
+// a q/k head (and thus K, Q) share that XCD's L2.
+__device__ __forceinline__ int logical_wg(int remap_xcd) {
+    int wg = blockIdx.x;
+    if (remap_xcd) {
+        const int per = (int)(gridDim.x >> 3);
+        wg = (wg & 7) * per + (wg >> 3);
+    }
+    return wg;
+}
+
+// ----------------------------------------------------------------------------
+// staging of K, Q (row-major, K^T for bf16) and a V column slice (V^T for
+// bf16, row-major for fp32) through registers, one chunk ahead.
+
+template <typename DT, int D, int NTH, int DVS> struct Stager {
+    using P = ChunkPitch<DT, D>;
+    static constexpr bool BF = P::BF;
+    static constexpr int EPP = 16 / (int)sizeof(DT);
+    static constexpr int PPR_K = D / EPP;
+    static constexpr int PPR_V = DVS / EPP;
+    static constexpr int TK = 32 * PPR_K;
+    static constexpr int TV = 32 * PPR_V;
+    static constexpr int NTK = (TK + NTH - 1) / NTH;
+    static constexpr int NTV = (TV + NTH - 1) / NTH;
+    static constexpr int PV = DVS + 4;
+
+    int kOffG[NTK], kOffL[NTK], kRow[NTK];
+    int vOffG[NTV], vOffL[NTV], vRow[NTV];
+    u32x4 rK[NTK][2], rQ[NTK][2], rV[NTV][2];
+
+    __device__ __forceinline__ void init(int tid) {
+#pragma unroll
+        for (int i = 0; i < NTK; ++i) {
+            int rp = 0, pc = 0;
+            task_coords<PPR_K>(tid + i * NTH, rp, pc);
+            kRow[i] = 2 * rp;
+            kOffG[i] = pc * EPP;
+            kOffL[i] = 2 * rp * P::PK + pc * EPP;
+        }
+#pragma unroll
+        for (int i = 0; i < NTV; ++i) {
+            int rp = 0, pc = 0;
+            task_coords<PPR_V>(tid + i * NTH, rp, pc);
+            vRow[i] = 2 * rp;
+            vOffG[i] = pc * EPP;
+            vOffL[i] = BF ? (pc * EPP) * P::PT + 2 * rp : 2 * rp * PV + pc * EPP;
+        }
+    }
+    // Raw loads of chunk rows [t0, t0 + 64); rows >= lenc are read from a
+    // valid row and zeroed at store time, so nothing consumes the loaded
+    // registers before the store (the loads stay in flight meanwhile).
+    __device__ __forceinline__ void load(const DT *kh, const DT *qh, const DT *vh, int64_t t0,
+                                         int lenc, int64_t sQK, int64_t sVO, int tid) {
+#pragma unroll
+        for (int i = 0; i < NTK; ++i) {
+            if (TK % NTH == 0 || tid + i * NTH < TK) {
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int r = kRow[i] + e;
+                    const int rr = r < lenc ? r : lenc - 1;
+                    const int64_t off = (t0 + rr) * sQK + kOffG[i];
+                    rK[i][e] = *reinterpret_cast<const u32x4 *>(kh + off);
+                    rQ[i][e] = *reinterpret_cast<const u32x4 *>(qh + off);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NTV; ++i) {
+            if (TV % NTH == 0 || tid + i * NTH < TV) {
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int r = vRow[i] + e;
+                    const int rr = r < lenc ? r : lenc - 1;
+                    rV[i][e] = *reinterpret_cast<const u32x4 *>(vh + (t0 + rr) * sVO + vOffG[i]);
+                }
+            }
+        }
+    }
+    __device__ __forceinline__ void store(DT *sK, DT *sQ, DT *sKT, DT *sV, int lenc, int tid) {
+        const u32x4 z4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < NTK; ++i) {
+            if (TK % NTH == 0 || tid + i * NTH < TK) {
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const bool ok = kRow[i] + e < lenc;
+                    rK[i][e] = ok ? rK[i][e] : z4;
+                    rQ[i][e] = ok ? rQ[i][e] : z4;
+                    *reinterpret_cast<u32x4 *>(sK + kOffL[i] + e * P::PK) = rK[i][e];
+                    *reinterpret_cast<u32x4 *>(sQ + kOffL[i] + e * P::PK) = rQ[i][e];
+                }
+                if constexpr (BF)
+                    store_pair_transposed<P::PT>(sKT + kOffG[i] * P::PT + kRow[i], rK[i][0], rK[i][1]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NTV; ++i) {
+            if (TV % NTH == 0 || tid + i * NTH < TV) {
+#pragma unroll
+                for (int e = 0; e < 2; ++e) rV[i][e] = vRow[i] + e < lenc ? rV[i][e] : z4;
+                if constexpr (BF) {
+                    store_pair_transposed<P::PT>(sV + vOffL[i], rV[i][0], rV[i][1]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 2; ++e)
+                        *reinterpret_cast<u32x4 *>(sV + vOffL[i] + e * PV) = rV[i][e];
+                }
+            }
+        }
+    }
+};
+
+// ----------------------------------------------------------------------------
+// fused kernel
+
+template <typename DT, int D, int NW, int DVW> struct FusedCfg {
+    using P = ChunkPitch<DT, D>;
     static constexpr int NTH = NW * 64;
-    static constexpr int DVS = NW * DVW;  // value columns per workgroup
-    static constexpr int NKT = D / 16;    // key-dim tiles of S^T
-    static constexpr int NB = DVW / 16;   // value-dim tiles per wave
-    static constexpr int KS = D / 32;     // 32-deep steps over the key dim
-    static constexpr bool BF = sizeof(DT) == 2;
-    static constexpr int EPP = 16 / (int)sizeof(DT);  // elements per 16-byte piece
-    static constexpr int PK = D + (BF ? 8 : 4);       // row pitch of K, Q
-    static constexpr int PT = kC + 4;                 // row pitch of T, P, K^T, V^T
-    static constexpr int PV = DVS + 4;                // row pitch of V (fp32 path)
-    static constexpr int PA = kC + 4;                 // row pitch of fp32 A and E
-    static constexpr int SZ_K = kC * PK * (int)sizeof(DT);
-    static constexpr int SZ_KT = BF ? D * PT * 2 : 0;
-    static constexpr int SZ_V = BF ? DVS * PT * 2 : kC * PV * 4;
-    static constexpr int SZ_T = kC * PT * (int)sizeof(DT);
-    static constexpr int SZ_A = kC * PA * 4;
+    static constexpr int DVS = NW * DVW;
+    static constexpr int PV = DVS + 4;
+    static constexpr int SZ_K = kC * P::PK * (int)sizeof(DT);
+    static constexpr int SZ_KT = P::BF ? D * P::PT * 2 : 0;
+    static constexpr int SZ_V = P::BF ? DVS * P::PT * 2 : kC * PV * 4;
+    static constexpr int SZ_T = kC * P::PT * (int)sizeof(DT);
+    static constexpr int SZ_A = kC * P::PA * 4;
     static constexpr int OFF_K = 0;
     static constexpr int OFF_Q = OFF_K + SZ_K;
     static constexpr int OFF_KT = OFF_Q + SZ_K;
@@ -70,66 +193,25 @@ template <typename DT, int D, int NW, int DVW> struct PrefillCfg {
     static constexpr int OFF_P = OFF_T + SZ_T;
     static constexpr int OFF_A = OFF_P + SZ_T;
     static constexpr int OFF_E = OFF_A + SZ_A;
-    static constexpr int OFF_VEC = OFF_E + SZ_A;  // g, gamma, dec, beta: 4 x 64 floats
+    static constexpr int OFF_VEC = OFF_E + SZ_A;  // g, gamma, dec, beta
     static constexpr int LDS = OFF_VEC + 4 * kC * 4;
-    // staging tasks: one task is one 16-byte piece of two consecutive rows
-    static constexpr int PPR_K = D / EPP;
-    static constexpr int PPR_V = DVS / EPP;
-    static constexpr int TK = 32 * PPR_K;
-    static constexpr int TV = 32 * PPR_V;
-    static constexpr int NTK = (TK + NTH - 1) / NTH;
-    static constexpr int NTV = (TV + NTH - 1) / NTH;
     static_assert(DVW % 16 == 0 && D % 32 == 0, "tile shapes");
     static_assert(LDS <= 160 * 1024, "LDS budget of a gfx950 CU");
 };
 
-// Task -> (row pair, piece). Within 64 consecutive tasks the row pair varies
-// fastest over 16 (or 32) values, so the transposed LDS writes of a wave
-// spread over all banks while each wave still reads whole 64-byte row
-// segments from global memory.
-template <int PPR>
-__device__ __forceinline__ void task_coords(int task, int &rp, int &pc) {
-    constexpr int PCB = PPR < 4 ? PPR : 4;  // pieces per 64-task group
-    constexpr int RPB = 64 / PCB;           // row pairs per 64-task group
-    constexpr int NRB = 32 / RPB;           // row-pair blocks
-    const int li = task & 63, grp = task >> 6;
-    rp = (li % RPB) + RPB * (grp % NRB);
-    pc = (li / RPB) + PCB * (grp / NRB);
-}
-
-// Two rows (lo = row r, hi = row r+1) of 8 bf16 each, written transposed:
-// column j of the pair goes to dst[j * PT .. +1] as one 32-bit word.
-template <int PT>
-__device__ __forceinline__ void store_pair_transposed(__bf16 *dst, const u32x4 &l, const u32x4 &h) {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        *reinterpret_cast<uint32_t *>(dst + (2 * w) * PT) = (l[w] & 0xFFFFu) | (h[w] << 16);
-        *reinterpret_cast<uint32_t *>(dst + (2 * w + 1) * PT) = (l[w] >> 16) | (h[w] & 0xFFFF0000u);
-    }
-}
-template <int PT>
-__device__ __forceinline__ void store_pair_transposed(float *, const u32x4 &, const u32x4 &) {}
-
-// Lower 16x16 tile pairs (ti, tj), tj <= ti, of a 64x64 chunk matrix.
-__device__ __forceinline__ constexpr int pair_i(int pr) {
-    return pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3;
-}
-__device__ __forceinline__ constexpr int pair_j(int pr) { return pr - pair_i(pr) * (pair_i(pr) + 1) / 2; }
-
 template <typename DT, int D, int NW, int DVW>
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p, int nsplit,
                                                           int remap_xcd) {
-    using Cf = PrefillCfg<DT, D, NW, DVW>;
-    constexpr int NTH = Cf::NTH, NKT = Cf::NKT, NB = Cf::NB, KS = Cf::KS;
-    constexpr int PK = Cf::PK, PT = Cf::PT, PV = Cf::PV, PA = Cf::PA;
-    constexpr bool BF = Cf::BF;
-    using F = Frag<DT>;
+    using Cf = FusedCfg<DT, D, NW, DVW>;
+    using Pi = ChunkPitch<DT, D>;
+    constexpr int NTH = Cf::NTH, NKT = D / 16, NB = DVW / 16, KS = D / 32;
+    constexpr int PK = Pi::PK, PT = Pi::PT, PA = Pi::PA, PV = Cf::PV;
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::LDS];
     DT *sK = reinterpret_cast<DT *>(smem + Cf::OFF_K);
     DT *sQ = reinterpret_cast<DT *>(smem + Cf::OFF_Q);
-    DT *sKT = reinterpret_cast<DT *>(smem + Cf::OFF_KT);  // bf16 only: [D][PT]
-    DT *sV = reinterpret_cast<DT *>(smem + Cf::OFF_V);    // bf16: V^T [DVS][PT]; fp32: V [kC][PV]
+    DT *sKT = reinterpret_cast<DT *>(smem + Cf::OFF_KT);
+    DT *sV = reinterpret_cast<DT *>(smem + Cf::OFF_V);
     DT *sT = reinterpret_cast<DT *>(smem + Cf::OFF_T);
     DT *sP = reinterpret_cast<DT *>(smem + Cf::OFF_P);
     float *sA = reinterpret_cast<float *>(smem + Cf::OFF_A);
@@ -145,30 +227,16 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p, int n
     const int g4 = lane >> 4;
     const int c16 = lane & 15;
 
-    // ---- which (sequence, value head, slice) this workgroup owns
-    int wg = blockIdx.x;
-    if (remap_xcd) {
-        // Workgroups are dispatched to the 8 XCDs round-robin; give each XCD
-        // a contiguous range of logical ids so that the value heads (and
-        // slices) sharing one q/k head share that XCD's L2.
-        const int per = (int)(gridDim.x >> 3);
-        wg = (wg & 7) * per + (wg >> 3);
-    }
+    const int wg = logical_wg(remap_xcd);
     const int slice = wg % nsplit;
     const int nh = wg / nsplit;
     const int h = nh % p.Hv;
     const int n = nh / p.Hv;
     const int grp = h / (p.Hv / p.Hk);
     int64_t tok0, len;
-    if (p.cu_seqlens) {
-        tok0 = p.cu_seqlens[n];
-        len = (int64_t)p.cu_seqlens[n + 1] - tok0;
-    } else {
-        tok0 = (int64_t)n * p.seq_len;
-        len = p.seq_len;
-    }
+    seq_bounds(p, n, tok0, len);
     const int dv0 = slice * Cf::DVS;
-    const int wdv = wave * DVW;  // this wave's first column inside the slice
+    const int wdv = wave * DVW;
 
     const int64_t sQK = (int64_t)p.Hk * D;
     const int64_t sVO = (int64_t)p.Hv * D;
@@ -183,7 +251,6 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p, int n
     for (int i = tid; i < 2 * Cf::SZ_T / 4; i += NTH)
         reinterpret_cast<float *>(smem + Cf::OFF_T)[i] = 0.f;
 
-    // ---- state S^T for this wave's columns: st[a][b] = S^T tile (dk a, dv b)
     f32x4 st[NKT][NB];
     {
         const float *s0 = p.s0 ? p.s0 + ((int64_t)n * p.Hv + h) * D * D : nullptr;
@@ -196,59 +263,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p, int n
                               : zero4();
     }
 
-    // ---- staging: per-thread task coordinates (fixed for the whole call)
-    int kOffG[Cf::NTK], kOffL[Cf::NTK], kRow[Cf::NTK];
-    int vOffG[Cf::NTV], vOffL[Cf::NTV], vRow[Cf::NTV];
-#pragma unroll
-    for (int i = 0; i < Cf::NTK; ++i) {
-        int rp = 0, pc = 0;
-        task_coords<Cf::PPR_K>(tid + i * NTH, rp, pc);
-        kRow[i] = 2 * rp;
-        kOffG[i] = pc * Cf::EPP;
-        kOffL[i] = 2 * rp * PK + pc * Cf::EPP;
-    }
-#pragma unroll
-    for (int i = 0; i < Cf::NTV; ++i) {
-        int rp = 0, pc = 0;
-        task_coords<Cf::PPR_V>(tid + i * NTH, rp, pc);
-        vRow[i] = 2 * rp;
-        vOffG[i] = pc * Cf::EPP;
-        vOffL[i] = BF ? (pc * Cf::EPP) * PT + 2 * rp : 2 * rp * PV + pc * Cf::EPP;
-    }
-    u32x4 rK[Cf::NTK][2], rQ[Cf::NTK][2], rV[Cf::NTV][2];
+    Stager<DT, D, NTH, Cf::DVS> sg;
+    sg.init(tid);
     float rAl = 1.f, rBe = 0.f;  // wave 0: alpha, beta of token `lane` of the next chunk
-
-    // The loads below are kept raw; rows past the end of the sequence are
-    // read from a valid row and zeroed at store time, so nothing consumes
-    // the loaded registers before the next chunk's store (the loads stay in
-    // flight while this chunk computes).
-    auto stage_load = [&](int64_t c) {
+    auto load_chunk = [&](int64_t c) {
         const int64_t t0 = c * kC;
         const int lenc = (int)((len - t0) < kC ? (len - t0) : kC);
-#pragma unroll
-        for (int i = 0; i < Cf::NTK; ++i) {
-            if (Cf::TK % NTH == 0 || tid + i * NTH < Cf::TK) {
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const int r = kRow[i] + e;
-                    const int rr = r < lenc ? r : lenc - 1;  // always a valid row
-                    const int64_t off = (t0 + rr) * sQK + kOffG[i];
-                    rK[i][e] = *reinterpret_cast<const u32x4 *>(kh + off);
-                    rQ[i][e] = *reinterpret_cast<const u32x4 *>(qh + off);
-                }
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < Cf::NTV; ++i) {
-            if (Cf::TV % NTH == 0 || tid + i * NTH < Cf::TV) {
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const int r = vRow[i] + e;
-                    const int rr = r < lenc ? r : lenc - 1;
-                    rV[i][e] = *reinterpret_cast<const u32x4 *>(vh + (t0 + rr) * sVO + vOffG[i]);
-                }
-            }
-        }
+        sg.load(kh, qh, vh, t0, lenc, sQK, sVO, tid);
         if (wave == 0) {
             const int rr = lane < lenc ? lane : lenc - 1;
             rAl = ah[(t0 + rr) * p.Hv];
@@ -256,354 +277,47 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p, int n
         }
     };
 
-    const u32x4 z4 = {0u, 0u, 0u, 0u};
-    auto stage_store = [&](int lenc) {
-#pragma unroll
-        for (int i = 0; i < Cf::NTK; ++i) {
-            if (Cf::TK % NTH == 0 || tid + i * NTH < Cf::TK) {
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const bool ok = kRow[i] + e < lenc;
-                    rK[i][e] = ok ? rK[i][e] : z4;
-                    rQ[i][e] = ok ? rQ[i][e] : z4;
-                    *reinterpret_cast<u32x4 *>(sK + kOffL[i] + e * PK) = rK[i][e];
-                    *reinterpret_cast<u32x4 *>(sQ + kOffL[i] + e * PK) = rQ[i][e];
-                }
-                if constexpr (BF)  // K^T[col][row pair]: two rows per 32-bit word
-                    store_pair_transposed<PT>(sKT + kOffG[i] * PT + kRow[i], rK[i][0], rK[i][1]);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < Cf::NTV; ++i) {
-            if (Cf::TV % NTH == 0 || tid + i * NTH < Cf::TV) {
-#pragma unroll
-                for (int e = 0; e < 2; ++e) rV[i][e] = vRow[i] + e < lenc ? rV[i][e] : z4;
-                if constexpr (BF) {
-                    store_pair_transposed<PT>(sV + vOffL[i], rV[i][0], rV[i][1]);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 2; ++e)
-                        *reinterpret_cast<u32x4 *>(sV + vOffL[i] + e * PV) = rV[i][e];
-                }
-            }
-        }
-        if (wave == 0) {
-            // chunk-local cumulative log decay: inclusive scan over the 64 lanes
-            const bool ok = lane < lenc;
-            const float al = ok ? rAl : 1.f;
-            const float be = ok ? rBe : 0.f;
-            float x = __logf(fmaxf(al, FLT_MIN));
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(x, off, 64);
-                x += lane >= off ? y : 0.f;
-            }
-            const float glast = __shfl(x, 63, 64);
-            sG[lane] = x;
-            sGam[lane] = __expf(x);
-            sDec[lane] = __expf(glast - x);
-            sBeta[lane] = be;
-        }
-    };
-
     const int64_t nchunks = (len + kC - 1) / kC;
-    if (nchunks > 0) stage_load(0);
+    if (nchunks > 0) load_chunk(0);
     // Drain the initial-state and first-chunk loads here (the first store
-    // needs them anyway). Without this, the state registers count as
-    // possibly pending inside the loop and each chunk would wait for its own
-    // prefetch before touching the state.
+    // needs them anyway). Otherwise the state registers count as possibly
+    // pending inside the loop and each chunk would wait on its prefetch.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
     for (int64_t c = 0; c < nchunks; ++c) {
         const int lenc = (int)((len - c * kC) < kC ? (len - c * kC) : kC);
         __syncthreads();  // the previous chunk is done with LDS
-        stage_store(lenc);
-        if (c + 1 < nchunks) stage_load(c + 1);
+        sg.store(sK, sQ, sKT, sV, lenc, tid);
+        if (wave == 0) {
+            const bool ok = lane < lenc;
+            const float x = wave_inclusive_scan(__logf(fmaxf(ok ? rAl : 1.f, FLT_MIN)));
+            const float glast = __shfl(x, 63, 64);
+            sG[lane] = x;
+            sGam[lane] = __expf(x);
+            sDec[lane] = __expf(glast - x);
+            sBeta[lane] = ok ? rBe : 0.f;
+        }
+        if (c + 1 < nchunks) load_chunk(c + 1);
         __syncthreads();
 
-        // ---- Gram tiles, transposed: X[s][t] = k_s . k_t and k_s . q_t for
-        // the lower tile pair (ti, tj) (s in tile tj, t in tile ti); decay
-        // masks applied in registers; rows of A (fp32) and P written.
 #pragma unroll
         for (int pr = 0; pr < 10; ++pr) {
             if (pr % NW != wave) continue;
-            const int ti = pair_i(pr), tj = pair_j(pr);
-            f32x4 gk = zero4(), gq = zero4();
-            F fks[KS], fkt[KS], fqt[KS];
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                ld_nat(sK + (16 * tj + c16) * PK + 32 * kk + 8 * g4, fks[kk]);
-                ld_nat(sK + (16 * ti + c16) * PK + 32 * kk + 8 * g4, fkt[kk]);
-                ld_nat(sQ + (16 * ti + c16) * PK + 32 * kk + 8 * g4, fqt[kk]);
-            }
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                gk = mma(fks[kk], fkt[kk], gk);
-                gq = mma(fks[kk], fqt[kk], gq);
-            }
-            const int t = 16 * ti + c16;
-            const float gt = sG[t];
-            const float bt = sBeta[t];
-            const f32x4 gs = *reinterpret_cast<const f32x4 *>(sG + 16 * tj + 4 * g4);
-            f32x4 av;
-            float pv[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int s = 16 * tj + 4 * g4 + r;
-                // for s > t (diagonal tiles only) the value is discarded below
-                const float dec = __expf(gt - gs[r]);
-                const float a = bt * dec * gk[r];
-                const float pp = dec * gq[r];
-                if (ti == tj) {
-                    av[r] = s < t ? a : 0.f;
-                    pv[r] = s <= t ? pp : 0.f;
-                } else {
-                    av[r] = a;
-                    pv[r] = pp;
-                }
-            }
-            *reinterpret_cast<f32x4 *>(sA + t * PA + 16 * tj + 4 * g4) = av;
-            if constexpr (BF) {
-                bf16x4 pb;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) pb[r] = (__bf16)pv[r];
-                *reinterpret_cast<bf16x4 *>(sP + t * PT + 16 * tj + 4 * g4) = pb;
-            } else {
-                *reinterpret_cast<f32x4 *>(sP + t * PT + 16 * tj + 4 * g4) =
-                    f32x4{pv[0], pv[1], pv[2], pv[3]};
-            }
+            f32x4 gk, gq;
+            gram_pair<DT, D, PK>(sK, sQ, pair_i(pr), pair_j(pr), g4, c16, gk, gq);
+            mask_pair<DT, PA, PT>(gk, gq, pair_i(pr), pair_j(pr), g4, c16, sG, sBeta, sA, sP);
         }
         __syncthreads();
 
-        // ---- T = (I + A)^{-1} on wave 0
-        if (wave == 0) {
-            // diagonal blocks E_b = (I + A_bb)^{-1}: lane = 16 b + column. Rows
-            // are solved four at a time; a batch's rows of A are read before
-            // any of its arithmetic so that one LDS latency covers the batch.
-            {
-                const int blk = g4, col = c16;
-                const float *ab = sA + (16 * blk) * PA + 16 * blk;
-                float x[16];
-#pragma unroll
-                for (int rb = 0; rb < 4; ++rb) {
-                    f32x4 arow[4][4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int m4 = 0; m4 <= rb; ++m4)
-                            arow[i][m4] = *reinterpret_cast<const f32x4 *>(ab + (4 * rb + i) * PA + 4 * m4);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = 4 * rb + i;
-                        float acc = r == col ? 1.f : 0.f;
-#pragma unroll
-                        for (int m = 0; m < r; ++m) acc -= arow[i][m >> 2][m & 3] * x[m];
-                        x[r] = acc;
-                    }
-                }
-                float *eb = sE + (16 * blk) * PA + 16 * blk + col;
-                DT *tb = sT + (16 * blk) * PT + 16 * blk + col;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    eb[r * PA] = x[r];
-                    tb[r * PT] = from_f32<DT>(x[r]);
-                }
-            }
-            // block rows 1..3: T_ij = -E_i * sum_{m=j}^{i-1} A_im T_mj, with the
-            // off-diagonal T_mj kept in registers (accumulator layout).
-            f32x4 Toff[4][4];
-            // columns of E_0..E_2 as B operands (k = 4 g4 + e)
-            float ecol[3][4];
-#pragma unroll
-            for (int m = 0; m < 3; ++m)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) ecol[m][e] = sE[(16 * m + 4 * g4 + e) * PA + 16 * m + c16];
-#pragma unroll
-            for (int ti = 1; ti < 4; ++ti) {
-                f32x4 aim[3];
-#pragma unroll
-                for (int m = 0; m < ti; ++m)
-                    aim[m] = *reinterpret_cast<const f32x4 *>(sA + (16 * ti + c16) * PA + 16 * m + 4 * g4);
-                const f32x4 ev =
-                    *reinterpret_cast<const f32x4 *>(sE + (16 * ti + c16) * PA + 16 * ti + 4 * g4);
-#pragma unroll
-                for (int tj = 0; tj < ti; ++tj) {
-                    f32x4 X = zero4();
-#pragma unroll
-                    for (int m = tj; m < ti; ++m) {
-                        float a4[4], b4[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            a4[e] = aim[m][e];
-                            b4[e] = m == tj ? ecol[m][e] : Toff[m][tj][e];
-                        }
-                        X = mma_k16(a4, b4, X, DT{});
-                    }
-                    float a4[4], b4[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        a4[e] = ev[e];
-                        b4[e] = X[e];
-                    }
-                    const f32x4 Y = mma_k16(a4, b4, zero4(), DT{});
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) Toff[ti][tj][r] = -Y[r];
-                    DT *tb = sT + (16 * ti + 4 * g4) * PT + 16 * tj + c16;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) tb[r * PT] = from_f32<DT>(-Y[r]);
-                }
-            }
-        }
+        if (wave == 0) solve_unit_lower<DT, PA, PT>(sA, sE, sT, g4, c16);
 
-        // ---- chain, state-only half: R_raw = K S^T and O^T = S Q^T
-        F sf[KS][NB];
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-            for (int b = 0; b < NB; ++b) c_to_frag(st[2 * kk][b], st[2 * kk + 1][b], sf[kk][b]);
+        const ChainSmem<DT> m{sK, sQ, sKT, sV, sT, sP, sGam, sDec, sBeta};
+        Frag<DT> sf[KS][NB];
         f32x4 racc[4][NB], oT[4][NB];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                racc[mt][b] = zero4();
-                oT[mt][b] = zero4();
-            }
-            F fk[KS], fq[KS];
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                ld_chain(sK + (16 * mt + c16) * PK + 32 * kk + 4 * g4, fk[kk]);
-                ld_chain(sQ + (16 * mt + c16) * PK + 32 * kk + 4 * g4, fq[kk]);
-            }
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    racc[mt][b] = mma(fk[kk], sf[kk][b], racc[mt][b]);  // C[t][dv]
-                    oT[mt][b] = mma(sf[kk][b], fq[kk], oT[mt][b]);      // C[dv][t]
-                }
-            }
-        }
+        chain_state_half<DT, D, NB, PK, (NW < 8)>(m, st, sf, racc, oT, g4, c16);
         __syncthreads();  // T is ready
-
-        // ---- R = beta (V - gamma K S^T)           (C layout [t][dv])
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const int tb = 16 * mt + 4 * g4;
-            const f32x4 bet = *reinterpret_cast<const f32x4 *>(sBeta + tb);
-            const f32x4 gam = *reinterpret_cast<const f32x4 *>(sGam + tb);
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const int dvl = wdv + 16 * b + c16;
-                float vv[4];
-                if constexpr (BF) {
-                    const bf16x4 v4 = *reinterpret_cast<const bf16x4 *>(sV + dvl * PT + tb);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) vv[r] = (float)v4[r];
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) vv[r] = to_f32(sV[(tb + r) * PV + dvl]);
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    racc[mt][b][r] = bet[r] * (vv[r] - gam[r] * racc[mt][b][r]);
-            }
-        }
-        // ---- U = T R (T lower triangular: block row mt needs k steps 0..mt/2)
-        F fr[2][NB];
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-            for (int b = 0; b < NB; ++b) c_to_frag(racc[2 * k2][b], racc[2 * k2 + 1][b], fr[k2][b]);
-        f32x4 u[4][NB];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-            for (int b = 0; b < NB; ++b) u[mt][b] = zero4();
-#pragma unroll
-            for (int k2 = 0; k2 <= (mt >> 1); ++k2) {
-                F ft;
-                ld_chain(sT + (16 * mt + c16) * PT + 32 * k2 + 4 * g4, ft);
-#pragma unroll
-                for (int b = 0; b < NB; ++b) u[mt][b] = mma(ft, fr[k2][b], u[mt][b]);
-            }
-        }
-        // ---- O^T = (S Q^T) diag(gamma) + U^T P^T, stored for valid rows
-        F fu[2][NB];
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-            for (int b = 0; b < NB; ++b) c_to_frag(u[2 * k2][b], u[2 * k2 + 1][b], fu[k2][b]);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const float gam = sGam[16 * mt + c16];
-#pragma unroll
-            for (int b = 0; b < NB; ++b) oT[mt][b] *= gam;
-#pragma unroll
-            for (int k2 = 0; k2 <= (mt >> 1); ++k2) {
-                F fp;
-                ld_chain(sP + (16 * mt + c16) * PT + 32 * k2 + 4 * g4, fp);
-#pragma unroll
-                for (int b = 0; b < NB; ++b) oT[mt][b] = mma(fu[k2][b], fp, oT[mt][b]);
-            }
-        }
-        {
-            DT *oc = oh + (c * kC + c16) * sVO + 4 * g4;
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                if (16 * mt + c16 < lenc) {
-#pragma unroll
-                    for (int b = 0; b < NB; ++b) {
-                        DT *dst = oc + (int64_t)(16 * mt) * sVO + 16 * b;
-                        if constexpr (BF) {
-                            bf16x4 ob;
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) ob[r] = (__bf16)(p.scale * oT[mt][b][r]);
-                            *reinterpret_cast<bf16x4 *>(dst) = ob;
-                        } else {
-                            *reinterpret_cast<f32x4 *>(dst) = p.scale * oT[mt][b];
-                        }
-                    }
-                }
-            }
-        }
-        // ---- S^T <- gamma_C S^T + K^T diag(e^{g_C - g}) U
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const f32x4 dec = *reinterpret_cast<const f32x4 *>(sDec + 16 * mt + 4 * g4);
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) u[mt][b][r] *= dec[r];
-        }
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-            for (int b = 0; b < NB; ++b) c_to_frag(u[2 * k2][b], u[2 * k2 + 1][b], fu[k2][b]);
-        const float gC = sGam[kC - 1];
-#pragma unroll
-        for (int a0 = 0; a0 < NKT; a0 += 4) {
-            F fkt[4][2];
-#pragma unroll
-            for (int a = a0; a < a0 + 4 && a < NKT; ++a)
-#pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2) {
-                    if constexpr (BF)
-                        ld_chain(sKT + (16 * a + c16) * PT + 32 * k2 + 4 * g4, fkt[a - a0][k2]);
-                    else
-                        ld_chain_col<DT>(sK + (32 * k2 + 4 * g4) * PK + 16 * a + c16, PK,
-                                         fkt[a - a0][k2]);
-                }
-#pragma unroll
-            for (int a = a0; a < a0 + 4 && a < NKT; ++a) {
-#pragma unroll
-                for (int b = 0; b < NB; ++b) st[a][b] *= gC;
-#pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-                    for (int b = 0; b < NB; ++b) st[a][b] = mma(fkt[a - a0][k2], fu[k2][b], st[a][b]);
-            }
-        }
+        chain_finish<DT, D, NB, PK, PT, PV>(m, st, racc, oT, wdv, oh + c * kC * sVO, sVO, lenc,
+                                            p.scale, g4, c16);
     }
 
     if (p.s_final) {
@@ -617,63 +331,628 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p, int n
     }
 }
 
+// ----------------------------------------------------------------------------
+// two-pass path: per-chunk factors in the workspace
+//
+// Workspace record of one (chunk slot, value head), ws_bytes_per_chunk bytes:
+//   T [64][64] DT | P [64][64] DT | gamma [64] f32 | dec [64] f32 | beta [64] f32
+
+template <typename DT> constexpr int ws_bytes_per_chunk() {
+    return 2 * kC * kC * (int)sizeof(DT) + 3 * kC * 4;
+}
+
+template <typename DT, int D> struct PrepCfg {
+    using P = ChunkPitch<DT, D>;
+    static constexpr int SZ_K = kC * P::PK * (int)sizeof(DT);
+    static constexpr int SZ_T = kC * P::PT * (int)sizeof(DT);
+    static constexpr int SZ_A = kC * P::PA * 4;
+    static constexpr int OFF_K = 0;
+    static constexpr int OFF_Q = SZ_K;
+    static constexpr int OFF_A = 2 * SZ_K;
+    static constexpr int OFF_T = OFF_A + SZ_A;
+    static constexpr int OFF_P = OFF_T + SZ_T;
+    static constexpr int OFF_VEC = OFF_P + SZ_T;
+    static constexpr int LDS = OFF_VEC + 4 * kC * 4;
+    static_assert(LDS <= 160 * 1024, "LDS budget of a gfx950 CU");
+};
+
+// One workgroup (4 waves) per (chunk slot, value head): Gram products, decay,
+// T = (I + A)^{-1}; writes T, P, gamma, dec, beta to the workspace.
+template <typename DT, int D>
+__global__ __launch_bounds__(256) void prep_kernel(PrefillParams p, unsigned char *ws,
+                                                   int remap_xcd) {
+    using Cf = PrepCfg<DT, D>;
+    using Pi = ChunkPitch<DT, D>;
+    constexpr int PK = Pi::PK, PT = Pi::PT, PA = Pi::PA;
+    constexpr int EPP = 16 / (int)sizeof(DT);
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::LDS];
+    DT *sK = reinterpret_cast<DT *>(smem + Cf::OFF_K);
+    DT *sQ = reinterpret_cast<DT *>(smem + Cf::OFF_Q);
+    float *sA = reinterpret_cast<float *>(smem + Cf::OFF_A);
+    DT *sT = reinterpret_cast<DT *>(smem + Cf::OFF_T);
+    DT *sP = reinterpret_cast<DT *>(smem + Cf::OFF_P);
+    float *sG = reinterpret_cast<float *>(smem + Cf::OFF_VEC);
+    float *sGam = sG + kC;
+    float *sDec = sG + 2 * kC;
+    float *sBeta = sG + 3 * kC;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g4 = lane >> 4;
+    const int c16 = lane & 15;
+
+    // value heads of one chunk are consecutive logical ids: same XCD, so the
+    // heads sharing a q/k head read K and Q through one L2
+    const int wg = logical_wg(remap_xcd);
+    const int h = wg % p.Hv;
+    const int64_t slot = wg / p.Hv;
+    // which (sequence, chunk) owns this slot
+    int n;
+    if (p.cu_seqlens) {
+        int lo = 0, hi = p.nseq - 1;  // largest n with slot_base(n) <= slot
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (slot_base(p, mid) <= slot)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        n = lo;
+    } else {
+        const int64_t per = (p.seq_len + kC - 1) / kC;
+        n = (int)(slot / per);
+    }
+    int64_t tok0, len;
+    seq_bounds(p, n, tok0, len);
+    const int64_t c = slot - slot_base(p, n);
+    if (c < 0 || c * kC >= len) return;  // unused slot (uniform over the workgroup)
+    const int lenc = (int)((len - c * kC) < kC ? (len - c * kC) : kC);
+    const int64_t t0 = tok0 + c * kC;
+    const int grp = h / (p.Hv / p.Hk);
+    const int64_t sQK = (int64_t)p.Hk * D;
+    const DT *kh = reinterpret_cast<const DT *>(p.k) + t0 * sQK + (int64_t)grp * D;
+    const DT *qh = reinterpret_cast<const DT *>(p.q) + t0 * sQK + (int64_t)grp * D;
+
+    // K, Q rows -> LDS; T and P cleared (their upper blocks are never written)
+    {
+        constexpr int PPR = D / EPP;
+        const u32x4 z4 = {0u, 0u, 0u, 0u};
+        for (int i = tid; i < kC * PPR; i += 256) {
+            const int r = i / PPR, pc = i % PPR;
+            const int rr = r < lenc ? r : lenc - 1;
+            const u32x4 kv = *reinterpret_cast<const u32x4 *>(kh + (int64_t)rr * sQK + pc * EPP);
+            const u32x4 qv = *reinterpret_cast<const u32x4 *>(qh + (int64_t)rr * sQK + pc * EPP);
+            *reinterpret_cast<u32x4 *>(sK + r * PK + pc * EPP) = r < lenc ? kv : z4;
+            *reinterpret_cast<u32x4 *>(sQ + r * PK + pc * EPP) = r < lenc ? qv : z4;
+        }
+        for (int i = tid; i < 2 * Cf::SZ_T / 4; i += 256)
+            reinterpret_cast<float *>(smem + Cf::OFF_T)[i] = 0.f;
+    }
+    unsigned char *rec = ws + (slot * p.Hv + h) * (int64_t)ws_bytes_per_chunk<DT>();
+    if (wave == 0) {
+        const int rr = lane < lenc ? lane : lenc - 1;
+        const float a = p.alpha[(t0 + rr) * p.Hv + h];
+        const float b = p.beta[(t0 + rr) * p.Hv + h];
+        const bool ok = lane < lenc;
+        const float x = wave_inclusive_scan(__logf(fmaxf(ok ? a : 1.f, FLT_MIN)));
+        const float glast = __shfl(x, 63, 64);
+        const float gam = __expf(x), dec = __expf(glast - x), bet = ok ? b : 0.f;
+        sG[lane] = x;
+        sGam[lane] = gam;
+        sDec[lane] = dec;
+        sBeta[lane] = bet;
+        float *vec = reinterpret_cast<float *>(rec + 2 * kC * kC * sizeof(DT));
+        vec[lane] = gam;
+        vec[kC + lane] = dec;
+        vec[2 * kC + lane] = bet;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int pr = 0; pr < 10; ++pr) {
+        if (pr % 4 != wave) continue;
+        f32x4 gk, gq;
+        gram_pair<DT, D, PK>(sK, sQ, pair_i(pr), pair_j(pr), g4, c16, gk, gq);
+        mask_pair<DT, PA, PT>(gk, gq, pair_i(pr), pair_j(pr), g4, c16, sG, sBeta, sA, sP);
+    }
+    __syncthreads();
+    // E_b overwrite the diagonal blocks of A (each is read in full first)
+    if (wave == 0) solve_unit_lower<DT, PA, PT>(sA, sA, sT, g4, c16);
+    __syncthreads();
+    // T, P -> workspace as dense [64][64] rows
+    {
+        constexpr int PPR = kC / EPP;
+        DT *gT = reinterpret_cast<DT *>(rec);
+        DT *gP = gT + kC * kC;
+        for (int i = tid; i < kC * PPR; i += 256) {
+            const int r = i / PPR, pc = i % PPR;
+            *reinterpret_cast<u32x4 *>(gT + r * kC + pc * EPP) =
+                *reinterpret_cast<const u32x4 *>(sT + r * PT + pc * EPP);
+            *reinterpret_cast<u32x4 *>(gP + r * kC + pc * EPP) =
+                *reinterpret_cast<const u32x4 *>(sP + r * PT + pc * EPP);
+        }
+    }
+}
+
+template <typename DT, int D, int NC, int DVW> struct ChainCfg {
+    using P = ChunkPitch<DT, D>;
+    static constexpr int NTH = 256;
+    static constexpr int DVS = NC * DVW;
+    static constexpr int PV = DVS + 4;
+    static constexpr int SZ_K = kC * P::PK * (int)sizeof(DT);
+    static constexpr int SZ_KT = P::BF ? D * P::PT * 2 : 0;
+    static constexpr int SZ_V = P::BF ? DVS * P::PT * 2 : kC * PV * 4;
+    static constexpr int SZ_T = kC * P::PT * (int)sizeof(DT);
+    static constexpr int OFF_K = 0;
+    static constexpr int OFF_Q = OFF_K + SZ_K;
+    static constexpr int OFF_KT = OFF_Q + SZ_K;
+    static constexpr int OFF_V = OFF_KT + SZ_KT;
+    static constexpr int OFF_T = OFF_V + SZ_V;
+    static constexpr int OFF_P = OFF_T + SZ_T;
+    static constexpr int OFF_VEC = OFF_P + SZ_T;  // gamma, dec, beta
+    static constexpr int LDS = OFF_VEC + 3 * kC * 4;
+    // T and P pieces (16 bytes) per thread, decay-vector pieces
+    static constexpr int EPP = 16 / (int)sizeof(DT);
+    static constexpr int TP_PIECES = kC * kC / EPP;
+    static constexpr int NTP = (TP_PIECES + NTH - 1) / NTH;
+    static constexpr int VEC_PIECES = 3 * kC / 4;
+    static_assert(NC >= 1 && NC <= 4 && DVW % 16 == 0, "chain waves");
+    static_assert(LDS <= 160 * 1024, "LDS budget of a gfx950 CU");
+};
+
+// One workgroup (4 waves) per (sequence, value head, slice of DVS columns);
+// waves 0..NC-1 own DVW columns each and run the state chain, all four waves
+// stage the next chunk.
+template <typename DT, int D, int NC, int DVW>
+__global__ __launch_bounds__(256) void chain_kernel(PrefillParams p, const unsigned char *ws,
+                                                    int nsplit, int remap_xcd) {
+    using Cf = ChainCfg<DT, D, NC, DVW>;
+    using Pi = ChunkPitch<DT, D>;
+    constexpr int NKT = D / 16, NB = DVW / 16, KS = D / 32;
+    constexpr int PK = Pi::PK, PT = Pi::PT, PV = Cf::PV, EPP = Cf::EPP;
+    constexpr int WSB = ws_bytes_per_chunk<DT>();
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::LDS];
+    DT *sK = reinterpret_cast<DT *>(smem + Cf::OFF_K);
+    DT *sQ = reinterpret_cast<DT *>(smem + Cf::OFF_Q);
+    DT *sKT = reinterpret_cast<DT *>(smem + Cf::OFF_KT);
+    DT *sV = reinterpret_cast<DT *>(smem + Cf::OFF_V);
+    DT *sT = reinterpret_cast<DT *>(smem + Cf::OFF_T);
+    DT *sP = reinterpret_cast<DT *>(smem + Cf::OFF_P);
+    float *sVec = reinterpret_cast<float *>(smem + Cf::OFF_VEC);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g4 = lane >> 4;
+    const int c16 = lane & 15;
+
+    const int wg = logical_wg(remap_xcd);
+    const int slice = wg % nsplit;
+    const int nh = wg / nsplit;
+    const int h = nh % p.Hv;
+    const int n = nh / p.Hv;
+    const int grp = h / (p.Hv / p.Hk);
+    int64_t tok0, len;
+    seq_bounds(p, n, tok0, len);
+    const int dv0 = slice * Cf::DVS;
+    const int wdv = (wave < NC ? wave : 0) * DVW;
+    const int64_t base = slot_base(p, n);
+
+    const int64_t sQK = (int64_t)p.Hk * D;
+    const int64_t sVO = (int64_t)p.Hv * D;
+    const DT *qh = reinterpret_cast<const DT *>(p.q) + tok0 * sQK + (int64_t)grp * D;
+    const DT *kh = reinterpret_cast<const DT *>(p.k) + tok0 * sQK + (int64_t)grp * D;
+    const DT *vh = reinterpret_cast<const DT *>(p.v) + tok0 * sVO + (int64_t)h * D + dv0;
+    DT *oh = reinterpret_cast<DT *>(p.out) + tok0 * sVO + (int64_t)h * D + dv0 + wdv;
+
+    f32x4 st[NKT][NB];
+    {
+        const float *s0 = p.s0 && wave < NC ? p.s0 + ((int64_t)n * p.Hv + h) * D * D : nullptr;
+#pragma unroll
+        for (int a = 0; a < NKT; ++a)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                st[a][b] = s0 ? *reinterpret_cast<const f32x4 *>(
+                                    s0 + (int64_t)(dv0 + wdv + 16 * b + c16) * D + 16 * a + 4 * g4)
+                              : zero4();
+    }
+
+    Stager<DT, D, 256, Cf::DVS> sg;
+    sg.init(tid);
+    u32x4 rT[Cf::NTP], rP[Cf::NTP], rVec = {0u, 0u, 0u, 0u};
+    auto load_chunk = [&](int64_t c) {
+        const int64_t t0 = c * kC;
+        const int lenc = (int)((len - t0) < kC ? (len - t0) : kC);
+        sg.load(kh, qh, vh, t0, lenc, sQK, sVO, tid);
+        const unsigned char *rec = ws + ((base + c) * p.Hv + h) * (int64_t)WSB;
+#pragma unroll
+        for (int i = 0; i < Cf::NTP; ++i) {
+            const int pc = tid + i * 256;
+            if (Cf::TP_PIECES % 256 == 0 || pc < Cf::TP_PIECES) {
+                rT[i] = reinterpret_cast<const u32x4 *>(rec)[pc];
+                rP[i] = reinterpret_cast<const u32x4 *>(rec + kC * kC * sizeof(DT))[pc];
+            }
+        }
+        if (tid < Cf::VEC_PIECES)
+            rVec = reinterpret_cast<const u32x4 *>(rec + 2 * kC * kC * sizeof(DT))[tid];
+    };
+
+    const int64_t nchunks = (len + kC - 1) / kC;
+    if (nchunks > 0) load_chunk(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): see prefill_kernel
+
+    for (int64_t c = 0; c < nchunks; ++c) {
+        const int lenc = (int)((len - c * kC) < kC ? (len - c * kC) : kC);
+        __syncthreads();  // the previous chunk is done with LDS
+        sg.store(sK, sQ, sKT, sV, lenc, tid);
+#pragma unroll
+        for (int i = 0; i < Cf::NTP; ++i) {
+            const int pc = tid + i * 256;
+            if (Cf::TP_PIECES % 256 == 0 || pc < Cf::TP_PIECES) {
+                const int r = pc / (kC / EPP), col = (pc % (kC / EPP)) * EPP;
+                *reinterpret_cast<u32x4 *>(sT + r * PT + col) = rT[i];
+                *reinterpret_cast<u32x4 *>(sP + r * PT + col) = rP[i];
+            }
+        }
+        if (tid < Cf::VEC_PIECES) reinterpret_cast<u32x4 *>(sVec)[tid] = rVec;
+        if (c + 1 < nchunks) load_chunk(c + 1);
+        __syncthreads();
+
+        if (wave < NC) {
+            const ChainSmem<DT> m{sK, sQ, sKT, sV, sT, sP, sVec, sVec + kC, sVec + 2 * kC};
+            Frag<DT> sf[KS][NB];
+            f32x4 racc[4][NB], oT[4][NB];
+            chain_state_half<DT, D, NB, PK>(m, st, sf, racc, oT, g4, c16);
+            chain_finish<DT, D, NB, PK, PT, PV>(m, st, racc, oT, wdv, oh + c * kC * sVO, sVO, lenc,
+                                                p.scale, g4, c16);
+        }
+    }
+
+    if (p.s_final && wave < NC) {
+        float *sf = p.s_final + ((int64_t)n * p.Hv + h) * D * D;
+#pragma unroll
+        for (int a = 0; a < NKT; ++a)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                *reinterpret_cast<f32x4 *>(sf + (int64_t)(dv0 + wdv + 16 * b + c16) * D + 16 * a +
+                                           4 * g4) = st[a][b];
+    }
+}
+
+// Double-buffered variant (bf16): waves 0..NC-1 run the state chain on chunk
+// c from one LDS buffer while the helper waves NC..3 load chunk c+1 and write
+// it into the other buffer. One barrier per chunk; the chain waves never
+// stage.
+template <typename DT, int D, int NC, int DVW> struct ChainDbCfg {
+    using P = ChunkPitch<DT, D>;
+    static constexpr int NH = 4 - NC;  // helper waves
+    static constexpr int NTHH = NH * 64;
+    static constexpr int DVS = NC * DVW;
+    static constexpr int PV = DVS + 4;
+    static constexpr int SZ_K = kC * P::PK * (int)sizeof(DT);
+    static constexpr int SZ_KT = P::BF ? D * P::PT * 2 : 0;
+    static constexpr int SZ_V = P::BF ? DVS * P::PT * 2 : kC * PV * 4;
+    static constexpr int SZ_T = kC * P::PT * (int)sizeof(DT);
+    static constexpr int OFF_K = 0;
+    static constexpr int OFF_Q = OFF_K + SZ_K;
+    static constexpr int OFF_KT = OFF_Q + SZ_K;
+    static constexpr int OFF_V = OFF_KT + SZ_KT;
+    static constexpr int OFF_T = OFF_V + SZ_V;
+    static constexpr int OFF_P = OFF_T + SZ_T;
+    static constexpr int OFF_VEC = OFF_P + SZ_T;
+    static constexpr int BUF = OFF_VEC + 3 * kC * 4;  // one buffer
+    static constexpr int LDS = 2 * BUF;
+    static constexpr int EPP = 16 / (int)sizeof(DT);
+    static constexpr int TP_PIECES = kC * kC / EPP;
+    static constexpr int NTP = (TP_PIECES + NTHH - 1) / NTHH;
+    static constexpr int VEC_PIECES = 3 * kC / 4;
+    static constexpr int NVP = (VEC_PIECES + NTHH - 1) / NTHH;
+    static_assert(NC >= 1 && NC <= 3 && DVW % 16 == 0, "chain waves");
+    static_assert(LDS <= 160 * 1024, "LDS budget of a gfx950 CU");
+};
+
+template <typename DT, int D, int NC, int DVW>
+__global__ __launch_bounds__(256) void chain_db_kernel(PrefillParams p, const unsigned char *ws,
+                                                       int nsplit, int remap_xcd) {
+    using Cf = ChainDbCfg<DT, D, NC, DVW>;
+    using Pi = ChunkPitch<DT, D>;
+    constexpr int NKT = D / 16, NB = DVW / 16, KS = D / 32;
+    constexpr int PK = Pi::PK, PT = Pi::PT, PV = Cf::PV, EPP = Cf::EPP, NTHH = Cf::NTHH;
+    constexpr int WSB = ws_bytes_per_chunk<DT>();
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::LDS];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g4 = lane >> 4;
+    const int c16 = lane & 15;
+    const bool chain = wave < NC;
+    const int htid = tid - NC * 64;  // helper thread index (valid when !chain)
+
+    const int wg = logical_wg(remap_xcd);
+    const int slice = wg % nsplit;
+    const int nh = wg / nsplit;
+    const int h = nh % p.Hv;
+    const int n = nh / p.Hv;
+    const int grp = h / (p.Hv / p.Hk);
+    int64_t tok0, len;
+    seq_bounds(p, n, tok0, len);
+    const int dv0 = slice * Cf::DVS;
+    const int wdv = (chain ? wave : 0) * DVW;
+    const int64_t base = slot_base(p, n);
+
+    const int64_t sQK = (int64_t)p.Hk * D;
+    const int64_t sVO = (int64_t)p.Hv * D;
+    const DT *qh = reinterpret_cast<const DT *>(p.q) + tok0 * sQK + (int64_t)grp * D;
+    const DT *kh = reinterpret_cast<const DT *>(p.k) + tok0 * sQK + (int64_t)grp * D;
+    const DT *vh = reinterpret_cast<const DT *>(p.v) + tok0 * sVO + (int64_t)h * D + dv0;
+    DT *oh = reinterpret_cast<DT *>(p.out) + tok0 * sVO + (int64_t)h * D + dv0 + wdv;
+    const int64_t nchunks = (len + kC - 1) / kC;
+
+    f32x4 st[NKT][NB];
+    {
+        const float *s0 = p.s0 && chain ? p.s0 + ((int64_t)n * p.Hv + h) * D * D : nullptr;
+#pragma unroll
+        for (int a = 0; a < NKT; ++a)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                st[a][b] = s0 ? *reinterpret_cast<const f32x4 *>(
+                                    s0 + (int64_t)(dv0 + wdv + 16 * b + c16) * D + 16 * a + 4 * g4)
+                              : zero4();
+    }
+
+    // helper-side staging state
+    Stager<DT, D, NTHH, Cf::DVS> sg;
+    u32x4 rT[Cf::NTP], rP[Cf::NTP], rVec[Cf::NVP];
+    auto load_chunk = [&](int64_t c) {
+        const int64_t t0 = c * kC;
+        const int lenc = (int)((len - t0) < kC ? (len - t0) : kC);
+        sg.load(kh, qh, vh, t0, lenc, sQK, sVO, htid);
+        const unsigned char *rec = ws + ((base + c) * p.Hv + h) * (int64_t)WSB;
+#pragma unroll
+        for (int i = 0; i < Cf::NTP; ++i) {
+            const int pc = htid + i * NTHH;
+            if (Cf::TP_PIECES % NTHH == 0 || pc < Cf::TP_PIECES) {
+                rT[i] = reinterpret_cast<const u32x4 *>(rec)[pc];
+                rP[i] = reinterpret_cast<const u32x4 *>(rec + kC * kC * sizeof(DT))[pc];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < Cf::NVP; ++i) {
+            const int pc = htid + i * NTHH;
+            if (pc < Cf::VEC_PIECES)
+                rVec[i] = reinterpret_cast<const u32x4 *>(rec + 2 * kC * kC * sizeof(DT))[pc];
+        }
+    };
+    auto store_chunk = [&](int64_t c) {
+        unsigned char *b = smem + (c & 1) * Cf::BUF;
+        const int lenc = (int)((len - c * kC) < kC ? (len - c * kC) : kC);
+        sg.store(reinterpret_cast<DT *>(b + Cf::OFF_K), reinterpret_cast<DT *>(b + Cf::OFF_Q),
+                 reinterpret_cast<DT *>(b + Cf::OFF_KT), reinterpret_cast<DT *>(b + Cf::OFF_V), lenc,
+                 htid);
+        DT *sT = reinterpret_cast<DT *>(b + Cf::OFF_T);
+        DT *sP = reinterpret_cast<DT *>(b + Cf::OFF_P);
+#pragma unroll
+        for (int i = 0; i < Cf::NTP; ++i) {
+            const int pc = htid + i * NTHH;
+            if (Cf::TP_PIECES % NTHH == 0 || pc < Cf::TP_PIECES) {
+                const int r = pc / (kC / EPP), col = (pc % (kC / EPP)) * EPP;
+                *reinterpret_cast<u32x4 *>(sT + r * PT + col) = rT[i];
+                *reinterpret_cast<u32x4 *>(sP + r * PT + col) = rP[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < Cf::NVP; ++i) {
+            const int pc = htid + i * NTHH;
+            if (pc < Cf::VEC_PIECES) reinterpret_cast<u32x4 *>(b + Cf::OFF_VEC)[pc] = rVec[i];
+        }
+    };
+
+    if (!chain) {
+        sg.init(htid);
+        if (nchunks > 0) {
+            load_chunk(0);
+            store_chunk(0);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): initial state; see prefill_kernel
+    __syncthreads();
+
+    for (int64_t c = 0; c < nchunks; ++c) {
+        if (chain) {
+            const unsigned char *b = smem + (c & 1) * Cf::BUF;
+            const float *vec = reinterpret_cast<const float *>(b + Cf::OFF_VEC);
+            const ChainSmem<DT> m{reinterpret_cast<const DT *>(b + Cf::OFF_K),
+                                  reinterpret_cast<const DT *>(b + Cf::OFF_Q),
+                                  reinterpret_cast<const DT *>(b + Cf::OFF_KT),
+                                  reinterpret_cast<const DT *>(b + Cf::OFF_V),
+                                  reinterpret_cast<const DT *>(b + Cf::OFF_T),
+                                  reinterpret_cast<const DT *>(b + Cf::OFF_P),
+                                  vec, vec + kC, vec + 2 * kC};
+            const int lenc = (int)((len - c * kC) < kC ? (len - c * kC) : kC);
+            Frag<DT> sf[KS][NB];
+            f32x4 racc[4][NB], oT[4][NB];
+            chain_state_half<DT, D, NB, PK, false>(m, st, sf, racc, oT, g4, c16);
+            chain_finish<DT, D, NB, PK, PT, PV>(m, st, racc, oT, wdv, oh + c * kC * sVO, sVO, lenc,
+                                                p.scale, g4, c16);
+        } else if (c + 1 < nchunks) {
+            // load and store within the iteration: no staging registers stay
+            // live across the loop, so they do not add to the chain waves'
+            // register budget (the chain's state would otherwise move to
+            // AGPRs and every elementwise step would shuffle it)
+            load_chunk(c + 1);
+            store_chunk(c + 1);
+        }
+        __syncthreads();
+    }
+
+    if (p.s_final && chain) {
+        float *sf = p.s_final + ((int64_t)n * p.Hv + h) * D * D;
+#pragma unroll
+        for (int a = 0; a < NKT; ++a)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                *reinterpret_cast<f32x4 *>(sf + (int64_t)(dv0 + wdv + 16 * b + c16) * D + 16 * a +
+                                           4 * g4) = st[a][b];
+    }
+}
+
+// ----------------------------------------------------------------------------
+// launch
+
 template <typename DT, int D, int NW, int DVW>
-static hipError_t launch_cfg(const PrefillParams &p, int nsplit, hipStream_t stream) {
+static hipError_t launch_fused(const PrefillParams &p, int nsplit, hipStream_t stream) {
     const int64_t nblocks = (int64_t)p.nseq * p.Hv * nsplit;
     if (nblocks <= 0 || nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    const int remap = (nblocks % 8 == 0) ? 1 : 0;
     hipLaunchKernelGGL((prefill_kernel<DT, D, NW, DVW>), dim3((unsigned)nblocks), dim3(NW * 64), 0,
-                       stream, p, nsplit, remap);
+                       stream, p, nsplit, nblocks % 8 == 0 ? 1 : 0);
     return hipGetLastError();
 }
 
-// Choose the value-column slice per workgroup. With many chains
-// (sequences x value heads) a workgroup takes a whole head; with few, the
-// head is split so that more CUs work (each slice repeats the small
-// state-free part of a chunk).
-static int choose_split(int64_t chains, int D, int num_cus) {
-    if (const char *env = getenv("GDN_PREFILL_NSPLIT")) {
-        const int v = atoi(env);
-        if (v == 1 || v == 2 || v == 4 || v == 8) return (D == 64 && v == 8) ? 4 : v;
-    }
-    if (chains >= num_cus) return 1;
-    if (chains * 2 >= num_cus) return 2;
-    return D == 128 ? 4 : 2;
+template <typename DT, int D, int NC, int DVW>
+static hipError_t launch_split(const PrefillParams &p, unsigned char *ws, int64_t nslots,
+                               int nsplit, hipStream_t stream) {
+    const int64_t nprep = nslots * p.Hv;
+    const int64_t nchain = (int64_t)p.nseq * p.Hv * nsplit;
+    if (nprep <= 0 || nprep > 0x7FFFFFFF || nchain <= 0 || nchain > 0x7FFFFFFF)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((prep_kernel<DT, D>), dim3((unsigned)nprep), dim3(256), 0, stream, p, ws,
+                       nprep % 8 == 0 ? 1 : 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((chain_kernel<DT, D, NC, DVW>), dim3((unsigned)nchain), dim3(256), 0, stream,
+                       p, (const unsigned char *)ws, nsplit, nchain % 8 == 0 ? 1 : 0);
+    return hipGetLastError();
 }
 
-hipError_t launch_prefill(const PrefillParams &p, int dtype, int D, int num_cus,
-                          hipStream_t stream) {
-    int ns = choose_split((int64_t)p.nseq * p.Hv, D, num_cus);
+template <typename DT, int D, int NC, int DVW>
+static hipError_t launch_split_db(const PrefillParams &p, unsigned char *ws, int64_t nslots,
+                                  int nsplit, hipStream_t stream) {
+    const int64_t nprep = nslots * p.Hv;
+    const int64_t nchain = (int64_t)p.nseq * p.Hv * nsplit;
+    if (nprep <= 0 || nprep > 0x7FFFFFFF || nchain <= 0 || nchain > 0x7FFFFFFF)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((prep_kernel<DT, D>), dim3((unsigned)nprep), dim3(256), 0, stream, p, ws,
+                       nprep % 8 == 0 ? 1 : 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((chain_db_kernel<DT, D, NC, DVW>), dim3((unsigned)nchain), dim3(256), 0,
+                       stream, p, (const unsigned char *)ws, nsplit, nchain % 8 == 0 ? 1 : 0);
+    return hipGetLastError();
+}
+
+int64_t prefill_ws_slots(int64_t nseq, int64_t total_tokens, int64_t seq_len, bool packed) {
+    if (!packed) return nseq * ((seq_len + kC - 1) / kC);
+    return (total_tokens + kC - 1) / kC + nseq;
+}
+
+size_t prefill_ws_bytes(int64_t slots, int Hv, int dtype) {
+    const int per = dtype == 1 ? ws_bytes_per_chunk<__bf16>() : ws_bytes_per_chunk<float>();
+    return (size_t)slots * (size_t)Hv * (size_t)per;
+}
+
+static int env_int(const char *name, int dflt) {
+    const char *e = getenv(name);
+    return e ? atoi(e) : dflt;
+}
+
+// The two-pass path pays off when there are too few (sequence, value head)
+// chains to fill the chip with one workgroup each. GDN_PREFILL_PATH=fused or
+// =split overrides the choice (for tuning).
+bool prefill_wants_workspace(int64_t chains, int num_cus) {
+    const char *e = getenv("GDN_PREFILL_PATH");
+    if (e && e[0] == 'f') return false;
+    if (e && e[0] == 's') return true;
+    return chains < 2 * (int64_t)num_cus;
+}
+
+static int pow2_floor(int v) {
+    int r = 1;
+    while (r * 2 <= v) r *= 2;
+    return r;
+}
+
+hipError_t launch_prefill(const PrefillParams &p, int dtype, int D, int num_cus, void *ws,
+                          size_t ws_bytes, int64_t nslots, hipStream_t stream) {
+    const int64_t chains = (int64_t)p.nseq * p.Hv;
+    const bool split = ws != nullptr && nslots > 0 &&
+                       ws_bytes >= prefill_ws_bytes(nslots, p.Hv, dtype) &&
+                       prefill_wants_workspace(chains, num_cus);
+    if (split) {
+        // Value-column slices per head: about one workgroup per CU (the
+        // double-buffered chain kernel fills a CU's LDS), at most four.
+        int ns = env_int("GDN_PREFILL_NSPLIT", 0);
+        if (ns != 1 && ns != 2 && ns != 4 && ns != 8) {
+            const int64_t want = (int64_t)num_cus / (chains > 0 ? chains : 1);
+            ns = pow2_floor((int)(want < 4 ? (want < 1 ? 1 : want) : 4));
+        }
+        unsigned char *w = static_cast<unsigned char *>(ws);
+        if (dtype == 1 && D == 128) {
+            switch (ns) {
+            case 1: return launch_split<__bf16, 128, 4, 32>(p, w, nslots, 1, stream);
+            case 2: return launch_split_db<__bf16, 128, 2, 32>(p, w, nslots, 2, stream);
+            case 4: return launch_split_db<__bf16, 128, 2, 16>(p, w, nslots, 4, stream);
+            default: return launch_split_db<__bf16, 128, 1, 16>(p, w, nslots, 8, stream);
+            }
+        } else if (dtype == 1 && D == 64) {
+            switch (ns) {
+            case 1: return launch_split_db<__bf16, 64, 2, 32>(p, w, nslots, 1, stream);
+            case 2: return launch_split_db<__bf16, 64, 2, 16>(p, w, nslots, 2, stream);
+            default: return launch_split_db<__bf16, 64, 1, 16>(p, w, nslots, 4, stream);
+            }
+        } else if (dtype == 0 && D == 64) {
+            switch (ns) {
+            case 1: return launch_split<float, 64, 4, 16>(p, w, nslots, 1, stream);
+            case 2: return launch_split<float, 64, 2, 16>(p, w, nslots, 2, stream);
+            default: return launch_split<float, 64, 1, 16>(p, w, nslots, 4, stream);
+            }
+        } else if (dtype == 0 && D == 128) {
+            switch (ns) {
+            case 1:
+            case 2: return launch_split<float, 128, 4, 16>(p, w, nslots, 2, stream);
+            case 4: return launch_split<float, 128, 2, 16>(p, w, nslots, 4, stream);
+            default: return launch_split<float, 128, 1, 16>(p, w, nslots, 8, stream);
+            }
+        }
+        return hipErrorInvalidValue;
+    }
+
+    // Fused: with many chains a workgroup takes a whole head; with few, the
+    // head is split so that more CUs work.
+    int ns = env_int("GDN_PREFILL_NSPLIT", 0);
+    if (ns != 1 && ns != 2 && ns != 4 && ns != 8)
+        ns = chains >= num_cus ? 1 : chains * 2 >= num_cus ? 2 : (D == 128 ? 4 : 2);
+    if (D == 64 && ns == 8) ns = 4;
     if (dtype == 1) {
         if (D == 128) {
             switch (ns) {
-            case 1: return launch_cfg<__bf16, 128, 8, 16>(p, 1, stream);
-            case 2: return launch_cfg<__bf16, 128, 4, 16>(p, 2, stream);
-            case 4: return launch_cfg<__bf16, 128, 2, 16>(p, 4, stream);
-            default: return launch_cfg<__bf16, 128, 1, 16>(p, 8, stream);
+            case 1: return launch_fused<__bf16, 128, 8, 16>(p, 1, stream);
+            case 2: return launch_fused<__bf16, 128, 4, 16>(p, 2, stream);
+            case 4: return launch_fused<__bf16, 128, 2, 16>(p, 4, stream);
+            default: return launch_fused<__bf16, 128, 1, 16>(p, 8, stream);
             }
         } else if (D == 64) {
             switch (ns) {
-            case 1: return launch_cfg<__bf16, 64, 4, 16>(p, 1, stream);
-            case 2: return launch_cfg<__bf16, 64, 2, 16>(p, 2, stream);
-            default: return launch_cfg<__bf16, 64, 1, 16>(p, 4, stream);
+            case 1: return launch_fused<__bf16, 64, 4, 16>(p, 1, stream);
+            case 2: return launch_fused<__bf16, 64, 2, 16>(p, 2, stream);
+            default: return launch_fused<__bf16, 64, 1, 16>(p, 4, stream);
             }
         }
     } else if (dtype == 0) {
         if (D == 64) {
             switch (ns) {
-            case 1: return launch_cfg<float, 64, 4, 16>(p, 1, stream);
-            case 2: return launch_cfg<float, 64, 2, 16>(p, 2, stream);
-            default: return launch_cfg<float, 64, 1, 16>(p, 4, stream);
+            case 1: return launch_fused<float, 64, 4, 16>(p, 1, stream);
+            case 2: return launch_fused<float, 64, 2, 16>(p, 2, stream);
+            default: return launch_fused<float, 64, 1, 16>(p, 4, stream);
             }
         } else if (D == 128) {
-            // fp32 K, Q and V for a whole head exceed the LDS of a CU: at
-            // least two slices.
+            // fp32 K, Q and V of a whole head exceed a CU's LDS: two slices at least
             switch (ns) {
             case 1:
-            case 2: return launch_cfg<float, 128, 4, 16>(p, 2, stream);
-            case 4: return launch_cfg<float, 128, 2, 16>(p, 4, stream);
-            default: return launch_cfg<float, 128, 1, 16>(p, 8, stream);
+            case 2: return launch_fused<float, 128, 4, 16>(p, 2, stream);
+            case 4: return launch_fused<float, 128, 2, 16>(p, 4, stream);
+            default: return launch_fused<float, 128, 1, 16>(p, 8, stream);
             }
         }
     }

@@ -42,6 +42,7 @@
 #ifndef GDN_H_
 #define GDN_H_
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -77,6 +78,14 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype_t; /* type of q, k, v, out 
  * T == 0 writes the initial state (or zeros) to final_state.
  * The sequence is processed in chunks of 64 tokens; the result equals the
  * token recurrence up to rounding (the chunked form is an exact rewrite).
+ *
+ * workspace: optional device scratch of workspace_bytes bytes (16-byte
+ * aligned, disjoint from every other argument, contents ignored and
+ * overwritten; the caller keeps ownership). When it holds at least
+ * gdn_prefill_workspace_size() bytes the call may run in two passes: the
+ * state-independent per-chunk factors of all chunks first, then the
+ * sequential state chain. NULL (or too small) selects the single-pass
+ * kernel. Both give the same result up to rounding.
  */
 gdn_status_t gdn_prefill_chunked(const void *q, const void *k, const void *v,
                                  const float *alpha, const float *beta,
@@ -84,6 +93,7 @@ gdn_status_t gdn_prefill_chunked(const void *q, const void *k, const void *v,
                                  float *final_state, int32_t B, int64_t T,
                                  int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
                                  gdn_dtype_t dtype, float scale,
+                                 void *workspace, size_t workspace_bytes,
                                  hipStream_t stream);
 
 /*
@@ -120,7 +130,8 @@ gdn_status_t gdn_decode_step(const void *q, const void *k, const void *v,
  *   final_state   [N, Hv, Dv, Dk] fp32 or NULL; may equal initial_state
  *
  * Sizes: N >= 1, 0 <= total_T < 2^31, Hv a multiple of Hk, Dk == Dv in
- * {64, 128}. Chunks restart at every sequence boundary.
+ * {64, 128}. Chunks restart at every sequence boundary. workspace: as for
+ * gdn_prefill_chunked.
  */
 gdn_status_t gdn_varlen_prefill(const void *q, const void *k, const void *v,
                                 const float *alpha, const float *beta,
@@ -129,7 +140,25 @@ gdn_status_t gdn_varlen_prefill(const void *q, const void *k, const void *v,
                                 void *out, float *final_state, int32_t Hk,
                                 int32_t Hv, int32_t Dk, int32_t Dv,
                                 gdn_dtype_t dtype, float scale,
+                                void *workspace, size_t workspace_bytes,
                                 hipStream_t stream);
+
+/*
+ * gdn_prefill_workspace_size -- bytes of workspace the prefill calls can use.
+ *
+ *   packed = 0: gdn_prefill_chunked with num_seqs = B and tokens = T;
+ *   packed = 1: gdn_varlen_prefill with num_seqs = N and tokens = total_T.
+ *
+ * Returns 0 when the library would not use a workspace for this shape on the
+ * current device (enough (sequence, value head) pairs to fill it in one
+ * pass), when an argument is invalid, or when no device is available. The
+ * size is 17,152 bytes (bf16) or 33,536 bytes (fp32) per (64-token chunk,
+ * value head): B * ceil(T/64) chunks, or ceil(total_T/64) + N for packed
+ * batches.
+ */
+size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t tokens, int32_t Hk,
+                                  int32_t Hv, int32_t Dk, int32_t Dv,
+                                  gdn_dtype_t dtype, int32_t packed);
 
 /* Static description of a status; for GDN_ERR_HIP, the calling thread's
  * last HIP error detail. The pointer stays valid until the thread's next

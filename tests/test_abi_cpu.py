@@ -58,15 +58,15 @@ def P(i):
 
 
 def prefill(lib, q=P(0), k=P(1), v=P(2), a=P(3), b=P(4), s0=P(5), out=P(6), sf=P(7), B=1, T=64,
-            Hk=2, Hv=4, Dk=64, Dv=64, dtype=BF16):
+            Hk=2, Hv=4, Dk=64, Dv=64, dtype=BF16, ws=None, wsb=0):
     return lib.gdn_prefill_chunked(q, k, v, a, b, s0, out, sf, B, T, Hk, Hv, Dk, Dv, dtype, 1.0,
-                                   None)
+                                   ws, wsb, None)
 
 
 def varlen(lib, q=P(0), k=P(1), v=P(2), a=P(3), b=P(4), cu=P(8), N=2, total=64, s0=P(5),
-           out=P(6), sf=P(7), Hk=2, Hv=4, Dk=64, Dv=64, dtype=BF16):
+           out=P(6), sf=P(7), Hk=2, Hv=4, Dk=64, Dv=64, dtype=BF16, ws=None, wsb=0):
     return lib.gdn_varlen_prefill(q, k, v, a, b, cu, N, total, s0, out, sf, Hk, Hv, Dk, Dv, dtype,
-                                  1.0, None)
+                                  1.0, ws, wsb, None)
 
 
 def decode(lib, q=P(0), k=P(1), v=P(2), a=P(3), b=P(4), s=P(5), out=P(6), B=4, Hk=2, Hv=4,
@@ -92,6 +92,9 @@ def test_prefill_validation(lib):
     assert prefill(lib, sf=P(5) + 64) == ALIAS        # partial overlap with initial state
     assert prefill(lib, sf=P(0)) == ALIAS             # final state on top of q
     assert prefill(lib, B=1 << 30, T=1 << 30) == SHAPE  # byte counts overflow
+    assert prefill(lib, ws=P(9) + 8, wsb=1 << 20) == MISAL
+    assert prefill(lib, ws=P(6), wsb=1 << 20) == ALIAS    # workspace on top of out
+    assert prefill(lib, ws=P(7) + 4096, wsb=1 << 20) == ALIAS  # inside the final state
 
 
 def test_varlen_validation(lib):
@@ -102,6 +105,7 @@ def test_varlen_validation(lib):
     assert varlen(lib, cu=P(8) + 4) == MISAL
     assert varlen(lib, out=P(8)) == ALIAS             # out on top of cu_seqlens
     assert varlen(lib, Dk=32, Dv=32) == UNSUP
+    assert varlen(lib, ws=P(8), wsb=64) == ALIAS          # workspace on top of cu_seqlens
 
 
 def test_decode_validation(lib):
@@ -121,6 +125,13 @@ def test_valid_call_without_device_reports_hip_error(lib):
     assert prefill(lib) == HIPERR
     assert b"HIP" in lib.gdn_status_string(HIPERR)
     assert decode(lib) == HIPERR
+    assert lib.gdn_prefill_workspace_size(1, 4096, 16, 48, 128, 128, BF16, 0) == 0
+
+
+def test_workspace_size_rejects_bad_shapes(lib):
+    assert lib.gdn_prefill_workspace_size(1, 4096, 16, 47, 128, 128, BF16, 0) == 0
+    assert lib.gdn_prefill_workspace_size(0, 4096, 16, 48, 128, 128, BF16, 0) == 0
+    assert lib.gdn_prefill_workspace_size(1, 4096, 16, 48, 96, 96, BF16, 0) == 0
 
 
 def test_empty_prefill_without_final_state_is_a_no_op(lib):

@@ -73,13 +73,28 @@ SMALL = [
 
 @pytest.mark.parametrize("B,T,Hk,Hv,D,dtype,init", SMALL)
 @pytest.mark.parametrize("nsplit", ["auto", "1", "2", "4", "8"])
-def test_prefill_small(gdn, monkeypatch, B, T, Hk, Hv, D, dtype, init, nsplit):
+@pytest.mark.parametrize("path", ["fused", "split"])
+def test_prefill_small(gdn, monkeypatch, B, T, Hk, Hv, D, dtype, init, nsplit, path):
+    """Both the single-pass kernel and the two-pass (workspace) path, every
+    value-column split, against the oracle."""
+    monkeypatch.setenv("GDN_PREFILL_PATH", path)
     if nsplit != "auto":
         monkeypatch.setenv("GDN_PREFILL_NSPLIT", nsplit)
     d = small_prefill(B, T, Hk, Hv, D, dtype, seed=100 + T + D + Hv, init_state=init)
     o, S = gpu_prefill(gdn, d, scale=0.5)
     o_ref, S_ref = oracle_prefill(d, scale=0.5)
-    check(o, S, o_ref, S_ref, dtype, f"prefill B{B} T{T} Hk{Hk} Hv{Hv} D{D} {dtype} ns={nsplit}")
+    check(o, S, o_ref, S_ref, dtype,
+          f"prefill {path} B{B} T{T} Hk{Hk} Hv{Hv} D{D} {dtype} ns={nsplit}")
+
+
+def test_workspace_path_is_taken_for_small_batches(gdn):
+    """48 chains (B=1, the layer's value heads) ask for a workspace; a batch
+    with enough chains does not."""
+    n = gdn.gdn_prefill_workspace_size(1, 4096, 16, 48, 128, 128, gdn.GDN_BF16, 0)
+    assert n == 64 * 48 * (2 * 64 * 64 * 2 + 3 * 64 * 4)
+    assert gdn.gdn_prefill_workspace_size(64, 4096, 16, 48, 128, 128, gdn.GDN_BF16, 0) == 0
+    assert gdn.gdn_prefill_workspace_size(2, 130, 16, 48, 128, 128, gdn.GDN_BF16, 1) == \
+        (3 + 2) * 48 * (2 * 64 * 64 * 2 + 3 * 64 * 4)
 
 
 def test_tiny_f32_workload(gdn):
@@ -198,7 +213,9 @@ def gpu_varlen(gdn, d, use_init=True):
 
 
 @pytest.mark.parametrize("D,dtype", [(128, "bf16"), (64, "bf16"), (64, "f32")])
-def test_varlen_small(gdn, D, dtype):
+@pytest.mark.parametrize("path", ["fused", "split"])
+def test_varlen_small(gdn, monkeypatch, D, dtype, path):
+    monkeypatch.setenv("GDN_PREFILL_PATH", path)
     lengths = [5, 1, 70, 0, 129, 64, 200]
     d = generate_packed(2, 6, D, dtype, 40 + D, lengths, init_state=True)
     out, sf = gpu_varlen(gdn, d)
@@ -211,7 +228,7 @@ def test_varlen_small(gdn, D, dtype):
             continue
         e = max_error(o[cu[n]:cu[n + 1]][None], o_ref[cu[n]:cu[n + 1]][None], (0, 2))
         assert e <= TOL[dtype], (n, e)
-    check(o[:0], from_torch(sf), o_ref[:0], S_ref, dtype, f"varlen D{D} {dtype} states")
+    check(o[:0], from_torch(sf), o_ref[:0], S_ref, dtype, f"varlen {path} D{D} {dtype} states")
 
 
 def test_varlen_matches_per_sequence_prefill(gdn):
@@ -262,7 +279,10 @@ def test_long_prefill_256k_workload_sampled(gdn):
 
 
 @pytest.mark.slow
-def test_varlen_64seq_workload_sampled(gdn):
+@pytest.mark.parametrize("path", ["auto", "split"])
+def test_varlen_64seq_workload_sampled(gdn, monkeypatch, path):
+    if path != "auto":
+        monkeypatch.setenv("GDN_PREFILL_PATH", path)
     w = WORKLOADS["varlen_64seq"]
     d = generate(w)
     out, sf = gpu_varlen(gdn, d)
@@ -271,7 +291,7 @@ def test_varlen_64seq_workload_sampled(gdn):
     order = np.argsort(L)
     chains = [(int(order[-1]), 0), (int(order[0]), 47), (int(order[len(L) // 2]), 17),
               (5, 30)]
-    _chains_check(d, out, sf, chains, d["cu_seqlens"], w.name)
+    _chains_check(d, out, sf, chains, d["cu_seqlens"], f"{w.name} ({path})")
 
 
 def test_slow_decay_stress_diagnostic(gdn):
