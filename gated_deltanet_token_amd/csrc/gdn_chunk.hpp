@@ -149,14 +149,93 @@ __device__ __forceinline__ void mask_pair(const f32x4 &gk, const f32x4 &gq, int 
     }
 }
 
-// T = (I + A)^{-1} for one wave. A: fp32 rows (pitch PA), strictly lower.
-// E: fp32 scratch for the diagonal-block inverses (may be A itself: each
-// diagonal block is read in full before it is overwritten). Writes T to
-// sT (operand type, pitch PT); blocks above the diagonal are not written.
-//   diagonal blocks E_b = (I + A_bb)^{-1}: lane = 16 b + column, forward
-//   substitution four rows at a time (a batch's rows are read first);
-//   block rows 1..3: T_ij = -E_i sum_{m=j}^{i-1} A_im T_mj on MFMA, with the
-//   finished off-diagonal blocks kept in registers.
+// T = (I + A)^{-1}, A strictly lower triangular (fp32 rows, pitch PA), in 16x16
+// blocks. T is written to sT (operand type, pitch PT); blocks above the
+// diagonal are not written.
+//   diagonal blocks E_b = (I + A_bb)^{-1} (solve_diag_blocks, one wave):
+//   lane = 16 b + column, forward substitution four rows at a time (a batch's
+//   rows are read first). E goes to sE (may be A itself: each diagonal block
+//   is read in full before it is overwritten) and to the diagonal of T.
+//   below the diagonal (solve_column, one wave per block column j):
+//   T_ij = -E_i sum_{m=j}^{i-1} A_im T_mj for i = j+1 .. 3 on MFMA. A column
+//   needs only its own earlier blocks, so the three columns can run on three
+//   waves at once; the finished blocks stay in registers.
+template <typename DT, int PA, int PT>
+__device__ __forceinline__ void solve_diag_blocks(const float *sA, float *sE, DT *sT, int g4, int c16) {
+    const int blk = g4, col = c16;
+    const float *ab = sA + (16 * blk) * PA + 16 * blk;
+    float x[16];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+        f32x4 arow[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int m4 = 0; m4 <= rb; ++m4)
+                arow[i][m4] = *reinterpret_cast<const f32x4 *>(ab + (4 * rb + i) * PA + 4 * m4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * rb + i;
+            float acc = r == col ? 1.f : 0.f;
+#pragma unroll
+            for (int m = 0; m < r; ++m) acc -= arow[i][m >> 2][m & 3] * x[m];
+            x[r] = acc;
+        }
+    }
+    float *eb = sE + (16 * blk) * PA + 16 * blk + col;
+    DT *tb = sT + (16 * blk) * PT + 16 * blk + col;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        eb[r * PA] = x[r];
+        tb[r * PT] = from_f32<DT>(x[r]);
+    }
+}
+
+template <typename DT, int PA, int PT>
+__device__ __forceinline__ void solve_column(const float *sA, const float *sE, DT *sT, int j, int g4,
+                                             int c16) {
+    f32x4 Tc[4];  // finished blocks T_mj of this column (C layout)
+    float ecol[4];  // column of E_j as a B operand (k = 4 g4 + e)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ecol[e] = sE[(16 * j + 4 * g4 + e) * PA + 16 * j + c16];
+#pragma unroll
+    for (int ti = 1; ti < 4; ++ti) {
+        if (ti <= j) continue;
+        f32x4 aim[3];
+#pragma unroll
+        for (int m = 0; m < ti; ++m)
+            if (m >= j) aim[m] = *reinterpret_cast<const f32x4 *>(sA + (16 * ti + c16) * PA + 16 * m + 4 * g4);
+        const f32x4 ev = *reinterpret_cast<const f32x4 *>(sE + (16 * ti + c16) * PA + 16 * ti + 4 * g4);
+        f32x4 X = zero4();
+#pragma unroll
+        for (int m = 0; m < ti; ++m) {
+            if (m < j) continue;
+            float a4[4], b4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a4[e] = aim[m][e];
+                b4[e] = m == j ? ecol[e] : Tc[m][e];
+            }
+            X = mma_k16(a4, b4, X, DT{});
+        }
+        float a4[4], b4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            a4[e] = ev[e];
+            b4[e] = X[e];
+        }
+        const f32x4 Y = mma_k16(a4, b4, zero4(), DT{});
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Tc[ti][r] = -Y[r];
+        DT *tb = sT + (16 * ti + 4 * g4) * PT + 16 * j + c16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tb[r * PT] = from_f32<DT>(-Y[r]);
+    }
+}
+
+// The whole solve on one wave (same arithmetic as solve_diag_blocks followed
+// by solve_column for j = 0, 1, 2, scheduled by block row so that the
+// finished off-diagonal blocks of every column stay in registers).
 template <typename DT, int PA, int PT>
 __device__ __forceinline__ void solve_unit_lower(const float *sA, float *sE, DT *sT, int g4, int c16) {
     {
@@ -442,6 +521,287 @@ __device__ __forceinline__ void chain_finish(const ChainSmem<DT> &m, f32x4 (&st)
             for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
                 for (int b = 0; b < NB; ++b) st[a][b] = mma(fkt[a - a0][k2], fu[k2][b], st[a][b]);
+        }
+    }
+}
+
+// One whole chunk of the state chain for one wave with bf16 operands, for a
+// wave that does nothing else (its LDS buffer is filled by other waves).
+// Same arithmetic as chain_state_half + chain_finish; the difference is the
+// schedule: every LDS read is issued one phase before the MFMAs that consume
+// it (K, Q two k steps ahead; T during the state products; P, V and the
+// decay vectors before R; K^T before U), so that the wave, which runs alone
+// on its SIMD, rarely waits on LDS latency.
+// ----------------------------------------------------------------------------
+// Two-pass chain with bf16 operands: the state chain and the output are split
+// between a "chain" wave and an "output" wave that own the same 16*NB value
+// columns. Per chunk the chain wave forms K S^T, R, U = T R and the state
+// update (the sequential part); the output wave forms O^T = S Q^T diag(gamma)
+// + U^T P^T from the chain wave's S^T and U, handed over through LDS.
+
+// Keeps the instruction scheduler from moving anything across this point:
+// the reads issued before it stay ahead of the MFMAs that follow, however
+// the scheduler weighs register pressure.
+__device__ __forceinline__ void phase_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read of 4 bf16 per lane (ds_read_b64_tr_b16). Within each
+// group of 16 lanes, lane i receives element i % 4 of the 8-byte chunks
+// addressed by lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 of its group
+// (in that order). If lane s of a group points at row r0 + s / 4, columns
+// c0 + 4 (s % 4) .. +3 of a row-major tile, lane i receives column c0 + i of
+// rows r0 .. r0 + 3: a column read of a row-major tile.
+__device__ __forceinline__ bf16x4 ld_tr(const __bf16 *p) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4 *)(const_cast<__bf16 *>(p)));
+    return __builtin_bit_cast(bf16x4, v);
+}
+
+// A fragment (chain assignment) of K^T for rows 16 a .. 16 a + 15 of K^T (dk)
+// and the 32 tokens of block k2, read from row-major K (pitch PK).
+template <int PK>
+__device__ __forceinline__ void ld_kt_frag(const __bf16 *K, int a, int k2, int g4, int c16,
+                                           bf16x8 &f) {
+    const __bf16 *p = K + (32 * k2 + 4 * g4 + (c16 >> 2)) * PK + 16 * a + 4 * (c16 & 3);
+    const bf16x4 lo = ld_tr(p), hi = ld_tr(p + 16 * PK);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f[e] = lo[e];
+        f[e + 4] = hi[e];
+    }
+}
+
+// LDS handoff from a chain wave to its output wave: S^T fragments and U
+// fragments in lane order (each lane reads back what the same lane wrote).
+template <int D, int NB> struct Handoff {
+    static constexpr int KS = D / 32;
+    static constexpr int BYTES = (KS + 2) * NB * 64 * 16;
+    bf16x8 *sf, *fu;  // [KS][NB][64], [2][NB][64]
+    __device__ __forceinline__ Handoff(unsigned char *base)
+        : sf(reinterpret_cast<bf16x8 *>(base)),
+          fu(reinterpret_cast<bf16x8 *>(base) + KS * NB * 64) {}
+};
+
+// Bounded wait for a workgroup-local flag (an int in LDS) to reach `target`.
+// The writer is another wave of the same workgroup, which is always resident,
+// so the wait ends; the bound only guarantees that a wrong flag protocol
+// cannot hang the device.
+__device__ __forceinline__ void wait_flag(int *flag, int target) {
+    for (int spin = 0; spin < (1 << 20); ++spin) {
+        if (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target)
+            return;
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+__device__ __forceinline__ void set_flag(int *flag, int v) {
+    __hip_atomic_store(flag, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Chain wave, one chunk. LDS: K, Q row-major (pitch PK), V row-major with the
+// workgroup's value columns (pitch PV), T (pitch PT), decay vectors. Publishes
+// S^T (flag value 2c + 1) and U (2c + 2) for the output wave, then updates S.
+// KT_LATE: read the second half of the K^T fragments only after U (fewer
+// live registers, for workgroups with three waves per SIMD).
+template <int D, int NB, int PK, int PT, int PV, bool KT_LATE = false>
+__device__ __forceinline__ void chain_core_bf16(const ChainSmem<__bf16> &m, f32x4 (&st)[D / 16][NB],
+                                                int wdv, Handoff<D, NB> ho, int *flag, int c, int g4,
+                                                int c16, int lane) {
+    using F = bf16x8;
+    constexpr int KS = D / 32;
+    constexpr int NKT = D / 16;
+    // S^T as B fragments, published first
+    F sf[KS][NB];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            c_to_frag(st[2 * kk][b], st[2 * kk + 1][b], sf[kk][b]);
+            ho.sf[(kk * NB + b) * 64 + lane] = sf[kk][b];
+        }
+    set_flag(flag, 2 * c + 1);
+    // operands of K S^T and of U = T R first
+    const __bf16 *kp = m.K + c16 * PK + 4 * g4;
+    F fk[KS][4], ft[6], fkt[NKT][2];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) ld_chain(kp + 16 * mt * PK + 32 * kk, fk[kk][mt]);
+    ld_chain(m.T + c16 * PT + 4 * g4, ft[0]);
+    ld_chain(m.T + (16 + c16) * PT + 4 * g4, ft[1]);
+    ld_chain(m.T + (32 + c16) * PT + 4 * g4, ft[2]);
+    ld_chain(m.T + (32 + c16) * PT + 32 + 4 * g4, ft[3]);
+    ld_chain(m.T + (48 + c16) * PT + 4 * g4, ft[4]);
+    ld_chain(m.T + (48 + c16) * PT + 32 + 4 * g4, ft[5]);
+    phase_fence();
+    // K S^T; meanwhile the operands of R and of the state update are read
+    f32x4 racc[4][NB];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) racc[mt][b] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) racc[mt][b] = mma(fk[kk][mt], sf[kk][b], racc[mt][b]);
+    bf16x4 v4[4][NB];
+    f32x4 bet[4], gam[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        const int tb = 16 * mt + 4 * g4;
+        bet[mt] = *reinterpret_cast<const f32x4 *>(m.beta + tb);
+        gam[mt] = *reinterpret_cast<const f32x4 *>(m.gam + tb);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            v4[mt][b] = ld_tr(m.V + (16 * mt + 4 * g4 + (c16 >> 2)) * PV + wdv + 16 * b +
+                              4 * (c16 & 3));
+    }
+#pragma unroll
+    for (int a = 0; a < (KT_LATE ? NKT / 2 : NKT); ++a)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) ld_kt_frag<PK>(m.K, a, k2, g4, c16, fkt[a][k2]);
+    phase_fence();
+    // R = beta (V - gamma K S^T), U = T R
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                racc[mt][b][r] = bet[mt][r] * ((float)v4[mt][b][r] - gam[mt][r] * racc[mt][b][r]);
+    F fr[2][NB];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) c_to_frag(racc[2 * k2][b], racc[2 * k2 + 1][b], fr[k2][b]);
+    f32x4 u[4][NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        u[0][b] = mma(ft[0], fr[0][b], zero4());
+        u[1][b] = mma(ft[1], fr[0][b], zero4());
+        u[2][b] = mma(ft[2], fr[0][b], zero4());
+        u[3][b] = mma(ft[4], fr[0][b], zero4());
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        u[2][b] = mma(ft[3], fr[1][b], u[2][b]);
+        u[3][b] = mma(ft[5], fr[1][b], u[3][b]);
+    }
+    if constexpr (KT_LATE) {
+#pragma unroll
+        for (int a = NKT / 2; a < NKT; ++a)
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) ld_kt_frag<PK>(m.K, a, k2, g4, c16, fkt[a][k2]);
+    }
+    f32x4 dec[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) dec[mt] = *reinterpret_cast<const f32x4 *>(m.dec + 16 * mt + 4 * g4);
+    const float gC = m.gam[kC - 1];
+    // publish U; S^T <- gamma_C S^T + K^T diag(dec) U
+    F fd[2][NB];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            F fu;
+            c_to_frag(u[2 * k2][b], u[2 * k2 + 1][b], fu);
+            ho.fu[(k2 * NB + b) * 64 + lane] = fu;
+            f32x4 lo = u[2 * k2][b], hi = u[2 * k2 + 1][b];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                lo[r] *= dec[2 * k2][r];
+                hi[r] *= dec[2 * k2 + 1][r];
+            }
+            c_to_frag(lo, hi, fd[k2][b]);
+        }
+    set_flag(flag, 2 * c + 2);
+#pragma unroll
+    for (int a = 0; a < NKT; ++a)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            st[a][b] *= gC;
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) st[a][b] = mma(fkt[a][k2], fd[k2][b], st[a][b]);
+        }
+}
+
+// Output wave, one chunk: O^T = (S Q^T) diag(gamma) + U^T P^T for the chain
+// wave's columns, stored for rows t < lenc (`oc` points at token 0 of the
+// chunk, first column of the wave).
+template <int D, int NB, int PK, int PT>
+__device__ __forceinline__ void out_core_bf16(const ChainSmem<__bf16> &m, Handoff<D, NB> ho,
+                                              int *flag, int c, __bf16 *oc, int64_t sVO, int lenc,
+                                              float scale, int g4, int c16, int lane) {
+    using F = bf16x8;
+    constexpr int KS = D / 32;
+    const __bf16 *qp = m.Q + c16 * PK + 4 * g4;
+    F fq[KS][4], fp[6];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) ld_chain(qp + 16 * mt * PK + 32 * kk, fq[kk][mt]);
+    ld_chain(m.P + c16 * PT + 4 * g4, fp[0]);
+    ld_chain(m.P + (16 + c16) * PT + 4 * g4, fp[1]);
+    ld_chain(m.P + (32 + c16) * PT + 4 * g4, fp[2]);
+    ld_chain(m.P + (32 + c16) * PT + 32 + 4 * g4, fp[3]);
+    ld_chain(m.P + (48 + c16) * PT + 4 * g4, fp[4]);
+    ld_chain(m.P + (48 + c16) * PT + 32 + 4 * g4, fp[5]);
+    float gamr[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) gamr[mt] = m.gam[16 * mt + c16];
+    wait_flag(flag, 2 * c + 1);
+    F sf[KS][NB];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) sf[kk][b] = ho.sf[(kk * NB + b) * 64 + lane];
+    f32x4 oT[4][NB];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) oT[mt][b] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) oT[mt][b] = mma(sf[kk][b], fq[kk][mt], oT[mt][b]);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) oT[mt][b] *= gamr[mt];
+    wait_flag(flag, 2 * c + 2);
+    F fu[2][NB];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) fu[k2][b] = ho.fu[(k2 * NB + b) * 64 + lane];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        oT[0][b] = mma(fu[0][b], fp[0], oT[0][b]);
+        oT[1][b] = mma(fu[0][b], fp[1], oT[1][b]);
+        oT[2][b] = mma(fu[0][b], fp[2], oT[2][b]);
+        oT[3][b] = mma(fu[0][b], fp[4], oT[3][b]);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        oT[2][b] = mma(fu[1][b], fp[3], oT[2][b]);
+        oT[3][b] = mma(fu[1][b], fp[5], oT[3][b]);
+    }
+    __bf16 *o0 = oc + (int64_t)c16 * sVO + 4 * g4;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        if (16 * mt + c16 < lenc) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                bf16x4 ob;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ob[r] = (__bf16)(scale * oT[mt][b][r]);
+                *reinterpret_cast<bf16x4 *>(o0 + (int64_t)(16 * mt) * sVO + 16 * b) = ob;
+            }
         }
     }
 }

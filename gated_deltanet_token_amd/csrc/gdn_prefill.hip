@@ -90,11 +90,15 @@ template <typename DT, int D, int NTH, int DVS> struct Stager {
     int vOffG[NTV], vOffL[NTV], vRow[NTV];
     u32x4 rK[NTK][2], rQ[NTK][2], rV[NTV][2];
 
+    // Threads past the last task take the last task again: every thread
+    // issues every load (a load skipped by a whole wave would leave the
+    // compiler unsure how many loads are in flight, and it would then wait for
+    // all of them), and duplicate LDS writes store identical bytes.
     __device__ __forceinline__ void init(int tid) {
 #pragma unroll
         for (int i = 0; i < NTK; ++i) {
             int rp = 0, pc = 0;
-            task_coords<PPR_K>(tid + i * NTH, rp, pc);
+            task_coords<PPR_K>(min(tid + i * NTH, TK - 1), rp, pc);
             kRow[i] = 2 * rp;
             kOffG[i] = pc * EPP;
             kOffL[i] = 2 * rp * P::PK + pc * EPP;
@@ -102,7 +106,7 @@ template <typename DT, int D, int NTH, int DVS> struct Stager {
 #pragma unroll
         for (int i = 0; i < NTV; ++i) {
             int rp = 0, pc = 0;
-            task_coords<PPR_V>(tid + i * NTH, rp, pc);
+            task_coords<PPR_V>(min(tid + i * NTH, TV - 1), rp, pc);
             vRow[i] = 2 * rp;
             vOffG[i] = pc * EPP;
             vOffL[i] = BF ? (pc * EPP) * P::PT + 2 * rp : 2 * rp * PV + pc * EPP;
@@ -112,61 +116,53 @@ template <typename DT, int D, int NTH, int DVS> struct Stager {
     // valid row and zeroed at store time, so nothing consumes the loaded
     // registers before the store (the loads stay in flight meanwhile).
     __device__ __forceinline__ void load(const DT *kh, const DT *qh, const DT *vh, int64_t t0,
-                                         int lenc, int64_t sQK, int64_t sVO, int tid) {
+                                         int lenc, int64_t sQK, int64_t sVO, int) {
 #pragma unroll
         for (int i = 0; i < NTK; ++i) {
-            if (TK % NTH == 0 || tid + i * NTH < TK) {
 #pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const int r = kRow[i] + e;
-                    const int rr = r < lenc ? r : lenc - 1;
-                    const int64_t off = (t0 + rr) * sQK + kOffG[i];
-                    rK[i][e] = *reinterpret_cast<const u32x4 *>(kh + off);
-                    rQ[i][e] = *reinterpret_cast<const u32x4 *>(qh + off);
-                }
+            for (int e = 0; e < 2; ++e) {
+                const int r = kRow[i] + e;
+                const int rr = r < lenc ? r : lenc - 1;
+                const int64_t off = (t0 + rr) * sQK + kOffG[i];
+                rK[i][e] = *reinterpret_cast<const u32x4 *>(kh + off);
+                rQ[i][e] = *reinterpret_cast<const u32x4 *>(qh + off);
             }
         }
 #pragma unroll
         for (int i = 0; i < NTV; ++i) {
-            if (TV % NTH == 0 || tid + i * NTH < TV) {
 #pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const int r = vRow[i] + e;
-                    const int rr = r < lenc ? r : lenc - 1;
-                    rV[i][e] = *reinterpret_cast<const u32x4 *>(vh + (t0 + rr) * sVO + vOffG[i]);
-                }
+            for (int e = 0; e < 2; ++e) {
+                const int r = vRow[i] + e;
+                const int rr = r < lenc ? r : lenc - 1;
+                rV[i][e] = *reinterpret_cast<const u32x4 *>(vh + (t0 + rr) * sVO + vOffG[i]);
             }
         }
     }
-    __device__ __forceinline__ void store(DT *sK, DT *sQ, DT *sKT, DT *sV, int lenc, int tid) {
+    __device__ __forceinline__ void store(DT *sK, DT *sQ, DT *sKT, DT *sV, int lenc, int) {
         const u32x4 z4 = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int i = 0; i < NTK; ++i) {
-            if (TK % NTH == 0 || tid + i * NTH < TK) {
 #pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const bool ok = kRow[i] + e < lenc;
-                    rK[i][e] = ok ? rK[i][e] : z4;
-                    rQ[i][e] = ok ? rQ[i][e] : z4;
-                    *reinterpret_cast<u32x4 *>(sK + kOffL[i] + e * P::PK) = rK[i][e];
-                    *reinterpret_cast<u32x4 *>(sQ + kOffL[i] + e * P::PK) = rQ[i][e];
-                }
-                if constexpr (BF)
-                    store_pair_transposed<P::PT>(sKT + kOffG[i] * P::PT + kRow[i], rK[i][0], rK[i][1]);
+            for (int e = 0; e < 2; ++e) {
+                const bool ok = kRow[i] + e < lenc;
+                rK[i][e] = ok ? rK[i][e] : z4;
+                rQ[i][e] = ok ? rQ[i][e] : z4;
+                *reinterpret_cast<u32x4 *>(sK + kOffL[i] + e * P::PK) = rK[i][e];
+                *reinterpret_cast<u32x4 *>(sQ + kOffL[i] + e * P::PK) = rQ[i][e];
             }
+            if constexpr (BF)
+                store_pair_transposed<P::PT>(sKT + kOffG[i] * P::PT + kRow[i], rK[i][0], rK[i][1]);
         }
 #pragma unroll
         for (int i = 0; i < NTV; ++i) {
-            if (TV % NTH == 0 || tid + i * NTH < TV) {
 #pragma unroll
-                for (int e = 0; e < 2; ++e) rV[i][e] = vRow[i] + e < lenc ? rV[i][e] : z4;
-                if constexpr (BF) {
-                    store_pair_transposed<P::PT>(sV + vOffL[i], rV[i][0], rV[i][1]);
-                } else {
+            for (int e = 0; e < 2; ++e) rV[i][e] = vRow[i] + e < lenc ? rV[i][e] : z4;
+            if constexpr (BF) {
+                store_pair_transposed<P::PT>(sV + vOffL[i], rV[i][0], rV[i][1]);
+            } else {
 #pragma unroll
-                    for (int e = 0; e < 2; ++e)
-                        *reinterpret_cast<u32x4 *>(sV + vOffL[i] + e * PV) = rV[i][e];
-                }
+                for (int e = 0; e < 2; ++e)
+                    *reinterpret_cast<u32x4 *>(sV + vOffL[i] + e * PV) = rV[i][e];
             }
         }
     }
@@ -344,12 +340,14 @@ template <typename DT> constexpr int ws_bytes_per_chunk() {
 template <typename DT, int D> struct PrepCfg {
     using P = ChunkPitch<DT, D>;
     static constexpr int SZ_K = kC * P::PK * (int)sizeof(DT);
-    static constexpr int SZ_T = kC * P::PT * (int)sizeof(DT);
     static constexpr int SZ_A = kC * P::PA * 4;
+    // K and Q are dead once the Gram products are formed; A then takes their place
+    static constexpr int SZ_KQ = 2 * SZ_K > SZ_A ? 2 * SZ_K : SZ_A;
+    static constexpr int SZ_T = kC * P::PT * (int)sizeof(DT);
     static constexpr int OFF_K = 0;
     static constexpr int OFF_Q = SZ_K;
-    static constexpr int OFF_A = 2 * SZ_K;
-    static constexpr int OFF_T = OFF_A + SZ_A;
+    static constexpr int OFF_A = 0;
+    static constexpr int OFF_T = SZ_KQ;
     static constexpr int OFF_P = OFF_T + SZ_T;
     static constexpr int OFF_VEC = OFF_P + SZ_T;
     static constexpr int LDS = OFF_VEC + 4 * kC * 4;
@@ -357,7 +355,9 @@ template <typename DT, int D> struct PrepCfg {
 };
 
 // One workgroup (4 waves) per (chunk slot, value head): Gram products, decay,
-// T = (I + A)^{-1}; writes T, P, gamma, dec, beta to the workspace.
+// T = (I + A)^{-1}; writes T, P, gamma, dec, beta to the workspace. About 52
+// KiB of LDS (bf16, D = 128), so three workgroups share a CU and hide each
+// other's latencies.
 template <typename DT, int D>
 __global__ __launch_bounds__(256) void prep_kernel(PrefillParams p, unsigned char *ws,
                                                    int remap_xcd) {
@@ -414,7 +414,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillParams p, unsigned cha
     const DT *kh = reinterpret_cast<const DT *>(p.k) + t0 * sQK + (int64_t)grp * D;
     const DT *qh = reinterpret_cast<const DT *>(p.q) + t0 * sQK + (int64_t)grp * D;
 
-    // K, Q rows -> LDS; T and P cleared (their upper blocks are never written)
+    // K, Q rows -> LDS (rows past the end of the sequence are zero)
     {
         constexpr int PPR = D / EPP;
         const u32x4 z4 = {0u, 0u, 0u, 0u};
@@ -426,8 +426,6 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillParams p, unsigned cha
             *reinterpret_cast<u32x4 *>(sK + r * PK + pc * EPP) = r < lenc ? kv : z4;
             *reinterpret_cast<u32x4 *>(sQ + r * PK + pc * EPP) = r < lenc ? qv : z4;
         }
-        for (int i = tid; i < 2 * Cf::SZ_T / 4; i += 256)
-            reinterpret_cast<float *>(smem + Cf::OFF_T)[i] = 0.f;
     }
     unsigned char *rec = ws + (slot * p.Hv + h) * (int64_t)ws_bytes_per_chunk<DT>();
     if (wave == 0) {
@@ -448,28 +446,40 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillParams p, unsigned cha
         vec[2 * kC + lane] = bet;
     }
     __syncthreads();
+    // Gram products of this wave's lower tile pairs (pr = wave, wave + 4, ...)
+    f32x4 gk[3], gq[3];
 #pragma unroll
-    for (int pr = 0; pr < 10; ++pr) {
-        if (pr % 4 != wave) continue;
-        f32x4 gk, gq;
-        gram_pair<DT, D, PK>(sK, sQ, pair_i(pr), pair_j(pr), g4, c16, gk, gq);
-        mask_pair<DT, PA, PT>(gk, gq, pair_i(pr), pair_j(pr), g4, c16, sG, sBeta, sA, sP);
+    for (int k = 0; k < 3; ++k) {
+        const int pr = wave + 4 * k;
+        if (pr < 10) gram_pair<DT, D, PK>(sK, sQ, pair_i(pr), pair_j(pr), g4, c16, gk[k], gq[k]);
+    }
+    __syncthreads();  // K and Q are dead from here on: A overlays them
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const int pr = wave + 4 * k;
+        if (pr < 10)
+            mask_pair<DT, PA, PT>(gk[k], gq[k], pair_i(pr), pair_j(pr), g4, c16, sG, sBeta, sA, sP);
     }
     __syncthreads();
     // E_b overwrite the diagonal blocks of A (each is read in full first)
-    if (wave == 0) solve_unit_lower<DT, PA, PT>(sA, sA, sT, g4, c16);
+    if (wave == 0) solve_diag_blocks<DT, PA, PT>(sA, sA, sT, g4, c16);
     __syncthreads();
-    // T, P -> workspace as dense [64][64] rows
+    if (wave < 3) solve_column<DT, PA, PT>(sA, sA, sT, wave, g4, c16);
+    __syncthreads();
+    // T, P -> workspace as dense [64][64] rows; blocks above the diagonal
+    // (never written in LDS) are stored as zeros
     {
         constexpr int PPR = kC / EPP;
+        const u32x4 z4 = {0u, 0u, 0u, 0u};
         DT *gT = reinterpret_cast<DT *>(rec);
         DT *gP = gT + kC * kC;
         for (int i = tid; i < kC * PPR; i += 256) {
             const int r = i / PPR, pc = i % PPR;
+            const bool upper = (pc * EPP) / 16 > r / 16;
             *reinterpret_cast<u32x4 *>(gT + r * kC + pc * EPP) =
-                *reinterpret_cast<const u32x4 *>(sT + r * PT + pc * EPP);
+                upper ? z4 : *reinterpret_cast<const u32x4 *>(sT + r * PT + pc * EPP);
             *reinterpret_cast<u32x4 *>(gP + r * kC + pc * EPP) =
-                *reinterpret_cast<const u32x4 *>(sP + r * PT + pc * EPP);
+                upper ? z4 : *reinterpret_cast<const u32x4 *>(sP + r * PT + pc * EPP);
         }
     }
 }
@@ -620,45 +630,65 @@ __global__ __launch_bounds__(256) void chain_kernel(PrefillParams p, const unsig
     }
 }
 
-// Double-buffered variant (bf16): waves 0..NC-1 run the state chain on chunk
-// c from one LDS buffer while the helper waves NC..3 load chunk c+1 and write
-// it into the other buffer. One barrier per chunk; the chain waves never
-// stage.
-template <typename DT, int D, int NC, int DVW> struct ChainDbCfg {
-    using P = ChunkPitch<DT, D>;
-    static constexpr int NH = 4 - NC;  // helper waves
+// Double-buffered two-pass chain (bf16). Wave roles, per workgroup of
+// NW = 2 NC + 1 + NH waves owning DVS = 16 NC value columns of one head:
+//   waves 0 .. NC-1        chain: K S^T, R, U = T R, state update (the
+//                          sequential part); each owns 16 value columns;
+//   waves NC .. 2 NC-1     output: O for the same columns, from the chain
+//                          wave's S^T and U handed over through LDS;
+//   wave 2 NC              L2 prefetch: touches the lines of chunk
+//                          c + 1 + DEPTH + PF_AHEAD once per owner workgroup;
+//   the rest               helpers: copy chunk c + 1 into the other LDS buffer
+//                          while chunk c is processed, and load chunk c + 2.
+// One barrier per chunk. All staging is plain row copies: the chain reads
+// the columns of K and V with transposing LDS reads.
+template <int D, int NC, int NH> struct ChainDbCfg {
+    using DT = __bf16;
+    static constexpr int NW = 2 * NC + 1 + NH;
     static constexpr int NTHH = NH * 64;
-    static constexpr int DVS = NC * DVW;
-    static constexpr int PV = DVS + 4;
-    static constexpr int SZ_K = kC * P::PK * (int)sizeof(DT);
-    static constexpr int SZ_KT = P::BF ? D * P::PT * 2 : 0;
-    static constexpr int SZ_V = P::BF ? DVS * P::PT * 2 : kC * PV * 4;
-    static constexpr int SZ_T = kC * P::PT * (int)sizeof(DT);
+    static constexpr int DVS = 16 * NC;
+    static constexpr int DEPTH = 1;
+    static constexpr int PF_AHEAD = 4;   // chunks a line is touched ahead of its load
+    static constexpr int PF_LOADS = 8;   // line touches per lane per chunk (at most)
+    static constexpr int PK = D + 8;     // K, Q row pitch (elements): 16 B skew per row
+    static constexpr int PT = kC + 4;    // T, P row pitch
+    // V row pitch: an odd multiple of 32 bytes, so that the transposing reads
+    // (8 rows x 32 bytes per 32 lanes) hit distinct banks
+    static constexpr int PVB = ((DVS * 2 / 32) % 2 == 1) ? DVS * 2 : DVS * 2 + 32;
+    static constexpr int PV = PVB / 2;
+    static constexpr int SZ_K = kC * PK * 2;
+    static constexpr int SZ_V = kC * PVB;
+    static constexpr int SZ_T = kC * PT * 2;
     static constexpr int OFF_K = 0;
     static constexpr int OFF_Q = OFF_K + SZ_K;
-    static constexpr int OFF_KT = OFF_Q + SZ_K;
-    static constexpr int OFF_V = OFF_KT + SZ_KT;
+    static constexpr int OFF_V = OFF_Q + SZ_K;
     static constexpr int OFF_T = OFF_V + SZ_V;
     static constexpr int OFF_P = OFF_T + SZ_T;
     static constexpr int OFF_VEC = OFF_P + SZ_T;
-    static constexpr int BUF = OFF_VEC + 3 * kC * 4;  // one buffer
-    static constexpr int LDS = 2 * BUF;
-    static constexpr int EPP = 16 / (int)sizeof(DT);
-    static constexpr int TP_PIECES = kC * kC / EPP;
-    static constexpr int NTP = (TP_PIECES + NTHH - 1) / NTHH;
+    static constexpr int BUF = OFF_VEC + 64 * 16;  // gamma, dec, beta + padding pieces
+    static constexpr int OFF_HO = 2 * BUF;          // chain -> output handoff, per chain wave
+    static constexpr int OFF_FLAG = OFF_HO + NC * Handoff<D, 1>::BYTES;
+    static constexpr int OFF_SINK = OFF_FLAG + 64;  // landing area of the L2 touches
+    static constexpr int LDS = OFF_SINK + 64 * 4;
+    // helper tasks: 16-byte pieces, pieces fastest within a row
+    static constexpr int PPK = D / 8, PPV = DVS / 8, PPT = kC / 8;
+    static constexpr int NK = (kC * PPK + NTHH - 1) / NTHH;
+    static constexpr int NV = (kC * PPV + NTHH - 1) / NTHH;
+    static constexpr int NT = (kC * PPT + NTHH - 1) / NTHH;
     static constexpr int VEC_PIECES = 3 * kC / 4;
-    static constexpr int NVP = (VEC_PIECES + NTHH - 1) / NTHH;
-    static_assert(NC >= 1 && NC <= 3 && DVW % 16 == 0, "chain waves");
+    static constexpr int NVEC = (VEC_PIECES + NTHH - 1) / NTHH;
+    static_assert(NC >= 1 && NH >= 1 && NW <= 16, "wave roles");
     static_assert(LDS <= 160 * 1024, "LDS budget of a gfx950 CU");
 };
 
-template <typename DT, int D, int NC, int DVW>
-__global__ __launch_bounds__(256) void chain_db_kernel(PrefillParams p, const unsigned char *ws,
-                                                       int nsplit, int remap_xcd) {
-    using Cf = ChainDbCfg<DT, D, NC, DVW>;
-    using Pi = ChunkPitch<DT, D>;
-    constexpr int NKT = D / 16, NB = DVW / 16, KS = D / 32;
-    constexpr int PK = Pi::PK, PT = Pi::PT, PV = Cf::PV, EPP = Cf::EPP, NTHH = Cf::NTHH;
+// The LDS buffers allow one workgroup per CU.
+template <int D, int NC, int NH>
+__global__ __launch_bounds__((ChainDbCfg<D, NC, NH>::NW * 64)) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int remap_xcd) {
+    using DT = __bf16;
+    using Cf = ChainDbCfg<D, NC, NH>;
+    constexpr int NKT = D / 16, PK = Cf::PK, PT = Cf::PT, PV = Cf::PV, NTHH = Cf::NTHH;
+    constexpr int DEPTH = Cf::DEPTH;
     constexpr int WSB = ws_bytes_per_chunk<DT>();
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::LDS];
@@ -667,8 +697,6 @@ __global__ __launch_bounds__(256) void chain_db_kernel(PrefillParams p, const un
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g4 = lane >> 4;
     const int c16 = lane & 15;
-    const bool chain = wave < NC;
-    const int htid = tid - NC * 64;  // helper thread index (valid when !chain)
 
     const int wg = logical_wg(remap_xcd);
     const int slice = wg % nsplit;
@@ -679,122 +707,219 @@ __global__ __launch_bounds__(256) void chain_db_kernel(PrefillParams p, const un
     int64_t tok0, len;
     seq_bounds(p, n, tok0, len);
     const int dv0 = slice * Cf::DVS;
-    const int wdv = (chain ? wave : 0) * DVW;
     const int64_t base = slot_base(p, n);
-
     const int64_t sQK = (int64_t)p.Hk * D;
     const int64_t sVO = (int64_t)p.Hv * D;
+    const int64_t nchunks = (len + kC - 1) / kC;
+    int *flags = reinterpret_cast<int *>(smem + Cf::OFF_FLAG);
+
+    auto smem_view = [&](int64_t c) {
+        const unsigned char *b = smem + (c & 1) * Cf::BUF;
+        const float *vec = reinterpret_cast<const float *>(b + Cf::OFF_VEC);
+        return ChainSmem<DT>{reinterpret_cast<const DT *>(b + Cf::OFF_K),
+                             reinterpret_cast<const DT *>(b + Cf::OFF_Q),
+                             nullptr,
+                             reinterpret_cast<const DT *>(b + Cf::OFF_V),
+                             reinterpret_cast<const DT *>(b + Cf::OFF_T),
+                             reinterpret_cast<const DT *>(b + Cf::OFF_P),
+                             vec, vec + kC, vec + 2 * kC};
+    };
+
+    if (wave < 2 * NC) {
+        const int w = wave < NC ? wave : wave - NC;  // column group
+        const int wdv = 16 * w;
+        Handoff<D, 1> ho(smem + Cf::OFF_HO + w * Handoff<D, 1>::BYTES);
+        int *flag = flags + w;
+        if (wave < NC) {
+            // chain wave
+            f32x4 st[NKT][1];
+            const float *s0 = p.s0 ? p.s0 + ((int64_t)n * p.Hv + h) * D * D : nullptr;
+#pragma unroll
+            for (int a = 0; a < NKT; ++a)
+                st[a][0] = s0 ? *reinterpret_cast<const f32x4 *>(
+                                    s0 + (int64_t)(dv0 + wdv + c16) * D + 16 * a + 4 * g4)
+                              : zero4();
+            if (lane == 0) *flag = 0;
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): initial state; see prefill_kernel
+            __syncthreads();
+            for (int64_t c = 0; c < nchunks; ++c) {
+                chain_core_bf16<D, 1, PK, PT, PV, (Cf::NW > 8)>(smem_view(c), st, wdv, ho, flag,
+                                                                (int)c, g4, c16, lane);
+                __syncthreads();
+            }
+            if (p.s_final) {
+                float *sf = p.s_final + ((int64_t)n * p.Hv + h) * D * D;
+#pragma unroll
+                for (int a = 0; a < NKT; ++a)
+                    *reinterpret_cast<f32x4 *>(sf + (int64_t)(dv0 + wdv + c16) * D + 16 * a +
+                                               4 * g4) = st[a][0];
+            }
+        } else {
+            // output wave
+            DT *oh = reinterpret_cast<DT *>(p.out) + tok0 * sVO + (int64_t)h * D + dv0 + wdv;
+            __syncthreads();
+            for (int64_t c = 0; c < nchunks; ++c) {
+                const int lenc = (int)((len - c * kC) < kC ? (len - c * kC) : kC);
+                out_core_bf16<D, 1, PK, PT>(smem_view(c), ho, flag, (int)c, oh + c * kC * sVO, sVO,
+                                            lenc, p.scale, g4, c16, lane);
+                __syncthreads();
+            }
+        }
+        return;
+    }
+
+    if (wave == 2 * NC) {
+        // L2 prefetch wave. Owners: K and Q lines of q/k head grp belong to its
+        // first value head's slice 0; T, P and the decay vectors of head h to
+        // slice 0; a V line to the slice that starts it. A touch is a 4-byte
+        // load that lands in a scratch area of LDS nobody reads: it produces no
+        // register, so this wave never waits for one (plain barriers, no fence)
+        // and many chunks of touches stay in flight.
+        constexpr int NL = Cf::PF_LOADS;
+        constexpr int LEAD = 1 + DEPTH + Cf::PF_AHEAD;  // chunk touched in iteration c: c + LEAD
+        constexpr int QKL = (D * 2 + 127) / 128;        // lines per K or Q row
+        constexpr int VL = (Cf::DVS * 2 + 127) / 128;   // lines per V row slice
+        static_assert(NL * 64 >= 2 * QKL * kC + VL * kC + (WSB + 127) / 128, "touch budget");
+        const int G = p.Hv / p.Hk;
+        const int nqk = (h % G == 0 && slice == 0) ? 2 * QKL * kC : 0;
+        const int nv = ((dv0 * 2) % 128 == 0) ? VL * kC : 0;
+        const int ntp = slice == 0 ? (WSB + 127) / 128 : 0;
+        const int ntot = nqk + nv + ntp;
+        const unsigned char *kb = reinterpret_cast<const unsigned char *>(p.k) +
+                                  (tok0 * sQK + (int64_t)grp * D) * 2;
+        const unsigned char *qb = reinterpret_cast<const unsigned char *>(p.q) +
+                                  (tok0 * sQK + (int64_t)grp * D) * 2;
+        const unsigned char *vb = reinterpret_cast<const unsigned char *>(p.v) +
+                                  (tok0 * sVO + (int64_t)h * D + dv0) * 2;
+        const int64_t rowqk = sQK * 2, rowv = sVO * 2;
+        uint32_t *sink = reinterpret_cast<uint32_t *>(smem + Cf::OFF_SINK);
+        auto touch = [&](int64_t c) {
+            const int64_t t0 = c * kC;
+            const int rows = c < nchunks ? (int)((len - t0) < kC ? (len - t0) : kC) : 0;
+            const unsigned char *rec = ws + ((base + c) * p.Hv + h) * (int64_t)WSB;
+#pragma unroll
+            for (int j = 0; j < NL; ++j) {
+                const int i = lane + 64 * j;
+                const unsigned char *a = kb;  // lanes without a line re-touch row 0
+                if (i < nqk) {
+                    const int iq = i % (QKL * kC), r = iq / QKL, part = iq % QKL;
+                    if (r < rows) a = (i < QKL * kC ? kb : qb) + (t0 + r) * rowqk + part * 128;
+                } else if (i < nqk + nv) {
+                    const int r = (i - nqk) / VL, part = (i - nqk) % VL;
+                    if (r < rows) a = vb + (t0 + r) * rowv + part * 128;
+                } else if (i < ntot && rows > 0) {
+                    a = rec + (int64_t)(i - nqk - nv) * 128;
+                }
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t *>(a), sink, 4, 0, 0);
+            }
+        };
+        // chunk c + 1 + DEPTH is loaded by the helpers in iteration c and was
+        // touched PF_AHEAD iterations earlier (chunks 1 + DEPTH .. LEAD - 1
+        // here). The dummy line, row 0 of the sequence, exists only if the
+        // sequence is not empty.
+        if (nchunks > 0) {
+#pragma unroll
+            for (int j = 1 + DEPTH; j < LEAD; ++j) touch(j);
+        }
+        __builtin_amdgcn_s_barrier();
+        for (int64_t c = 0; c < nchunks; ++c) {
+            touch(c + LEAD);
+            __builtin_amdgcn_s_barrier();
+        }
+        __builtin_amdgcn_s_waitcnt(0);  // no touch may land after the workgroup ends
+        return;
+    }
+
+    // helper waves. Every thread issues every load (tasks past the end take
+    // the last task again; duplicate LDS writes store identical bytes), so
+    // the compiler always knows how many loads are in flight and waits only
+    // for the ones it needs.
+    const int htid = tid - (2 * NC + 1) * 64;
     const DT *qh = reinterpret_cast<const DT *>(p.q) + tok0 * sQK + (int64_t)grp * D;
     const DT *kh = reinterpret_cast<const DT *>(p.k) + tok0 * sQK + (int64_t)grp * D;
     const DT *vh = reinterpret_cast<const DT *>(p.v) + tok0 * sVO + (int64_t)h * D + dv0;
-    DT *oh = reinterpret_cast<DT *>(p.out) + tok0 * sVO + (int64_t)h * D + dv0 + wdv;
-    const int64_t nchunks = (len + kC - 1) / kC;
-
-    f32x4 st[NKT][NB];
-    {
-        const float *s0 = p.s0 && chain ? p.s0 + ((int64_t)n * p.Hv + h) * D * D : nullptr;
+    int kRow[Cf::NK], kPc[Cf::NK], vRow[Cf::NV], vPc[Cf::NV], tPc[Cf::NT], ePc[Cf::NVEC];
 #pragma unroll
-        for (int a = 0; a < NKT; ++a)
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-                st[a][b] = s0 ? *reinterpret_cast<const f32x4 *>(
-                                    s0 + (int64_t)(dv0 + wdv + 16 * b + c16) * D + 16 * a + 4 * g4)
-                              : zero4();
+    for (int i = 0; i < Cf::NK; ++i) {
+        const int t = min(htid + i * NTHH, kC * Cf::PPK - 1);
+        kRow[i] = t / Cf::PPK;
+        kPc[i] = t % Cf::PPK;
     }
-
-    // helper-side staging state
-    Stager<DT, D, NTHH, Cf::DVS> sg;
-    u32x4 rT[Cf::NTP], rP[Cf::NTP], rVec[Cf::NVP];
+#pragma unroll
+    for (int i = 0; i < Cf::NV; ++i) {
+        const int t = min(htid + i * NTHH, kC * Cf::PPV - 1);
+        vRow[i] = t / Cf::PPV;
+        vPc[i] = t % Cf::PPV;
+    }
+#pragma unroll
+    for (int i = 0; i < Cf::NT; ++i) tPc[i] = min(htid + i * NTHH, kC * Cf::PPT - 1);
+#pragma unroll
+    for (int i = 0; i < Cf::NVEC; ++i) ePc[i] = min(htid + i * NTHH, Cf::VEC_PIECES - 1);
+    u32x4 rK[Cf::NK], rQ[Cf::NK], rV[Cf::NV], rT[Cf::NT], rP[Cf::NT], rE[Cf::NVEC];
     auto load_chunk = [&](int64_t c) {
         const int64_t t0 = c * kC;
         const int lenc = (int)((len - t0) < kC ? (len - t0) : kC);
-        sg.load(kh, qh, vh, t0, lenc, sQK, sVO, htid);
+#pragma unroll
+        for (int i = 0; i < Cf::NK; ++i) {
+            const int64_t off = (t0 + min(kRow[i], lenc - 1)) * sQK + 8 * kPc[i];
+            rK[i] = *reinterpret_cast<const u32x4 *>(kh + off);
+            rQ[i] = *reinterpret_cast<const u32x4 *>(qh + off);
+        }
+#pragma unroll
+        for (int i = 0; i < Cf::NV; ++i)
+            rV[i] = *reinterpret_cast<const u32x4 *>(vh + (t0 + min(vRow[i], lenc - 1)) * sVO +
+                                                     8 * vPc[i]);
         const unsigned char *rec = ws + ((base + c) * p.Hv + h) * (int64_t)WSB;
 #pragma unroll
-        for (int i = 0; i < Cf::NTP; ++i) {
-            const int pc = htid + i * NTHH;
-            if (Cf::TP_PIECES % NTHH == 0 || pc < Cf::TP_PIECES) {
-                rT[i] = reinterpret_cast<const u32x4 *>(rec)[pc];
-                rP[i] = reinterpret_cast<const u32x4 *>(rec + kC * kC * sizeof(DT))[pc];
-            }
+        for (int i = 0; i < Cf::NT; ++i) {
+            rT[i] = reinterpret_cast<const u32x4 *>(rec)[tPc[i]];
+            rP[i] = reinterpret_cast<const u32x4 *>(rec + kC * kC * 2)[tPc[i]];
         }
 #pragma unroll
-        for (int i = 0; i < Cf::NVP; ++i) {
-            const int pc = htid + i * NTHH;
-            if (pc < Cf::VEC_PIECES)
-                rVec[i] = reinterpret_cast<const u32x4 *>(rec + 2 * kC * kC * sizeof(DT))[pc];
-        }
+        for (int i = 0; i < Cf::NVEC; ++i)
+            rE[i] = reinterpret_cast<const u32x4 *>(rec + 2 * kC * kC * 2)[ePc[i]];
     };
     auto store_chunk = [&](int64_t c) {
         unsigned char *b = smem + (c & 1) * Cf::BUF;
         const int lenc = (int)((len - c * kC) < kC ? (len - c * kC) : kC);
-        sg.store(reinterpret_cast<DT *>(b + Cf::OFF_K), reinterpret_cast<DT *>(b + Cf::OFF_Q),
-                 reinterpret_cast<DT *>(b + Cf::OFF_KT), reinterpret_cast<DT *>(b + Cf::OFF_V), lenc,
-                 htid);
+        const u32x4 z4 = {0u, 0u, 0u, 0u};
+        DT *sK = reinterpret_cast<DT *>(b + Cf::OFF_K);
+        DT *sQ = reinterpret_cast<DT *>(b + Cf::OFF_Q);
+#pragma unroll
+        for (int i = 0; i < Cf::NK; ++i) {
+            const bool ok = kRow[i] < lenc;  // rows past the end are zero
+            *reinterpret_cast<u32x4 *>(sK + kRow[i] * PK + 8 * kPc[i]) = ok ? rK[i] : z4;
+            *reinterpret_cast<u32x4 *>(sQ + kRow[i] * PK + 8 * kPc[i]) = ok ? rQ[i] : z4;
+        }
+#pragma unroll
+        for (int i = 0; i < Cf::NV; ++i)
+            *reinterpret_cast<u32x4 *>(b + Cf::OFF_V + vRow[i] * Cf::PVB + 16 * vPc[i]) =
+                vRow[i] < lenc ? rV[i] : z4;
         DT *sT = reinterpret_cast<DT *>(b + Cf::OFF_T);
         DT *sP = reinterpret_cast<DT *>(b + Cf::OFF_P);
 #pragma unroll
-        for (int i = 0; i < Cf::NTP; ++i) {
-            const int pc = htid + i * NTHH;
-            if (Cf::TP_PIECES % NTHH == 0 || pc < Cf::TP_PIECES) {
-                const int r = pc / (kC / EPP), col = (pc % (kC / EPP)) * EPP;
-                *reinterpret_cast<u32x4 *>(sT + r * PT + col) = rT[i];
-                *reinterpret_cast<u32x4 *>(sP + r * PT + col) = rP[i];
-            }
+        for (int i = 0; i < Cf::NT; ++i) {
+            const int r = tPc[i] / Cf::PPT, col = (tPc[i] % Cf::PPT) * 8;
+            *reinterpret_cast<u32x4 *>(sT + r * PT + col) = rT[i];
+            *reinterpret_cast<u32x4 *>(sP + r * PT + col) = rP[i];
         }
 #pragma unroll
-        for (int i = 0; i < Cf::NVP; ++i) {
-            const int pc = htid + i * NTHH;
-            if (pc < Cf::VEC_PIECES) reinterpret_cast<u32x4 *>(b + Cf::OFF_VEC)[pc] = rVec[i];
-        }
+        for (int i = 0; i < Cf::NVEC; ++i) reinterpret_cast<u32x4 *>(b + Cf::OFF_VEC)[ePc[i]] = rE[i];
     };
 
-    if (!chain) {
-        sg.init(htid);
-        if (nchunks > 0) {
-            load_chunk(0);
-            store_chunk(0);
-        }
+    // Loads are never skipped either: past the last chunk the loads repeat the
+    // last chunk (never stored).
+    const int64_t last = nchunks - 1;
+    if (nchunks > 0) {
+        load_chunk(0);
+        store_chunk(0);
+        load_chunk(last < 1 ? last : 1);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): initial state; see prefill_kernel
     __syncthreads();
-
     for (int64_t c = 0; c < nchunks; ++c) {
-        if (chain) {
-            const unsigned char *b = smem + (c & 1) * Cf::BUF;
-            const float *vec = reinterpret_cast<const float *>(b + Cf::OFF_VEC);
-            const ChainSmem<DT> m{reinterpret_cast<const DT *>(b + Cf::OFF_K),
-                                  reinterpret_cast<const DT *>(b + Cf::OFF_Q),
-                                  reinterpret_cast<const DT *>(b + Cf::OFF_KT),
-                                  reinterpret_cast<const DT *>(b + Cf::OFF_V),
-                                  reinterpret_cast<const DT *>(b + Cf::OFF_T),
-                                  reinterpret_cast<const DT *>(b + Cf::OFF_P),
-                                  vec, vec + kC, vec + 2 * kC};
-            const int lenc = (int)((len - c * kC) < kC ? (len - c * kC) : kC);
-            Frag<DT> sf[KS][NB];
-            f32x4 racc[4][NB], oT[4][NB];
-            chain_state_half<DT, D, NB, PK, false>(m, st, sf, racc, oT, g4, c16);
-            chain_finish<DT, D, NB, PK, PT, PV>(m, st, racc, oT, wdv, oh + c * kC * sVO, sVO, lenc,
-                                                p.scale, g4, c16);
-        } else if (c + 1 < nchunks) {
-            // load and store within the iteration: no staging registers stay
-            // live across the loop, so they do not add to the chain waves'
-            // register budget (the chain's state would otherwise move to
-            // AGPRs and every elementwise step would shuffle it)
-            load_chunk(c + 1);
-            store_chunk(c + 1);
-        }
+        if (c + 1 < nchunks) store_chunk(c + 1);
+        load_chunk(c + 2 < last ? c + 2 : last);
         __syncthreads();
-    }
-
-    if (p.s_final && chain) {
-        float *sf = p.s_final + ((int64_t)n * p.Hv + h) * D * D;
-#pragma unroll
-        for (int a = 0; a < NKT; ++a)
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-                *reinterpret_cast<f32x4 *>(sf + (int64_t)(dv0 + wdv + 16 * b + c16) * D + 16 * a +
-                                           4 * g4) = st[a][b];
     }
 }
 
@@ -826,19 +951,21 @@ static hipError_t launch_split(const PrefillParams &p, unsigned char *ws, int64_
     return hipGetLastError();
 }
 
-template <typename DT, int D, int NC, int DVW>
+template <int D, int NC, int NH>
 static hipError_t launch_split_db(const PrefillParams &p, unsigned char *ws, int64_t nslots,
                                   int nsplit, hipStream_t stream) {
     const int64_t nprep = nslots * p.Hv;
     const int64_t nchain = (int64_t)p.nseq * p.Hv * nsplit;
     if (nprep <= 0 || nprep > 0x7FFFFFFF || nchain <= 0 || nchain > 0x7FFFFFFF)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((prep_kernel<DT, D>), dim3((unsigned)nprep), dim3(256), 0, stream, p, ws,
+    if (ChainDbCfg<D, NC, NH>::DVS * nsplit != D) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((prep_kernel<__bf16, D>), dim3((unsigned)nprep), dim3(256), 0, stream, p, ws,
                        nprep % 8 == 0 ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((chain_db_kernel<DT, D, NC, DVW>), dim3((unsigned)nchain), dim3(256), 0,
-                       stream, p, (const unsigned char *)ws, nsplit, nchain % 8 == 0 ? 1 : 0);
+    hipLaunchKernelGGL((chain_db_kernel<D, NC, NH>), dim3((unsigned)nchain),
+                       dim3(ChainDbCfg<D, NC, NH>::NW * 64), 0, stream, p,
+                       (const unsigned char *)ws, nsplit, nchain % 8 == 0 ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -891,15 +1018,15 @@ hipError_t launch_prefill(const PrefillParams &p, int dtype, int D, int num_cus,
         if (dtype == 1 && D == 128) {
             switch (ns) {
             case 1: return launch_split<__bf16, 128, 4, 32>(p, w, nslots, 1, stream);
-            case 2: return launch_split_db<__bf16, 128, 2, 32>(p, w, nslots, 2, stream);
-            case 4: return launch_split_db<__bf16, 128, 2, 16>(p, w, nslots, 4, stream);
-            default: return launch_split_db<__bf16, 128, 1, 16>(p, w, nslots, 8, stream);
+            case 2: return launch_split_db<128, 4, 3>(p, w, nslots, 2, stream);
+            case 4: return launch_split_db<128, 2, 3>(p, w, nslots, 4, stream);
+            default: return launch_split_db<128, 1, 5>(p, w, nslots, 8, stream);
             }
         } else if (dtype == 1 && D == 64) {
             switch (ns) {
-            case 1: return launch_split_db<__bf16, 64, 2, 32>(p, w, nslots, 1, stream);
-            case 2: return launch_split_db<__bf16, 64, 2, 16>(p, w, nslots, 2, stream);
-            default: return launch_split_db<__bf16, 64, 1, 16>(p, w, nslots, 4, stream);
+            case 1: return launch_split_db<64, 4, 3>(p, w, nslots, 1, stream);
+            case 2: return launch_split_db<64, 2, 3>(p, w, nslots, 2, stream);
+            default: return launch_split_db<64, 1, 5>(p, w, nslots, 4, stream);
             }
         } else if (dtype == 0 && D == 64) {
             switch (ns) {
