@@ -160,25 +160,54 @@ __device__ __forceinline__ void mask_pair(const f32x4 &gk, const f32x4 &gq, int 
 //   T_ij = -E_i sum_{m=j}^{i-1} A_im T_mj for i = j+1 .. 3 on MFMA. A column
 //   needs only its own earlier blocks, so the three columns can run on three
 //   waves at once; the finished blocks stay in registers.
-template <typename DT, int PA, int PT>
+template <typename DT, int PA, int PT, bool PREFETCH = true>
 __device__ __forceinline__ void solve_diag_blocks(const float *sA, float *sE, DT *sT, int g4, int c16) {
     const int blk = g4, col = c16;
     const float *ab = sA + (16 * blk) * PA + 16 * blk;
     float x[16];
+    // row r of the block: x_r = [r == col] - sum_{m<r} a_rm x_m. Rows go four
+    // at a time; the part of each sum over earlier batches uses four partial
+    // sums (independent chains), only the part inside the batch is serial.
+    f32x4 arow[PREFETCH ? 2 : 1][4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) arow[0][i][0] = *reinterpret_cast<const f32x4 *>(ab + i * PA);
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
-        f32x4 arow[4][4];
+        const int cur = PREFETCH ? (rb & 1) : 0;
+        if (!PREFETCH && rb > 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int m4 = 0; m4 <= rb; ++m4)
-                arow[i][m4] = *reinterpret_cast<const f32x4 *>(ab + (4 * rb + i) * PA + 4 * m4);
+                for (int m4 = 0; m4 <= rb; ++m4)
+                    arow[0][i][m4] = *reinterpret_cast<const f32x4 *>(ab + (4 * rb + i) * PA + 4 * m4);
+        }
+        if (PREFETCH && rb + 1 < 4) {  // next batch's rows, read while this batch computes
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int m4 = 0; m4 <= rb + 1; ++m4)
+                    arow[PREFETCH ? (cur ^ 1) : 0][i][m4] =
+                        *reinterpret_cast<const f32x4 *>(ab + (4 * (rb + 1) + i) * PA + 4 * m4);
+        }
+        float part[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+#pragma unroll
+            for (int m4 = 0; m4 < rb; ++m4) {
+                p0 = fmaf(arow[cur][i][m4][0], x[4 * m4 + 0], p0);
+                p1 = fmaf(arow[cur][i][m4][1], x[4 * m4 + 1], p1);
+                p2 = fmaf(arow[cur][i][m4][2], x[4 * m4 + 2], p2);
+                p3 = fmaf(arow[cur][i][m4][3], x[4 * m4 + 3], p3);
+            }
+            part[i] = (p0 + p1) + (p2 + p3);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 4 * rb + i;
-            float acc = r == col ? 1.f : 0.f;
+            float acc = (r == col ? 1.f : 0.f) - part[i];
 #pragma unroll
-            for (int m = 0; m < r; ++m) acc -= arow[i][m >> 2][m & 3] * x[m];
+            for (int m = 4 * rb; m < r; ++m) acc = fmaf(-arow[cur][i][rb][m - 4 * rb], x[m], acc);
             x[r] = acc;
         }
     }
@@ -238,6 +267,7 @@ __device__ __forceinline__ void solve_column(const float *sA, const float *sE, D
 // finished off-diagonal blocks of every column stay in registers).
 template <typename DT, int PA, int PT>
 __device__ __forceinline__ void solve_unit_lower(const float *sA, float *sE, DT *sT, int g4, int c16) {
+    // diagonal blocks with one serial chain per row: the fewest live registers
     {
         const int blk = g4, col = c16;
         const float *ab = sA + (16 * blk) * PA + 16 * blk;

@@ -1074,12 +1074,12 @@ hipError_t launch_prefill(const PrefillParams &p, int dtype, int D, int num_cus,
             default: return launch_fused<float, 64, 1, 16>(p, 4, stream);
             }
         } else if (D == 128) {
-            // fp32 K, Q and V of a whole head exceed a CU's LDS: two slices at least
+            // fp32 K, Q and V of a whole head exceed a CU's LDS: two slices at
+            // least; a one-wave workgroup would not fit its registers
             switch (ns) {
             case 1:
             case 2: return launch_fused<float, 128, 4, 16>(p, 2, stream);
-            case 4: return launch_fused<float, 128, 2, 16>(p, 4, stream);
-            default: return launch_fused<float, 128, 1, 16>(p, 8, stream);
+            default: return launch_fused<float, 128, 2, 16>(p, 4, stream);
             }
         }
     }
