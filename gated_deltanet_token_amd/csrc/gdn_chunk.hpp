@@ -614,19 +614,26 @@ template <int D, int NB> struct Handoff {
           fu(reinterpret_cast<bf16x8 *>(base) + KS * NB * 64) {}
 };
 
-// Bounded wait for a workgroup-local flag (an int in LDS) to reach `target`.
-// The writer is another wave of the same workgroup, which is always resident,
-// so the wait ends; the bound only guarantees that a wrong flag protocol
-// cannot hang the device.
+// Workgroup-local flags (an int in LDS) between two waves. The LDS executes
+// the requests of one wave in order, so a flag written after the data it
+// announces becomes visible after that data, and data read after the flag
+// was seen is read after it was written: only the compiler must be kept from
+// moving the accesses across the flag (the asm memory clobbers), no wait for
+// outstanding LDS requests is needed.
+// The wait is bounded: the writer is another wave of the same workgroup,
+// which is always resident, so it ends; the bound only guarantees that a
+// wrong protocol cannot hang the device.
 __device__ __forceinline__ void wait_flag(int *flag, int target) {
     for (int spin = 0; spin < (1 << 20); ++spin) {
-        if (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target)
-            return;
+        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target)
+            break;
         __builtin_amdgcn_s_sleep(1);
     }
+    asm volatile("" ::: "memory");
 }
 __device__ __forceinline__ void set_flag(int *flag, int v) {
-    __hip_atomic_store(flag, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    asm volatile("" ::: "memory");
+    __hip_atomic_store(flag, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // Chain wave, one chunk. LDS: K, Q row-major (pitch PK), V row-major with the
@@ -678,12 +685,14 @@ __device__ __forceinline__ void chain_core_bf16(const ChainSmem<__bf16> &m, f32x
 #pragma unroll
             for (int b = 0; b < NB; ++b) racc[mt][b] = mma(fk[kk][mt], sf[kk][b], racc[mt][b]);
     bf16x4 v4[4][NB];
-    f32x4 bet[4], gam[4];
+    f32x4 bet[4], gam[4], dec[4];
+    const float gC = m.gam[kC - 1];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
         const int tb = 16 * mt + 4 * g4;
         bet[mt] = *reinterpret_cast<const f32x4 *>(m.beta + tb);
         gam[mt] = *reinterpret_cast<const f32x4 *>(m.gam + tb);
+        if constexpr (!KT_LATE) dec[mt] = *reinterpret_cast<const f32x4 *>(m.dec + tb);
 #pragma unroll
         for (int b = 0; b < NB; ++b)
             v4[mt][b] = ld_tr(m.V + (16 * mt + 4 * g4 + (c16 >> 2)) * PV + wdv + 16 * b +
@@ -725,11 +734,10 @@ __device__ __forceinline__ void chain_core_bf16(const ChainSmem<__bf16> &m, f32x
         for (int a = NKT / 2; a < NKT; ++a)
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) ld_kt_frag<PK>(m.K, a, k2, g4, c16, fkt[a][k2]);
-    }
-    f32x4 dec[4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) dec[mt] = *reinterpret_cast<const f32x4 *>(m.dec + 16 * mt + 4 * g4);
-    const float gC = m.gam[kC - 1];
+        for (int mt = 0; mt < 4; ++mt)
+            dec[mt] = *reinterpret_cast<const f32x4 *>(m.dec + 16 * mt + 4 * g4);
+    }
     // publish U; S^T <- gamma_C S^T + K^T diag(dec) U
     F fd[2][NB];
 #pragma unroll

@@ -31,6 +31,8 @@
 #include <stdlib.h>
 
 #include "gdn_chunk.hpp"
+#include <type_traits>
+
 #include "gdn_launch.hpp"
 
 namespace gdn {
@@ -651,7 +653,7 @@ template <int D, int NC, int NH> struct ChainDbCfg {
     static constexpr int PF_AHEAD = 4;   // chunks a line is touched ahead of its load
     static constexpr int PF_LOADS = 8;   // line touches per lane per chunk (at most)
     static constexpr int PK = D + 8;     // K, Q row pitch (elements): 16 B skew per row
-    static constexpr int PT = kC + 4;    // T, P row pitch
+    static constexpr int PT = kC + 8;    // T, P row pitch: 144 B, a whole number of 16 B slots
     // V row pitch: an odd multiple of 32 bytes, so that the transposing reads
     // (8 rows x 32 bytes per 32 lanes) hit distinct banks
     static constexpr int PVB = ((DVS * 2 / 32) % 2 == 1) ? DVS * 2 : DVS * 2 + 32;
@@ -670,13 +672,14 @@ template <int D, int NC, int NH> struct ChainDbCfg {
     static constexpr int OFF_FLAG = OFF_HO + NC * Handoff<D, 1>::BYTES;
     static constexpr int OFF_SINK = OFF_FLAG + 64;  // landing area of the L2 touches
     static constexpr int LDS = OFF_SINK + 64 * 4;
-    // helper tasks: 16-byte pieces, pieces fastest within a row
-    static constexpr int PPK = D / 8, PPV = DVS / 8, PPT = kC / 8;
-    static constexpr int NK = (kC * PPK + NTHH - 1) / NTHH;
-    static constexpr int NV = (kC * PPV + NTHH - 1) / NTHH;
-    static constexpr int NT = (kC * PPT + NTHH - 1) / NTHH;
+    // helper copies: LDS-DMA blocks of 64 16-byte slots; a row of a region is
+    // `slots` slots of which the first `pieces` hold data (the rest pad)
+    static constexpr int SK = PK * 2 / 16, SV = PVB / 16, ST = PT * 2 / 16;
+    static constexpr int BLK_K = kC * SK / 64, BLK_V = kC * SV / 64, BLK_T = kC * ST / 64;
+    static constexpr int NBLK = 2 * BLK_K + BLK_V + 2 * BLK_T + 1;  // K, Q, V, T, P, vectors
     static constexpr int VEC_PIECES = 3 * kC / 4;
-    static constexpr int NVEC = (VEC_PIECES + NTHH - 1) / NTHH;
+    static_assert(PK * 2 % 16 == 0 && PVB % 16 == 0 && PT * 2 % 16 == 0, "slot pitches");
+    static_assert(kC * SK % 64 == 0 && kC * SV % 64 == 0 && kC * ST % 64 == 0, "whole blocks");
     static_assert(NC >= 1 && NH >= 1 && NW <= 16, "wave roles");
     static_assert(LDS <= 160 * 1024, "LDS budget of a gfx950 CU");
 };
@@ -687,7 +690,7 @@ __global__ __launch_bounds__((ChainDbCfg<D, NC, NH>::NW * 64)) __attribute__((am
 void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int remap_xcd) {
     using DT = __bf16;
     using Cf = ChainDbCfg<D, NC, NH>;
-    constexpr int NKT = D / 16, PK = Cf::PK, PT = Cf::PT, PV = Cf::PV, NTHH = Cf::NTHH;
+    constexpr int NKT = D / 16, PK = Cf::PK, PT = Cf::PT, PV = Cf::PV;
     constexpr int DEPTH = Cf::DEPTH;
     constexpr int WSB = ws_bytes_per_chunk<DT>();
 
@@ -830,95 +833,75 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
         return;
     }
 
-    // helper waves. Every thread issues every load (tasks past the end take
-    // the last task again; duplicate LDS writes store identical bytes), so
-    // the compiler always knows how many loads are in flight and waits only
-    // for the ones it needs.
-    const int htid = tid - (2 * NC + 1) * 64;
-    const DT *qh = reinterpret_cast<const DT *>(p.q) + tok0 * sQK + (int64_t)grp * D;
-    const DT *kh = reinterpret_cast<const DT *>(p.k) + tok0 * sQK + (int64_t)grp * D;
-    const DT *vh = reinterpret_cast<const DT *>(p.v) + tok0 * sVO + (int64_t)h * D + dv0;
-    int kRow[Cf::NK], kPc[Cf::NK], vRow[Cf::NV], vPc[Cf::NV], tPc[Cf::NT], ePc[Cf::NVEC];
-#pragma unroll
-    for (int i = 0; i < Cf::NK; ++i) {
-        const int t = min(htid + i * NTHH, kC * Cf::PPK - 1);
-        kRow[i] = t / Cf::PPK;
-        kPc[i] = t % Cf::PPK;
-    }
-#pragma unroll
-    for (int i = 0; i < Cf::NV; ++i) {
-        const int t = min(htid + i * NTHH, kC * Cf::PPV - 1);
-        vRow[i] = t / Cf::PPV;
-        vPc[i] = t % Cf::PPV;
-    }
-#pragma unroll
-    for (int i = 0; i < Cf::NT; ++i) tPc[i] = min(htid + i * NTHH, kC * Cf::PPT - 1);
-#pragma unroll
-    for (int i = 0; i < Cf::NVEC; ++i) ePc[i] = min(htid + i * NTHH, Cf::VEC_PIECES - 1);
-    u32x4 rK[Cf::NK], rQ[Cf::NK], rV[Cf::NV], rT[Cf::NT], rP[Cf::NT], rE[Cf::NVEC];
-    auto load_chunk = [&](int64_t c) {
+    // helper waves: copy chunk c + 1 into the other buffer with LDS-DMA loads
+    // (global -> LDS without registers). Block j of a chunk is issued by
+    // helper j % NH; rows past the end of the sequence repeat its last row
+    // (finite values that the decay and beta of those rows cancel exactly) and
+    // pad slots re-load a valid piece of their row.
+    const int hw = wave - (2 * NC + 1);
+    const unsigned char *qb = reinterpret_cast<const unsigned char *>(p.q) +
+                              (tok0 * sQK + (int64_t)grp * D) * 2;
+    const unsigned char *kb = reinterpret_cast<const unsigned char *>(p.k) +
+                              (tok0 * sQK + (int64_t)grp * D) * 2;
+    const unsigned char *vb = reinterpret_cast<const unsigned char *>(p.v) +
+                              (tok0 * sVO + (int64_t)h * D + dv0) * 2;
+    const int64_t rowqk = sQK * 2, rowv = sVO * 2;
+    // one 1 KiB block: slots 64 b .. 64 b + 63 of a region whose rows have
+    // SLOTS slots of which PIECES hold data; src(row, piece) gives the source
+    auto block = [&](unsigned char *dst, int b, int ln, auto slots_c, auto pieces_c, auto src) {
+        constexpr int SLOTS = decltype(slots_c)::value, PIECES = decltype(pieces_c)::value;
+        const int slot = 64 * b + ln;
+        const int row = slot / SLOTS;
+        const int pc = min(slot % SLOTS, PIECES - 1);  // pad slots re-load a data piece
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t *>(src(row, pc)),
+                                         dst + 1024 * b, 16, 0, 0);
+    };
+    using SK_c = std::integral_constant<int, Cf::SK>;
+    using SV_c = std::integral_constant<int, Cf::SV>;
+    using ST_c = std::integral_constant<int, Cf::ST>;
+    using PK_c = std::integral_constant<int, D / 8>;
+    using PV_c = std::integral_constant<int, Cf::DVS / 8>;
+    using PT_c = std::integral_constant<int, kC / 8>;
+    using S64_c = std::integral_constant<int, 64>;
+    using PE_c = std::integral_constant<int, Cf::VEC_PIECES>;
+    auto copy_chunk = [&](int64_t c) {
+        unsigned char *buf = smem + (c & 1) * Cf::BUF;
         const int64_t t0 = c * kC;
         const int lenc = (int)((len - t0) < kC ? (len - t0) : kC);
-#pragma unroll
-        for (int i = 0; i < Cf::NK; ++i) {
-            const int64_t off = (t0 + min(kRow[i], lenc - 1)) * sQK + 8 * kPc[i];
-            rK[i] = *reinterpret_cast<const u32x4 *>(kh + off);
-            rQ[i] = *reinterpret_cast<const u32x4 *>(qh + off);
-        }
-#pragma unroll
-        for (int i = 0; i < Cf::NV; ++i)
-            rV[i] = *reinterpret_cast<const u32x4 *>(vh + (t0 + min(vRow[i], lenc - 1)) * sVO +
-                                                     8 * vPc[i]);
         const unsigned char *rec = ws + ((base + c) * p.Hv + h) * (int64_t)WSB;
+        auto srcK = [&](int row, int pc) { return kb + (t0 + min(row, lenc - 1)) * rowqk + 16 * pc; };
+        auto srcQ = [&](int row, int pc) { return qb + (t0 + min(row, lenc - 1)) * rowqk + 16 * pc; };
+        auto srcV = [&](int row, int pc) { return vb + (t0 + min(row, lenc - 1)) * rowv + 16 * pc; };
+        auto srcT = [&](int row, int pc) { return rec + row * 128 + 16 * pc; };
+        auto srcP = [&](int row, int pc) { return rec + kC * kC * 2 + row * 128 + 16 * pc; };
+        auto srcE = [&](int, int pc) { return rec + 2 * kC * kC * 2 + 16 * pc; };
+        // With three waves per SIMD (168 registers each) the per-block
+        // offsets do not fit when hoisted out of the chunk loop: there the
+        // lane index is made opaque so that they are recomputed each chunk.
+        int ln = lane;
+        if constexpr (Cf::NW > 8) asm volatile("" : "+v"(ln));
 #pragma unroll
-        for (int i = 0; i < Cf::NT; ++i) {
-            rT[i] = reinterpret_cast<const u32x4 *>(rec)[tPc[i]];
-            rP[i] = reinterpret_cast<const u32x4 *>(rec + kC * kC * 2)[tPc[i]];
+        for (int j = 0; j < Cf::NBLK; ++j) {
+            if (j % NH != hw) continue;  // uniform over the wave
+            if (j < Cf::BLK_K) {
+                block(buf + Cf::OFF_K, j, ln, SK_c{}, PK_c{}, srcK);
+            } else if (j < 2 * Cf::BLK_K) {
+                block(buf + Cf::OFF_Q, j - Cf::BLK_K, ln, SK_c{}, PK_c{}, srcQ);
+            } else if (j < 2 * Cf::BLK_K + Cf::BLK_V) {
+                block(buf + Cf::OFF_V, j - 2 * Cf::BLK_K, ln, SV_c{}, PV_c{}, srcV);
+            } else if (j < 2 * Cf::BLK_K + Cf::BLK_V + Cf::BLK_T) {
+                block(buf + Cf::OFF_T, j - 2 * Cf::BLK_K - Cf::BLK_V, ln, ST_c{}, PT_c{}, srcT);
+            } else if (j < 2 * Cf::BLK_K + Cf::BLK_V + 2 * Cf::BLK_T) {
+                block(buf + Cf::OFF_P, j - 2 * Cf::BLK_K - Cf::BLK_V - Cf::BLK_T, ln, ST_c{}, PT_c{}, srcP);
+            } else {
+                block(buf + Cf::OFF_VEC, 0, ln, S64_c{}, PE_c{}, srcE);
+            }
         }
-#pragma unroll
-        for (int i = 0; i < Cf::NVEC; ++i)
-            rE[i] = reinterpret_cast<const u32x4 *>(rec + 2 * kC * kC * 2)[ePc[i]];
     };
-    auto store_chunk = [&](int64_t c) {
-        unsigned char *b = smem + (c & 1) * Cf::BUF;
-        const int lenc = (int)((len - c * kC) < kC ? (len - c * kC) : kC);
-        const u32x4 z4 = {0u, 0u, 0u, 0u};
-        DT *sK = reinterpret_cast<DT *>(b + Cf::OFF_K);
-        DT *sQ = reinterpret_cast<DT *>(b + Cf::OFF_Q);
-#pragma unroll
-        for (int i = 0; i < Cf::NK; ++i) {
-            const bool ok = kRow[i] < lenc;  // rows past the end are zero
-            *reinterpret_cast<u32x4 *>(sK + kRow[i] * PK + 8 * kPc[i]) = ok ? rK[i] : z4;
-            *reinterpret_cast<u32x4 *>(sQ + kRow[i] * PK + 8 * kPc[i]) = ok ? rQ[i] : z4;
-        }
-#pragma unroll
-        for (int i = 0; i < Cf::NV; ++i)
-            *reinterpret_cast<u32x4 *>(b + Cf::OFF_V + vRow[i] * Cf::PVB + 16 * vPc[i]) =
-                vRow[i] < lenc ? rV[i] : z4;
-        DT *sT = reinterpret_cast<DT *>(b + Cf::OFF_T);
-        DT *sP = reinterpret_cast<DT *>(b + Cf::OFF_P);
-#pragma unroll
-        for (int i = 0; i < Cf::NT; ++i) {
-            const int r = tPc[i] / Cf::PPT, col = (tPc[i] % Cf::PPT) * 8;
-            *reinterpret_cast<u32x4 *>(sT + r * PT + col) = rT[i];
-            *reinterpret_cast<u32x4 *>(sP + r * PT + col) = rP[i];
-        }
-#pragma unroll
-        for (int i = 0; i < Cf::NVEC; ++i) reinterpret_cast<u32x4 *>(b + Cf::OFF_VEC)[ePc[i]] = rE[i];
-    };
-
-    // Loads are never skipped either: past the last chunk the loads repeat the
-    // last chunk (never stored).
-    const int64_t last = nchunks - 1;
-    if (nchunks > 0) {
-        load_chunk(0);
-        store_chunk(0);
-        load_chunk(last < 1 ? last : 1);
-    }
-    __syncthreads();
+    if (nchunks > 0) copy_chunk(0);
+    __syncthreads();  // waits for this wave's copies, then the workgroup barrier
     for (int64_t c = 0; c < nchunks; ++c) {
-        if (c + 1 < nchunks) store_chunk(c + 1);
-        load_chunk(c + 2 < last ? c + 2 : last);
+        if (c + 1 < nchunks) copy_chunk(c + 1);
         __syncthreads();
     }
 }
