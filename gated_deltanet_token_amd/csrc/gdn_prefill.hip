@@ -402,8 +402,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillParams p, unsigned cha
         }
         n = lo;
     } else {
-        const int64_t per = (p.seq_len + kC - 1) / kC;
-        n = (int)(slot / per);
+        // chunks per sequence and slots both fit 32 bits (the ABI bounds them)
+        const uint32_t per = (uint32_t)((p.seq_len + kC - 1) / kC);
+        n = (int)((uint32_t)slot / per);
     }
     int64_t tok0, len;
     seq_bounds(p, n, tok0, len);
@@ -416,24 +417,38 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillParams p, unsigned cha
     const DT *kh = reinterpret_cast<const DT *>(p.k) + t0 * sQK + (int64_t)grp * D;
     const DT *qh = reinterpret_cast<const DT *>(p.q) + t0 * sQK + (int64_t)grp * D;
 
+    // alpha, beta (wave 0) and the K, Q rows are all requested before any
+    // of them is used, so their latencies overlap
+    float a_t = 1.f, b_t = 0.f;
+    if (wave == 0) {
+        const int rr = lane < lenc ? lane : lenc - 1;
+        a_t = p.alpha[(t0 + rr) * p.Hv + h];
+        b_t = p.beta[(t0 + rr) * p.Hv + h];
+    }
     // K, Q rows -> LDS (rows past the end of the sequence are zero)
     {
         constexpr int PPR = D / EPP;
+        constexpr int NPC = kC * PPR / 256;  // pieces per thread
+        static_assert(kC * PPR % 256 == 0, "whole pieces per thread");
         const u32x4 z4 = {0u, 0u, 0u, 0u};
-        for (int i = tid; i < kC * PPR; i += 256) {
-            const int r = i / PPR, pc = i % PPR;
+        u32x4 kv[NPC], qv[NPC];
+#pragma unroll
+        for (int j = 0; j < NPC; ++j) {
+            const int i = tid + 256 * j, r = i / PPR, pc = i % PPR;
             const int rr = r < lenc ? r : lenc - 1;
-            const u32x4 kv = *reinterpret_cast<const u32x4 *>(kh + (int64_t)rr * sQK + pc * EPP);
-            const u32x4 qv = *reinterpret_cast<const u32x4 *>(qh + (int64_t)rr * sQK + pc * EPP);
-            *reinterpret_cast<u32x4 *>(sK + r * PK + pc * EPP) = r < lenc ? kv : z4;
-            *reinterpret_cast<u32x4 *>(sQ + r * PK + pc * EPP) = r < lenc ? qv : z4;
+            kv[j] = *reinterpret_cast<const u32x4 *>(kh + (int64_t)rr * sQK + pc * EPP);
+            qv[j] = *reinterpret_cast<const u32x4 *>(qh + (int64_t)rr * sQK + pc * EPP);
+        }
+#pragma unroll
+        for (int j = 0; j < NPC; ++j) {
+            const int i = tid + 256 * j, r = i / PPR, pc = i % PPR;
+            *reinterpret_cast<u32x4 *>(sK + r * PK + pc * EPP) = r < lenc ? kv[j] : z4;
+            *reinterpret_cast<u32x4 *>(sQ + r * PK + pc * EPP) = r < lenc ? qv[j] : z4;
         }
     }
     unsigned char *rec = ws + (slot * p.Hv + h) * (int64_t)ws_bytes_per_chunk<DT>();
     if (wave == 0) {
-        const int rr = lane < lenc ? lane : lenc - 1;
-        const float a = p.alpha[(t0 + rr) * p.Hv + h];
-        const float b = p.beta[(t0 + rr) * p.Hv + h];
+        const float a = a_t, b = b_t;
         const bool ok = lane < lenc;
         const float x = wave_inclusive_scan(__logf(fmaxf(ok ? a : 1.f, FLT_MIN)));
         const float glast = __shfl(x, 63, 64);
@@ -670,8 +685,7 @@ template <int D, int NC, int NH> struct ChainDbCfg {
     static constexpr int BUF = OFF_VEC + 64 * 16;  // gamma, dec, beta + padding pieces
     static constexpr int OFF_HO = 2 * BUF;          // chain -> output handoff, per chain wave
     static constexpr int OFF_FLAG = OFF_HO + NC * Handoff<D, 1>::BYTES;
-    static constexpr int OFF_SINK = OFF_FLAG + 64;  // landing area of the L2 touches
-    static constexpr int LDS = OFF_SINK + 64 * 4;
+    static constexpr int LDS = OFF_FLAG + 64;
     // helper copies: LDS-DMA blocks of 64 16-byte slots; a row of a region is
     // `slots` slots of which the first `pieces` hold data (the rest pad)
     static constexpr int SK = PK * 2 / 16, SV = PVB / 16, ST = PT * 2 / 16;
@@ -775,9 +789,9 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
         // L2 prefetch wave. Owners: K and Q lines of q/k head grp belong to its
         // first value head's slice 0; T, P and the decay vectors of head h to
         // slice 0; a V line to the slice that starts it. A touch is a 4-byte
-        // load that lands in a scratch area of LDS nobody reads: it produces no
-        // register, so this wave never waits for one (plain barriers, no fence)
-        // and many chunks of touches stay in flight.
+        // load whose value is folded into a dummy one iteration later (the
+        // load has long completed by then); the helper's LDS-DMA copies run
+        // fastest when no other wave issues LDS-DMA loads.
         constexpr int NL = Cf::PF_LOADS;
         constexpr int LEAD = 1 + DEPTH + Cf::PF_AHEAD;  // chunk touched in iteration c: c + LEAD
         constexpr int QKL = (D * 2 + 127) / 128;        // lines per K or Q row
@@ -795,7 +809,9 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
         const unsigned char *vb = reinterpret_cast<const unsigned char *>(p.v) +
                                   (tok0 * sVO + (int64_t)h * D + dv0) * 2;
         const int64_t rowqk = sQK * 2, rowv = sVO * 2;
-        uint32_t *sink = reinterpret_cast<uint32_t *>(smem + Cf::OFF_SINK);
+        uint32_t pend[NL], acc = 0;
+#pragma unroll
+        for (int j = 0; j < NL; ++j) pend[j] = 0;
         auto touch = [&](int64_t c) {
             const int64_t t0 = c * kC;
             const int rows = c < nchunks ? (int)((len - t0) < kC ? (len - t0) : kC) : 0;
@@ -813,7 +829,8 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
                 } else if (i < ntot && rows > 0) {
                     a = rec + (int64_t)(i - nqk - nv) * 128;
                 }
-                __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t *>(a), sink, 4, 0, 0);
+                acc ^= pend[j];
+                pend[j] = *reinterpret_cast<const uint32_t *>(a);
             }
         };
         // chunk c + 1 + DEPTH is loaded by the helpers in iteration c and was
@@ -824,12 +841,14 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
 #pragma unroll
             for (int j = 1 + DEPTH; j < LEAD; ++j) touch(j);
         }
-        __builtin_amdgcn_s_barrier();
+        __syncthreads();
         for (int64_t c = 0; c < nchunks; ++c) {
             touch(c + LEAD);
-            __builtin_amdgcn_s_barrier();
+            __syncthreads();
         }
-        __builtin_amdgcn_s_waitcnt(0);  // no touch may land after the workgroup ends
+#pragma unroll
+        for (int j = 0; j < NL; ++j) acc ^= pend[j];
+        asm volatile("" ::"v"(acc));  // keeps the touches
         return;
     }
 
@@ -1001,15 +1020,15 @@ hipError_t launch_prefill(const PrefillParams &p, int dtype, int D, int num_cus,
         if (dtype == 1 && D == 128) {
             switch (ns) {
             case 1: return launch_split<__bf16, 128, 4, 32>(p, w, nslots, 1, stream);
-            case 2: return launch_split_db<128, 4, 3>(p, w, nslots, 2, stream);
-            case 4: return launch_split_db<128, 2, 3>(p, w, nslots, 4, stream);
-            default: return launch_split_db<128, 1, 5>(p, w, nslots, 8, stream);
+            case 2: return launch_split_db<128, 4, 1>(p, w, nslots, 2, stream);
+            case 4: return launch_split_db<128, 2, 1>(p, w, nslots, 4, stream);
+            default: return launch_split_db<128, 1, 1>(p, w, nslots, 8, stream);
             }
         } else if (dtype == 1 && D == 64) {
             switch (ns) {
-            case 1: return launch_split_db<64, 4, 3>(p, w, nslots, 1, stream);
-            case 2: return launch_split_db<64, 2, 3>(p, w, nslots, 2, stream);
-            default: return launch_split_db<64, 1, 5>(p, w, nslots, 4, stream);
+            case 1: return launch_split_db<64, 4, 1>(p, w, nslots, 1, stream);
+            case 2: return launch_split_db<64, 2, 1>(p, w, nslots, 2, stream);
+            default: return launch_split_db<64, 1, 1>(p, w, nslots, 4, stream);
             }
         } else if (dtype == 0 && D == 64) {
             switch (ns) {
