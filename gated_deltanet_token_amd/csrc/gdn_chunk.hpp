@@ -589,19 +589,73 @@ __device__ __forceinline__ bf16x4 ld_tr(const __bf16 *p) {
     return __builtin_bit_cast(bf16x4, v);
 }
 
+// Unpadded LDS rows of ROWB bytes for the double-buffered chain: data piece
+// p (16 bytes) of row r sits in slot p ^ swz_f(r). The chain reads a staged
+// tile in two ways: one piece of 16 consecutive rows (fragments in chain
+// assignment) and two adjacent pieces of 8 consecutive rows (transposing
+// reads); with this f both touch every bank once per 32 lanes, for rows of
+// 32, 64, 128 and 256 bytes. f depends on r only through r % 16.
+template <int ROWB> __host__ __device__ constexpr int swz_f(int r) {
+    constexpr int NP = ROWB / 16;
+    static_assert(NP == 2 || NP == 4 || NP == 8 || NP == 16, "row length");
+    constexpr int S = NP == 16 ? 0 : NP == 8 ? 1 : NP == 4 ? 2 : 3;
+    return (((r >> S) & (NP / 2 - 1)) << 1) | ((r >> 3) & 1);
+}
+
+// Columns col .. col + 3 (col % 4 == 0) of row rb + rl of a swizzled tile;
+// rb is a multiple of 16 and 0 <= rl < 16.
+template <int ROWB>
+__device__ __forceinline__ const __bf16 *swz_at(const __bf16 *base, int rb, int rl, int col) {
+    const int off = (rb + rl) * ROWB + (((col >> 3) ^ swz_f<ROWB>(rl)) << 4) + ((col & 7) << 1);
+    return reinterpret_cast<const __bf16 *>(reinterpret_cast<const unsigned char *>(base) + off);
+}
+
+// Fragment in chain assignment from a swizzled tile: row rb + rl, columns
+// c0 .. c0 + 3 and c0 + 16 .. c0 + 19.
+template <int ROWB>
+__device__ __forceinline__ void ld_chain_s(const __bf16 *base, int rb, int rl, int c0, bf16x8 &f) {
+    const bf16x4 a = *reinterpret_cast<const bf16x4 *>(swz_at<ROWB>(base, rb, rl, c0));
+    const bf16x4 b = *reinterpret_cast<const bf16x4 *>(swz_at<ROWB>(base, rb, rl, c0 + 16));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f[e] = a[e];
+        f[e + 4] = b[e];
+    }
+}
+
 // A fragment (chain assignment) of K^T for rows 16 a .. 16 a + 15 of K^T (dk)
-// and the 32 tokens of block k2, read from row-major K (pitch PK).
-template <int PK>
-__device__ __forceinline__ void ld_kt_frag(const __bf16 *K, int a, int k2, int g4, int c16,
-                                           bf16x8 &f) {
-    const __bf16 *p = K + (32 * k2 + 4 * g4 + (c16 >> 2)) * PK + 16 * a + 4 * (c16 & 3);
-    const bf16x4 lo = ld_tr(p), hi = ld_tr(p + 16 * PK);
+// and the 32 tokens of block k2, read from the swizzled row-major K.
+template <int ROWB>
+__device__ __forceinline__ void ld_kt_frag_s(const __bf16 *K, int a, int k2, int g4, int c16,
+                                             bf16x8 &f) {
+    const int rl = 4 * g4 + (c16 >> 2), col = 16 * a + 4 * (c16 & 3);
+    const bf16x4 lo = ld_tr(swz_at<ROWB>(K, 32 * k2, rl, col));
+    const bf16x4 hi = ld_tr(swz_at<ROWB>(K, 32 * k2 + 16, rl, col));
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         f[e] = lo[e];
         f[e + 4] = hi[e];
     }
 }
+
+// Fragments of a lower-triangular 64x64 chunk matrix M (T or P) in chain
+// assignment, the order in which they are staged: fragment i, lane
+// l = 16 g4 + c16, element e holds M[16 rb + c16][32 k2 + 4 g4 + (e & 3) +
+// 16 (e >> 2)] with (rb, k2) = (0,0), (1,0), (2,0), (2,1), (3,0), (3,1) for
+// i = 0..5. These cover every nonzero block of M; entries above the block
+// diagonal are zero.
+constexpr int kTriFrags = 6;
+__host__ __device__ constexpr int tri_rb(int i) { return i < 2 ? i : 2 + (i - 2) / 2; }
+__host__ __device__ constexpr int tri_k2(int i) { return (i == 3 || i == 5) ? 1 : 0; }
+
+// One staged chunk of the double-buffered chain (bf16): K, Q [64][D] and
+// V [64][DVS] (the workgroup's value columns) as swizzled rows; T and P as
+// kTriFrags fragments x 64 lanes x 16 bytes; decay vectors gamma, dec, beta.
+struct DbSmem {
+    const __bf16 *K, *Q, *V;
+    const bf16x8 *T, *P;
+    const float *gam, *dec, *beta;
+};
 
 // LDS handoff from a chain wave to its output wave: S^T fragments and U
 // fragments in lane order (each lane reads back what the same lane wrote).
@@ -636,18 +690,22 @@ __device__ __forceinline__ void set_flag(int *flag, int v) {
     __hip_atomic_store(flag, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// Chain wave, one chunk. LDS: K, Q row-major (pitch PK), V row-major with the
-// workgroup's value columns (pitch PV), T (pitch PT), decay vectors. Publishes
-// S^T (flag value 2c + 1) and U (2c + 2) for the output wave, then updates S.
-// KT_LATE: read the second half of the K^T fragments only after U (fewer
-// live registers, for workgroups with three waves per SIMD).
-template <int D, int NB, int PK, int PT, int PV, bool KT_LATE = false>
-__device__ __forceinline__ void chain_core_bf16(const ChainSmem<__bf16> &m, f32x4 (&st)[D / 16][NB],
-                                                int wdv, Handoff<D, NB> ho, int *flag, int c, int g4,
-                                                int c16, int lane) {
+// Chain wave, one chunk (columns wdv .. wdv + 16 NB of the staged V).
+// Publishes S^T (flag value 2c + 1) and U (2c + 2) for the output wave, then
+// updates S. KT_LATE: read the second half of the K^T fragments only after U
+// (fewer live registers, for workgroups with three waves per SIMD).
+template <int D, int DVS, int NB, bool KT_LATE = false>
+__device__ __forceinline__ void chain_core_db(const DbSmem &m, f32x4 (&st)[D / 16][NB], int wdv,
+                                              Handoff<D, NB> ho, int *flag, int c, int g4, int c16,
+                                              int lane) {
     using F = bf16x8;
     constexpr int KS = D / 32;
     constexpr int NKT = D / 16;
+    constexpr int KR = D * 2, VR = DVS * 2;
+    // With three waves per SIMD the swizzled offsets do not fit when hoisted
+    // out of the chunk loop: the lane coordinates are made opaque there, so
+    // that the offsets are recomputed for every chunk.
+    if constexpr (KT_LATE) asm volatile("" : "+v"(g4), "+v"(c16));
     // S^T as B fragments, published first
     F sf[KS][NB];
 #pragma unroll
@@ -659,18 +717,13 @@ __device__ __forceinline__ void chain_core_bf16(const ChainSmem<__bf16> &m, f32x
         }
     set_flag(flag, 2 * c + 1);
     // operands of K S^T and of U = T R first
-    const __bf16 *kp = m.K + c16 * PK + 4 * g4;
     F fk[KS][4], ft[6], fkt[NKT][2];
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) ld_chain(kp + 16 * mt * PK + 32 * kk, fk[kk][mt]);
-    ld_chain(m.T + c16 * PT + 4 * g4, ft[0]);
-    ld_chain(m.T + (16 + c16) * PT + 4 * g4, ft[1]);
-    ld_chain(m.T + (32 + c16) * PT + 4 * g4, ft[2]);
-    ld_chain(m.T + (32 + c16) * PT + 32 + 4 * g4, ft[3]);
-    ld_chain(m.T + (48 + c16) * PT + 4 * g4, ft[4]);
-    ld_chain(m.T + (48 + c16) * PT + 32 + 4 * g4, ft[5]);
+        for (int mt = 0; mt < 4; ++mt) ld_chain_s<KR>(m.K, 16 * mt, c16, 32 * kk + 4 * g4, fk[kk][mt]);
+#pragma unroll
+    for (int i = 0; i < kTriFrags; ++i) ft[i] = m.T[i * 64 + lane];
     phase_fence();
     // K S^T; meanwhile the operands of R and of the state update are read
     f32x4 racc[4][NB];
@@ -695,13 +748,13 @@ __device__ __forceinline__ void chain_core_bf16(const ChainSmem<__bf16> &m, f32x
         if constexpr (!KT_LATE) dec[mt] = *reinterpret_cast<const f32x4 *>(m.dec + tb);
 #pragma unroll
         for (int b = 0; b < NB; ++b)
-            v4[mt][b] = ld_tr(m.V + (16 * mt + 4 * g4 + (c16 >> 2)) * PV + wdv + 16 * b +
-                              4 * (c16 & 3));
+            v4[mt][b] = ld_tr(swz_at<VR>(m.V, 16 * mt, 4 * g4 + (c16 >> 2),
+                                         wdv + 16 * b + 4 * (c16 & 3)));
     }
 #pragma unroll
     for (int a = 0; a < (KT_LATE ? NKT / 2 : NKT); ++a)
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) ld_kt_frag<PK>(m.K, a, k2, g4, c16, fkt[a][k2]);
+        for (int k2 = 0; k2 < 2; ++k2) ld_kt_frag_s<KR>(m.K, a, k2, g4, c16, fkt[a][k2]);
     phase_fence();
     // R = beta (V - gamma K S^T), U = T R
 #pragma unroll
@@ -733,7 +786,7 @@ __device__ __forceinline__ void chain_core_bf16(const ChainSmem<__bf16> &m, f32x
 #pragma unroll
         for (int a = NKT / 2; a < NKT; ++a)
 #pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) ld_kt_frag<PK>(m.K, a, k2, g4, c16, fkt[a][k2]);
+            for (int k2 = 0; k2 < 2; ++k2) ld_kt_frag_s<KR>(m.K, a, k2, g4, c16, fkt[a][k2]);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
             dec[mt] = *reinterpret_cast<const f32x4 *>(m.dec + 16 * mt + 4 * g4);
@@ -768,25 +821,23 @@ __device__ __forceinline__ void chain_core_bf16(const ChainSmem<__bf16> &m, f32x
 
 // Output wave, one chunk: O^T = (S Q^T) diag(gamma) + U^T P^T for the chain
 // wave's columns, stored for rows t < lenc (`oc` points at token 0 of the
-// chunk, first column of the wave).
-template <int D, int NB, int PK, int PT>
-__device__ __forceinline__ void out_core_bf16(const ChainSmem<__bf16> &m, Handoff<D, NB> ho,
-                                              int *flag, int c, __bf16 *oc, int64_t sVO, int lenc,
-                                              float scale, int g4, int c16, int lane) {
+// chunk, first column of the wave). S^T and U come from the chain wave
+// (flags 2c + 1, 2c + 2 on `flag`). The staged P fragments are, read as B
+// operands, the six fragments of P^T that U^T P^T needs.
+template <int D, int NB>
+__device__ __forceinline__ void out_core_db(const DbSmem &m, Handoff<D, NB> ho, int *flag, int c,
+                                            __bf16 *oc, int64_t sVO, int lenc, float scale, int g4,
+                                            int c16, int lane) {
     using F = bf16x8;
     constexpr int KS = D / 32;
-    const __bf16 *qp = m.Q + c16 * PK + 4 * g4;
-    F fq[KS][4], fp[6];
+    constexpr int KR = D * 2;
+    F fq[KS][4], fp[kTriFrags];
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) ld_chain(qp + 16 * mt * PK + 32 * kk, fq[kk][mt]);
-    ld_chain(m.P + c16 * PT + 4 * g4, fp[0]);
-    ld_chain(m.P + (16 + c16) * PT + 4 * g4, fp[1]);
-    ld_chain(m.P + (32 + c16) * PT + 4 * g4, fp[2]);
-    ld_chain(m.P + (32 + c16) * PT + 32 + 4 * g4, fp[3]);
-    ld_chain(m.P + (48 + c16) * PT + 4 * g4, fp[4]);
-    ld_chain(m.P + (48 + c16) * PT + 32 + 4 * g4, fp[5]);
+        for (int mt = 0; mt < 4; ++mt) ld_chain_s<KR>(m.Q, 16 * mt, c16, 32 * kk + 4 * g4, fq[kk][mt]);
+#pragma unroll
+    for (int i = 0; i < kTriFrags; ++i) fp[i] = m.P[i * 64 + lane];
     float gamr[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) gamr[mt] = m.gam[16 * mt + c16];

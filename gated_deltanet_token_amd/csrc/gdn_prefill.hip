@@ -339,6 +339,15 @@ template <typename DT> constexpr int ws_bytes_per_chunk() {
     return 2 * kC * kC * (int)sizeof(DT) + 3 * kC * 4;
 }
 
+// Fragment record (bf16, read by chain_db_kernel): T and P each as the
+// kTriFrags MFMA fragments that cover their nonzero blocks, in lane order
+// (6 KiB each), then gamma [64] | dec [64] | beta [64] (f32) padded to 1 KiB.
+// The chain copies it into LDS unchanged and reads one fragment per lane
+// with a single 16-byte load.
+constexpr int kFragBytes = kTriFrags * 64 * 16;
+constexpr int ws_bytes_frag() { return 2 * kFragBytes + 1024; }
+static_assert(ws_bytes_frag() <= ws_bytes_per_chunk<__bf16>(), "fragment record fits the query");
+
 template <typename DT, int D> struct PrepCfg {
     using P = ChunkPitch<DT, D>;
     static constexpr int SZ_K = kC * P::PK * (int)sizeof(DT);
@@ -357,12 +366,13 @@ template <typename DT, int D> struct PrepCfg {
 };
 
 // One workgroup (4 waves) per (chunk slot, value head): Gram products, decay,
-// T = (I + A)^{-1}; writes T, P, gamma, dec, beta to the workspace. About 52
-// KiB of LDS (bf16, D = 128), so three workgroups share a CU and hide each
-// other's latencies.
-template <typename DT, int D>
+// T = (I + A)^{-1}; writes T, P, gamma, dec, beta to the workspace (52 KiB
+// of LDS for bf16, D = 128: three workgroups share a CU and hide each
+// other's latencies). FRAG: the fragment record instead of dense rows.
+template <typename DT, int D, bool FRAG>
 __global__ __launch_bounds__(256) void prep_kernel(PrefillParams p, unsigned char *ws,
                                                    int remap_xcd) {
+    static_assert(!FRAG || sizeof(DT) == 2, "fragment records are bf16");
     using Cf = PrepCfg<DT, D>;
     using Pi = ChunkPitch<DT, D>;
     constexpr int PK = Pi::PK, PT = Pi::PT, PA = Pi::PA;
@@ -446,7 +456,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillParams p, unsigned cha
             *reinterpret_cast<u32x4 *>(sQ + r * PK + pc * EPP) = r < lenc ? qv[j] : z4;
         }
     }
-    unsigned char *rec = ws + (slot * p.Hv + h) * (int64_t)ws_bytes_per_chunk<DT>();
+    constexpr int WSB = FRAG ? ws_bytes_frag() : ws_bytes_per_chunk<DT>();
+    unsigned char *rec = ws + (slot * p.Hv + h) * (int64_t)WSB;
     if (wave == 0) {
         const float a = a_t, b = b_t;
         const bool ok = lane < lenc;
@@ -457,7 +468,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillParams p, unsigned cha
         sGam[lane] = gam;
         sDec[lane] = dec;
         sBeta[lane] = bet;
-        float *vec = reinterpret_cast<float *>(rec + 2 * kC * kC * sizeof(DT));
+        float *vec = reinterpret_cast<float *>(
+            rec + (FRAG ? 2 * kFragBytes : 2 * kC * kC * (int)sizeof(DT)));
         vec[lane] = gam;
         vec[kC + lane] = dec;
         vec[2 * kC + lane] = bet;
@@ -485,7 +497,22 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillParams p, unsigned cha
     __syncthreads();
     // T, P -> workspace as dense [64][64] rows; blocks above the diagonal
     // (never written in LDS) are stored as zeros
-    {
+    if constexpr (FRAG) {
+        // piece q: matrix q / (kTriFrags 64) (T, then P), fragment i, lane l;
+        // its halves are columns 32 k2 + 4 g4 .. +3 and 16 further of row
+        // 16 rb + c16, zero where the column block lies above the diagonal
+        const u32x2 z2 = {0u, 0u};
+        for (int q = tid; q < 2 * kTriFrags * 64; q += 256) {
+            const bool isP = q >= kTriFrags * 64;
+            const int qi = isP ? q - kTriFrags * 64 : q;
+            const int i = qi / 64, l = qi % 64, lg4 = l >> 4, lc16 = l & 15;
+            const int rb = tri_rb(i), k2 = tri_k2(i);
+            const DT *src = (isP ? sP : sT) + (16 * rb + lc16) * PT + 32 * k2 + 4 * lg4;
+            const u32x2 lo = 2 * k2 > rb ? z2 : *reinterpret_cast<const u32x2 *>(src);
+            const u32x2 hi = 2 * k2 + 1 > rb ? z2 : *reinterpret_cast<const u32x2 *>(src + 16);
+            *reinterpret_cast<u32x4 *>(rec + (int64_t)q * 16) = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+    } else {
         constexpr int PPR = kC / EPP;
         const u32x4 z4 = {0u, 0u, 0u, 0u};
         DT *gT = reinterpret_cast<DT *>(rec);
@@ -651,14 +678,16 @@ __global__ __launch_bounds__(256) void chain_kernel(PrefillParams p, const unsig
 // NW = 2 NC + 1 + NH waves owning DVS = 16 NC value columns of one head:
 //   waves 0 .. NC-1        chain: K S^T, R, U = T R, state update (the
 //                          sequential part); each owns 16 value columns;
-//   waves NC .. 2 NC-1     output: O for the same columns, from the chain
-//                          wave's S^T and U handed over through LDS;
+//   waves NC .. 2 NC-1     output: O for the same columns from the chain
+//                          wave's S^T and U, handed over through LDS;
 //   wave 2 NC              L2 prefetch: touches the lines of chunk
 //                          c + 1 + DEPTH + PF_AHEAD once per owner workgroup;
 //   the rest               helpers: copy chunk c + 1 into the other LDS buffer
-//                          while chunk c is processed, and load chunk c + 2.
-// One barrier per chunk. All staging is plain row copies: the chain reads
-// the columns of K and V with transposing LDS reads.
+//                          while chunk c is processed.
+// One barrier per chunk. K, Q and V are staged as unpadded rows whose 16-byte
+// pieces are permuted per row (swz_f); the copies apply the permutation
+// through their source addresses. T, P and the decay vectors are the
+// workspace record copied unchanged. Every copy is one LDS-DMA load per KiB.
 template <int D, int NC, int NH> struct ChainDbCfg {
     using DT = __bf16;
     static constexpr int NW = 2 * NC + 1 + NH;
@@ -667,36 +696,43 @@ template <int D, int NC, int NH> struct ChainDbCfg {
     static constexpr int DEPTH = 1;
     static constexpr int PF_AHEAD = 4;   // chunks a line is touched ahead of its load
     static constexpr int PF_LOADS = 8;   // line touches per lane per chunk (at most)
-    static constexpr int PK = D + 8;     // K, Q row pitch (elements): 16 B skew per row
-    static constexpr int PT = kC + 8;    // T, P row pitch: 144 B, a whole number of 16 B slots
-    // V row pitch: an odd multiple of 32 bytes, so that the transposing reads
-    // (8 rows x 32 bytes per 32 lanes) hit distinct banks
-    static constexpr int PVB = ((DVS * 2 / 32) % 2 == 1) ? DVS * 2 : DVS * 2 + 32;
-    static constexpr int PV = PVB / 2;
-    static constexpr int SZ_K = kC * PK * 2;
-    static constexpr int SZ_V = kC * PVB;
-    static constexpr int SZ_T = kC * PT * 2;
+    static constexpr int KR = D * 2;     // K, Q row bytes
+    static constexpr int VR = DVS * 2;   // V row bytes
+    static constexpr int WSB = ws_bytes_frag();
+    static constexpr int SZ_K = kC * KR;
+    static constexpr int SZ_V = kC * VR;
     static constexpr int OFF_K = 0;
     static constexpr int OFF_Q = OFF_K + SZ_K;
     static constexpr int OFF_V = OFF_Q + SZ_K;
-    static constexpr int OFF_T = OFF_V + SZ_V;
-    static constexpr int OFF_P = OFF_T + SZ_T;
-    static constexpr int OFF_VEC = OFF_P + SZ_T;
-    static constexpr int BUF = OFF_VEC + 64 * 16;  // gamma, dec, beta + padding pieces
+    static constexpr int OFF_REC = OFF_V + SZ_V;  // the workspace record: T, P, vectors
+    static constexpr int OFF_T = OFF_REC;
+    static constexpr int OFF_P = OFF_T + kFragBytes;
+    static constexpr int OFF_VEC = OFF_P + kFragBytes;
+    static constexpr int BUF = OFF_REC + WSB;
     static constexpr int OFF_HO = 2 * BUF;          // chain -> output handoff, per chain wave
     static constexpr int OFF_FLAG = OFF_HO + NC * Handoff<D, 1>::BYTES;
     static constexpr int LDS = OFF_FLAG + 64;
-    // helper copies: LDS-DMA blocks of 64 16-byte slots; a row of a region is
-    // `slots` slots of which the first `pieces` hold data (the rest pad)
-    static constexpr int SK = PK * 2 / 16, SV = PVB / 16, ST = PT * 2 / 16;
-    static constexpr int BLK_K = kC * SK / 64, BLK_V = kC * SV / 64, BLK_T = kC * ST / 64;
-    static constexpr int NBLK = 2 * BLK_K + BLK_V + 2 * BLK_T + 1;  // K, Q, V, T, P, vectors
-    static constexpr int VEC_PIECES = 3 * kC / 4;
-    static_assert(PK * 2 % 16 == 0 && PVB % 16 == 0 && PT * 2 % 16 == 0, "slot pitches");
-    static_assert(kC * SK % 64 == 0 && kC * SV % 64 == 0 && kC * ST % 64 == 0, "whole blocks");
+    // helper copies: LDS-DMA blocks of 64 16-byte slots
+    static constexpr int BLK_K = SZ_K / 1024, BLK_V = SZ_V / 1024, BLK_R = WSB / 1024;
+    static constexpr int NBLK = 2 * BLK_K + BLK_V + BLK_R;  // K, Q, V, record
+    static_assert(SZ_K % 1024 == 0 && SZ_V % 1024 == 0 && WSB % 1024 == 0, "whole blocks");
     static_assert(NC >= 1 && NH >= 1 && NW <= 16, "wave roles");
     static_assert(LDS <= 160 * 1024, "LDS budget of a gfx950 CU");
+    // Role of hardware wave w. Waves w and w + 4 of a workgroup share a SIMD
+    // (and its MFMA unit). With two chain waves they take hardware waves 2
+    // and 3, alone on their SIMDs, and the P / prefetch wave and the helper
+    // pair with the output waves, which mostly wait; otherwise roles follow
+    // the wave order (with four chain waves each shares with its output wave).
+    static __device__ __forceinline__ int role(int w) {
+        return NC == 2 && NH == 1 ? (w < 2 ? w + 2 : w < 4 ? w - 2 : w) : w;
+    }
 };
+
+// LDS-DMA load of 16 bytes per lane (global -> LDS without registers): lane l
+// writes lds + 16 l, so a wave fills one contiguous KiB.
+__device__ __forceinline__ void dma16(const unsigned char *src, unsigned char *lds) {
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t *>(src), lds, 16, 0, 0);
+}
 
 // The LDS buffers allow one workgroup per CU.
 template <int D, int NC, int NH>
@@ -704,14 +740,14 @@ __global__ __launch_bounds__((ChainDbCfg<D, NC, NH>::NW * 64)) __attribute__((am
 void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int remap_xcd) {
     using DT = __bf16;
     using Cf = ChainDbCfg<D, NC, NH>;
-    constexpr int NKT = D / 16, PK = Cf::PK, PT = Cf::PT, PV = Cf::PV;
+    constexpr int NKT = D / 16;
     constexpr int DEPTH = Cf::DEPTH;
-    constexpr int WSB = ws_bytes_per_chunk<DT>();
+    constexpr int WSB = Cf::WSB;
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::LDS];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = Cf::role(__builtin_amdgcn_readfirstlane(tid >> 6));
     const int g4 = lane >> 4;
     const int c16 = lane & 15;
 
@@ -733,13 +769,12 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
     auto smem_view = [&](int64_t c) {
         const unsigned char *b = smem + (c & 1) * Cf::BUF;
         const float *vec = reinterpret_cast<const float *>(b + Cf::OFF_VEC);
-        return ChainSmem<DT>{reinterpret_cast<const DT *>(b + Cf::OFF_K),
-                             reinterpret_cast<const DT *>(b + Cf::OFF_Q),
-                             nullptr,
-                             reinterpret_cast<const DT *>(b + Cf::OFF_V),
-                             reinterpret_cast<const DT *>(b + Cf::OFF_T),
-                             reinterpret_cast<const DT *>(b + Cf::OFF_P),
-                             vec, vec + kC, vec + 2 * kC};
+        return DbSmem{reinterpret_cast<const DT *>(b + Cf::OFF_K),
+                      reinterpret_cast<const DT *>(b + Cf::OFF_Q),
+                      reinterpret_cast<const DT *>(b + Cf::OFF_V),
+                      reinterpret_cast<const bf16x8 *>(b + Cf::OFF_T),
+                      reinterpret_cast<const bf16x8 *>(b + Cf::OFF_P),
+                      vec, vec + kC, vec + 2 * kC};
     };
 
     if (wave < 2 * NC) {
@@ -760,8 +795,8 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): initial state; see prefill_kernel
             __syncthreads();
             for (int64_t c = 0; c < nchunks; ++c) {
-                chain_core_bf16<D, 1, PK, PT, PV, (Cf::NW > 8)>(smem_view(c), st, wdv, ho, flag,
-                                                                (int)c, g4, c16, lane);
+                chain_core_db<D, Cf::DVS, 1, (Cf::NW > 8)>(smem_view(c), st, wdv, ho, flag, (int)c,
+                                                           g4, c16, lane);
                 __syncthreads();
             }
             if (p.s_final) {
@@ -777,8 +812,8 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
             __syncthreads();
             for (int64_t c = 0; c < nchunks; ++c) {
                 const int lenc = (int)((len - c * kC) < kC ? (len - c * kC) : kC);
-                out_core_bf16<D, 1, PK, PT>(smem_view(c), ho, flag, (int)c, oh + c * kC * sVO, sVO,
-                                            lenc, p.scale, g4, c16, lane);
+                out_core_db<D, 1>(smem_view(c), ho, flag, (int)c, oh + c * kC * sVO, sVO, lenc,
+                                  p.scale, g4, c16, lane);
                 __syncthreads();
             }
         }
@@ -816,9 +851,12 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
             const int64_t t0 = c * kC;
             const int rows = c < nchunks ? (int)((len - t0) < kC ? (len - t0) : kC) : 0;
             const unsigned char *rec = ws + ((base + c) * p.Hv + h) * (int64_t)WSB;
+            // three waves per SIMD: line offsets recomputed per chunk (see copy_chunk)
+            int ln = lane;
+            if constexpr (Cf::NW > 8) asm volatile("" : "+v"(ln));
 #pragma unroll
             for (int j = 0; j < NL; ++j) {
-                const int i = lane + 64 * j;
+                const int i = ln + 64 * j;
                 const unsigned char *a = kb;  // lanes without a line re-touch row 0
                 if (i < nqk) {
                     const int iq = i % (QKL * kC), r = iq / QKL, part = iq % QKL;
@@ -855,8 +893,7 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
     // helper waves: copy chunk c + 1 into the other buffer with LDS-DMA loads
     // (global -> LDS without registers). Block j of a chunk is issued by
     // helper j % NH; rows past the end of the sequence repeat its last row
-    // (finite values that the decay and beta of those rows cancel exactly) and
-    // pad slots re-load a valid piece of their row.
+    // (finite values that the decay and beta of those rows cancel exactly).
     const int hw = wave - (2 * NC + 1);
     const unsigned char *qb = reinterpret_cast<const unsigned char *>(p.q) +
                               (tok0 * sQK + (int64_t)grp * D) * 2;
@@ -865,24 +902,18 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
     const unsigned char *vb = reinterpret_cast<const unsigned char *>(p.v) +
                               (tok0 * sVO + (int64_t)h * D + dv0) * 2;
     const int64_t rowqk = sQK * 2, rowv = sVO * 2;
-    // one 1 KiB block: slots 64 b .. 64 b + 63 of a region whose rows have
-    // SLOTS slots of which PIECES hold data; src(row, piece) gives the source
-    auto block = [&](unsigned char *dst, int b, int ln, auto slots_c, auto pieces_c, auto src) {
-        constexpr int SLOTS = decltype(slots_c)::value, PIECES = decltype(pieces_c)::value;
+    // one 1 KiB block: slots 64 b .. 64 b + 63 of a swizzled region with rows
+    // of ROWB bytes; LDS slot s of row r receives data piece s ^ swz_f(r),
+    // src(row, piece) gives its address
+    auto block = [&](unsigned char *dst, int b, int ln, auto rowb_c, auto src) {
+        constexpr int ROWB = decltype(rowb_c)::value, NP = ROWB / 16;
         const int slot = 64 * b + ln;
-        const int row = slot / SLOTS;
-        const int pc = min(slot % SLOTS, PIECES - 1);  // pad slots re-load a data piece
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t *>(src(row, pc)),
-                                         dst + 1024 * b, 16, 0, 0);
+        const int row = slot / NP;
+        const int pc = (slot % NP) ^ swz_f<ROWB>(row % 16);
+        dma16(src(row, pc), dst + 1024 * b);
     };
-    using SK_c = std::integral_constant<int, Cf::SK>;
-    using SV_c = std::integral_constant<int, Cf::SV>;
-    using ST_c = std::integral_constant<int, Cf::ST>;
-    using PK_c = std::integral_constant<int, D / 8>;
-    using PV_c = std::integral_constant<int, Cf::DVS / 8>;
-    using PT_c = std::integral_constant<int, kC / 8>;
-    using S64_c = std::integral_constant<int, 64>;
-    using PE_c = std::integral_constant<int, Cf::VEC_PIECES>;
+    using KR_c = std::integral_constant<int, Cf::KR>;
+    using VR_c = std::integral_constant<int, Cf::VR>;
     auto copy_chunk = [&](int64_t c) {
         unsigned char *buf = smem + (c & 1) * Cf::BUF;
         const int64_t t0 = c * kC;
@@ -891,29 +922,23 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
         auto srcK = [&](int row, int pc) { return kb + (t0 + min(row, lenc - 1)) * rowqk + 16 * pc; };
         auto srcQ = [&](int row, int pc) { return qb + (t0 + min(row, lenc - 1)) * rowqk + 16 * pc; };
         auto srcV = [&](int row, int pc) { return vb + (t0 + min(row, lenc - 1)) * rowv + 16 * pc; };
-        auto srcT = [&](int row, int pc) { return rec + row * 128 + 16 * pc; };
-        auto srcP = [&](int row, int pc) { return rec + kC * kC * 2 + row * 128 + 16 * pc; };
-        auto srcE = [&](int, int pc) { return rec + 2 * kC * kC * 2 + 16 * pc; };
         // With three waves per SIMD (168 registers each) the per-block
         // offsets do not fit when hoisted out of the chunk loop: there the
         // lane index is made opaque so that they are recomputed each chunk.
         int ln = lane;
         if constexpr (Cf::NW > 8) asm volatile("" : "+v"(ln));
+        constexpr int J1 = Cf::BLK_K, J2 = 2 * Cf::BLK_K, J3 = J2 + Cf::BLK_V;
 #pragma unroll
         for (int j = 0; j < Cf::NBLK; ++j) {
             if (j % NH != hw) continue;  // uniform over the wave
-            if (j < Cf::BLK_K) {
-                block(buf + Cf::OFF_K, j, ln, SK_c{}, PK_c{}, srcK);
-            } else if (j < 2 * Cf::BLK_K) {
-                block(buf + Cf::OFF_Q, j - Cf::BLK_K, ln, SK_c{}, PK_c{}, srcQ);
-            } else if (j < 2 * Cf::BLK_K + Cf::BLK_V) {
-                block(buf + Cf::OFF_V, j - 2 * Cf::BLK_K, ln, SV_c{}, PV_c{}, srcV);
-            } else if (j < 2 * Cf::BLK_K + Cf::BLK_V + Cf::BLK_T) {
-                block(buf + Cf::OFF_T, j - 2 * Cf::BLK_K - Cf::BLK_V, ln, ST_c{}, PT_c{}, srcT);
-            } else if (j < 2 * Cf::BLK_K + Cf::BLK_V + 2 * Cf::BLK_T) {
-                block(buf + Cf::OFF_P, j - 2 * Cf::BLK_K - Cf::BLK_V - Cf::BLK_T, ln, ST_c{}, PT_c{}, srcP);
+            if (j < J1) {
+                block(buf + Cf::OFF_K, j, ln, KR_c{}, srcK);
+            } else if (j < J2) {
+                block(buf + Cf::OFF_Q, j - J1, ln, KR_c{}, srcQ);
+            } else if (j < J3) {
+                block(buf + Cf::OFF_V, j - J2, ln, VR_c{}, srcV);
             } else {
-                block(buf + Cf::OFF_VEC, 0, ln, S64_c{}, PE_c{}, srcE);
+                dma16(rec + 1024 * (j - J3) + 16 * ln, buf + Cf::OFF_REC + 1024 * (j - J3));
             }
         }
     };
@@ -944,7 +969,7 @@ static hipError_t launch_split(const PrefillParams &p, unsigned char *ws, int64_
     const int64_t nchain = (int64_t)p.nseq * p.Hv * nsplit;
     if (nprep <= 0 || nprep > 0x7FFFFFFF || nchain <= 0 || nchain > 0x7FFFFFFF)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((prep_kernel<DT, D>), dim3((unsigned)nprep), dim3(256), 0, stream, p, ws,
+    hipLaunchKernelGGL((prep_kernel<DT, D, false>), dim3((unsigned)nprep), dim3(256), 0, stream, p, ws,
                        nprep % 8 == 0 ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -961,7 +986,7 @@ static hipError_t launch_split_db(const PrefillParams &p, unsigned char *ws, int
     if (nprep <= 0 || nprep > 0x7FFFFFFF || nchain <= 0 || nchain > 0x7FFFFFFF)
         return hipErrorInvalidValue;
     if (ChainDbCfg<D, NC, NH>::DVS * nsplit != D) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((prep_kernel<__bf16, D>), dim3((unsigned)nprep), dim3(256), 0, stream, p, ws,
+    hipLaunchKernelGGL((prep_kernel<__bf16, D, true>), dim3((unsigned)nprep), dim3(256), 0, stream, p, ws,
                        nprep % 8 == 0 ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
