@@ -659,13 +659,16 @@ struct DbSmem {
 
 // LDS handoff from a chain wave to its output wave: S^T fragments and U
 // fragments in lane order (each lane reads back what the same lane wrote).
+// U has two slots, by chunk parity: the output wave consumes U of chunk c
+// during chunk c + 1.
 template <int D, int NB> struct Handoff {
     static constexpr int KS = D / 32;
-    static constexpr int BYTES = (KS + 2) * NB * 64 * 16;
-    bf16x8 *sf, *fu;  // [KS][NB][64], [2][NB][64]
+    static constexpr int BYTES = (KS + 4) * NB * 64 * 16;
+    bf16x8 *sf, *fu;  // [KS][NB][64], [2 slots][2][NB][64]
     __device__ __forceinline__ Handoff(unsigned char *base)
         : sf(reinterpret_cast<bf16x8 *>(base)),
           fu(reinterpret_cast<bf16x8 *>(base) + KS * NB * 64) {}
+    __device__ __forceinline__ bf16x8 *u_slot(int c) const { return fu + (c & 1) * 2 * NB * 64; }
 };
 
 // Workgroup-local flags (an int in LDS) between two waves. The LDS executes
@@ -799,7 +802,7 @@ __device__ __forceinline__ void chain_core_db(const DbSmem &m, f32x4 (&st)[D / 1
         for (int b = 0; b < NB; ++b) {
             F fu;
             c_to_frag(u[2 * k2][b], u[2 * k2 + 1][b], fu);
-            ho.fu[(k2 * NB + b) * 64 + lane] = fu;
+            ho.u_slot(c)[(k2 * NB + b) * 64 + lane] = fu;
             f32x4 lo = u[2 * k2][b], hi = u[2 * k2 + 1][b];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -819,23 +822,42 @@ __device__ __forceinline__ void chain_core_db(const DbSmem &m, f32x4 (&st)[D / 1
         }
 }
 
-// Output wave, one chunk: O^T = (S Q^T) diag(gamma) + U^T P^T for the chain
-// wave's columns, stored for rows t < lenc (`oc` points at token 0 of the
-// chunk, first column of the wave). S^T and U come from the chain wave
-// (flags 2c + 1, 2c + 2 on `flag`). The staged P fragments are, read as B
-// operands, the six fragments of P^T that U^T P^T needs.
+// Output wave: O^T = (S Q^T) diag(gamma) + U^T P^T for the chain wave's
+// columns. out_step(c) reads the staged Q and P of chunk c, waits for S^T
+// (flag value 2c + 1) and forms S Q^T; then it finishes the previous chunk
+// (out_tail: waits for its U, 2c, adds U^T P^T, stores rows t < lenc) and
+// leaves acc = (S Q^T) diag(gamma) of chunk c with its P fragments in the
+// carry. The tail of the last chunk follows the loop. The workgroup's
+// barrier after a step thus waits only for work that is ready early in the
+// chunk, not for U; the stores leave after the chunk's copies are issued.
+// EARLY_TAIL: the tail runs right after the Q reads, before this chunk's P
+// fragments are live (fewer registers, for three waves per SIMD).
+template <int D, int NB> struct OutCarry {
+    f32x4 acc[4][NB];
+    bf16x8 fp[kTriFrags];
+};
+
 template <int D, int NB>
-__device__ __forceinline__ void out_core_db(const DbSmem &m, Handoff<D, NB> ho, int *flag, int c,
-                                            __bf16 *oc, int64_t sVO, int lenc, float scale, int g4,
-                                            int c16, int lane) {
+__device__ __forceinline__ void out_tail(Handoff<D, NB> ho, int *flag, int c, OutCarry<D, NB> &o,
+                                         __bf16 *oc, int64_t sVO, int lenc, float scale, int g4,
+                                         int c16, int lane);
+
+template <int D, int NB, bool EARLY_TAIL = false>
+__device__ __forceinline__ void out_step(const DbSmem &m, Handoff<D, NB> ho, int *flag, int c,
+                                         OutCarry<D, NB> &o, __bf16 *oc_prev, int64_t sVO,
+                                         int lenc_prev, float scale, int g4, int c16, int lane) {
     using F = bf16x8;
     constexpr int KS = D / 32;
     constexpr int KR = D * 2;
-    F fq[KS][4], fp[kTriFrags];
+    F fq[KS][4];
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) ld_chain_s<KR>(m.Q, 16 * mt, c16, 32 * kk + 4 * g4, fq[kk][mt]);
+    if constexpr (EARLY_TAIL) {
+        if (c > 0) out_tail<D, NB>(ho, flag, c - 1, o, oc_prev, sVO, lenc_prev, scale, g4, c16, lane);
+    }
+    F fp[kTriFrags];
 #pragma unroll
     for (int i = 0; i < kTriFrags; ++i) fp[i] = m.P[i * 64 + lane];
     float gamr[4];
@@ -847,38 +869,51 @@ __device__ __forceinline__ void out_core_db(const DbSmem &m, Handoff<D, NB> ho, 
     for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
         for (int b = 0; b < NB; ++b) sf[kk][b] = ho.sf[(kk * NB + b) * 64 + lane];
-    f32x4 oT[4][NB];
+    f32x4 acc[4][NB];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int b = 0; b < NB; ++b) oT[mt][b] = zero4();
+        for (int b = 0; b < NB; ++b) acc[mt][b] = zero4();
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int b = 0; b < NB; ++b) oT[mt][b] = mma(sf[kk][b], fq[kk][mt], oT[mt][b]);
+            for (int b = 0; b < NB; ++b) acc[mt][b] = mma(sf[kk][b], fq[kk][mt], acc[mt][b]);
+    if constexpr (!EARLY_TAIL) {
+        if (c > 0) out_tail<D, NB>(ho, flag, c - 1, o, oc_prev, sVO, lenc_prev, scale, g4, c16, lane);
+    }
+#pragma unroll
+    for (int i = 0; i < kTriFrags; ++i) o.fp[i] = fp[i];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int b = 0; b < NB; ++b) oT[mt][b] *= gamr[mt];
+        for (int b = 0; b < NB; ++b) o.acc[mt][b] = acc[mt][b] * gamr[mt];
+}
+
+template <int D, int NB>
+__device__ __forceinline__ void out_tail(Handoff<D, NB> ho, int *flag, int c, OutCarry<D, NB> &o,
+                                         __bf16 *oc, int64_t sVO, int lenc, float scale, int g4,
+                                         int c16, int lane) {
+    using F = bf16x8;
     wait_flag(flag, 2 * c + 2);
+    const F *us = ho.u_slot(c);
     F fu[2][NB];
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-        for (int b = 0; b < NB; ++b) fu[k2][b] = ho.fu[(k2 * NB + b) * 64 + lane];
+        for (int b = 0; b < NB; ++b) fu[k2][b] = us[(k2 * NB + b) * 64 + lane];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-        oT[0][b] = mma(fu[0][b], fp[0], oT[0][b]);
-        oT[1][b] = mma(fu[0][b], fp[1], oT[1][b]);
-        oT[2][b] = mma(fu[0][b], fp[2], oT[2][b]);
-        oT[3][b] = mma(fu[0][b], fp[4], oT[3][b]);
+        o.acc[0][b] = mma(fu[0][b], o.fp[0], o.acc[0][b]);
+        o.acc[1][b] = mma(fu[0][b], o.fp[1], o.acc[1][b]);
+        o.acc[2][b] = mma(fu[0][b], o.fp[2], o.acc[2][b]);
+        o.acc[3][b] = mma(fu[0][b], o.fp[4], o.acc[3][b]);
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-        oT[2][b] = mma(fu[1][b], fp[3], oT[2][b]);
-        oT[3][b] = mma(fu[1][b], fp[5], oT[3][b]);
+        o.acc[2][b] = mma(fu[1][b], o.fp[3], o.acc[2][b]);
+        o.acc[3][b] = mma(fu[1][b], o.fp[5], o.acc[3][b]);
     }
     __bf16 *o0 = oc + (int64_t)c16 * sVO + 4 * g4;
 #pragma unroll
@@ -888,7 +923,7 @@ __device__ __forceinline__ void out_core_db(const DbSmem &m, Handoff<D, NB> ho, 
             for (int b = 0; b < NB; ++b) {
                 bf16x4 ob;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) ob[r] = (__bf16)(scale * oT[mt][b][r]);
+                for (int r = 0; r < 4; ++r) ob[r] = (__bf16)(scale * o.acc[mt][b][r]);
                 *reinterpret_cast<bf16x4 *>(o0 + (int64_t)(16 * mt) * sVO + 16 * b) = ob;
             }
         }

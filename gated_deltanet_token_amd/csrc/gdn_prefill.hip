@@ -810,39 +810,48 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
             // output wave
             DT *oh = reinterpret_cast<DT *>(p.out) + tok0 * sVO + (int64_t)h * D + dv0 + wdv;
             __syncthreads();
+            OutCarry<D, 1> carry;
+            auto lenc_of = [&](int64_t c) { return (int)((len - c * kC) < kC ? (len - c * kC) : kC); };
             for (int64_t c = 0; c < nchunks; ++c) {
-                const int lenc = (int)((len - c * kC) < kC ? (len - c * kC) : kC);
-                out_core_db<D, 1>(smem_view(c), ho, flag, (int)c, oh + c * kC * sVO, sVO, lenc,
-                                  p.scale, g4, c16, lane);
+                const int64_t cp = c > 0 ? c - 1 : 0;
+                out_step<D, 1, (Cf::NW > 8)>(smem_view(c), ho, flag, (int)c, carry, oh + cp * kC * sVO, sVO,
+                               lenc_of(cp), p.scale, g4, c16, lane);
                 __syncthreads();
             }
+            if (nchunks > 0)
+                out_tail<D, 1>(ho, flag, (int)nchunks - 1, carry, oh + (nchunks - 1) * kC * sVO,
+                               sVO, lenc_of(nchunks - 1), p.scale, g4, c16, lane);
         }
         return;
     }
 
     if (wave == 2 * NC) {
-        // L2 prefetch wave. Owners: K and Q lines of q/k head grp belong to its
-        // first value head's slice 0; T, P and the decay vectors of head h to
-        // slice 0; a V line to the slice that starts it. A touch is a 4-byte
-        // load whose value is folded into a dummy one iteration later (the
-        // load has long completed by then); the helper's LDS-DMA copies run
-        // fastest when no other wave issues LDS-DMA loads.
+        // L2 prefetch wave: the lines of chunk c + LEAD are touched in
+        // iteration c, spread over the workgroups that share them (consecutive
+        // logical ids, so one XCD and one L2): the K and Q lines of q/k head
+        // grp over its G value heads x nsplit slices, the V and workspace-record
+        // lines of head h over its slices. One CU misses L2 at a limited rate,
+        // so lines left to a single owner would arrive late. A touch is a
+        // 4-byte load whose value is folded into a dummy one iteration later
+        // (the load has long completed by then).
         constexpr int NL = Cf::PF_LOADS;
         constexpr int LEAD = 1 + DEPTH + Cf::PF_AHEAD;  // chunk touched in iteration c: c + LEAD
-        constexpr int QKL = (D * 2 + 127) / 128;        // lines per K or Q row
-        constexpr int VL = (Cf::DVS * 2 + 127) / 128;   // lines per V row slice
-        static_assert(NL * 64 >= 2 * QKL * kC + VL * kC + (WSB + 127) / 128, "touch budget");
+        constexpr int QKL = D * 2 / 128;                // lines per K, Q or V (head) row
+        constexpr int NQKL = 2 * QKL * kC, NVL = QKL * kC, NRL = WSB / 128;
+        static_assert(D * 2 % 128 == 0 && WSB % 128 == 0, "whole lines");
+        static_assert(NL * 64 >= NQKL + NVL + NRL, "touch budget of a workgroup alone");
         const int G = p.Hv / p.Hk;
-        const int nqk = (h % G == 0 && slice == 0) ? 2 * QKL * kC : 0;
-        const int nv = ((dv0 * 2) % 128 == 0) ? VL * kC : 0;
-        const int ntp = slice == 0 ? (WSB + 127) / 128 : 0;
-        const int ntot = nqk + nv + ntp;
+        const int nsh = G * nsplit;               // workgroups sharing K and Q
+        const int rq = (h % G) * nsplit + slice;  // this one among them
+        const int nqk = (NQKL - rq + nsh - 1) / nsh;      // lines rq, rq + nsh, ...
+        const int nv = (NVL - slice + nsplit - 1) / nsplit;  // lines slice, slice + nsplit, ...
+        const int ntot = nqk + nv + (NRL - slice + nsplit - 1) / nsplit;
         const unsigned char *kb = reinterpret_cast<const unsigned char *>(p.k) +
                                   (tok0 * sQK + (int64_t)grp * D) * 2;
         const unsigned char *qb = reinterpret_cast<const unsigned char *>(p.q) +
                                   (tok0 * sQK + (int64_t)grp * D) * 2;
-        const unsigned char *vb = reinterpret_cast<const unsigned char *>(p.v) +
-                                  (tok0 * sVO + (int64_t)h * D + dv0) * 2;
+        const unsigned char *vhb = reinterpret_cast<const unsigned char *>(p.v) +
+                                   (tok0 * sVO + (int64_t)h * D) * 2;
         const int64_t rowqk = sQK * 2, rowv = sVO * 2;
         uint32_t pend[NL], acc = 0;
 #pragma unroll
@@ -856,16 +865,18 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
             if constexpr (Cf::NW > 8) asm volatile("" : "+v"(ln));
 #pragma unroll
             for (int j = 0; j < NL; ++j) {
+                if (64 * j >= ntot) break;  // uniform over the wave
                 const int i = ln + 64 * j;
                 const unsigned char *a = kb;  // lanes without a line re-touch row 0
                 if (i < nqk) {
-                    const int iq = i % (QKL * kC), r = iq / QKL, part = iq % QKL;
-                    if (r < rows) a = (i < QKL * kC ? kb : qb) + (t0 + r) * rowqk + part * 128;
+                    const int L = rq + nsh * i, mat = L / (QKL * kC), w = L % (QKL * kC);
+                    const int r = w / QKL, part = w % QKL;
+                    if (r < rows) a = (mat ? qb : kb) + (t0 + r) * rowqk + part * 128;
                 } else if (i < nqk + nv) {
-                    const int r = (i - nqk) / VL, part = (i - nqk) % VL;
-                    if (r < rows) a = vb + (t0 + r) * rowv + part * 128;
+                    const int L = slice + nsplit * (i - nqk), r = L / QKL, part = L % QKL;
+                    if (r < rows) a = vhb + (t0 + r) * rowv + part * 128;
                 } else if (i < ntot && rows > 0) {
-                    a = rec + (int64_t)(i - nqk - nv) * 128;
+                    a = rec + (int64_t)(slice + nsplit * (i - nqk - nv)) * 128;
                 }
                 acc ^= pend[j];
                 pend[j] = *reinterpret_cast<const uint32_t *>(a);
