@@ -58,6 +58,17 @@ __device__ __forceinline__ void store_pair_transposed(__bf16 *dst, const u32x4 &
 template <int PT>
 __device__ __forceinline__ void store_pair_transposed(float *, const u32x4 &, const u32x4 &) {}
 
+// Fragments of a lower-triangular 64x64 chunk matrix M (T or P) in chain
+// assignment, the order in which they are staged: fragment i, lane
+// l = 16 g4 + c16, element e holds M[16 rb + c16][32 k2 + 4 g4 + (e & 3) +
+// 16 (e >> 2)] with (rb, k2) = (0,0), (1,0), (2,0), (2,1), (3,0), (3,1) for
+// i = 0..5. These cover every nonzero block of M; entries above the block
+// diagonal are zero.
+constexpr int kTriFrags = 6;
+__host__ __device__ constexpr int tri_rb(int i) { return i < 2 ? i : 2 + (i - 2) / 2; }
+__host__ __device__ constexpr int tri_k2(int i) { return (i == 3 || i == 5) ? 1 : 0; }
+__host__ __device__ constexpr int tri_frag(int rb, int k2) { return rb < 2 ? rb : 2 * rb - 2 + k2; }
+
 // Lower 16x16 tile pairs (ti, tj), tj <= ti, of a 64x64 chunk matrix.
 __device__ __forceinline__ constexpr int pair_i(int pr) {
     return pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3;
@@ -112,11 +123,14 @@ __device__ __forceinline__ void gram_pair(const DT *sK, const DT *sQ, int ti, in
 
 // Apply the decay masks to a transposed Gram pair and write rows of A
 // (fp32, pitch PA) and P (operand type, pitch PT): row t gets columns
-// s = 16 tj + 4 g4 .. +3 from this lane.
-template <typename DT, int PA, int PT>
+// s = 16 tj + 4 g4 .. +3 from this lane. PFRAG (bf16): P goes instead
+// straight to its fragments at pfr (kTriFrags x 64 lanes x 16 bytes): this
+// lane's four values are one half of its fragment (rb, k2) = (ti, tj / 2);
+// the pairs on even diagonal blocks also zero the half above the diagonal.
+template <typename DT, int PA, int PT, bool PFRAG = false>
 __device__ __forceinline__ void mask_pair(const f32x4 &gk, const f32x4 &gq, int ti, int tj, int g4,
                                           int c16, const float *sG, const float *sBeta, float *sA,
-                                          DT *sP) {
+                                          DT *sP, unsigned char *pfr = nullptr) {
     const int t = 16 * ti + c16;
     const float gt = sG[t];
     const float bt = sBeta[t];
@@ -139,7 +153,15 @@ __device__ __forceinline__ void mask_pair(const f32x4 &gk, const f32x4 &gq, int 
         }
     }
     *reinterpret_cast<f32x4 *>(sA + t * PA + 16 * tj + 4 * g4) = av;
-    if constexpr (sizeof(DT) == 2) {
+    if constexpr (PFRAG) {
+        static_assert(sizeof(DT) == 2, "fragments are bf16");
+        bf16x4 pb;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pb[r] = (__bf16)pv[r];
+        unsigned char *f = pfr + (tri_frag(ti, tj >> 1) * 64 + 16 * g4 + c16) * 16;
+        *reinterpret_cast<bf16x4 *>(f + (tj & 1) * 8) = pb;
+        if (ti == tj && (tj & 1) == 0) *reinterpret_cast<uint2 *>(f + 8) = uint2{0u, 0u};
+    } else if constexpr (sizeof(DT) == 2) {
         bf16x4 pb;
 #pragma unroll
         for (int r = 0; r < 4; ++r) pb[r] = (__bf16)pv[r];
@@ -638,15 +660,6 @@ __device__ __forceinline__ void ld_kt_frag_s(const __bf16 *K, int a, int k2, int
     }
 }
 
-// Fragments of a lower-triangular 64x64 chunk matrix M (T or P) in chain
-// assignment, the order in which they are staged: fragment i, lane
-// l = 16 g4 + c16, element e holds M[16 rb + c16][32 k2 + 4 g4 + (e & 3) +
-// 16 (e >> 2)] with (rb, k2) = (0,0), (1,0), (2,0), (2,1), (3,0), (3,1) for
-// i = 0..5. These cover every nonzero block of M; entries above the block
-// diagonal are zero.
-constexpr int kTriFrags = 6;
-__host__ __device__ constexpr int tri_rb(int i) { return i < 2 ? i : 2 + (i - 2) / 2; }
-__host__ __device__ constexpr int tri_k2(int i) { return (i == 3 || i == 5) ? 1 : 0; }
 
 // One staged chunk of the double-buffered chain (bf16): K, Q [64][D] and
 // V [64][DVS] (the workgroup's value columns) as swizzled rows; T and P as

@@ -348,19 +348,21 @@ constexpr int kFragBytes = kTriFrags * 64 * 16;
 constexpr int ws_bytes_frag() { return 2 * kFragBytes + 1024; }
 static_assert(ws_bytes_frag() <= ws_bytes_per_chunk<__bf16>(), "fragment record fits the query");
 
-template <typename DT, int D> struct PrepCfg {
+template <typename DT, int D, bool FRAG> struct PrepCfg {
     using P = ChunkPitch<DT, D>;
     static constexpr int SZ_K = kC * P::PK * (int)sizeof(DT);
     static constexpr int SZ_A = kC * P::PA * 4;
-    // K and Q are dead once the Gram products are formed; A then takes their place
-    static constexpr int SZ_KQ = 2 * SZ_K > SZ_A ? 2 * SZ_K : SZ_A;
     static constexpr int SZ_T = kC * P::PT * (int)sizeof(DT);
+    // K and Q are dead once the Gram products are formed; A (and with FRAG
+    // also T) then take their place. FRAG writes P straight to the workspace.
+    static constexpr int AT = FRAG ? SZ_A + SZ_T : SZ_A;
+    static constexpr int SZ_KQ = 2 * SZ_K > AT ? 2 * SZ_K : AT;
     static constexpr int OFF_K = 0;
     static constexpr int OFF_Q = SZ_K;
     static constexpr int OFF_A = 0;
-    static constexpr int OFF_T = SZ_KQ;
-    static constexpr int OFF_P = OFF_T + SZ_T;
-    static constexpr int OFF_VEC = OFF_P + SZ_T;
+    static constexpr int OFF_T = FRAG ? SZ_A : SZ_KQ;
+    static constexpr int OFF_P = FRAG ? SZ_KQ : OFF_T + SZ_T;
+    static constexpr int OFF_VEC = FRAG ? SZ_KQ : OFF_P + SZ_T;
     static constexpr int LDS = OFF_VEC + 4 * kC * 4;
     static_assert(LDS <= 160 * 1024, "LDS budget of a gfx950 CU");
 };
@@ -368,12 +370,14 @@ template <typename DT, int D> struct PrepCfg {
 // One workgroup (4 waves) per (chunk slot, value head): Gram products, decay,
 // T = (I + A)^{-1}; writes T, P, gamma, dec, beta to the workspace (52 KiB
 // of LDS for bf16, D = 128: three workgroups share a CU and hide each
-// other's latencies). FRAG: the fragment record instead of dense rows.
+// other's latencies). FRAG: the fragment record instead of dense rows, with
+// T in the dead K/Q staging and P written from registers (35 KiB, at most
+// 128 registers: four workgroups per CU).
 template <typename DT, int D, bool FRAG>
-__global__ __launch_bounds__(256) void prep_kernel(PrefillParams p, unsigned char *ws,
-                                                   int remap_xcd) {
+__global__ __launch_bounds__(256, FRAG ? 4 : 1) void prep_kernel(PrefillParams p, unsigned char *ws,
+                                                                 int remap_xcd) {
     static_assert(!FRAG || sizeof(DT) == 2, "fragment records are bf16");
-    using Cf = PrepCfg<DT, D>;
+    using Cf = PrepCfg<DT, D, FRAG>;
     using Pi = ChunkPitch<DT, D>;
     constexpr int PK = Pi::PK, PT = Pi::PT, PA = Pi::PA;
     constexpr int EPP = 16 / (int)sizeof(DT);
@@ -487,7 +491,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillParams p, unsigned cha
     for (int k = 0; k < 3; ++k) {
         const int pr = wave + 4 * k;
         if (pr < 10)
-            mask_pair<DT, PA, PT>(gk[k], gq[k], pair_i(pr), pair_j(pr), g4, c16, sG, sBeta, sA, sP);
+            mask_pair<DT, PA, PT, FRAG>(gk[k], gq[k], pair_i(pr), pair_j(pr), g4, c16, sG, sBeta, sA,
+                                        sP, rec + kFragBytes);
     }
     __syncthreads();
     // E_b overwrite the diagonal blocks of A (each is read in full first)
@@ -498,16 +503,14 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillParams p, unsigned cha
     // T, P -> workspace as dense [64][64] rows; blocks above the diagonal
     // (never written in LDS) are stored as zeros
     if constexpr (FRAG) {
-        // piece q: matrix q / (kTriFrags 64) (T, then P), fragment i, lane l;
-        // its halves are columns 32 k2 + 4 g4 .. +3 and 16 further of row
+        // T (P is written by mask_pair): piece q is fragment i, lane l; its
+        // halves are columns 32 k2 + 4 g4 .. +3 and 16 further of row
         // 16 rb + c16, zero where the column block lies above the diagonal
         const u32x2 z2 = {0u, 0u};
-        for (int q = tid; q < 2 * kTriFrags * 64; q += 256) {
-            const bool isP = q >= kTriFrags * 64;
-            const int qi = isP ? q - kTriFrags * 64 : q;
-            const int i = qi / 64, l = qi % 64, lg4 = l >> 4, lc16 = l & 15;
+        for (int q = tid; q < kTriFrags * 64; q += 256) {
+            const int i = q / 64, l = q % 64, lg4 = l >> 4, lc16 = l & 15;
             const int rb = tri_rb(i), k2 = tri_k2(i);
-            const DT *src = (isP ? sP : sT) + (16 * rb + lc16) * PT + 32 * k2 + 4 * lg4;
+            const DT *src = sT + (16 * rb + lc16) * PT + 32 * k2 + 4 * lg4;
             const u32x2 lo = 2 * k2 > rb ? z2 : *reinterpret_cast<const u32x2 *>(src);
             const u32x2 hi = 2 * k2 + 1 > rb ? z2 : *reinterpret_cast<const u32x2 *>(src + 16);
             *reinterpret_cast<u32x4 *>(rec + (int64_t)q * 16) = u32x4{lo[0], lo[1], hi[0], hi[1]};
