@@ -103,6 +103,11 @@ def main():
     ap.add_argument("--prefill-workload", default="layer_prefill_4k",
                     help="prefill workload name from gdn_synth.WORKLOADS")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=5,
+                    help="extra prefill calls, each after overwriting a 1 GiB scratch buffer "
+                         "(evicts the 256 MiB Infinity Cache), reported as ms_cold")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured ceilings (library copy and bf16 GEMM)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy three times (the "
                          "reference for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -183,6 +188,49 @@ def main():
     pre_avg = float(np.mean(pre_ms))
     dec_avg = float(np.mean(dec_ms))
 
+    # cold prefill: the inputs are evicted from the Infinity Cache first
+    cold_ms = []
+    if args.cold_steps > 0:
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        evc = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+               for _ in range(args.cold_steps)]
+        for i in range(args.cold_steps):
+            scratch.fill_(i & 0xFF)
+            evc[i][0].record(stream)
+            step_prefill()
+            evc[i][1].record(stream)
+        torch.cuda.synchronize()
+        cold_ms = [e0.elapsed_time(e1) for e0, e1 in evc]
+        del scratch
+
+    # measured ceilings beside the spec peaks: a device-to-device copy and a
+    # large bf16 GEMM, both through the runtime's own libraries
+    ceilings = None
+    if not args.no_ceilings:
+        def timed(fn, reps=5):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps * 1e-3
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        t_copy = timed(lambda: dst.copy_(src))
+        del src, dst
+        n = 8192
+        a = torch.randn(n, n, device=dev).to(torch.bfloat16)
+        b = torch.randn(n, n, device=dev).to(torch.bfloat16)
+        t_gemm = timed(lambda: torch.matmul(a, b))
+        del a, b
+        ceilings = {"copy_GBps": round(2 * (1 << 30) / t_copy / 1e9, 1),
+                    "copy": "1 GiB device-to-device copy, bytes read + written",
+                    "bf16_gemm_tflops": round(2 * n ** 3 / t_gemm / 1e12, 1),
+                    "gemm": "torch.matmul bf16 8192 x 8192 x 8192"}
+
     tokens = int(pt["v"].shape[0] * (1 if varlen else pt["v"].shape[1]))
     f_tok = prefill_flops_per_token(wp.Hk, wp.Hv, wp.D, wp.D)
     pre_tflops = tokens * f_tok / (pre_avg * 1e-3) / 1e12
@@ -219,11 +267,14 @@ def main():
                        "state": "fp32, updated in place"},
         },
         "prefill": {"tokens_per_s": round(pre_tok_s, 1), "ms": round(pre_avg, 5),
+                    "ms_median": round(float(np.median(pre_ms)), 5),
                     "ms_min": round(float(np.min(pre_ms)), 5),
+                    "ms_cold": round(float(np.median(cold_ms)), 5) if cold_ms else None,
                     "algorithmic_tflops": round(pre_tflops, 2),
                     "frac_mfma_peak": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
                     "required_io_GBps": round(pre_gbs, 1)},
         "decode": {"GB_per_s": round(dec_gbs, 1), "ms": round(dec_avg, 5),
+                   "ms_median": round(float(np.median(dec_ms)), 5),
                    "ms_min": round(float(np.min(dec_ms)), 5),
                    "frac_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4),
                    "tokens_per_s": round(wd.B / (dec_avg * 1e-3), 1)},
@@ -237,6 +288,10 @@ def main():
                              "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
                              "traffic": _traffic("prefill_" + wp.name, pdig)},
     }
+    if ceilings is not None:
+        ceilings["decode_frac_of_copy"] = round(dec_gbs / ceilings["copy_GBps"], 4)
+        ceilings["prefill_frac_of_gemm"] = round(pre_tflops / ceilings["bf16_gemm_tflops"], 4)
+        res["measured_ceilings"] = ceilings
     if not args.no_cpu_baseline and not varlen:
         res["cpu_baseline"] = cpu_baseline(dp, wp)
     print(json.dumps(res), flush=True)
