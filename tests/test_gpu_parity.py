@@ -184,6 +184,44 @@ def test_decode_small(gdn, D, dtype):
     check(o, S, o_ref, S_ref, dtype, f"decode D{D} {dtype}", o_axes=(0, 1), s_axes=(0, 1))
 
 
+def _edge_gates(d, case):
+    """Gates at the edges of their range: beta = 0 (pure decay of the initial
+    state), alpha = beta = 1 (no decay, full overwrite of each key's slot) and
+    alpha = 0 on every 37th token (the carried state restarts there). The
+    inputs use slow decay (alpha ~ 0.993): at the workloads' decay the exact
+    beta = 0 state after 200 tokens, (prod alpha) S0 ~ e^-420 S0, lies below
+    the fp32 range, so any fp32 state is 0 against a nonzero fp64 reference."""
+    a, b = d["alpha"].copy(), d["beta"].copy()
+    if case == "beta0":
+        b[...] = 0.0
+    elif case == "alpha1_beta1":
+        a[...] = 1.0
+        b[...] = 1.0
+    else:
+        a.reshape(-1, a.shape[-1])[::37] = 0.0
+    return dict(d, alpha=a, beta=b)
+
+
+@pytest.mark.parametrize("case", ["beta0", "alpha1_beta1", "alpha0"])
+@pytest.mark.parametrize("path", ["fused", "split"])
+def test_prefill_edge_gates(gdn, monkeypatch, case, path):
+    monkeypatch.setenv("GDN_PREFILL_PATH", path)
+    d = _edge_gates(small_prefill(1, 200, 2, 6, 128, "bf16", seed=71, alpha_shift=-5.0,
+                                  init_state=True), case)
+    o, S = gpu_prefill(gdn, d)
+    o_ref, S_ref = oracle_prefill(d)
+    check(o, S, o_ref, S_ref, "bf16", f"edge gates {case} ({path})")
+
+
+@pytest.mark.parametrize("case", ["beta0", "alpha1_beta1", "alpha0"])
+def test_decode_edge_gates(gdn, case):
+    d = _edge_gates(generate_packed(2, 6, 128, "bf16", 72, [1] * 40, alpha_shift=-5.0,
+                                    init_state=True), case)
+    o, S = gpu_decode(gdn, d)
+    o_ref, S_ref = oracle.decode(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"])
+    check(o, S, o_ref, S_ref, "bf16", f"decode edge gates {case}", o_axes=(0, 1), s_axes=(0, 1))
+
+
 def test_decode_b256_workload(gdn):
     w = WORKLOADS["decode_b256"]
     d = generate(w)
