@@ -63,13 +63,12 @@ __device__ __forceinline__ int64_t slot_base(const PrefillParams &p, int n) {
 // Logical workgroup id: workgroups are dispatched to the 8 XCDs round-robin;
 // give each XCD a contiguous range of logical ids so that workgroups sharing
 // a q/k head (and thus K, Q) share that XCD's L2.
+// A select, not a branch: the compiler then loads the kernel arguments in
+// one batch instead of waiting for remap_xcd before reading the grid size.
 __device__ __forceinline__ int logical_wg(int remap_xcd) {
-    int wg = blockIdx.x;
-    if (remap_xcd) {
-        const int per = (int)(gridDim.x >> 3);
-        wg = (wg & 7) * per + (wg >> 3);
-    }
-    return wg;
+    const int wg = blockIdx.x;
+    const int remapped = (wg & 7) * (int)(gridDim.x >> 3) + (wg >> 3);
+    return remap_xcd ? remapped : wg;
 }
 
 // ----------------------------------------------------------------------------
