@@ -306,12 +306,25 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p, int n
         }
         __syncthreads();
 
-        if (wave == 0) solve_unit_lower<DT, PA, PT>(sA, sE, sT, g4, c16);
+        // T = (I + A)^{-1}: the diagonal blocks on wave 0 while the others
+        // form their state-dependent half; then, with four or more waves, the
+        // three block columns below the diagonal on waves 0 .. 2 at once
+        constexpr bool PAR = NW >= 4;
+        if (wave == 0) {
+            if constexpr (PAR)
+                solve_diag_blocks<DT, PA, PT, false>(sA, sE, sT, g4, c16);
+            else
+                solve_unit_lower<DT, PA, PT>(sA, sE, sT, g4, c16);
+        }
 
         const ChainSmem<DT> m{sK, sQ, sKT, sV, sT, sP, sGam, sDec, sBeta};
         Frag<DT> sf[KS][NB];
         f32x4 racc[4][NB], oT[4][NB];
         chain_state_half<DT, D, NB, PK, (NW < 8)>(m, st, sf, racc, oT, g4, c16);
+        if constexpr (PAR) {
+            __syncthreads();  // the diagonal blocks E_b are ready
+            if (wave < 3) solve_column<DT, PA, PT>(sA, sE, sT, wave, g4, c16);
+        }
         __syncthreads();  // T is ready
         chain_finish<DT, D, NB, PK, PT, PV>(m, st, racc, oT, wdv, oh + c * kC * sVO, sVO, lenc,
                                             p.scale, g4, c16);
