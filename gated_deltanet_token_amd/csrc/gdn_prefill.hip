@@ -798,7 +798,9 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
         Handoff<D, 1> ho(smem + Cf::OFF_HO + w * Handoff<D, 1>::BYTES);
         int *flag = flags + w;
         if (wave < NC) {
-            // chain wave
+            // chain wave: the sequential path, so it wins instruction issue
+            // (and with it LDS request) arbitration against the other waves
+            __builtin_amdgcn_s_setprio(3);
             f32x4 st[NKT][1];
             const float *s0 = p.s0 ? p.s0 + ((int64_t)n * p.Hv + h) * D * D : nullptr;
 #pragma unroll
@@ -916,6 +918,8 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
         return;
     }
 
+    // the copies come next after the chain waves
+    __builtin_amdgcn_s_setprio(2);
     // helper waves: copy chunk c + 1 into the other buffer with LDS-DMA loads
     // (global -> LDS without registers). Block j of a chunk is issued by
     // helper j % NH; rows past the end of the sequence repeat its last row
