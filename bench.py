@@ -13,7 +13,9 @@ attention multiplies on top of that").
 Reported: prefill tokens/s (value) with its fraction of the bf16 MFMA peak,
 decode state-update GB/s with its fraction of HBM bandwidth, both from HIP
 events on the stream the kernels run on; and the fp64 oracle timed on the
-host cores as a CPU baseline.
+host cores as a CPU baseline. Timed apart from the step, under
+"decode_multi": the K-token decode against a slot pool (B=256 sequences
+verifying K=4 tokens each), in tokens/s and HBM GB/s.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3]
 """
@@ -49,6 +51,15 @@ def decode_bytes_per_step(B, Hk, Hv, dk, dv, es=2):
     """Required HBM bytes of one decode step: each fp32 state read and written
     once, q, k, v read, o written, alpha and beta read."""
     return B * (Hv * dv * dk * 4 * 2 + 2 * Hk * dk * es + 2 * Hv * dv * es + 2 * Hv * 4)
+
+
+def decode_multi_bytes(B, K, Hk, Hv, dk, dv, es=2):
+    """Required HBM bytes of one K-token decode against a slot pool: each
+    sequence's fp32 state read from its source slot and written to its
+    destination slot once, K tokens of q, k, v read and o written, alpha and
+    beta read, and the two slot indices per sequence."""
+    return (B * Hv * dv * dk * 4 * 2
+            + B * K * (2 * Hk * dk * es + 2 * Hv * dv * es + 2 * Hv * 4) + B * 8)
 
 
 def _src_digest(*names):
@@ -108,6 +119,8 @@ def main():
                          "(evicts the 256 MiB Infinity Cache), reported as ms_cold")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured ceilings (library copy and bf16 GEMM)")
+    ap.add_argument("--no-multi", action="store_true",
+                    help="skip the K-token slot-pool decode measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy three times (the "
                          "reference for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -203,6 +216,49 @@ def main():
         cold_ms = [e0.elapsed_time(e1) for e0, e1 in evc]
         del scratch
 
+    # K tokens per sequence against a slot pool (speculative verification):
+    # timed on its own, after the step, on the same stream
+    multi = None
+    if not args.no_multi:
+        from gdn_synth import SPEC_DECODE, multi_decode
+        wm = SPEC_DECODE
+        dm = multi_decode(wm["B"], wm["K"], wm["Hk"], wm["Hv"], wm["D"], wm["dtype"],
+                          wm["seed"], plan=wm["plan"])
+        mt = {n: to_torch(dm[n], dev) for n in ("q", "k", "v", "alpha", "beta", "pool",
+                                                 "src_slot", "dst_slot")}
+        m_out = torch.empty(mt["v"].shape, dtype=mt["q"].dtype, device=dev)
+
+        def step_multi():
+            gdn.gdn_decode_multi(mt["q"], mt["k"], mt["v"], mt["alpha"], mt["beta"], mt["pool"],
+                                 mt["src_slot"], mt["dst_slot"], out=m_out, stream=stream)
+        for _ in range(max(args.warmup, 1)):
+            step_multi()
+        torch.cuda.synchronize()
+        evm = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        for i in range(K):
+            evm[i][0].record(stream)
+            step_multi()
+            evm[i][1].record(stream)
+        torch.cuda.synchronize()
+        m_ms = [e0.elapsed_time(e1) for e0, e1 in evm]
+        m_avg = float(np.mean(m_ms))
+        m_bytes = decode_multi_bytes(wm["B"], wm["K"], wm["Hk"], wm["Hv"], wm["D"], wm["D"])
+        m_gbs = m_bytes / (m_avg * 1e-3) / 1e9
+        multi = {"workload": wm["name"], "B": wm["B"], "K": wm["K"], "Hk": wm["Hk"],
+                 "Hv": wm["Hv"], "d": wm["D"],
+                 "slots": f"pool of {dm['pool'].shape[0]} fp32 states; sequence b reads slot "
+                          f"2b and writes slot 2b+1",
+                 "ms": round(m_avg, 5), "ms_median": round(float(np.median(m_ms)), 5),
+                 "ms_min": round(float(np.min(m_ms)), 5),
+                 "tokens_per_s": round(wm["B"] * wm["K"] / (m_avg * 1e-3), 1),
+                 "roofline": {"kernel": "decode_multi_kernel", "bound": "hbm",
+                              "achieved": round(m_gbs, 1), "peak": PEAK_HBM_GBS,
+                              "unit": "GB/s", "frac": round(m_gbs / PEAK_HBM_GBS, 4),
+                              "traffic": _traffic("decode_multi_" + wm["name"],
+                                                  _src_digest("gdn_decode.hip",
+                                                              "gdn_device.hpp"))}}
+        del mt, dm
+
     # measured ceilings beside the spec peaks: a device-to-device copy and a
     # large bf16 GEMM, both through the runtime's own libraries
     ceilings = None
@@ -288,6 +344,8 @@ def main():
                              "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
                              "traffic": _traffic("prefill_" + wp.name, pdig)},
     }
+    if multi is not None:
+        res["decode_multi"] = multi
     if ceilings is not None:
         ceilings["decode_frac_of_copy"] = round(dec_gbs / ceilings["copy_GBps"], 4)
         ceilings["prefill_frac_of_gemm"] = round(pre_tflops / ceilings["bf16_gemm_tflops"], 4)

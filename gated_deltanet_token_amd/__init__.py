@@ -26,7 +26,7 @@ GDN_F32, GDN_BF16 = 0, 1
 _STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL_POINTER", 2: "GDN_ERR_BAD_SHAPE",
            3: "GDN_ERR_UNSUPPORTED", 4: "GDN_ERR_MISALIGNED", 5: "GDN_ERR_ALIAS",
            6: "GDN_ERR_HIP"}
-EXPORTS = ("gdn_prefill_chunked", "gdn_decode_step", "gdn_varlen_prefill",
+EXPORTS = ("gdn_prefill_chunked", "gdn_decode_step", "gdn_varlen_prefill", "gdn_decode_multi",
            "gdn_prefill_workspace_size", "gdn_status_string", "gdn_version")
 
 _lib = None
@@ -55,6 +55,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                     ctypes.c_int, f32, vp]
     lib.gdn_decode_step.restype = ctypes.c_int
+    lib.gdn_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32,
+                                     i32, i32, i32, ctypes.c_int, f32, vp]
+    lib.gdn_decode_multi.restype = ctypes.c_int
     lib.gdn_varlen_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, i32, i32,
                                        i32, i32, ctypes.c_int, f32, vp, sz, vp]
     lib.gdn_varlen_prefill.restype = ctypes.c_int
@@ -215,6 +218,43 @@ def gdn_decode_step(q, k, v, alpha, beta, state, *, out=None, scale: float = 1.0
         _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state), _ptr(out), B, Hk, Hv,
         Dk, Dv, _dtype_code(q), float(scale), _stream(dev, stream).cuda_stream))
     return out
+
+
+def gdn_decode_multi(q, k, v, alpha, beta, state_pool, src_slot, dst_slot, *, out=None,
+                     step_states=None, want_step_states: bool = False, scale: float = 1.0,
+                     stream=None):
+    """K tokens per sequence against a pool of state slots.
+    q,k [B,K,Hk,D]; v [B,K,Hv,D]; alpha,beta [B,K,Hv] fp32; state_pool
+    [num_slots,Hv,D,D] fp32; src_slot, dst_slot int32 [B] on the device
+    (negative src = zero state, negative dst = final state not written).
+    Returns (out [B,K,Hv,D], step_states [B,K,Hv,D,D] fp32 or None)."""
+    lib = load_library()
+    B, K, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    dev = q.device
+    _need(q, "q", device=dev)
+    _need(k, "k", q.dtype, q.shape, dev)
+    _need(v, "v", q.dtype, (B, K, Hv, Dv), dev)
+    _need(alpha, "alpha", torch.float32, (B, K, Hv), dev)
+    _need(beta, "beta", torch.float32, (B, K, Hv), dev)
+    _need(state_pool, "state_pool", torch.float32, device=dev)
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (Hv, Dv, Dk):
+        raise ValueError(f"state_pool must have shape [num_slots, {Hv}, {Dv}, {Dk}], "
+                         f"got {tuple(state_pool.shape)}")
+    _need(src_slot, "src_slot", torch.int32, (B,), dev)
+    _need(dst_slot, "dst_slot", torch.int32, (B,), dev)
+    if out is None:
+        out = torch.empty((B, K, Hv, Dv), dtype=q.dtype, device=dev)
+    _need(out, "out", q.dtype, (B, K, Hv, Dv), dev)
+    if step_states is None and want_step_states:
+        step_states = torch.empty((B, K, Hv, Dv, Dk), dtype=torch.float32, device=dev)
+    if step_states is not None:
+        _need(step_states, "step_states", torch.float32, (B, K, Hv, Dv, Dk), dev)
+    _check(lib.gdn_decode_multi(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_pool),
+        state_pool.shape[0], _ptr(src_slot), _ptr(dst_slot), _ptr(out), _ptr(step_states), B, K,
+        Hk, Hv, Dk, Dv, _dtype_code(q), float(scale), _stream(dev, stream).cuda_stream))
+    return out, step_states
 
 
 def gdn_version() -> int:

@@ -124,7 +124,7 @@ const char *gdn_status_string(gdn_status_t s) {
     return "unknown status";
 }
 
-int32_t gdn_version(void) { return 200; }
+int32_t gdn_version(void) { return 300; }
 
 size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t tokens, int32_t Hk, int32_t Hv,
                                   int32_t Dk, int32_t Dv, gdn_dtype_t dtype, int32_t packed) {
@@ -225,6 +225,54 @@ gdn_status_t gdn_decode_step(const void *q, const void *k, const void *v, const 
     gdn::DecodeParams p{q, k, v, alpha, beta, state, out, B, Hk, Hv, scale};
     e = gdn::launch_decode(p, dtype == GDN_BF16 ? 1 : 0, Dk, stream);
     if (e != hipSuccess) return hip_fail(e, "gdn_decode_step launch");
+    return GDN_OK;
+}
+
+gdn_status_t gdn_decode_multi(const void *q, const void *k, const void *v, const float *alpha,
+                              const float *beta, float *state_pool, int32_t num_slots,
+                              const int32_t *src_slot, const int32_t *dst_slot, void *out,
+                              float *step_states, int32_t B, int32_t K, int32_t Hk, int32_t Hv,
+                              int32_t Dk, int32_t Dv, gdn_dtype_t dtype, float scale,
+                              hipStream_t stream) {
+    gdn_status_t st = check_heads(Hk, Hv, Dk, Dv);
+    if (st != GDN_OK) return st;
+    if (B < 1 || K < 0 || num_slots < 1) return GDN_ERR_BAD_SHAPE;
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (!state_pool || !src_slot || !dst_slot) return GDN_ERR_NULL_POINTER;
+    if (K > 0 && (!q || !k || !v || !alpha || !beta || !out)) return GDN_ERR_NULL_POINTER;
+    const int64_t es = dtype == GDN_BF16 ? 2 : 4;
+    int64_t ntok = B;
+    if (!mul_ok(ntok, K)) return GDN_ERR_BAD_SHAPE;
+    int64_t nqk = ntok, nv = ntok, nab = ntok, nsteps = ntok, npool = num_slots;
+    if (!mul_ok(nqk, Hk) || !mul_ok(nqk, Dk) || !mul_ok(nqk, es)) return GDN_ERR_BAD_SHAPE;
+    if (!mul_ok(nv, Hv) || !mul_ok(nv, Dv) || !mul_ok(nv, es)) return GDN_ERR_BAD_SHAPE;
+    if (!mul_ok(nab, Hv) || !mul_ok(nab, 4)) return GDN_ERR_BAD_SHAPE;
+    if (!mul_ok(nsteps, Hv) || !mul_ok(nsteps, Dv) || !mul_ok(nsteps, Dk) || !mul_ok(nsteps, 4))
+        return GDN_ERR_BAD_SHAPE;
+    if (!mul_ok(npool, Hv) || !mul_ok(npool, Dv) || !mul_ok(npool, Dk) || !mul_ok(npool, 4))
+        return GDN_ERR_BAD_SHAPE;
+    if ((int64_t)B * Hv > 0x7FFFFFFF) return GDN_ERR_BAD_SHAPE;
+    const void *ptrs[] = {q, k, v, alpha, beta, state_pool, out, step_states};
+    for (const void *ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return GDN_ERR_MISALIGNED;
+    if ((reinterpret_cast<uintptr_t>(src_slot) | reinterpret_cast<uintptr_t>(dst_slot)) & 3u)
+        return GDN_ERR_MISALIGNED;
+    const Range rq = range_of(q, nqk), rk = range_of(k, nqk), rv = range_of(v, nv);
+    const Range ra = range_of(alpha, nab), rb = range_of(beta, nab);
+    const Range rss = range_of(src_slot, (int64_t)B * 4), rds = range_of(dst_slot, (int64_t)B * 4);
+    const Range rp = range_of(state_pool, npool), ro = range_of(out, nv);
+    const Range rst = range_of(step_states, nsteps);
+    const Range reads[] = {rq, rk, rv, ra, rb, rss, rds};
+    const Range writes[] = {rp, ro, rst};
+    for (const Range &w : writes)
+        for (const Range &r : reads)
+            if (overlap(w, r)) return GDN_ERR_ALIAS;
+    if (overlap(rp, ro) || overlap(rp, rst) || overlap(ro, rst)) return GDN_ERR_ALIAS;
+    gdn::DecodeMultiParams p{q,        k,        v,   alpha,       beta, state_pool,
+                             src_slot, dst_slot, out, step_states, B,    K,
+                             Hk,       Hv,       num_slots, scale};
+    hipError_t e = gdn::launch_decode_multi(p, dtype == GDN_BF16 ? 1 : 0, Dk, stream);
+    if (e != hipSuccess) return hip_fail(e, "gdn_decode_multi launch");
     return GDN_OK;
 }
 

@@ -27,6 +27,18 @@ struct DecodeParams {
     float scale;
 };
 
+// Several tokens per sequence; states live in a pool of slots.
+struct DecodeMultiParams {
+    const void *q, *k, *v;
+    const float *alpha, *beta;
+    float *pool;
+    const int32_t *src_slot, *dst_slot;
+    void *out;
+    float *steps;  // per-token states, or nullptr
+    int32_t B, K, Hk, Hv, num_slots;
+    float scale;
+};
+
 // dtype: 0 = fp32, 1 = bf16. D: 64 or 128. Returns a hipError_t. With a
 // workspace of at least prefill_ws_bytes(nslots, ...) bytes (and when
 // prefill_wants_workspace agrees) the two-pass path runs; otherwise the
@@ -39,5 +51,6 @@ int64_t prefill_ws_slots(int64_t nseq, int64_t total_tokens, int64_t seq_len, bo
 size_t prefill_ws_bytes(int64_t slots, int Hv, int dtype);
 bool prefill_wants_workspace(int64_t chains, int num_cus);
 hipError_t launch_decode(const DecodeParams &p, int dtype, int D, hipStream_t stream);
+hipError_t launch_decode_multi(const DecodeMultiParams &p, int dtype, int D, hipStream_t stream);
 
 }  // namespace gdn

@@ -105,6 +105,14 @@ WORKLOADS = {
 }
 
 
+# The multi-token decode workload: B=256 sequences each verifying K=4 tokens
+# (three drafted plus one) at the layer's head shapes, two pool slots per
+# sequence (read slot 2b, write slot 2b+1, so the pre-verification state is
+# kept for rollback).
+SPEC_DECODE = dict(name="spec_decode_b256_k4", B=256, K=4, Hk=16, Hv=48, D=128, dtype="bf16",
+                   seed=1005, plan="pairs")
+
+
 def _threads():
     env = os.environ.get("GDN_SYNTH_THREADS")
     if env:
@@ -220,6 +228,51 @@ def small_prefill(B, T, Hk, Hv, D, dtype="bf16", seed=0, alpha_shift=2.0, init_s
                         beta_shift=beta_shift)
     for name in ("q", "k", "v", "alpha", "beta"):
         d[name] = d[name].reshape((B, T) + d[name].shape[1:])
+    return d
+
+
+def multi_decode(B, K, Hk, Hv, D, dtype, seed, num_slots=None, plan="permute",
+                 alpha_shift=2.0):
+    """Inputs of a K-tokens-per-sequence decode against a slot pool.
+
+    q, k [B,K,Hk,D]; v [B,K,Hv,D]; alpha, beta [B,K,Hv]: the token recipe of
+    generate_packed (each sequence K tokens); pool [num_slots,Hv,D,D] fp32
+    0.1*N(0,1); src_slot, dst_slot int32 [B]. Slot plans:
+      "permute": 2B distinct slots in random order, src then dst
+      "pairs"  : sequence b reads slot 2b and writes slot 2b+1
+      "inplace": src = dst = a random permutation of B slots
+    num_slots defaults to 2B (B for "inplace")."""
+    d = generate_packed(Hk, Hv, D, dtype, seed, [K] * B, alpha_shift)
+    for name in ("q", "k", "v", "alpha", "beta"):
+        d[name] = d[name].reshape((B, K) + d[name].shape[1:])
+    if num_slots is None:
+        num_slots = B if plan == "inplace" else 2 * B
+    ss = np.random.SeedSequence([seed, 7])
+    pool_child, plan_child = ss.spawn(2)
+    pool = np.empty((num_slots, Hv, D, D), np.float32)
+    kids = pool_child.spawn(max(num_slots, 1))
+
+    def _slot(n):
+        rng = np.random.Generator(np.random.PCG64(kids[n]))
+        pool[n] = np.float32(0.1) * rng.standard_normal((Hv, D, D), dtype=np.float32)
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(_slot, range(num_slots)))
+    rng = np.random.Generator(np.random.PCG64(plan_child))
+    if plan == "pairs":
+        src = 2 * np.arange(B)
+        dst = src + 1
+    elif plan == "inplace":
+        src = rng.permutation(num_slots)[:B]
+        dst = src.copy()
+    elif plan == "permute":
+        perm = rng.permutation(num_slots)[:2 * B]
+        src, dst = perm[:B], perm[B:]
+    else:
+        raise ValueError(f"unknown slot plan {plan!r}")
+    d["pool"] = pool
+    d["src_slot"] = np.asarray(src, np.int32)
+    d["dst_slot"] = np.asarray(dst, np.int32)
+    del d["cu_seqlens"], d["S0"], d["lengths"]
     return d
 
 

@@ -117,6 +117,50 @@ gdn_status_t gdn_decode_step(const void *q, const void *k, const void *v,
                              float scale, hipStream_t stream);
 
 /*
+ * gdn_decode_multi -- K new tokens per sequence against a pool of state
+ * slots, for checking several drafted tokens in one call. "The economics of
+ * hybrid attention" names the model's multi-token prediction head (section
+ * "The stack, verified") and the speculation head's draft buffers served at
+ * two slots (section "Where the constraint moved"); this call is the mixer's
+ * side of that: the K tokens of each sequence run in order on one state that
+ * crosses HBM once per call instead of once per token.
+ *
+ *   q, k         [B, K, Hk, Dk]      dtype
+ *   v            [B, K, Hv, Dv]      dtype
+ *   alpha, beta  [B, K, Hv]          fp32
+ *   state_pool   [num_slots, Hv, Dv, Dk] fp32, DEVICE memory
+ *   src_slot     [B] int32, DEVICE memory: sequence b starts from the state
+ *                in slot src_slot[b]; a negative value means a zero state
+ *   dst_slot     [B] int32, DEVICE memory: S_K of sequence b is written to
+ *                slot dst_slot[b]; a negative value means it is not written
+ *   out          [B, K, Hv, Dv]      dtype  o_t = scale * S_t q_t
+ *   step_states  [B, K, Hv, Dv, Dk]  fp32 or NULL: S_t after each token t
+ *                (for rolling back to any accepted prefix); NULL skips them
+ *
+ * Sizes: B >= 1, K >= 0, num_slots >= 1, Hk >= 1, Hv a multiple of Hk,
+ * Dk == Dv in {64, 128}. K == 0 copies slot src_slot[b] (or zeros) to slot
+ * dst_slot[b]. A token with alpha = 1 and beta = 0 leaves the state unchanged,
+ * so a batch with fewer real tokens in some sequences can be padded with such
+ * tokens.
+ *
+ * The slot indices are read on the device. An index >= num_slots is not
+ * an error the call can return: that sequence touches no slot and its
+ * outputs (and step states) are set to NaN. The caller guarantees that the
+ * non-negative dst_slot values are distinct and that no sequence's dst slot
+ * is another sequence's src slot (src_slot[b] == dst_slot[b] updates in
+ * place); otherwise workgroups race and the result is unspecified. Slots not
+ * named in dst_slot are left untouched. state_pool, out, step_states and the
+ * slot arrays must not overlap each other or the inputs (GDN_ERR_ALIAS).
+ */
+gdn_status_t gdn_decode_multi(const void *q, const void *k, const void *v,
+                              const float *alpha, const float *beta,
+                              float *state_pool, int32_t num_slots,
+                              const int32_t *src_slot, const int32_t *dst_slot,
+                              void *out, float *step_states, int32_t B, int32_t K,
+                              int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
+                              gdn_dtype_t dtype, float scale, hipStream_t stream);
+
+/*
  * gdn_varlen_prefill -- chunked prefill of N packed sequences.
  *
  *   q, k          [total_T, Hk, Dk] dtype

@@ -171,3 +171,56 @@ def decode(q, k, v, alpha, beta, state, scale=1.0, threads=None):
     B = q.shape[0]
     cu = np.arange(B + 1, dtype=np.int64)
     return varlen(q, k, v, alpha, beta, cu, state, scale, None, threads)
+
+
+def decode_multi(q, k, v, alpha, beta, pool, src_slot, dst_slot, scale=1.0, want_steps=False,
+                 threads=None):
+    """K tokens per sequence against a pool of state slots.
+
+    q,k [B,K,Hk,Dk]; v [B,K,Hv,Dv]; alpha,beta [B,K,Hv] fp32; pool
+    [num_slots,Hv,Dv,Dk] (not modified); src_slot, dst_slot: B integers.
+    Sequence b starts from pool[src_slot[b]] (zero state when the index is
+    negative), runs its K tokens in order, one call of the token recurrence
+    per token, and its final state goes to pool[dst_slot[b]] (nowhere when
+    that index is negative). A sequence with an index >= num_slots touches no
+    slot and gets NaN outputs and step states.
+
+    Returns (o [B,K,Hv,Dv] fp64, pool' [num_slots,Hv,Dv,Dk] fp64,
+    steps [B,K,Hv,Dv,Dk] fp64 = the state after each token, or None)."""
+    B, K = q.shape[0], q.shape[1]
+    Hv, Dv = v.shape[2], v.shape[3]
+    Dk = q.shape[3]
+    nslots = pool.shape[0]
+    src = [int(x) for x in np.asarray(src_slot)]
+    dst = [int(x) for x in np.asarray(dst_slot)]
+    o = np.full((B, K, Hv, Dv), np.nan)
+    steps = np.full((B, K, Hv, Dv, Dk), np.nan) if want_steps else None
+    out_pool = np.array(pool, np.float64)
+    finals = {}
+
+    def work(bh):
+        b, h = bh
+        if src[b] >= nslots or dst[b] >= nslots:
+            return
+        S = None if src[b] < 0 else pool[src[b], h]
+        for t in range(K):
+            ot, S = chain(q[b], k[b], v[b], alpha[b], beta[b], t, t + 1, h, S, scale)
+            o[b, t, h] = ot[0]
+            if steps is not None:
+                steps[b, t, h] = S
+        if S is None:
+            S = np.zeros((Dv, Dk))
+        finals[bh] = S
+
+    pairs = [(b, h) for b in range(B) for h in range(Hv)]
+    nthreads = threads or default_threads()
+    if nthreads == 1:
+        for bh in pairs:
+            work(bh)
+    else:
+        with ThreadPoolExecutor(nthreads) as ex:
+            list(ex.map(work, pairs))
+    for (b, h), S in finals.items():
+        if dst[b] >= 0:
+            out_pool[dst[b], h] = S
+    return o, out_pool, steps

@@ -31,7 +31,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = set(declared_functions())
-    assert {"gdn_prefill_chunked", "gdn_decode_step", "gdn_varlen_prefill",
+    assert {"gdn_prefill_chunked", "gdn_decode_step", "gdn_varlen_prefill", "gdn_decode_multi",
             "gdn_status_string", "gdn_version"} <= names
 
 
@@ -118,6 +118,36 @@ def test_decode_validation(lib):
     assert decode(lib, v=P(2) + 2) == MISAL
 
 
+def multi(lib, q=P(0), k=P(1), v=P(2), a=P(3), b=P(4), pool=P(5), ns=8, src=P(8), dst=P(9),
+          out=P(6), steps=P(7), B=4, K=3, Hk=2, Hv=4, Dk=64, Dv=64, dtype=BF16):
+    return lib.gdn_decode_multi(q, k, v, a, b, pool, ns, src, dst, out, steps, B, K, Hk, Hv, Dk,
+                                Dv, dtype, 1.0, None)
+
+
+def test_decode_multi_validation(lib):
+    assert multi(lib, pool=None) == NULLP
+    assert multi(lib, src=None) == NULLP
+    assert multi(lib, dst=None) == NULLP
+    assert multi(lib, out=None) == NULLP
+    assert multi(lib, B=0) == SHAPE
+    assert multi(lib, K=-1) == SHAPE
+    assert multi(lib, ns=0) == SHAPE
+    assert multi(lib, Hk=3, Hv=4) == SHAPE
+    assert multi(lib, Dk=96, Dv=96) == UNSUP
+    assert multi(lib, dtype=5) == UNSUP
+    assert multi(lib, pool=P(5) + 8) == MISAL
+    assert multi(lib, steps=P(7) + 4) == MISAL
+    assert multi(lib, src=P(8) + 2) == MISAL
+    assert multi(lib, out=P(2)) == ALIAS              # out on top of v
+    assert multi(lib, pool=P(0)) == ALIAS             # pool on top of q
+    assert multi(lib, src=P(5) + 64) == ALIAS         # slot ids inside the pool
+    assert multi(lib, dst=P(7)) == ALIAS              # slot ids inside the step states
+    assert multi(lib, steps=P(6)) == ALIAS            # step states on top of out
+    assert multi(lib, steps=P(5) + 4096) == ALIAS     # step states inside the pool
+    assert multi(lib, B=1 << 24, K=1 << 24) == SHAPE  # step-state bytes overflow
+    assert multi(lib, ns=1 << 30, Hv=1 << 20) == SHAPE  # pool bytes overflow
+
+
 def test_valid_call_without_device_reports_hip_error(lib):
     torch = pytest.importorskip("torch")
     if torch.cuda.device_count() > 0:
@@ -125,6 +155,8 @@ def test_valid_call_without_device_reports_hip_error(lib):
     assert prefill(lib) == HIPERR
     assert b"HIP" in lib.gdn_status_string(HIPERR)
     assert decode(lib) == HIPERR
+    assert multi(lib) == HIPERR
+    assert multi(lib, steps=None, K=0, q=None, k=None, v=None, a=None, b=None, out=None) == HIPERR
     assert lib.gdn_prefill_workspace_size(1, 4096, 16, 48, 128, 128, BF16, 0) == 0
 
 

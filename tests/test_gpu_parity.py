@@ -14,8 +14,8 @@ import numpy as np
 import pytest
 
 import oracle
-from gdn_synth import (WORKLOADS, from_torch, generate, generate_packed, lengths_for,
-                       small_prefill, to_torch)
+from gdn_synth import (SPEC_DECODE, WORKLOADS, from_torch, generate, generate_packed,
+                       lengths_for, multi_decode, small_prefill, to_torch)
 from tests.parity import TOL, max_error, slice_error
 
 torch = pytest.importorskip("torch")
@@ -238,6 +238,132 @@ def test_decode_matches_prefill_T1(gdn):
     op, Sp = gpu_prefill(gdn, dp)
     assert max_error(o, op[:, 0], (0, 1)) <= TOL["bf16"]
     assert max_error(S, Sp, (0, 1)) <= TOL["bf16"]  # prefill rounds S to bf16 as an operand
+
+
+# ------------------------------------------------- K tokens against a slot pool
+def gpu_multi(gdn, d, scale=1.0, steps=False):
+    q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
+    pool = to_torch(d["pool"], DEV)
+    src = to_torch(d["src_slot"], DEV)
+    dst = to_torch(d["dst_slot"], DEV)
+    out, st = gdn.gdn_decode_multi(q, k, v, a, b, pool, src, dst, scale=scale,
+                                   want_step_states=steps)
+    torch.cuda.synchronize()
+    return from_torch(out), from_torch(pool), (from_torch(st) if steps else None)
+
+
+def check_multi(d, o, pool, st, ref, dtype, label):
+    """Outputs and step states per (sequence, head); written slots per
+    (slot, head) against the oracle; every other slot bit for bit unchanged."""
+    o_ref, pool_ref, st_ref = ref
+    B, K = d["q"].shape[:2]
+    eo = max_error(o, o_ref, (0, 2)) if K else 0.0
+    dst = [int(x) for x in d["dst_slot"] if x >= 0]
+    es = max_error(pool[dst], pool_ref[dst], (0, 1)) if dst else 0.0
+    et = max_error(st, st_ref, (0, 1, 2)) if st is not None and K else 0.0
+    print(f"[parity] {label}: out {eo:.3e} slots {es:.3e} steps {et:.3e} "
+          f"(tol {TOL[dtype]:.0e})", flush=True)
+    assert eo <= TOL[dtype] and es <= TOL[dtype] and et <= TOL[dtype], label
+    keep = sorted(set(range(pool.shape[0])) - set(dst))
+    np.testing.assert_array_equal(pool[keep], d["pool"][keep])
+    if st is not None and K:
+        for b, s in enumerate(d["dst_slot"]):
+            if s >= 0:   # the last step state and the written slot are the same registers
+                np.testing.assert_array_equal(st[b, K - 1], pool[s])
+
+
+MULTI = [
+    # B, K, Hk, Hv, D, dtype, slot plan
+    (3, 1, 1, 2, 64, "bf16", "permute"),
+    (4, 4, 2, 6, 128, "bf16", "pairs"),
+    (5, 7, 2, 4, 128, "bf16", "inplace"),
+    (1, 16, 1, 1, 128, "bf16", "permute"),
+    (2, 3, 1, 3, 64, "f32", "permute"),
+    (3, 5, 2, 4, 128, "f32", "pairs"),
+]
+
+
+@pytest.mark.parametrize("B,K,Hk,Hv,D,dtype,plan", MULTI)
+@pytest.mark.parametrize("steps", [False, True])
+def test_decode_multi_small(gdn, B, K, Hk, Hv, D, dtype, plan, steps):
+    d = multi_decode(B, K, Hk, Hv, D, dtype, seed=80 + K + D, plan=plan)
+    o, pool, st = gpu_multi(gdn, d, 0.8, steps)
+    ref = oracle.decode_multi(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["pool"],
+                              d["src_slot"], d["dst_slot"], 0.8, steps)
+    check_multi(d, o, pool, st, ref, dtype, f"multi B{B} K{K} D{D} {dtype} {plan} steps={steps}")
+
+
+def test_decode_multi_zero_source_and_no_destination(gdn):
+    d = multi_decode(4, 3, 2, 4, 128, "bf16", seed=90, plan="permute")
+    d["src_slot"][[0, 2]] = -1       # new sequences: zero state
+    d["dst_slot"][[1, 2]] = -1       # verification only: nothing written
+    o, pool, st = gpu_multi(gdn, d, 1.0, True)
+    ref = oracle.decode_multi(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["pool"],
+                              d["src_slot"], d["dst_slot"], 1.0, True)
+    check_multi(d, o, pool, st, ref, "bf16", "multi src<0 / dst<0")
+
+
+def test_decode_multi_zero_tokens_copies_slots(gdn):
+    d = multi_decode(3, 0, 1, 2, 64, "f32", seed=91, plan="permute")
+    d["src_slot"][1] = -1
+    o, pool, _ = gpu_multi(gdn, d)
+    assert o.shape == (3, 0, 2, 64)
+    for b in range(3):
+        s, t = int(d["src_slot"][b]), int(d["dst_slot"][b])
+        np.testing.assert_array_equal(pool[t], d["pool"][s] if s >= 0 else 0.0)
+
+
+def test_decode_multi_slot_past_pool_gives_nan(gdn):
+    d = multi_decode(3, 2, 1, 2, 128, "bf16", seed=92, plan="permute")
+    d["dst_slot"][1] = d["pool"].shape[0]          # one past the end
+    o, pool, st = gpu_multi(gdn, d, 1.0, True)
+    from tests.parity import as_f64
+    assert np.isnan(as_f64(o[1])).all() and np.isnan(st[1]).all()
+    ref = oracle.decode_multi(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["pool"],
+                              d["src_slot"], d["dst_slot"], 1.0, True)
+    keep_b = [0, 2]
+    assert max_error(o[keep_b], ref[0][keep_b], (0, 2)) <= TOL["bf16"]
+    written = [int(d["dst_slot"][b]) for b in keep_b]
+    assert max_error(pool[written], ref[1][written], (0, 1)) <= TOL["bf16"]
+    keep = sorted(set(range(pool.shape[0])) - set(written))
+    np.testing.assert_array_equal(pool[keep], d["pool"][keep])
+
+
+def test_decode_multi_padding_tokens_keep_state(gdn):
+    """alpha = 1, beta = 0 is an exact identity step on the GPU as well."""
+    d = multi_decode(3, 6, 2, 4, 128, "bf16", seed=93, plan="pairs")
+    d["alpha"][:, 2:] = 1.0
+    d["beta"][:, 2:] = 0.0
+    o, pool, st = gpu_multi(gdn, d, 1.0, True)
+    for t in range(2, 6):
+        np.testing.assert_array_equal(st[:, t], st[:, 1])
+    ref = oracle.decode_multi(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["pool"],
+                              d["src_slot"], d["dst_slot"], 1.0, True)
+    check_multi(d, o, pool, st, ref, "bf16", "multi padding tokens")
+
+
+def test_decode_multi_K1_matches_decode_step(gdn):
+    d = multi_decode(5, 1, 2, 6, 128, "bf16", seed=94, plan="inplace")
+    o_m, pool, _ = gpu_multi(gdn, d)
+    src = d["src_slot"]
+    state = to_torch(d["pool"][src], DEV)
+    q, k, v, a, b = (to_torch(np.ascontiguousarray(d[n][:, 0]), DEV)
+                     for n in ("q", "k", "v", "alpha", "beta"))
+    o_s = from_torch(gdn.gdn_decode_step(q, k, v, a, b, state))
+    torch.cuda.synchronize()
+    S_s = from_torch(state)
+    assert max_error(o_m[:, 0], o_s, (0, 1)) <= 1e-5
+    assert max_error(pool[src], S_s, (0, 1)) <= 1e-5
+
+
+def test_spec_decode_workload(gdn):
+    w = SPEC_DECODE
+    d = multi_decode(w["B"], w["K"], w["Hk"], w["Hv"], w["D"], w["dtype"], w["seed"],
+                     plan=w["plan"])
+    o, pool, _ = gpu_multi(gdn, d)
+    ref = oracle.decode_multi(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["pool"],
+                              d["src_slot"], d["dst_slot"])
+    check_multi(d, o, pool, None, ref, "bf16", w["name"])
 
 
 # ----------------------------------------------------------------- varlen

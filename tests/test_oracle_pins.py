@@ -19,6 +19,8 @@ Which planted mistake each pin catches:
   linearity    : a hidden non-linearity in (S0, V)
   split        : state hand-over between calls
   chunk mirror : the chunked algebra the GPU evaluates
+  slot pool    : src/dst routing, per-token states, padding tokens, K = 0,
+                 out-of-range slots (the multi-token decode)
 """
 import json
 import os
@@ -297,3 +299,126 @@ def test_generator_rounding_is_rne():
     np.testing.assert_array_equal(bf16_to_f32(bf16_bits(x))[:2], [1.0, 1.0])
     assert bf16_to_f32(bf16_bits(x))[2] == np.float32(1.0078125)
     assert bf16_to_f32(bf16_bits(x))[3] == np.float32(-2.5)
+
+
+# ------------------------------------------------- K tokens against a slot pool
+# The multi-token oracle routes states between pool slots and walks the token
+# recurrence. Its pins use closed forms of the recurrence and exact facts of
+# the routing, with slot plans in which a transposed src/dst, an off-by-one
+# slot, a step state from the wrong token or a write to an unnamed slot fails.
+def _multi_inputs(rng, B, K, Hk, Hv, d, nslots):
+    q, k, v, alpha, beta = (x.reshape((B, K) + x.shape[1:])
+                            for x in _rand_inputs(rng, B * K, Hk, Hv, d, d))
+    pool = rng.standard_normal((nslots, Hv, d, d)).astype(np.float32)
+    return q, k, v, alpha, beta, pool
+
+
+def test_multi_decay_only_routes_slots():
+    """beta = 0: the state after token t is (prod_{s<=t} a_s) S_src, o_t is
+    that state times q_t, the dst slot receives the last one, and every slot
+    that is no dst keeps its value bit for bit."""
+    rng = np.random.default_rng(41)
+    B, K, Hk, Hv, d, ns = 3, 5, 2, 4, 8, 9
+    q, k, v, alpha, _, pool = _multi_inputs(rng, B, K, Hk, Hv, d, ns)
+    beta = np.zeros((B, K, Hv), np.float32)
+    src = np.array([7, 2, 4], np.int32)
+    dst = np.array([0, 5, 4], np.int32)          # sequence 2 in place
+    o, pool2, steps = oracle.decode_multi(q, k, v, alpha, beta, pool, src, dst, scale=0.5,
+                                          want_steps=True)
+    for b in range(B):
+        for h in range(Hv):
+            g = h // (Hv // Hk)
+            cp = np.cumprod(_f64(alpha[b, :, h]))
+            S0 = _f64(pool[src[b], h])
+            for t in range(K):
+                np.testing.assert_allclose(steps[b, t, h], cp[t] * S0, rtol=1e-12, atol=1e-300)
+                np.testing.assert_allclose(o[b, t, h], 0.5 * cp[t] * (S0 @ _f64(q[b, t, g])),
+                                           rtol=1e-12, atol=1e-14)
+            np.testing.assert_allclose(pool2[dst[b], h], cp[-1] * S0, rtol=1e-12, atol=1e-300)
+    for n in set(range(ns)) - set(dst.tolist()):
+        np.testing.assert_array_equal(pool2[n], _f64(pool[n]))
+
+
+def test_multi_zero_source_first_token():
+    """src < 0: token 0 starts from S = 0, so o_0 = scale b (k.q) v."""
+    rng = np.random.default_rng(42)
+    B, K, Hk, Hv, d = 2, 3, 1, 3, 16
+    q, k, v, alpha, beta, pool = _multi_inputs(rng, B, K, Hk, Hv, d, 4)
+    src = np.array([-1, -1], np.int32)
+    dst = np.array([3, 1], np.int32)
+    o, _, steps = oracle.decode_multi(q, k, v, alpha, beta, pool, src, dst, scale=1.25,
+                                      want_steps=True)
+    for b in range(B):
+        for h in range(Hv):
+            kq = float(_f64(k[b, 0, 0]) @ _f64(q[b, 0, 0]))
+            np.testing.assert_allclose(o[b, 0, h], 1.25 * float(beta[b, 0, h]) * kq * _f64(v[b, 0, h]),
+                                       rtol=1e-12, atol=1e-14)
+            np.testing.assert_allclose(steps[b, 0, h],
+                                       float(beta[b, 0, h]) * np.outer(_f64(v[b, 0, h]), _f64(k[b, 0, 0])),
+                                       rtol=1e-12, atol=1e-14)
+
+
+def test_multi_identity_padding_tokens():
+    """alpha = 1, beta = 0 leaves S unchanged exactly (1*S + 0*k = S), and
+    the output of such a token is S q."""
+    rng = np.random.default_rng(43)
+    B, K, Hk, Hv, d = 2, 6, 2, 4, 8
+    q, k, v, alpha, beta, pool = _multi_inputs(rng, B, K, Hk, Hv, d, 4)
+    alpha[:, 3:] = 1.0
+    beta[:, 3:] = 0.0
+    src = np.array([0, 1], np.int32)
+    dst = np.array([2, 3], np.int32)
+    o, pool2, steps = oracle.decode_multi(q, k, v, alpha, beta, pool, src, dst, want_steps=True)
+    for b in range(B):
+        for h in range(Hv):
+            g = h // (Hv // Hk)
+            for t in range(3, K):
+                np.testing.assert_array_equal(steps[b, t, h], steps[b, 2, h])
+                np.testing.assert_allclose(o[b, t, h], steps[b, 2, h] @ _f64(q[b, t, g]),
+                                           rtol=1e-12, atol=1e-14)
+            np.testing.assert_array_equal(pool2[dst[b], h], steps[b, 2, h])
+
+
+def test_multi_overwrite_each_step():
+    """beta = 1 and exactly unit keys: after every token S_t k_t = v_t."""
+    rng = np.random.default_rng(44)
+    B, K, Hk, Hv, d = 2, 4, 2, 4, 64
+    q, _, v, alpha, beta, pool = _multi_inputs(rng, B, K, Hk, Hv, d, 5)
+    k = _exact_unit_keys(rng, B * K, Hk, d, 16).reshape(B, K, Hk, d)
+    beta[...] = 1.0
+    src = np.array([4, 1], np.int32)
+    dst = np.array([0, 2], np.int32)
+    _, _, steps = oracle.decode_multi(q, k, v, alpha, beta, pool, src, dst, want_steps=True)
+    for b in range(B):
+        for h in range(Hv):
+            g = h // (Hv // Hk)
+            for t in range(K):
+                np.testing.assert_allclose(steps[b, t, h] @ _f64(k[b, t, g]), _f64(v[b, t, h]),
+                                           rtol=0, atol=1e-12)
+
+
+def test_multi_zero_tokens_copies_slot():
+    """K = 0: dst receives src (zeros for a negative src); no other slot changes."""
+    rng = np.random.default_rng(45)
+    q, k, v, alpha, beta, pool = _multi_inputs(rng, 3, 1, 1, 2, 8, 6)
+    q, k, v, alpha, beta = (x[:, :0] for x in (q, k, v, alpha, beta))
+    src = np.array([5, -1, 0], np.int32)
+    dst = np.array([1, 2, -1], np.int32)
+    o, pool2, _ = oracle.decode_multi(q, k, v, alpha, beta, pool, src, dst)
+    assert o.shape == (3, 0, 2, 8)
+    np.testing.assert_array_equal(pool2[1], _f64(pool[5]))
+    np.testing.assert_array_equal(pool2[2], 0.0)
+    for n in (0, 3, 4, 5):
+        np.testing.assert_array_equal(pool2[n], _f64(pool[n]))
+
+
+def test_multi_slot_out_of_range_is_nan_and_untouched():
+    rng = np.random.default_rng(46)
+    q, k, v, alpha, beta, pool = _multi_inputs(rng, 2, 2, 1, 2, 8, 3)
+    src = np.array([0, 3], np.int32)
+    dst = np.array([1, 2], np.int32)
+    o, pool2, steps = oracle.decode_multi(q, k, v, alpha, beta, pool, src, dst, want_steps=True)
+    assert np.isnan(o[1]).all() and np.isnan(steps[1]).all()
+    assert np.isfinite(o[0]).all()
+    np.testing.assert_array_equal(pool2[2], _f64(pool[2]))
+    np.testing.assert_array_equal(pool2[0], _f64(pool[0]))
