@@ -134,42 +134,102 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
 // state write for all K tokens, plus the optional per-token states. A padding
 // token with alpha = 1, beta = 0 leaves the state unchanged.
 //
-// The inputs of token t + 1 are loaded while token t is computed (clamped to
-// the last token, so every load is unconditional). Each of the 16 lanes that
-// share a row holds the row's dot products after the DPP reduction, and lane
-// j == 0 stores the output element.
+// The token inputs (k, q, v, alpha, beta) of up to kStage tokens are staged
+// in LDS once per workgroup, v permuted so that a lane's STEPS value rows are
+// contiguous (one LDS read per token). Their global loads are issued before
+// the state loads, so the wait for them leaves the state loads in flight.
+// With the token inputs out of registers the kernel fits 128 VGPRs: four
+// workgroups per CU, so one workgroup's arithmetic overlaps the others'
+// state traffic. The state is kept as a scalar times a matrix so that the
+// decay costs one multiply per row instead of one per element (three fp32
+// operations per state element and token instead of four).
+template <typename DT, int D> struct MultiShape {
+    using Sh = DecodeShape<D>;
+    static constexpr int kStage = 8;                       // tokens per LDS stage
+    // v position of row r: lane group (wave, rsub) holds rows
+    // wave*RPW + rsub + 4*st at [(wave*4 + rsub)*STEPS + st]
+    static __device__ __forceinline__ int vpos(int r) {
+        const int wave = r / Sh::kRowsPerWave, rem = r % Sh::kRowsPerWave;
+        return (wave * 4 + (rem & 3)) * Sh::kSteps + (rem >> 2);
+    }
+};
+
+template <typename DT, int D>
+struct MultiSmem {
+    DT k[MultiShape<DT, D>::kStage][D];
+    DT q[MultiShape<DT, D>::kStage][D];
+    DT v[MultiShape<DT, D>::kStage][D];
+    float ab[MultiShape<DT, D>::kStage][2];
+};
+
 template <typename DT> struct Vec4Of;
 template <> struct Vec4Of<__bf16> { using type = bf16x4; };
 template <> struct Vec4Of<float> { using type = f32x4; };
 
-template <typename DT, int V4, int STEPS> struct TokenInputs {
-    typename Vec4Of<DT>::type k[V4], q[V4];
-    DT v[STEPS];
-    float alpha, beta;
+// Global loads of tokens [t0, t0 + n) into registers: thread i covers the
+// 4-element pieces i, i + 256, ... of the n*D/4 pieces of k, q and v each.
+template <typename DT, int D> struct StageRegs {
+    static constexpr int kPieces = MultiShape<DT, D>::kStage * D / 4;
+    static constexpr int kPerThread = (kPieces + 255) / 256;
+    typename Vec4Of<DT>::type k[kPerThread], q[kPerThread], v[kPerThread];
+    float ab;
 };
 
 template <typename DT, int D>
-__device__ __forceinline__ void load_token(TokenInputs<DT, D / 64, D / 16> &x, const DT *kp,
-                                           const DT *qp, const DT *vp, const float *ap,
-                                           const float *bp, int j, int row0) {
+__device__ __forceinline__ void stage_load(StageRegs<DT, D> &r, const DecodeMultiParams &p,
+                                           size_t tok0, int g, int h, int n) {
     using V = typename Vec4Of<DT>::type;
+    using R = StageRegs<DT, D>;
+    const int tid = threadIdx.x;
 #pragma unroll
-    for (int c = 0; c < D / 64; ++c) {
-        x.k[c] = *reinterpret_cast<const V *>(kp + 64 * c + 4 * j);
-        x.q[c] = *reinterpret_cast<const V *>(qp + 64 * c + 4 * j);
+    for (int i = 0; i < R::kPerThread; ++i) {
+        // clamped to the last valid piece: every load is unconditional
+        const int pc = min(tid + 256 * i, n * D / 4 - 1);
+        const int t = pc / (D / 4), c4 = pc % (D / 4);
+        const size_t tok = tok0 + t;
+        r.k[i] = *reinterpret_cast<const V *>(reinterpret_cast<const DT *>(p.k) +
+                                              (tok * p.Hk + g) * D + 4 * c4);
+        r.q[i] = *reinterpret_cast<const V *>(reinterpret_cast<const DT *>(p.q) +
+                                              (tok * p.Hk + g) * D + 4 * c4);
+        r.v[i] = *reinterpret_cast<const V *>(reinterpret_cast<const DT *>(p.v) +
+                                              (tok * p.Hv + h) * D + 4 * c4);
     }
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st) x.v[st] = vp[row0 + 4 * st];
-    x.alpha = *ap;
-    x.beta = *bp;
+    const int ta = min(tid >> 1, n - 1);
+    r.ab = ((tid & 1) ? p.beta : p.alpha)[(tok0 + ta) * p.Hv + h];
 }
 
 template <typename DT, int D>
-__global__ __launch_bounds__(256) void decode_multi_kernel(DecodeMultiParams p) {
+__device__ __forceinline__ void stage_store(MultiSmem<DT, D> &sm, const StageRegs<DT, D> &r,
+                                            int n) {
+    using V = typename Vec4Of<DT>::type;
+    using R = StageRegs<DT, D>;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < R::kPerThread; ++i) {
+        const int pc = tid + 256 * i;
+        if (pc < n * D / 4) {
+            const int t = pc / (D / 4), c4 = pc % (D / 4);
+            *reinterpret_cast<V *>(&sm.k[t][4 * c4]) = r.k[i];
+            *reinterpret_cast<V *>(&sm.q[t][4 * c4]) = r.q[i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm.v[t][MultiShape<DT, D>::vpos(4 * c4 + e)] = r.v[i][e];
+        }
+    }
+    if (tid < 2 * n) sm.ab[tid >> 1][tid & 1] = r.ab;
+}
+
+template <typename DT, int D>
+// fp32 token inputs need more registers: three workgroups per CU for them
+__global__ __launch_bounds__(256, sizeof(DT) == 2 ? 4 : 3) void decode_multi_kernel(
+    DecodeMultiParams p) {
     using Sh = DecodeShape<D>;
+    using Ms = MultiShape<DT, D>;
+    using V = typename Vec4Of<DT>::type;
     constexpr int V4 = Sh::kV4;
     constexpr int STEPS = Sh::kSteps;
+    constexpr int KS = Ms::kStage;
     constexpr size_t DD = (size_t)D * D;
+    __shared__ MultiSmem<DT, D> sm;
 
     const int bh = blockIdx.x;
     const int b = bh / p.Hv;
@@ -188,12 +248,7 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(DecodeMultiParams p) 
     // ((b*K + t)*Hv + h)*D, alpha/beta at (b*K + t)*Hv + h, per-token state
     // at ((b*K + t)*Hv + h)*D*D.
     const size_t tok0 = (size_t)b * K;
-    const size_t qk_step = (size_t)p.Hk * D, v_step = (size_t)p.Hv * D;
-    const DT *q0 = reinterpret_cast<const DT *>(p.q) + (tok0 * p.Hk + g) * D;
-    const DT *k0 = reinterpret_cast<const DT *>(p.k) + (tok0 * p.Hk + g) * D;
-    const DT *v0 = reinterpret_cast<const DT *>(p.v) + (tok0 * p.Hv + h) * D;
-    const float *a0 = p.alpha + tok0 * p.Hv + h;
-    const float *b0 = p.beta + tok0 * p.Hv + h;
+    const size_t v_step = (size_t)p.Hv * D;
     DT *o0 = reinterpret_cast<DT *>(p.out) + (tok0 * p.Hv + h) * D;
     float *st0 = p.steps ? p.steps + (tok0 * p.Hv + h) * DD : nullptr;
 
@@ -210,6 +265,9 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(DecodeMultiParams p) 
         return;
     }
 
+    // First stage's token loads, then the state loads.
+    StageRegs<DT, D> sr;
+    if (K > 0) stage_load<DT, D>(sr, p, tok0, g, h, min(K, KS));
     f32x4 s[STEPS][V4];
     if (src >= 0) {
         const float *S = p.pool + ((size_t)src * p.Hv + h) * DD;
@@ -226,53 +284,84 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(DecodeMultiParams p) 
             for (int c = 0; c < V4; ++c) s[st][c] = zero4();
     }
 
-    TokenInputs<DT, V4, STEPS> cur, nxt;
-    if (K > 0) load_token<DT, D>(cur, k0, q0, v0, a0, b0, j, row0);
-    for (int t = 0; t < K; ++t) {
-        const int tn = t + 1 < K ? t + 1 : t;
-        load_token<DT, D>(nxt, k0 + tn * qk_step, q0 + tn * qk_step, v0 + tn * v_step,
-                          a0 + (size_t)tn * p.Hv, b0 + (size_t)tn * p.Hv, j, row0);
-        float kk[V4][4], qq[V4][4];
-        float kq = 0.f;
+    // The state is cs * s, and the decay goes into the scalar: with
+    // cn = cs * alpha the update is one FMA per element, s += (u / cn) k,
+    // then cs = cn. When cn would leave [2^-64, 2^64] (alpha = 0 restarts
+    // the state), and for every token when per-token states are stored, a
+    // pass s *= cn first folds cs and alpha into s; the token then runs with
+    // cs = 1 and an effective alpha of 1, and s is the state itself after it.
+    float cs = 1.f;
+    for (int t0 = 0; t0 < K; t0 += KS) {
+        const int n = min(K - t0, KS);
+        if (t0 > 0) {
+            __syncthreads();  // every wave is done with the previous stage
+            stage_load<DT, D>(sr, p, tok0 + t0, g, h, n);
+        }
+        stage_store<DT, D>(sm, sr, n);
+        __syncthreads();
+        for (int tl = 0; tl < n; ++tl) {
+            const int t = t0 + tl;
+            float kk[V4][4], qq[V4][4];
+            float kq = 0.f;
 #pragma unroll
-        for (int c = 0; c < V4; ++c)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                kk[c][e] = to_f32(cur.k[c][e]);
-                qq[c][e] = to_f32(cur.q[c][e]);
-                kq += kk[c][e] * qq[c][e];
-            }
-        kq = row16_sum(kq);
-        const float alpha = cur.alpha, beta = cur.beta;
-        DT *ot = o0 + t * v_step;
-        float *stt = st0 ? st0 + (size_t)t * p.Hv * DD : nullptr;
-#pragma unroll
-        for (int st = 0; st < STEPS; ++st) {
-            float sk = 0.f, sq = 0.f;
-#pragma unroll
-            for (int c = 0; c < V4; ++c)
+            for (int c = 0; c < V4; ++c) {
+                const V kv = *reinterpret_cast<const V *>(&sm.k[tl][64 * c + 4 * j]);
+                const V qv = *reinterpret_cast<const V *>(&sm.q[tl][64 * c + 4 * j]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    sk += s[st][c][e] * kk[c][e];
-                    sq += s[st][c][e] * qq[c][e];
+                    kk[c][e] = to_f32(kv[e]);
+                    qq[c][e] = to_f32(qv[e]);
+                    kq += kk[c][e] * qq[c][e];
                 }
-            sk = row16_sum(sk);
-            sq = row16_sum(sq);
-            const float u = beta * (to_f32(cur.v[st]) - alpha * sk);
+            }
+            DT vr[STEPS];
 #pragma unroll
-            for (int c = 0; c < V4; ++c)
+            for (int st = 0; st < STEPS; ++st) vr[st] = sm.v[tl][(wave * 4 + rsub) * STEPS + st];
+            const float beta = sm.ab[tl][1];
+            float alpha = sm.ab[tl][0];
+            float cn = cs * alpha;
+            DT *ot = o0 + t * v_step;
+            float *stt = st0 ? st0 + (size_t)t * p.Hv * DD : nullptr;
+            if (stt || !(cn >= 0x1p-64f && cn <= 0x1p64f)) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) s[st][c][e] = alpha * s[st][c][e] + u * kk[c][e];
-            if (j == 0) ot[row0 + 4 * st] = from_f32<DT>(p.scale * (alpha * sq + u * kq));
-            if (stt) {
+                for (int st = 0; st < STEPS; ++st)
+#pragma unroll
+                    for (int c = 0; c < V4; ++c) s[st][c] *= cn;
+                cs = 1.f;
+                alpha = 1.f;
+                cn = 1.f;
+            }
+            const float inv = 1.f / cn;
+            kq = row16_sum(kq);
+#pragma unroll
+            for (int st = 0; st < STEPS; ++st) {
+                float sk = 0.f, sq = 0.f;
 #pragma unroll
                 for (int c = 0; c < V4; ++c)
-                    __builtin_nontemporal_store(
-                        s[st][c], reinterpret_cast<f32x4 *>(stt + (size_t)(row0 + 4 * st) * D +
-                                                            64 * c + 4 * j));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        sk += s[st][c][e] * kk[c][e];
+                        sq += s[st][c][e] * qq[c][e];
+                    }
+                sk = cs * row16_sum(sk);
+                sq = cs * row16_sum(sq);
+                const float u = beta * (to_f32(vr[st]) - alpha * sk);
+                const float w = u * inv;
+#pragma unroll
+                for (int c = 0; c < V4; ++c)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) s[st][c][e] += w * kk[c][e];
+                if (j == 0) ot[row0 + 4 * st] = from_f32<DT>(p.scale * (alpha * sq + u * kq));
+                if (stt) {
+#pragma unroll
+                    for (int c = 0; c < V4; ++c)
+                        __builtin_nontemporal_store(
+                            s[st][c], reinterpret_cast<f32x4 *>(stt + (size_t)(row0 + 4 * st) * D +
+                                                                64 * c + 4 * j));
+                }
             }
+            cs = cn;
         }
-        cur = nxt;
     }
 
     if (dst >= 0) {
@@ -282,7 +371,7 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(DecodeMultiParams p) 
 #pragma unroll
             for (int c = 0; c < V4; ++c)
                 __builtin_nontemporal_store(
-                    s[st][c],
+                    s[st][c] * cs,
                     reinterpret_cast<f32x4 *>(S + (size_t)(row0 + 4 * st) * D + 64 * c + 4 * j));
     }
 }

@@ -356,6 +356,34 @@ def test_decode_multi_K1_matches_decode_step(gdn):
     assert max_error(pool[src], S_s, (0, 1)) <= 1e-5
 
 
+@pytest.mark.parametrize("case", ["beta0", "alpha1_beta1", "alpha0"])
+def test_decode_multi_edge_gates(gdn, case):
+    """The gate edges through the multi-token path: alpha = 0 restarts the
+    state (the kernel's decay scalar cannot carry it), beta = 0 is pure
+    decay, alpha = beta = 1 overwrites without decay."""
+    d = multi_decode(3, 40, 2, 4, 128, "bf16", seed=95, plan="permute", alpha_shift=-5.0)
+    d = _edge_gates(d, case)
+    o, pool, st = gpu_multi(gdn, d)
+    ref = oracle.decode_multi(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["pool"],
+                              d["src_slot"], d["dst_slot"])
+    check_multi(d, o, pool, st, ref, "bf16", f"multi edge gates {case}")
+
+
+@pytest.mark.parametrize("alpha_shift", [2.0, -5.0])
+def test_decode_multi_many_stages(gdn, alpha_shift):
+    """K = 37 spans five LDS stages of 8 tokens; at the workloads' decay the
+    running product of alpha leaves the scalar's range and is folded back."""
+    d = multi_decode(2, 37, 1, 3, 128, "bf16", seed=96, plan="pairs", alpha_shift=alpha_shift)
+    o, pool, st = gpu_multi(gdn, d, 0.9, False)
+    ref = oracle.decode_multi(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["pool"],
+                              d["src_slot"], d["dst_slot"], 0.9)
+    check_multi(d, o, pool, st, ref, "bf16", f"multi K=37 alpha_shift={alpha_shift}")
+    o2, pool2, st2 = gpu_multi(gdn, d, 0.9, True)   # the per-token-state form
+    check_multi(d, o2, pool2, st2, ref[:2] + (oracle.decode_multi(
+        d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["pool"], d["src_slot"], d["dst_slot"],
+        0.9, True)[2],), "bf16", f"multi K=37 alpha_shift={alpha_shift} steps")
+
+
 def test_spec_decode_workload(gdn):
     w = SPEC_DECODE
     d = multi_decode(w["B"], w["K"], w["Hk"], w["Hv"], w["D"], w["dtype"], w["seed"],
