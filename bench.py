@@ -13,9 +13,10 @@ attention multiplies on top of that").
 Reported: prefill tokens/s (value) with its fraction of the bf16 MFMA peak,
 decode state-update GB/s with its fraction of HBM bandwidth, both from HIP
 events on the stream the kernels run on; and the fp64 oracle timed on the
-host cores as a CPU baseline. Timed apart from the step, under
-"decode_multi": the K-token decode against a slot pool (B=256 sequences
-verifying K=4 tokens each), in tokens/s and HBM GB/s.
+host cores as a CPU baseline. Timed apart from the step: under
+"prefill_prefix_states" the same prefill also writing the state after every
+1024 tokens, and under "decode_multi" the K-token decode against a slot pool
+(B=256 sequences verifying K=4 tokens each), in tokens/s and HBM GB/s.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3]
 """
@@ -216,6 +217,35 @@ def main():
         cold_ms = [e0.elapsed_time(e1) for e0, e1 in evc]
         del scratch
 
+    # the same prefill emitting block-aligned prefix states (one per 1024
+    # tokens): what a prefix cache keeps
+    prefix = None
+    if not varlen and wp.T >= 1024:
+        every = 16
+        rows = gdn.prefix_state_rows(wp.B, wp.T, every, False)
+        p_pre = torch.empty((rows, wp.Hv, wp.D, wp.D), dtype=torch.float32, device=dev)
+
+        def step_prefill_prefix():
+            gdn.gdn_prefill_chunked(pt["q"], pt["k"], pt["v"], pt["alpha"], pt["beta"], p_s0,
+                                    out=p_out, final_state=p_sf, prefix_states=p_pre,
+                                    prefix_interval=every, workspace=p_ws, stream=stream)
+        step_prefill_prefix()
+        torch.cuda.synchronize()
+        evp = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        for i in range(K):
+            evp[i][0].record(stream)
+            step_prefill_prefix()
+            evp[i][1].record(stream)
+        torch.cuda.synchronize()
+        pp_ms = [e0.elapsed_time(e1) for e0, e1 in evp]
+        prefix = {"block_tokens": 64 * every, "states": rows * wp.Hv,
+                  "bytes_written": rows * wp.Hv * wp.D * wp.D * 4,
+                  "ms": round(float(np.mean(pp_ms)), 5),
+                  "ms_median": round(float(np.median(pp_ms)), 5),
+                  "overhead_vs_plain": round(float(np.median(pp_ms)) / float(np.median(pre_ms)) - 1,
+                                             4)}
+        del p_pre
+
     # K tokens per sequence against a slot pool (speculative verification):
     # timed on its own, after the step, on the same stream
     multi = None
@@ -344,6 +374,8 @@ def main():
                              "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
                              "traffic": _traffic("prefill_" + wp.name, pdig)},
     }
+    if prefix is not None:
+        res["prefill_prefix_states"] = prefix
     if multi is not None:
         res["decode_multi"] = multi
     if ceilings is not None:

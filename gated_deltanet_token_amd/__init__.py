@@ -49,8 +49,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     sz = ctypes.c_size_t
-    lib.gdn_prefill_chunked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
-                                        i32, ctypes.c_int, f32, vp, sz, vp]
+    lib.gdn_prefill_chunked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i64, i32,
+                                        i32, i32, i32, ctypes.c_int, f32, vp, sz, vp]
     lib.gdn_prefill_chunked.restype = ctypes.c_int
     lib.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                     ctypes.c_int, f32, vp]
@@ -58,8 +58,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32,
                                      i32, i32, i32, ctypes.c_int, f32, vp]
     lib.gdn_decode_multi.restype = ctypes.c_int
-    lib.gdn_varlen_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, i32, i32,
-                                       i32, i32, ctypes.c_int, f32, vp, sz, vp]
+    lib.gdn_varlen_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, vp, i32,
+                                       i32, i32, i32, i32, ctypes.c_int, f32, vp, sz, vp]
     lib.gdn_varlen_prefill.restype = ctypes.c_int
     lib.gdn_prefill_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, ctypes.c_int, i32]
     lib.gdn_prefill_workspace_size.restype = sz
@@ -130,11 +130,31 @@ def _workspace(workspace, num_seqs, tokens, Hk, Hv, Dk, Dv, dtype_code, packed, 
     return workspace.data_ptr(), workspace.numel() * workspace.element_size(), workspace
 
 
+def prefix_state_rows(num_seqs: int, tokens: int, interval: int, packed: bool) -> int:
+    """Rows of the prefix_states buffer for blocks of 64 * interval tokens:
+    num_seqs * floor(T / L) for a dense batch (tokens = T per sequence),
+    floor(total / L) + N for a packed one (tokens = total)."""
+    L = 64 * interval
+    return tokens // L + num_seqs if packed else num_seqs * (tokens // L)
+
+
+def _prefix(prefix_states, prefix_interval, rows, Hv, Dv, Dk, dev):
+    if prefix_states is None:
+        return None, 0
+    if int(prefix_interval) < 1:
+        raise ValueError("prefix_interval must be >= 1 with prefix_states")
+    _need(prefix_states, "prefix_states", torch.float32, (rows, Hv, Dv, Dk), dev)
+    return prefix_states, int(prefix_interval)
+
+
 def gdn_prefill_chunked(q, k, v, alpha, beta, initial_state=None, *, out=None,
                         final_state=None, scale: float = 1.0, want_final_state: bool = True,
+                        prefix_states=None, prefix_interval: int = 0,
                         workspace="auto", stream=None):
     """Chunked prefill. q,k [B,T,Hk,D]; v [B,T,Hv,D]; alpha,beta [B,T,Hv] fp32;
     initial_state [B,Hv,D,D] fp32 or None. Returns (out, final_state).
+    prefix_states: optional fp32 [B * floor(T / L), Hv, D, D] (L = 64 *
+    prefix_interval) receiving the state after every whole block of L tokens.
     workspace: "auto" (allocate what the library asks for), None, or a
     device uint8 tensor."""
     lib = load_library()
@@ -155,20 +175,26 @@ def gdn_prefill_chunked(q, k, v, alpha, beta, initial_state=None, *, out=None,
         final_state = torch.empty((B, Hv, Dv, Dk), dtype=torch.float32, device=dev)
     if final_state is not None:
         _need(final_state, "final_state", torch.float32, (B, Hv, Dv, Dk), dev)
+    pre, pint = _prefix(prefix_states, prefix_interval,
+                        prefix_state_rows(B, T, max(int(prefix_interval), 1), False), Hv, Dv, Dk,
+                        dev)
     st = _stream(dev, stream)
     wp, wb, _keep = _workspace(workspace, B, T, Hk, Hv, Dk, Dv, _dtype_code(q), False, dev, st)
     _check(lib.gdn_prefill_chunked(
         _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state), _ptr(out),
-        _ptr(final_state), B, T, Hk, Hv, Dk, Dv, _dtype_code(q), float(scale), wp, wb,
-        st.cuda_stream))
+        _ptr(final_state), _ptr(pre), pint, B, T, Hk, Hv, Dk, Dv, _dtype_code(q), float(scale),
+        wp, wb, st.cuda_stream))
     return out, final_state
 
 
 def gdn_varlen_prefill(q, k, v, alpha, beta, cu_seqlens, initial_state=None, *, out=None,
                        final_state=None, scale: float = 1.0, want_final_state: bool = True,
+                       prefix_states=None, prefix_interval: int = 0,
                        workspace="auto", stream=None):
     """Packed prefill. q,k [total,Hk,D]; v [total,Hv,D]; alpha,beta [total,Hv];
-    cu_seqlens int32 [N+1] on the device. Returns (out, final_state [N,Hv,D,D])."""
+    cu_seqlens int32 [N+1] on the device. Returns (out, final_state [N,Hv,D,D]).
+    prefix_states: optional fp32 [floor(total / L) + N, Hv, D, D]; block i of
+    sequence n lands in row floor(cu_seqlens[n] / L) + n + i."""
     lib = load_library()
     total, Hk, Dk = q.shape
     Hv, Dv = v.shape[1], v.shape[2]
@@ -189,12 +215,15 @@ def gdn_varlen_prefill(q, k, v, alpha, beta, cu_seqlens, initial_state=None, *, 
         final_state = torch.empty((N, Hv, Dv, Dk), dtype=torch.float32, device=dev)
     if final_state is not None:
         _need(final_state, "final_state", torch.float32, (N, Hv, Dv, Dk), dev)
+    pre, pint = _prefix(prefix_states, prefix_interval,
+                        prefix_state_rows(N, total, max(int(prefix_interval), 1), True), Hv, Dv,
+                        Dk, dev)
     st = _stream(dev, stream)
     wp, wb, _keep = _workspace(workspace, N, total, Hk, Hv, Dk, Dv, _dtype_code(q), True, dev, st)
     _check(lib.gdn_varlen_prefill(
         _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(cu_seqlens), N, total,
-        _ptr(initial_state), _ptr(out), _ptr(final_state), Hk, Hv, Dk, Dv, _dtype_code(q),
-        float(scale), wp, wb, st.cuda_stream))
+        _ptr(initial_state), _ptr(out), _ptr(final_state), _ptr(pre), pint, Hk, Hv, Dk, Dv,
+        _dtype_code(q), float(scale), wp, wb, st.cuda_stream))
     return out, final_state
 
 

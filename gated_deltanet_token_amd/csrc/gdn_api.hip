@@ -64,6 +64,7 @@ gdn_status_t device_cus(int *cus) {
 // `nstates` is B or N.
 gdn_status_t check_prefill(const void *q, const void *k, const void *v, const float *alpha,
                            const float *beta, const float *s0, const void *out, const float *sf,
+                           const float *prefix, int64_t prefix_rows,
                            const int32_t *cu, int64_t cu_count, int64_t tokens, int64_t nstates,
                            int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv, gdn_dtype_t dtype,
                            const void *ws, size_t ws_bytes) {
@@ -76,10 +77,13 @@ gdn_status_t check_prefill(const void *q, const void *k, const void *v, const fl
     if (!mul_ok(nst, Hv) || !mul_ok(nst, Dv) || !mul_ok(nst, Dk) || !mul_ok(nst, 4))
         return GDN_ERR_BAD_SHAPE;
     if (nstates * Hv > 0x7FFFFFFF / 8) return GDN_ERR_BAD_SHAPE;  // grid size
+    int64_t npre = prefix ? prefix_rows : 0;
+    if (!mul_ok(npre, Hv) || !mul_ok(npre, Dv) || !mul_ok(npre, Dk) || !mul_ok(npre, 4))
+        return GDN_ERR_BAD_SHAPE;
 
     if (tokens > 0 && (!q || !k || !v || !alpha || !beta || !out)) return GDN_ERR_NULL_POINTER;
     if (cu_count > 0 && !cu) return GDN_ERR_NULL_POINTER;
-    const void *ptrs[] = {q, k, v, alpha, beta, s0, out, sf, cu, ws};
+    const void *ptrs[] = {q, k, v, alpha, beta, s0, out, sf, prefix, cu, ws};
     for (const void *ptr : ptrs)
         if (ptr && !aligned16(ptr)) return GDN_ERR_MISALIGNED;
     if (ws_bytes > (size_t)INT64_MAX) return GDN_ERR_BAD_SHAPE;
@@ -104,6 +108,10 @@ gdn_status_t check_prefill(const void *q, const void *k, const void *v, const fl
     const Range all[] = {rq, rk, rv, ra, rb, rs0, ro, rsf, rcu};
     for (const Range &r : all)
         if (overlap(rws, r)) return GDN_ERR_ALIAS;
+    const Range rpre = range_of(prefix, npre);
+    for (const Range &r : all)
+        if (overlap(rpre, r)) return GDN_ERR_ALIAS;
+    if (overlap(rpre, rws)) return GDN_ERR_ALIAS;
     return GDN_OK;
 }
 
@@ -124,7 +132,7 @@ const char *gdn_status_string(gdn_status_t s) {
     return "unknown status";
 }
 
-int32_t gdn_version(void) { return 300; }
+int32_t gdn_version(void) { return 400; }
 
 size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t tokens, int32_t Hk, int32_t Hv,
                                   int32_t Dk, int32_t Dv, gdn_dtype_t dtype, int32_t packed) {
@@ -143,22 +151,29 @@ size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t tokens, int32_t Hk, 
 
 gdn_status_t gdn_prefill_chunked(const void *q, const void *k, const void *v, const float *alpha,
                                  const float *beta, const float *initial_state, void *out,
-                                 float *final_state, int32_t B, int64_t T, int32_t Hk, int32_t Hv,
-                                 int32_t Dk, int32_t Dv, gdn_dtype_t dtype, float scale,
-                                 void *workspace, size_t workspace_bytes, hipStream_t stream) {
+                                 float *final_state, float *prefix_states, int32_t prefix_interval,
+                                 int32_t B, int64_t T, int32_t Hk, int32_t Hv, int32_t Dk,
+                                 int32_t Dv, gdn_dtype_t dtype, float scale, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
     gdn_status_t st = check_heads(Hk, Hv, Dk, Dv);
     if (st != GDN_OK) return st;
     if (B < 1 || T < 0) return GDN_ERR_BAD_SHAPE;
+    if (prefix_states && prefix_interval < 1) return GDN_ERR_BAD_SHAPE;
     int64_t tokens = B;
     if (!mul_ok(tokens, T)) return GDN_ERR_BAD_SHAPE;
-    st = check_prefill(q, k, v, alpha, beta, initial_state, out, final_state, nullptr, 0, tokens,
-                       B, Hk, Hv, Dk, Dv, dtype, workspace, workspace_bytes);
+    // B * floor(T / (64 m)) prefix rows
+    const int64_t prefix_rows = prefix_states ? (int64_t)B * (T / (64 * (int64_t)prefix_interval)) : 0;
+    st = check_prefill(q, k, v, alpha, beta, initial_state, out, final_state, prefix_states,
+                       prefix_rows, nullptr, 0, tokens, B, Hk, Hv, Dk, Dv, dtype, workspace,
+                       workspace_bytes);
     if (st != GDN_OK) return st;
     if (tokens == 0 && !final_state) return GDN_OK;  // nothing to write
     int cus = 0;
     if ((st = device_cus(&cus)) != GDN_OK) return st;
-    gdn::PrefillParams p{q, k, v, alpha, beta, initial_state, out, final_state, nullptr, T, B,
-                         Hk, Hv, scale};
+    gdn::PrefillParams p{q,  k,     v,     alpha,         beta,
+                         initial_state, out, final_state, nullptr, T,
+                         B,  Hk,    Hv,    scale,         prefix_rows ? prefix_states : nullptr,
+                         prefix_interval};
     const int64_t slots = gdn::prefill_ws_slots(B, tokens, T, false);
     const hipError_t e = gdn::launch_prefill(p, dtype == GDN_BF16 ? 1 : 0, Dk, cus, workspace,
                                              workspace_bytes, slots, stream);
@@ -169,22 +184,28 @@ gdn_status_t gdn_prefill_chunked(const void *q, const void *k, const void *v, co
 gdn_status_t gdn_varlen_prefill(const void *q, const void *k, const void *v, const float *alpha,
                                 const float *beta, const int32_t *cu_seqlens, int32_t N,
                                 int64_t total_T, const float *initial_state, void *out,
-                                float *final_state, int32_t Hk, int32_t Hv, int32_t Dk,
-                                int32_t Dv, gdn_dtype_t dtype, float scale, void *workspace,
-                                size_t workspace_bytes, hipStream_t stream) {
+                                float *final_state, float *prefix_states, int32_t prefix_interval,
+                                int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv, gdn_dtype_t dtype,
+                                float scale, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
     gdn_status_t st = check_heads(Hk, Hv, Dk, Dv);
     if (st != GDN_OK) return st;
     if (N < 1 || total_T < 0 || total_T > 0x7FFFFFFF) return GDN_ERR_BAD_SHAPE;
     if (!cu_seqlens) return GDN_ERR_NULL_POINTER;
-    st = check_prefill(q, k, v, alpha, beta, initial_state, out, final_state, cu_seqlens,
-                       (int64_t)N + 1, total_T, N, Hk, Hv, Dk, Dv, dtype, workspace,
-                       workspace_bytes);
+    if (prefix_states && prefix_interval < 1) return GDN_ERR_BAD_SHAPE;
+    // floor(total_T / (64 m)) + N prefix rows
+    const int64_t prefix_rows =
+        prefix_states ? total_T / (64 * (int64_t)prefix_interval) + N : 0;
+    st = check_prefill(q, k, v, alpha, beta, initial_state, out, final_state, prefix_states,
+                       prefix_rows, cu_seqlens, (int64_t)N + 1, total_T, N, Hk, Hv, Dk, Dv, dtype,
+                       workspace, workspace_bytes);
     if (st != GDN_OK) return st;
     if (total_T == 0 && !final_state) return GDN_OK;
     int cus = 0;
     if ((st = device_cus(&cus)) != GDN_OK) return st;
-    gdn::PrefillParams p{q, k, v, alpha, beta, initial_state, out, final_state, cu_seqlens, 0, N,
-                         Hk, Hv, scale};
+    gdn::PrefillParams p{q,          k,  v,  alpha, beta, initial_state, out, final_state,
+                         cu_seqlens, 0,  N,  Hk,    Hv,   scale,         prefix_states,
+                         prefix_interval};
     const int64_t slots = gdn::prefill_ws_slots(N, total_T, 0, true);
     const hipError_t e = gdn::launch_prefill(p, dtype == GDN_BF16 ? 1 : 0, Dk, cus, workspace,
                                              workspace_bytes, slots, stream);

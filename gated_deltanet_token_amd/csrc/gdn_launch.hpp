@@ -16,6 +16,8 @@ struct PrefillParams {
     int64_t seq_len;
     int32_t nseq, Hk, Hv;
     float scale;
+    float *prefix;         // block-aligned prefix states, or nullptr
+    int32_t prefix_every;  // block length in chunks (>= 1 when prefix is set)
 };
 
 struct DecodeParams {

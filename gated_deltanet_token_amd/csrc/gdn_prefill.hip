@@ -60,6 +60,31 @@ __device__ __forceinline__ int64_t slot_base(const PrefillParams &p, int n) {
     return (int64_t)n * ((p.seq_len + kC - 1) / kC);
 }
 
+// Prefix states: the state after every block of 64 * prefix_every tokens of
+// a sequence (whole blocks only). Block i of sequence n goes to row
+//   dense : n * floor(T / blk) + i
+//   packed: floor(cu[n] / blk) + n + i   (injective, below floor(total/blk) + N)
+// The divisions run once per workgroup; per chunk the check is one compare
+// (this sits on the sequential path of the chain).
+struct PrefixRows {
+    int64_t next;  // chunk after which the next state is due; -1: none left
+    int64_t row;   // its row
+    int64_t left;  // states still due
+    __device__ __forceinline__ PrefixRows(const PrefillParams &p, int n, int64_t len) {
+        const int64_t every = p.prefix ? p.prefix_every : 1, blk = every * kC;
+        left = p.prefix ? len / blk : 0;
+        next = left > 0 ? every - 1 : -1;
+        row = p.cu_seqlens ? (int64_t)p.cu_seqlens[n] / blk + n : (int64_t)n * (p.seq_len / blk);
+    }
+    // Row for the state after chunk c, or -1; advances when one is due.
+    __device__ __forceinline__ int64_t take(const PrefillParams &p, int64_t c) {
+        if (c != next) return -1;
+        const int64_t r = row++;
+        next = --left > 0 ? next + p.prefix_every : -1;
+        return r;
+    }
+};
+
 // Logical workgroup id: workgroups are dispatched to the 8 XCDs round-robin;
 // give each XCD a contiguous range of logical ids so that workgroups sharing
 // a q/k head (and thus K, Q) share that XCD's L2.
@@ -196,7 +221,9 @@ template <typename DT, int D, int NW, int DVW> struct FusedCfg {
     static_assert(LDS <= 160 * 1024, "LDS budget of a gfx950 CU");
 };
 
-template <typename DT, int D, int NW, int DVW>
+// PREFIX: also write the block-aligned prefix states (a separate
+// instantiation, so that the kernel without them carries no trace of it).
+template <typename DT, int D, int NW, int DVW, bool PREFIX>
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p, int nsplit,
                                                           int remap_xcd) {
     using Cf = FusedCfg<DT, D, NW, DVW>;
@@ -275,6 +302,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p, int n
     };
 
     const int64_t nchunks = (len + kC - 1) / kC;
+    PrefixRows pre(p, n, len);
     if (nchunks > 0) load_chunk(0);
     // Drain the initial-state and first-chunk loads here (the first store
     // needs them anyway). Otherwise the state registers count as possibly
@@ -328,6 +356,16 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p, int n
         __syncthreads();  // T is ready
         chain_finish<DT, D, NB, PK, PT, PV>(m, st, racc, oT, wdv, oh + c * kC * sVO, sVO, lenc,
                                             p.scale, g4, c16);
+        const int64_t prow = PREFIX ? pre.take(p, c) : -1;
+        if (prow >= 0) {
+            float *ps = p.prefix + (prow * p.Hv + h) * D * D;
+#pragma unroll
+            for (int a = 0; a < NKT; ++a)
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    *reinterpret_cast<f32x4 *>(ps + (int64_t)(dv0 + wdv + 16 * b + c16) * D +
+                                               16 * a + 4 * g4) = st[a][b];
+        }
     }
 
     if (p.s_final) {
@@ -572,7 +610,7 @@ template <typename DT, int D, int NC, int DVW> struct ChainCfg {
 // One workgroup (4 waves) per (sequence, value head, slice of DVS columns);
 // waves 0..NC-1 own DVW columns each and run the state chain, all four waves
 // stage the next chunk.
-template <typename DT, int D, int NC, int DVW>
+template <typename DT, int D, int NC, int DVW, bool PREFIX>
 __global__ __launch_bounds__(256) void chain_kernel(PrefillParams p, const unsigned char *ws,
                                                     int nsplit, int remap_xcd) {
     using Cf = ChainCfg<DT, D, NC, DVW>;
@@ -648,6 +686,7 @@ __global__ __launch_bounds__(256) void chain_kernel(PrefillParams p, const unsig
     };
 
     const int64_t nchunks = (len + kC - 1) / kC;
+    PrefixRows pre(p, n, len);
     if (nchunks > 0) load_chunk(0);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): see prefill_kernel
 
@@ -675,6 +714,16 @@ __global__ __launch_bounds__(256) void chain_kernel(PrefillParams p, const unsig
             chain_state_half<DT, D, NB, PK>(m, st, sf, racc, oT, g4, c16);
             chain_finish<DT, D, NB, PK, PT, PV>(m, st, racc, oT, wdv, oh + c * kC * sVO, sVO, lenc,
                                                 p.scale, g4, c16);
+            const int64_t prow = PREFIX ? pre.take(p, c) : -1;
+            if (prow >= 0) {
+                float *ps = p.prefix + (prow * p.Hv + h) * D * D;
+#pragma unroll
+                for (int a = 0; a < NKT; ++a)
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+                        *reinterpret_cast<f32x4 *>(ps + (int64_t)(dv0 + wdv + 16 * b + c16) * D +
+                                                   16 * a + 4 * g4) = st[a][b];
+            }
         }
     }
 
@@ -750,7 +799,7 @@ __device__ __forceinline__ void dma16(const unsigned char *src, unsigned char *l
 }
 
 // The LDS buffers allow one workgroup per CU.
-template <int D, int NC, int NH>
+template <int D, int NC, int NH, bool PREFIX>
 __global__ __launch_bounds__((ChainDbCfg<D, NC, NH>::NW * 64)) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int remap_xcd) {
     using DT = __bf16;
@@ -809,11 +858,20 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
                                     s0 + (int64_t)(dv0 + wdv + c16) * D + 16 * a + 4 * g4)
                               : zero4();
             if (lane == 0) *flag = 0;
+            PrefixRows pre(p, n, len);
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): initial state; see prefill_kernel
             __syncthreads();
             for (int64_t c = 0; c < nchunks; ++c) {
                 chain_core_db<D, Cf::DVS, 1, (Cf::NW > 8)>(smem_view(c), st, wdv, ho, flag, (int)c,
                                                            g4, c16, lane);
+                const int64_t prow = PREFIX ? pre.take(p, c) : -1;
+                if (prow >= 0) {
+                    float *ps = p.prefix + (prow * p.Hv + h) * D * D;
+#pragma unroll
+                    for (int a = 0; a < NKT; ++a)
+                        *reinterpret_cast<f32x4 *>(ps + (int64_t)(dv0 + wdv + c16) * D + 16 * a +
+                                                   4 * g4) = st[a][0];
+                }
                 __syncthreads();
             }
             if (p.s_final) {
@@ -987,8 +1045,12 @@ template <typename DT, int D, int NW, int DVW>
 static hipError_t launch_fused(const PrefillParams &p, int nsplit, hipStream_t stream) {
     const int64_t nblocks = (int64_t)p.nseq * p.Hv * nsplit;
     if (nblocks <= 0 || nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((prefill_kernel<DT, D, NW, DVW>), dim3((unsigned)nblocks), dim3(NW * 64), 0,
-                       stream, p, nsplit, nblocks % 8 == 0 ? 1 : 0);
+    if (p.prefix)
+        hipLaunchKernelGGL((prefill_kernel<DT, D, NW, DVW, true>), dim3((unsigned)nblocks),
+                           dim3(NW * 64), 0, stream, p, nsplit, nblocks % 8 == 0 ? 1 : 0);
+    else
+        hipLaunchKernelGGL((prefill_kernel<DT, D, NW, DVW, false>), dim3((unsigned)nblocks),
+                           dim3(NW * 64), 0, stream, p, nsplit, nblocks % 8 == 0 ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -1003,8 +1065,14 @@ static hipError_t launch_split(const PrefillParams &p, unsigned char *ws, int64_
                        nprep % 8 == 0 ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((chain_kernel<DT, D, NC, DVW>), dim3((unsigned)nchain), dim3(256), 0, stream,
-                       p, (const unsigned char *)ws, nsplit, nchain % 8 == 0 ? 1 : 0);
+    if (p.prefix)
+        hipLaunchKernelGGL((chain_kernel<DT, D, NC, DVW, true>), dim3((unsigned)nchain), dim3(256),
+                           0, stream, p, (const unsigned char *)ws, nsplit,
+                           nchain % 8 == 0 ? 1 : 0);
+    else
+        hipLaunchKernelGGL((chain_kernel<DT, D, NC, DVW, false>), dim3((unsigned)nchain), dim3(256),
+                           0, stream, p, (const unsigned char *)ws, nsplit,
+                           nchain % 8 == 0 ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -1020,9 +1088,14 @@ static hipError_t launch_split_db(const PrefillParams &p, unsigned char *ws, int
                        nprep % 8 == 0 ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((chain_db_kernel<D, NC, NH>), dim3((unsigned)nchain),
-                       dim3(ChainDbCfg<D, NC, NH>::NW * 64), 0, stream, p,
-                       (const unsigned char *)ws, nsplit, nchain % 8 == 0 ? 1 : 0);
+    if (p.prefix)
+        hipLaunchKernelGGL((chain_db_kernel<D, NC, NH, true>), dim3((unsigned)nchain),
+                           dim3(ChainDbCfg<D, NC, NH>::NW * 64), 0, stream, p,
+                           (const unsigned char *)ws, nsplit, nchain % 8 == 0 ? 1 : 0);
+    else
+        hipLaunchKernelGGL((chain_db_kernel<D, NC, NH, false>), dim3((unsigned)nchain),
+                           dim3(ChainDbCfg<D, NC, NH>::NW * 64), 0, stream, p,
+                           (const unsigned char *)ws, nsplit, nchain % 8 == 0 ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -73,6 +73,16 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype_t; /* type of q, k, v, out 
  *   out           [B, T, Hv, Dv]  dtype  o_t (fp32 -> bf16 rounds to nearest even)
  *   final_state   [B, Hv, Dv, Dk] fp32   S_T; NULL means not written;
  *                                        may equal initial_state
+ *   prefix_states [B, floor(T / L), Hv, Dv, Dk] fp32, or NULL: the state
+ *                 after every block of L = 64 * prefix_interval tokens,
+ *                 row i of sequence b holding S_{L (i + 1)} (whole blocks
+ *                 only; the state after a partial last block is final_state).
+ *                 These are the block-aligned prefix states of "PHBA:
+ *                 Prefix-State Hybrid Block Attention" (Abstract, Figure 1),
+ *                 formed by the gated recurrence at block boundaries, and the
+ *                 states a prefix cache keeps. prefix_interval >= 1 when
+ *                 prefix_states is set (ignored otherwise); must not overlap
+ *                 any other argument.
  *
  * Sizes: B >= 1, T >= 0, Hk >= 1, Hv a multiple of Hk, Dk == Dv in {64, 128}.
  * T == 0 writes the initial state (or zeros) to final_state.
@@ -90,7 +100,8 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype_t; /* type of q, k, v, out 
 gdn_status_t gdn_prefill_chunked(const void *q, const void *k, const void *v,
                                  const float *alpha, const float *beta,
                                  const float *initial_state, void *out,
-                                 float *final_state, int32_t B, int64_t T,
+                                 float *final_state, float *prefix_states,
+                                 int32_t prefix_interval, int32_t B, int64_t T,
                                  int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
                                  gdn_dtype_t dtype, float scale,
                                  void *workspace, size_t workspace_bytes,
@@ -172,6 +183,12 @@ gdn_status_t gdn_decode_multi(const void *q, const void *k, const void *v,
  *                 not checked (malformed offsets are undefined behaviour).
  *   initial_state [N, Hv, Dv, Dk] fp32 or NULL (zero states)
  *   final_state   [N, Hv, Dv, Dk] fp32 or NULL; may equal initial_state
+ *   prefix_states [floor(total_T / L) + N, Hv, Dv, Dk] fp32 or NULL, with
+ *                 L = 64 * prefix_interval: as for gdn_prefill_chunked, the
+ *                 state after each whole block of L tokens of a sequence;
+ *                 block i of sequence n goes to row
+ *                 floor(cu_seqlens[n] / L) + n + i (rows that no block maps
+ *                 to are left untouched)
  *
  * Sizes: N >= 1, 0 <= total_T < 2^31, Hv a multiple of Hk, Dk == Dv in
  * {64, 128}. Chunks restart at every sequence boundary. workspace: as for
@@ -181,7 +198,9 @@ gdn_status_t gdn_varlen_prefill(const void *q, const void *k, const void *v,
                                 const float *alpha, const float *beta,
                                 const int32_t *cu_seqlens, int32_t N,
                                 int64_t total_T, const float *initial_state,
-                                void *out, float *final_state, int32_t Hk,
+                                void *out, float *final_state,
+                                float *prefix_states, int32_t prefix_interval,
+                                int32_t Hk,
                                 int32_t Hv, int32_t Dk, int32_t Dv,
                                 gdn_dtype_t dtype, float scale,
                                 void *workspace, size_t workspace_bytes,

@@ -224,3 +224,40 @@ def decode_multi(q, k, v, alpha, beta, pool, src_slot, dst_slot, scale=1.0, want
         if dst[b] >= 0:
             out_pool[dst[b], h] = S
     return o, out_pool, steps
+
+
+def prefix_states(q, k, v, alpha, beta, cu_seqlens, block, initial_state=None, chains=None,
+                  threads=None):
+    """Block-aligned prefix states of packed sequences: for sequence n and
+    value head h, the state after each whole block of ``block`` tokens,
+    S_{block * (i + 1)} for i < floor(L_n / block), obtained by running the
+    recurrence one block after the other from the initial state.
+
+    q,k [total,Hk,Dk]; v [total,Hv,Dv]; alpha,beta [total,Hv];
+    initial_state [N,Hv,Dv,Dk] or None. Returns a list over sequences of
+    fp64 arrays [floor(L_n / block), Hv, Dv, Dk] (NaN for chains not listed
+    in ``chains``)."""
+    cu = [int(x) for x in np.asarray(cu_seqlens)]
+    N = len(cu) - 1
+    Hv, Dv = v.shape[1], v.shape[2]
+    Dk = q.shape[2]
+    out = [np.full(((cu[n + 1] - cu[n]) // block, Hv, Dv, Dk), np.nan) for n in range(N)]
+    if chains is None:
+        chains = [(n, h) for n in range(N) for h in range(Hv)]
+
+    def work(nh):
+        n, h = nh
+        S = None if initial_state is None else initial_state[n, h]
+        for i in range(out[n].shape[0]):
+            t0 = cu[n] + i * block
+            _, S = chain(q, k, v, alpha, beta, t0, t0 + block, h, S, want_o=False)
+            out[n][i, h] = S
+
+    nthreads = threads or default_threads()
+    if nthreads == 1:
+        for nh in chains:
+            work(nh)
+    else:
+        with ThreadPoolExecutor(nthreads) as ex:
+            list(ex.map(work, chains))
+    return out

@@ -57,16 +57,17 @@ def P(i):
     return A + i * 64 * MB  # disjoint, aligned regions
 
 
-def prefill(lib, q=P(0), k=P(1), v=P(2), a=P(3), b=P(4), s0=P(5), out=P(6), sf=P(7), B=1, T=64,
-            Hk=2, Hv=4, Dk=64, Dv=64, dtype=BF16, ws=None, wsb=0):
-    return lib.gdn_prefill_chunked(q, k, v, a, b, s0, out, sf, B, T, Hk, Hv, Dk, Dv, dtype, 1.0,
-                                   ws, wsb, None)
+def prefill(lib, q=P(0), k=P(1), v=P(2), a=P(3), b=P(4), s0=P(5), out=P(6), sf=P(7), pre=None,
+            every=0, B=1, T=64, Hk=2, Hv=4, Dk=64, Dv=64, dtype=BF16, ws=None, wsb=0):
+    return lib.gdn_prefill_chunked(q, k, v, a, b, s0, out, sf, pre, every, B, T, Hk, Hv, Dk, Dv,
+                                   dtype, 1.0, ws, wsb, None)
 
 
 def varlen(lib, q=P(0), k=P(1), v=P(2), a=P(3), b=P(4), cu=P(8), N=2, total=64, s0=P(5),
-           out=P(6), sf=P(7), Hk=2, Hv=4, Dk=64, Dv=64, dtype=BF16, ws=None, wsb=0):
-    return lib.gdn_varlen_prefill(q, k, v, a, b, cu, N, total, s0, out, sf, Hk, Hv, Dk, Dv, dtype,
-                                  1.0, ws, wsb, None)
+           out=P(6), sf=P(7), pre=None, every=0, Hk=2, Hv=4, Dk=64, Dv=64, dtype=BF16, ws=None,
+           wsb=0):
+    return lib.gdn_varlen_prefill(q, k, v, a, b, cu, N, total, s0, out, sf, pre, every, Hk, Hv, Dk,
+                                  Dv, dtype, 1.0, ws, wsb, None)
 
 
 def decode(lib, q=P(0), k=P(1), v=P(2), a=P(3), b=P(4), s=P(5), out=P(6), B=4, Hk=2, Hv=4,
@@ -95,6 +96,22 @@ def test_prefill_validation(lib):
     assert prefill(lib, ws=P(9) + 8, wsb=1 << 20) == MISAL
     assert prefill(lib, ws=P(6), wsb=1 << 20) == ALIAS    # workspace on top of out
     assert prefill(lib, ws=P(7) + 4096, wsb=1 << 20) == ALIAS  # inside the final state
+
+
+def test_prefix_states_validation(lib):
+    assert prefill(lib, pre=P(9), every=0) == SHAPE           # interval required
+    assert prefill(lib, pre=P(9), every=-2) == SHAPE
+    assert prefill(lib, pre=P(9) + 4, every=1) == MISAL
+    assert prefill(lib, pre=P(6), every=1) == ALIAS           # on top of out
+    assert prefill(lib, pre=P(7) + 1024, every=1) == ALIAS    # inside the final state
+    assert prefill(lib, pre=P(0), every=1) == ALIAS           # on top of q
+    assert prefill(lib, pre=P(9), every=1, ws=P(9) + 4096, wsb=1 << 20) == ALIAS  # workspace
+    # T < 64 m: no rows, nothing can overlap
+    assert prefill(lib, pre=P(6), every=2, q=None, k=None, v=None, a=None, b=None, out=None,
+                   sf=None, T=0) == OK
+    assert varlen(lib, pre=P(9), every=0) == SHAPE
+    assert varlen(lib, pre=P(8), every=1) == ALIAS             # on top of cu_seqlens
+    assert varlen(lib, pre=P(5) + 64, every=4) == ALIAS        # N rows always exist
 
 
 def test_varlen_validation(lib):

@@ -439,6 +439,104 @@ def test_varlen_matches_per_sequence_prefill(gdn):
         np.testing.assert_array_equal(S[n], Sp[0])
 
 
+# ------------------------------------------------- block-aligned prefix states
+SENTINEL = 7.25
+
+
+def _check_prefix(pre, ref, rows_of, dtype, label):
+    """pre: GPU prefix buffer (numpy); ref: oracle list per sequence; rows_of(n, i)
+    the row the header assigns to block i of sequence n. Rows no block maps
+    to must keep the sentinel."""
+    worst = 0.0
+    used = set()
+    for n, r in enumerate(ref):
+        for i in range(r.shape[0]):
+            row = rows_of(n, i)
+            used.add(row)
+            worst = max(worst, max_error(pre[row], r[i], (0,)))
+    print(f"[parity] {label}: {len(used)} prefix states, max error {worst:.3e} "
+          f"(tol {TOL[dtype]:.0e})", flush=True)
+    assert worst <= TOL[dtype], label
+    free = sorted(set(range(pre.shape[0])) - used)
+    assert np.all(pre[free] == SENTINEL), "rows no block maps to were written"
+
+
+PREFIX_DENSE = [
+    # path, nsplit, dtype, D, every  (kernel reached)
+    ("fused", "auto", "bf16", 128, 1),   # prefill_kernel
+    ("fused", "8", "bf16", 128, 3),
+    ("split", "1", "bf16", 128, 2),      # chain_kernel
+    ("split", "4", "bf16", 128, 1),      # chain_db_kernel
+    ("split", "2", "bf16", 64, 3),       # chain_db_kernel, D = 64
+    ("split", "2", "f32", 64, 1),        # chain_kernel, fp32
+    ("fused", "auto", "f32", 128, 2),
+]
+
+
+@pytest.mark.parametrize("path,nsplit,dtype,D,every", PREFIX_DENSE)
+def test_prefill_prefix_states(gdn, monkeypatch, path, nsplit, dtype, D, every):
+    monkeypatch.setenv("GDN_PREFILL_PATH", path)
+    if nsplit != "auto":
+        monkeypatch.setenv("GDN_PREFILL_NSPLIT", nsplit)
+    B, T, Hk, Hv = 2, 450, 2, 6
+    d = small_prefill(B, T, Hk, Hv, D, dtype, seed=110 + every, init_state=True)
+    L = 64 * every
+    q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
+    s0 = to_torch(d["S0"], DEV)
+    pre = torch.full((gdn.prefix_state_rows(B, T, every, False), Hv, D, D), SENTINEL,
+                     dtype=torch.float32, device=DEV)
+    out, sf = gdn.gdn_prefill_chunked(q, k, v, a, b, s0, prefix_states=pre,
+                                      prefix_interval=every)
+    out0, sf0 = gdn.gdn_prefill_chunked(q, k, v, a, b, s0)
+    torch.cuda.synchronize()
+    # emitting prefix states leaves the outputs and final states bit for bit
+    assert torch.equal(out, out0) and torch.equal(sf, sf0)
+    flat = {n: d[n].reshape((-1,) + d[n].shape[2:]) for n in ("q", "k", "v", "alpha", "beta")}
+    ref = oracle.prefix_states(flat["q"], flat["k"], flat["v"], flat["alpha"], flat["beta"],
+                               [0, T, 2 * T], L, d["S0"])
+    _check_prefix(from_torch(pre), ref, lambda n, i: n * (T // L) + i, dtype,
+                  f"prefix states {path} ns={nsplit} {dtype} D{D} L={L}")
+
+
+@pytest.mark.parametrize("path", ["fused", "split"])
+def test_varlen_prefix_states(gdn, monkeypatch, path):
+    monkeypatch.setenv("GDN_PREFILL_PATH", path)
+    lengths = [300, 64, 1, 640, 127, 128, 0, 257]
+    every = 2
+    L = 64 * every
+    d = generate_packed(2, 6, 128, "bf16", 120, lengths, init_state=True)
+    q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
+    cu_t = to_torch(d["cu_seqlens"], DEV)
+    s0 = to_torch(d["S0"], DEV)
+    total, N = int(d["cu_seqlens"][-1]), len(lengths)
+    pre = torch.full((gdn.prefix_state_rows(N, total, every, True), 6, 128, 128), SENTINEL,
+                     dtype=torch.float32, device=DEV)
+    out, sf = gdn.gdn_varlen_prefill(q, k, v, a, b, cu_t, s0, prefix_states=pre,
+                                     prefix_interval=every)
+    out0, sf0 = gdn.gdn_varlen_prefill(q, k, v, a, b, cu_t, s0)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out0) and torch.equal(sf, sf0)
+    cu = d["cu_seqlens"]
+    ref = oracle.prefix_states(d["q"], d["k"], d["v"], d["alpha"], d["beta"], cu, L, d["S0"])
+    _check_prefix(from_torch(pre), ref, lambda n, i: int(cu[n]) // L + n + i, "bf16",
+                  f"varlen prefix states ({path})")
+
+
+def test_layer_prefill_4k_prefix_states(gdn):
+    """The layer workload with a state every 1024 tokens (16 chunks)."""
+    w = WORKLOADS["layer_prefill_4k"]
+    d = generate(w)
+    q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
+    pre = torch.full((gdn.prefix_state_rows(1, w.T, 16, False), w.Hv, w.D, w.D), SENTINEL,
+                     dtype=torch.float32, device=DEV)
+    gdn.gdn_prefill_chunked(q, k, v, a, b, None, prefix_states=pre, prefix_interval=16)
+    torch.cuda.synchronize()
+    flat = {n: d[n].reshape((-1,) + d[n].shape[2:]) for n in ("q", "k", "v", "alpha", "beta")}
+    ref = oracle.prefix_states(flat["q"], flat["k"], flat["v"], flat["alpha"], flat["beta"],
+                               [0, w.T], 1024)
+    _check_prefix(from_torch(pre), ref, lambda n, i: i, "bf16", f"{w.name} prefix states")
+
+
 # ----------------------------------------------------------------- full-size, sampled
 def _chains_check(d, out_t, sf_t, chains, cu, label):
     worst_o = worst_s = 0.0

@@ -422,3 +422,42 @@ def test_multi_slot_out_of_range_is_nan_and_untouched():
     assert np.isfinite(o[0]).all()
     np.testing.assert_array_equal(pool2[2], _f64(pool[2]))
     np.testing.assert_array_equal(pool2[0], _f64(pool[0]))
+
+
+# ------------------------------------------------- block-aligned prefix states
+def test_prefix_states_decay_only():
+    """beta = 0: the state after block i is (prod of alpha over its first
+    block * (i + 1) tokens) S0, per sequence of a ragged packed batch."""
+    rng = np.random.default_rng(51)
+    lens = [7, 20, 33]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q, k, v, alpha, _ = _rand_inputs(rng, int(cu[-1]), 2, 4, 8, 8)
+    alpha = rng.uniform(0.8, 1.0, alpha.shape).astype(np.float32)
+    beta = np.zeros_like(alpha)
+    S0 = rng.standard_normal((3, 4, 8, 8)).astype(np.float32)
+    blk = 6
+    pre = oracle.prefix_states(q, k, v, alpha, beta, cu, blk, S0)
+    for n, L in enumerate(lens):
+        assert pre[n].shape == (L // blk, 4, 8, 8)
+        for i in range(L // blk):
+            cp = np.prod(_f64(alpha[cu[n]:cu[n] + blk * (i + 1)]), axis=0)
+            for h in range(4):
+                np.testing.assert_allclose(pre[n][i, h], cp[h] * _f64(S0[n, h]), rtol=1e-12,
+                                           atol=1e-300)
+
+
+def test_prefix_states_overwrite_at_block_ends():
+    """beta = 1 and exactly unit keys: each prefix state satisfies S k = v for
+    the last token of its block."""
+    rng = np.random.default_rng(52)
+    T, Hk, Hv, d, blk = 40, 2, 4, 64, 8
+    q, _, v, alpha, _ = _rand_inputs(rng, T, Hk, Hv, d, d)
+    k = _exact_unit_keys(rng, T, Hk, d, 16)
+    beta = np.ones((T, Hv), np.float32)
+    pre = oracle.prefix_states(q, k, v, alpha, beta, [0, T], blk)[0]
+    assert pre.shape[0] == T // blk
+    for i in range(T // blk):
+        t = blk * (i + 1) - 1
+        for h in range(Hv):
+            np.testing.assert_allclose(pre[i, h] @ _f64(k[t, h // (Hv // Hk)]), _f64(v[t, h]),
+                                       rtol=0, atol=1e-12)
