@@ -363,8 +363,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p, int n
             for (int a = 0; a < NKT; ++a)
 #pragma unroll
                 for (int b = 0; b < NB; ++b)
-                    *reinterpret_cast<f32x4 *>(ps + (int64_t)(dv0 + wdv + 16 * b + c16) * D +
-                                               16 * a + 4 * g4) = st[a][b];
+                    __builtin_nontemporal_store(
+                        st[a][b], reinterpret_cast<f32x4 *>(
+                                      ps + (int64_t)(dv0 + wdv + 16 * b + c16) * D + 16 * a + 4 * g4));
         }
     }
 
@@ -721,8 +722,10 @@ __global__ __launch_bounds__(256) void chain_kernel(PrefillParams p, const unsig
                 for (int a = 0; a < NKT; ++a)
 #pragma unroll
                     for (int b = 0; b < NB; ++b)
-                        *reinterpret_cast<f32x4 *>(ps + (int64_t)(dv0 + wdv + 16 * b + c16) * D +
-                                                   16 * a + 4 * g4) = st[a][b];
+                        __builtin_nontemporal_store(
+                            st[a][b], reinterpret_cast<f32x4 *>(ps + (int64_t)(dv0 + wdv + 16 * b +
+                                                                               c16) * D +
+                                                                16 * a + 4 * g4));
             }
         }
     }
@@ -869,8 +872,9 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
                     float *ps = p.prefix + (prow * p.Hv + h) * D * D;
 #pragma unroll
                     for (int a = 0; a < NKT; ++a)
-                        *reinterpret_cast<f32x4 *>(ps + (int64_t)(dv0 + wdv + c16) * D + 16 * a +
-                                                   4 * g4) = st[a][0];
+                        __builtin_nontemporal_store(
+                            st[a][0], reinterpret_cast<f32x4 *>(ps + (int64_t)(dv0 + wdv + c16) * D +
+                                                                16 * a + 4 * g4));
                 }
                 __syncthreads();
             }
