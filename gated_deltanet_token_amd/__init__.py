@@ -11,6 +11,8 @@ The recurrence, per sequence and value head h (q/k head h // (Hv // Hk)):
     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
     o_t = scale * S_t q_t
 States are fp32 [.., Hv, Dv, Dk] (S in R^{Dv x Dk}, row-major).
+`flags` (GDN_QK_L2NORM | GDN_GATE_LOGITS) moves the input preparation into
+the kernels: raw q/k rows are L2-normalised, alpha/beta are given as logits.
 """
 from __future__ import annotations
 
@@ -23,6 +25,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
 
 GDN_F32, GDN_BF16 = 0, 1
+# input preparation inside the kernels (the `flags` argument)
+GDN_QK_L2NORM, GDN_GATE_LOGITS = 1, 2
 _STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL_POINTER", 2: "GDN_ERR_BAD_SHAPE",
            3: "GDN_ERR_UNSUPPORTED", 4: "GDN_ERR_MISALIGNED", 5: "GDN_ERR_ALIAS",
            6: "GDN_ERR_HIP"}
@@ -48,18 +52,19 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                           "`python -m gated_deltanet_token_amd.build`")
     lib = ctypes.CDLL(path)
     vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    u32 = ctypes.c_uint32
     sz = ctypes.c_size_t
     lib.gdn_prefill_chunked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i64, i32,
-                                        i32, i32, i32, ctypes.c_int, f32, vp, sz, vp]
+                                        i32, i32, i32, ctypes.c_int, f32, u32, vp, sz, vp]
     lib.gdn_prefill_chunked.restype = ctypes.c_int
     lib.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
-                                    ctypes.c_int, f32, vp]
+                                    ctypes.c_int, f32, u32, vp]
     lib.gdn_decode_step.restype = ctypes.c_int
     lib.gdn_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32,
-                                     i32, i32, i32, ctypes.c_int, f32, vp]
+                                     i32, i32, i32, ctypes.c_int, f32, u32, vp]
     lib.gdn_decode_multi.restype = ctypes.c_int
     lib.gdn_varlen_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, vp, i32,
-                                       i32, i32, i32, i32, ctypes.c_int, f32, vp, sz, vp]
+                                       i32, i32, i32, i32, ctypes.c_int, f32, u32, vp, sz, vp]
     lib.gdn_varlen_prefill.restype = ctypes.c_int
     lib.gdn_prefill_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, ctypes.c_int, i32]
     lib.gdn_prefill_workspace_size.restype = sz
@@ -149,7 +154,7 @@ def _prefix(prefix_states, prefix_interval, rows, Hv, Dv, Dk, dev):
 
 def gdn_prefill_chunked(q, k, v, alpha, beta, initial_state=None, *, out=None,
                         final_state=None, scale: float = 1.0, want_final_state: bool = True,
-                        prefix_states=None, prefix_interval: int = 0,
+                        prefix_states=None, prefix_interval: int = 0, flags: int = 0,
                         workspace="auto", stream=None):
     """Chunked prefill. q,k [B,T,Hk,D]; v [B,T,Hv,D]; alpha,beta [B,T,Hv] fp32;
     initial_state [B,Hv,D,D] fp32 or None. Returns (out, final_state).
@@ -183,13 +188,13 @@ def gdn_prefill_chunked(q, k, v, alpha, beta, initial_state=None, *, out=None,
     _check(lib.gdn_prefill_chunked(
         _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state), _ptr(out),
         _ptr(final_state), _ptr(pre), pint, B, T, Hk, Hv, Dk, Dv, _dtype_code(q), float(scale),
-        wp, wb, st.cuda_stream))
+        int(flags), wp, wb, st.cuda_stream))
     return out, final_state
 
 
 def gdn_varlen_prefill(q, k, v, alpha, beta, cu_seqlens, initial_state=None, *, out=None,
                        final_state=None, scale: float = 1.0, want_final_state: bool = True,
-                       prefix_states=None, prefix_interval: int = 0,
+                       prefix_states=None, prefix_interval: int = 0, flags: int = 0,
                        workspace="auto", stream=None):
     """Packed prefill. q,k [total,Hk,D]; v [total,Hv,D]; alpha,beta [total,Hv];
     cu_seqlens int32 [N+1] on the device. Returns (out, final_state [N,Hv,D,D]).
@@ -223,11 +228,12 @@ def gdn_varlen_prefill(q, k, v, alpha, beta, cu_seqlens, initial_state=None, *, 
     _check(lib.gdn_varlen_prefill(
         _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(cu_seqlens), N, total,
         _ptr(initial_state), _ptr(out), _ptr(final_state), _ptr(pre), pint, Hk, Hv, Dk, Dv,
-        _dtype_code(q), float(scale), wp, wb, st.cuda_stream))
+        _dtype_code(q), float(scale), int(flags), wp, wb, st.cuda_stream))
     return out, final_state
 
 
-def gdn_decode_step(q, k, v, alpha, beta, state, *, out=None, scale: float = 1.0, stream=None):
+def gdn_decode_step(q, k, v, alpha, beta, state, *, out=None, scale: float = 1.0, flags: int = 0,
+                    stream=None):
     """One token per sequence; `state` [B,Hv,D,D] fp32 is updated in place.
     q,k [B,Hk,D]; v [B,Hv,D]; alpha,beta [B,Hv]. Returns out [B,Hv,D]."""
     lib = load_library()
@@ -245,13 +251,13 @@ def gdn_decode_step(q, k, v, alpha, beta, state, *, out=None, scale: float = 1.0
     _need(out, "out", q.dtype, (B, Hv, Dv), dev)
     _check(lib.gdn_decode_step(
         _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state), _ptr(out), B, Hk, Hv,
-        Dk, Dv, _dtype_code(q), float(scale), _stream(dev, stream).cuda_stream))
+        Dk, Dv, _dtype_code(q), float(scale), int(flags), _stream(dev, stream).cuda_stream))
     return out
 
 
 def gdn_decode_multi(q, k, v, alpha, beta, state_pool, src_slot, dst_slot, *, out=None,
                      step_states=None, want_step_states: bool = False, scale: float = 1.0,
-                     stream=None):
+                     flags: int = 0, stream=None):
     """K tokens per sequence against a pool of state slots.
     q,k [B,K,Hk,D]; v [B,K,Hv,D]; alpha,beta [B,K,Hv] fp32; state_pool
     [num_slots,Hv,D,D] fp32; src_slot, dst_slot int32 [B] on the device
@@ -282,7 +288,7 @@ def gdn_decode_multi(q, k, v, alpha, beta, state_pool, src_slot, dst_slot, *, ou
     _check(lib.gdn_decode_multi(
         _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_pool),
         state_pool.shape[0], _ptr(src_slot), _ptr(dst_slot), _ptr(out), _ptr(step_states), B, K,
-        Hk, Hv, Dk, Dv, _dtype_code(q), float(scale), _stream(dev, stream).cuda_stream))
+        Hk, Hv, Dk, Dv, _dtype_code(q), float(scale), int(flags), _stream(dev, stream).cuda_stream))
     return out, step_states
 
 

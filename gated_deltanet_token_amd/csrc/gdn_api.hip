@@ -14,6 +14,10 @@ namespace {
 
 thread_local char g_detail[256];
 
+constexpr uint32_t kKnownFlags = GDN_QK_L2NORM | GDN_GATE_LOGITS;
+static_assert(GDN_QK_L2NORM == gdn::kQkL2Norm && GDN_GATE_LOGITS == gdn::kGateLogits,
+              "flag values of the ABI and the kernels");
+
 struct Range {
     uintptr_t lo, hi;  // [lo, hi); empty when lo == hi
 };
@@ -132,7 +136,7 @@ const char *gdn_status_string(gdn_status_t s) {
     return "unknown status";
 }
 
-int32_t gdn_version(void) { return 400; }
+int32_t gdn_version(void) { return 500; }
 
 size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t tokens, int32_t Hk, int32_t Hv,
                                   int32_t Dk, int32_t Dv, gdn_dtype_t dtype, int32_t packed) {
@@ -153,10 +157,11 @@ gdn_status_t gdn_prefill_chunked(const void *q, const void *k, const void *v, co
                                  const float *beta, const float *initial_state, void *out,
                                  float *final_state, float *prefix_states, int32_t prefix_interval,
                                  int32_t B, int64_t T, int32_t Hk, int32_t Hv, int32_t Dk,
-                                 int32_t Dv, gdn_dtype_t dtype, float scale, void *workspace,
-                                 size_t workspace_bytes, hipStream_t stream) {
+                                 int32_t Dv, gdn_dtype_t dtype, float scale, uint32_t flags,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream) {
     gdn_status_t st = check_heads(Hk, Hv, Dk, Dv);
     if (st != GDN_OK) return st;
+    if (flags & ~kKnownFlags) return GDN_ERR_UNSUPPORTED;
     if (B < 1 || T < 0) return GDN_ERR_BAD_SHAPE;
     if (prefix_states && prefix_interval < 1) return GDN_ERR_BAD_SHAPE;
     int64_t tokens = B;
@@ -173,7 +178,7 @@ gdn_status_t gdn_prefill_chunked(const void *q, const void *k, const void *v, co
     gdn::PrefillParams p{q,  k,     v,     alpha,         beta,
                          initial_state, out, final_state, nullptr, T,
                          B,  Hk,    Hv,    scale,         prefix_rows ? prefix_states : nullptr,
-                         prefix_interval};
+                         prefix_interval, flags};
     const int64_t slots = gdn::prefill_ws_slots(B, tokens, T, false);
     const hipError_t e = gdn::launch_prefill(p, dtype == GDN_BF16 ? 1 : 0, Dk, cus, workspace,
                                              workspace_bytes, slots, stream);
@@ -186,10 +191,11 @@ gdn_status_t gdn_varlen_prefill(const void *q, const void *k, const void *v, con
                                 int64_t total_T, const float *initial_state, void *out,
                                 float *final_state, float *prefix_states, int32_t prefix_interval,
                                 int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv, gdn_dtype_t dtype,
-                                float scale, void *workspace, size_t workspace_bytes,
-                                hipStream_t stream) {
+                                float scale, uint32_t flags, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
     gdn_status_t st = check_heads(Hk, Hv, Dk, Dv);
     if (st != GDN_OK) return st;
+    if (flags & ~kKnownFlags) return GDN_ERR_UNSUPPORTED;
     if (N < 1 || total_T < 0 || total_T > 0x7FFFFFFF) return GDN_ERR_BAD_SHAPE;
     if (!cu_seqlens) return GDN_ERR_NULL_POINTER;
     if (prefix_states && prefix_interval < 1) return GDN_ERR_BAD_SHAPE;
@@ -205,7 +211,7 @@ gdn_status_t gdn_varlen_prefill(const void *q, const void *k, const void *v, con
     if ((st = device_cus(&cus)) != GDN_OK) return st;
     gdn::PrefillParams p{q,          k,  v,  alpha, beta, initial_state, out, final_state,
                          cu_seqlens, 0,  N,  Hk,    Hv,   scale,         prefix_states,
-                         prefix_interval};
+                         prefix_interval, flags};
     const int64_t slots = gdn::prefill_ws_slots(N, total_T, 0, true);
     const hipError_t e = gdn::launch_prefill(p, dtype == GDN_BF16 ? 1 : 0, Dk, cus, workspace,
                                              workspace_bytes, slots, stream);
@@ -216,9 +222,10 @@ gdn_status_t gdn_varlen_prefill(const void *q, const void *k, const void *v, con
 gdn_status_t gdn_decode_step(const void *q, const void *k, const void *v, const float *alpha,
                              const float *beta, float *state, void *out, int32_t B, int32_t Hk,
                              int32_t Hv, int32_t Dk, int32_t Dv, gdn_dtype_t dtype, float scale,
-                             hipStream_t stream) {
+                             uint32_t flags, hipStream_t stream) {
     gdn_status_t st = check_heads(Hk, Hv, Dk, Dv);
     if (st != GDN_OK) return st;
+    if (flags & ~kKnownFlags) return GDN_ERR_UNSUPPORTED;
     if (B < 1) return GDN_ERR_BAD_SHAPE;
     if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
     if (!q || !k || !v || !alpha || !beta || !state || !out) return GDN_ERR_NULL_POINTER;
@@ -243,7 +250,7 @@ gdn_status_t gdn_decode_step(const void *q, const void *k, const void *v, const 
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    gdn::DecodeParams p{q, k, v, alpha, beta, state, out, B, Hk, Hv, scale};
+    gdn::DecodeParams p{q, k, v, alpha, beta, state, out, B, Hk, Hv, scale, flags};
     e = gdn::launch_decode(p, dtype == GDN_BF16 ? 1 : 0, Dk, stream);
     if (e != hipSuccess) return hip_fail(e, "gdn_decode_step launch");
     return GDN_OK;
@@ -254,9 +261,10 @@ gdn_status_t gdn_decode_multi(const void *q, const void *k, const void *v, const
                               const int32_t *src_slot, const int32_t *dst_slot, void *out,
                               float *step_states, int32_t B, int32_t K, int32_t Hk, int32_t Hv,
                               int32_t Dk, int32_t Dv, gdn_dtype_t dtype, float scale,
-                              hipStream_t stream) {
+                              uint32_t flags, hipStream_t stream) {
     gdn_status_t st = check_heads(Hk, Hv, Dk, Dv);
     if (st != GDN_OK) return st;
+    if (flags & ~kKnownFlags) return GDN_ERR_UNSUPPORTED;
     if (B < 1 || K < 0 || num_slots < 1) return GDN_ERR_BAD_SHAPE;
     if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
     if (!state_pool || !src_slot || !dst_slot) return GDN_ERR_NULL_POINTER;
@@ -291,7 +299,7 @@ gdn_status_t gdn_decode_multi(const void *q, const void *k, const void *v, const
     if (overlap(rp, ro) || overlap(rp, rst) || overlap(ro, rst)) return GDN_ERR_ALIAS;
     gdn::DecodeMultiParams p{q,        k,        v,   alpha,       beta, state_pool,
                              src_slot, dst_slot, out, step_states, B,    K,
-                             Hk,       Hv,       num_slots, scale};
+                             Hk,       Hv,       num_slots, scale, flags};
     hipError_t e = gdn::launch_decode_multi(p, dtype == GDN_BF16 ? 1 : 0, Dk, stream);
     if (e != hipSuccess) return hip_fail(e, "gdn_decode_multi launch");
     return GDN_OK;

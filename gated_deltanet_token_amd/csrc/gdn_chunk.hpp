@@ -18,6 +18,7 @@
 #include <float.h>
 
 #include "gdn_device.hpp"
+#include "gdn_launch.hpp"
 
 namespace gdn {
 
@@ -127,14 +128,20 @@ __device__ __forceinline__ void gram_pair(const DT *sK, const DT *sQ, int ti, in
 // straight to its fragments at pfr (kTriFrags x 64 lanes x 16 bytes): this
 // lane's four values are one half of its fragment (rb, k2) = (ti, tj / 2);
 // the pairs on even diagonal blocks also zero the half above the diagonal.
-template <typename DT, int PA, int PT, bool PFRAG = false>
+template <typename DT, int PA, int PT, bool PFRAG = false, bool NORMS = false>
 __device__ __forceinline__ void mask_pair(const f32x4 &gk, const f32x4 &gq, int ti, int tj, int g4,
-                                          int c16, const float *sG, const float *sBeta, float *sA,
+                                          int c16, const float *sGrA, const float *sGrP,
+                                          const float *sGc, const float *sBeta, float *sA,
                                           DT *sP, unsigned char *pfr = nullptr) {
+    // A_ts = beta_t e^{grA_t - gc_s} k_t.k_s, P_ts = e^{grP_t - gc_s} q_t.k_s: with
+    // q, k used as given all three exponent vectors are the log decay g; with
+    // raw rows (NORMS) they carry the log row norms (fold_qk_norms), and P's
+    // row factor e^{grP_t - grA_t} differs from 1.
     const int t = 16 * ti + c16;
-    const float gt = sG[t];
+    const float gt = sGrA[t];
+    const float rt = NORMS ? __expf(sGrP[t] - gt) : 1.f;
     const float bt = sBeta[t];
-    const f32x4 gs = *reinterpret_cast<const f32x4 *>(sG + 16 * tj + 4 * g4);
+    const f32x4 gs = *reinterpret_cast<const f32x4 *>(sGc + 16 * tj + 4 * g4);
     f32x4 av;
     float pv[4];
 #pragma unroll
@@ -143,7 +150,7 @@ __device__ __forceinline__ void mask_pair(const f32x4 &gk, const f32x4 &gq, int 
         // for s > t (diagonal tiles only) the product is discarded below
         const float dec = __expf(gt - gs[r]);
         const float a = bt * dec * gk[r];
-        const float pp = dec * gq[r];
+        const float pp = dec * gq[r] * rt;
         if (ti == tj) {
             av[r] = s < t ? a : 0.f;
             pv[r] = s <= t ? pp : 0.f;
@@ -168,6 +175,50 @@ __device__ __forceinline__ void mask_pair(const f32x4 &gk, const f32x4 &gq, int 
         *reinterpret_cast<bf16x4 *>(sP + t * PT + 16 * tj + 4 * g4) = pb;
     } else {
         *reinterpret_cast<f32x4 *>(sP + t * PT + 16 * tj + 4 * g4) = f32x4{pv[0], pv[1], pv[2], pv[3]};
+    }
+}
+
+// Raw q and k rows (L2-normalised inside the kernel): the norms of the
+// chunk's 64 K rows and 64 Q rows, folded into the decay vectors instead of
+// rescaling the staged rows. With ik_t = 1 / sqrt(|k_t|^2 + eps) and iq_t
+// likewise, and g, gamma = e^g, dec as the scan left them:
+//   gam_t = gamma_t ik_t, dec_t *= ik_t, gamq_t = gamma_t iq_t,
+//   grA_t = g_t + ln ik_t, grP_t = g_t + ln iq_t, gc_t = g_t - ln ik_t.
+// One thread per row (K rows first: a wave never holds both kinds).
+template <typename DT, int D, int PK, int NTH>
+__device__ __forceinline__ void fold_qk_norms(const DT *sK, const DT *sQ, const float *sG,
+                                              float *sGam, float *sDec, float *sGamQ,
+                                              float *sGrA, float *sGrP, float *sGc, int tid) {
+    constexpr int EPP = 16 / (int)sizeof(DT);
+    for (int r = tid; r < 2 * kC; r += NTH) {
+        const int t = r & (kC - 1);
+        const bool isq = r >= kC;
+        const DT *row = (isq ? sQ : sK) + t * PK;
+        float ss = 0.f;
+#pragma unroll
+        for (int c = 0; c < D; c += EPP) {
+            if constexpr (sizeof(DT) == 2) {
+                const bf16x8 x = *reinterpret_cast<const bf16x8 *>(row + c);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss += (float)x[e] * (float)x[e];
+            } else {
+                const f32x4 x = *reinterpret_cast<const f32x4 *>(row + c);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ss += x[e] * x[e];
+            }
+        }
+        const float inv = inv_norm(ss, kL2Eps);
+        const float li = logf(inv);
+        const float g = sG[t];
+        if (isq) {
+            sGrP[t] = g + li;
+            sGamQ[t] = __expf(g) * inv;
+        } else {
+            sGrA[t] = g + li;
+            sGc[t] = g - li;
+            sGam[t] = __expf(g) * inv;
+            sDec[t] *= inv;
+        }
     }
 }
 
@@ -362,12 +413,17 @@ __device__ __forceinline__ void solve_unit_lower(const float *sA, float *sE, DT 
 }
 
 // LDS views the state chain reads for one chunk.
+// Decay vectors [64]: gam (K side: R = beta (V - diag(gam) K S^T)), dec (the
+// state update's diag(dec) K), beta, gamq (Q side: O = diag(gamq) Q S^T + ...).
+// With q and k used as given, gam = gamq = gamma and dec = e^{g_63 - g}; when
+// the kernels L2-normalise raw rows, the norms are folded in: gam = gamma/|k|,
+// dec = e^{g_63 - g}/|k|, gamq = gamma/|q| (so gamma_63 = gam[63] / dec[63]).
 template <typename DT> struct ChainSmem {
     const DT *K, *Q;    // row-major [64][PK]
     const DT *KT;       // bf16: K^T [D][PT]; fp32: unused (K read by column)
     const DT *V;        // bf16: V^T [DVS][PT] (slice-local columns); fp32: V [64][PV]
     const DT *T, *P;    // row-major [64][PT]
-    const float *gam, *dec, *beta;  // [64]
+    const float *gam, *dec, *beta, *gamq;  // [64]
 };
 
 // State-only half of the chain for one wave: R_raw = K S^T (C[t][dv]) and
@@ -503,7 +559,7 @@ __device__ __forceinline__ void chain_finish(const ChainSmem<DT> &m, f32x4 (&st)
         for (int b = 0; b < NB; ++b) c_to_frag(u[2 * k2][b], u[2 * k2 + 1][b], fu[k2][b]);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-        const float gam = m.gam[16 * mt + c16];
+        const float gam = m.gamq[16 * mt + c16];
 #pragma unroll
         for (int b = 0; b < NB; ++b) oT[mt][b] *= gam;
     }
@@ -552,7 +608,7 @@ __device__ __forceinline__ void chain_finish(const ChainSmem<DT> &m, f32x4 (&st)
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
         for (int b = 0; b < NB; ++b) c_to_frag(u[2 * k2][b], u[2 * k2 + 1][b], fu[k2][b]);
-    const float gC = m.gam[kC - 1];
+    const float gC = m.gam[kC - 1] * __builtin_amdgcn_rcpf(m.dec[kC - 1]);  // dec[63] = 1 unless q, k are raw
 #pragma unroll
     for (int a0 = 0; a0 < NKT; a0 += 4) {
         F fkt[4][2];
@@ -667,7 +723,7 @@ __device__ __forceinline__ void ld_kt_frag_s(const __bf16 *K, int a, int k2, int
 struct DbSmem {
     const __bf16 *K, *Q, *V;
     const bf16x8 *T, *P;
-    const float *gam, *dec, *beta;
+    const float *gam, *dec, *beta, *gamq;  // as in ChainSmem
 };
 
 // LDS handoff from a chain wave to its output wave: S^T fragments and U
@@ -755,7 +811,7 @@ __device__ __forceinline__ void chain_core_db(const DbSmem &m, f32x4 (&st)[D / 1
             for (int b = 0; b < NB; ++b) racc[mt][b] = mma(fk[kk][mt], sf[kk][b], racc[mt][b]);
     bf16x4 v4[4][NB];
     f32x4 bet[4], gam[4], dec[4];
-    const float gC = m.gam[kC - 1];
+    const float gC = m.gam[kC - 1] * __builtin_amdgcn_rcpf(m.dec[kC - 1]);  // dec[63] = 1 unless q, k are raw
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
         const int tb = 16 * mt + 4 * g4;
@@ -875,7 +931,7 @@ __device__ __forceinline__ void out_step(const DbSmem &m, Handoff<D, NB> ho, int
     for (int i = 0; i < kTriFrags; ++i) fp[i] = m.P[i * 64 + lane];
     float gamr[4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) gamr[mt] = m.gam[16 * mt + c16];
+    for (int mt = 0; mt < 4; ++mt) gamr[mt] = m.gamq[16 * mt + c16];
     wait_flag(flag, 2 * c + 1);
     F sf[KS][NB];
 #pragma unroll

@@ -85,8 +85,31 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     float vrow[STEPS];
 #pragma unroll
     for (int st = 0; st < STEPS; ++st) vrow[st] = to_f32(vp[row0 + 4 * st]);
-    const float alpha = p.alpha[bh];
-    const float beta = p.beta[bh];
+    float alpha = p.alpha[bh];
+    float beta = p.beta[bh];
+    if (p.flags & kGateLogits) {
+        alpha = expf(neg_softplus(alpha));
+        beta = sigmoid_f(beta);
+    }
+    if (p.flags & kQkL2Norm) {
+        // the 16 lanes of a row hold all D elements of k and q
+        float k2 = 0.f, q2 = 0.f;
+#pragma unroll
+        for (int c = 0; c < V4; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                k2 += kk[c][e] * kk[c][e];
+                q2 += qq[c][e] * qq[c][e];
+            }
+        const float ik = inv_norm(row16_sum(k2), kL2Eps), iq = inv_norm(row16_sum(q2), kL2Eps);
+#pragma unroll
+        for (int c = 0; c < V4; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kk[c][e] *= ik;
+                qq[c][e] *= iq;
+            }
+    }
 
     float kq = 0.f;
 #pragma unroll
@@ -200,7 +223,7 @@ __device__ __forceinline__ void stage_load(StageRegs<DT, D> &r, const DecodeMult
 
 template <typename DT, int D>
 __device__ __forceinline__ void stage_store(MultiSmem<DT, D> &sm, const StageRegs<DT, D> &r,
-                                            int n) {
+                                            int n, uint32_t flags) {
     using V = typename Vec4Of<DT>::type;
     using R = StageRegs<DT, D>;
     const int tid = threadIdx.x;
@@ -215,7 +238,11 @@ __device__ __forceinline__ void stage_store(MultiSmem<DT, D> &sm, const StageReg
             for (int e = 0; e < 4; ++e) sm.v[t][MultiShape<DT, D>::vpos(4 * c4 + e)] = r.v[i][e];
         }
     }
-    if (tid < 2 * n) sm.ab[tid >> 1][tid & 1] = r.ab;
+    if (tid < 2 * n) {
+        float g = r.ab;
+        if (flags & kGateLogits) g = (tid & 1) ? sigmoid_f(g) : expf(neg_softplus(g));
+        sm.ab[tid >> 1][tid & 1] = g;
+    }
 }
 
 template <typename DT, int D>
@@ -297,12 +324,11 @@ __global__ __launch_bounds__(256, sizeof(DT) == 2 ? 4 : 3) void decode_multi_ker
             __syncthreads();  // every wave is done with the previous stage
             stage_load<DT, D>(sr, p, tok0 + t0, g, h, n);
         }
-        stage_store<DT, D>(sm, sr, n);
+        stage_store<DT, D>(sm, sr, n, p.flags);
         __syncthreads();
         for (int tl = 0; tl < n; ++tl) {
             const int t = t0 + tl;
             float kk[V4][4], qq[V4][4];
-            float kq = 0.f;
 #pragma unroll
             for (int c = 0; c < V4; ++c) {
                 const V kv = *reinterpret_cast<const V *>(&sm.k[tl][64 * c + 4 * j]);
@@ -311,9 +337,32 @@ __global__ __launch_bounds__(256, sizeof(DT) == 2 ? 4 : 3) void decode_multi_ker
                 for (int e = 0; e < 4; ++e) {
                     kk[c][e] = to_f32(kv[e]);
                     qq[c][e] = to_f32(qv[e]);
-                    kq += kk[c][e] * qq[c][e];
                 }
             }
+            if (p.flags & kQkL2Norm) {
+                float k2 = 0.f, q2 = 0.f;
+#pragma unroll
+                for (int c = 0; c < V4; ++c)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        k2 += kk[c][e] * kk[c][e];
+                        q2 += qq[c][e] * qq[c][e];
+                    }
+                const float ik = inv_norm(row16_sum(k2), kL2Eps);
+                const float iq = inv_norm(row16_sum(q2), kL2Eps);
+#pragma unroll
+                for (int c = 0; c < V4; ++c)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        kk[c][e] *= ik;
+                        qq[c][e] *= iq;
+                    }
+            }
+            float kq = 0.f;
+#pragma unroll
+            for (int c = 0; c < V4; ++c)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) kq += kk[c][e] * qq[c][e];
             DT vr[STEPS];
 #pragma unroll
             for (int st = 0; st < STEPS; ++st) vr[st] = sm.v[tl][(wave * 4 + rsub) * STEPS + st];

@@ -139,6 +139,16 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
+// Gates from logits: log(alpha) = -softplus(a) (stable for either sign of
+// a), beta = sigmoid(b).
+__device__ __forceinline__ float neg_softplus(float a) {
+    return -(fmaxf(a, 0.f) + log1pf(expf(-fabsf(a))));
+}
+__device__ __forceinline__ float sigmoid_f(float b) { return 1.f / (1.f + expf(-b)); }
+
+// 1 / sqrt(x + eps) with an IEEE square root and division (x: a sum of squares).
+__device__ __forceinline__ float inv_norm(float x, float eps) { return 1.f / sqrtf(x + eps); }
+
 // Conversions between the storage type and fp32.
 __device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(float x) { return x; }

@@ -18,7 +18,12 @@ struct PrefillParams {
     float scale;
     float *prefix;         // block-aligned prefix states, or nullptr
     int32_t prefix_every;  // block length in chunks (>= 1 when prefix is set)
+    uint32_t flags;        // input preparation (kQkL2Norm | kGateLogits)
 };
+
+// Input preparation flags (the ABI's GDN_QK_L2NORM, GDN_GATE_LOGITS).
+constexpr uint32_t kQkL2Norm = 1, kGateLogits = 2;
+constexpr float kL2Eps = 1e-6f;
 
 struct DecodeParams {
     const void *q, *k, *v;
@@ -27,6 +32,7 @@ struct DecodeParams {
     void *out;
     int32_t B, Hk, Hv;
     float scale;
+    uint32_t flags;
 };
 
 // Several tokens per sequence; states live in a pool of slots.
@@ -39,6 +45,7 @@ struct DecodeMultiParams {
     float *steps;  // per-token states, or nullptr
     int32_t B, K, Hk, Hv, num_slots;
     float scale;
+    uint32_t flags;
 };
 
 // dtype: 0 = fp32, 1 = bf16. D: 64 or 128. Returns a hipError_t. With a

@@ -215,15 +215,18 @@ template <typename DT, int D, int NW, int DVW> struct FusedCfg {
     static constexpr int OFF_P = OFF_T + SZ_T;
     static constexpr int OFF_A = OFF_P + SZ_T;
     static constexpr int OFF_E = OFF_A + SZ_A;
-    static constexpr int OFF_VEC = OFF_E + SZ_A;  // g, gamma, dec, beta
-    static constexpr int LDS = OFF_VEC + 4 * kC * 4;
+    // g, gam, dec, beta, gamq, grA, grP, gc (the last four with raw q, k)
+    static constexpr int OFF_VEC = OFF_E + SZ_A;
+    static constexpr int LDS = OFF_VEC + 8 * kC * 4;
     static_assert(DVW % 16 == 0 && D % 32 == 0, "tile shapes");
     static_assert(LDS <= 160 * 1024, "LDS budget of a gfx950 CU");
 };
 
-// PREFIX: also write the block-aligned prefix states (a separate
-// instantiation, so that the kernel without them carries no trace of it).
-template <typename DT, int D, int NW, int DVW, bool PREFIX>
+// PREFIX: also write the block-aligned prefix states; RAWQK: q and k rows
+// are raw and get L2-normalised here (their norms folded into the decay
+// vectors). Each is a separate instantiation, so that the kernel without
+// them carries no trace of either.
+template <typename DT, int D, int NW, int DVW, bool PREFIX, bool RAWQK>
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p, int nsplit,
                                                           int remap_xcd) {
     using Cf = FusedCfg<DT, D, NW, DVW>;
@@ -244,6 +247,12 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p, int n
     float *sGam = sG + kC;
     float *sDec = sG + 2 * kC;
     float *sBeta = sG + 3 * kC;
+    float *sGamQ = sG + 4 * kC;
+    float *sGrA = sG + 5 * kC;
+    float *sGrP = sG + 6 * kC;
+    float *sGc = sG + 7 * kC;
+    constexpr bool raw_qk = RAWQK;
+    const bool logits = p.flags & kGateLogits;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -315,22 +324,29 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p, int n
         sg.store(sK, sQ, sKT, sV, lenc, tid);
         if (wave == 0) {
             const bool ok = lane < lenc;
-            const float x = wave_inclusive_scan(__logf(fmaxf(ok ? rAl : 1.f, FLT_MIN)));
+            const float la = logits ? neg_softplus(rAl) : __logf(fmaxf(rAl, FLT_MIN));
+            const float x = wave_inclusive_scan(ok ? la : 0.f);
             const float glast = __shfl(x, 63, 64);
             sG[lane] = x;
             sGam[lane] = __expf(x);
             sDec[lane] = __expf(glast - x);
-            sBeta[lane] = ok ? rBe : 0.f;
+            sBeta[lane] = ok ? (logits ? sigmoid_f(rBe) : rBe) : 0.f;
         }
         if (c + 1 < nchunks) load_chunk(c + 1);
         __syncthreads();
+        if constexpr (raw_qk) {
+            fold_qk_norms<DT, D, PK, NTH>(sK, sQ, sG, sGam, sDec, sGamQ, sGrA, sGrP, sGc, tid);
+            __syncthreads();
+        }
 
 #pragma unroll
         for (int pr = 0; pr < 10; ++pr) {
             if (pr % NW != wave) continue;
             f32x4 gk, gq;
             gram_pair<DT, D, PK>(sK, sQ, pair_i(pr), pair_j(pr), g4, c16, gk, gq);
-            mask_pair<DT, PA, PT>(gk, gq, pair_i(pr), pair_j(pr), g4, c16, sG, sBeta, sA, sP);
+            mask_pair<DT, PA, PT, false, raw_qk>(gk, gq, pair_i(pr), pair_j(pr), g4, c16,
+                                                 raw_qk ? sGrA : sG,
+                                  raw_qk ? sGrP : sG, raw_qk ? sGc : sG, sBeta, sA, sP);
         }
         __syncthreads();
 
@@ -345,7 +361,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p, int n
                 solve_unit_lower<DT, PA, PT>(sA, sE, sT, g4, c16);
         }
 
-        const ChainSmem<DT> m{sK, sQ, sKT, sV, sT, sP, sGam, sDec, sBeta};
+        const ChainSmem<DT> m{sK,   sQ,   sKT,   sV,    sT,
+                              sP,   sGam, sDec,  sBeta, raw_qk ? sGamQ : sGam};
         Frag<DT> sf[KS][NB];
         f32x4 racc[4][NB], oT[4][NB];
         chain_state_half<DT, D, NB, PK, (NW < 8)>(m, st, sf, racc, oT, g4, c16);
@@ -384,15 +401,16 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p, int n
 // two-pass path: per-chunk factors in the workspace
 //
 // Workspace record of one (chunk slot, value head), ws_bytes_per_chunk bytes:
-//   T [64][64] DT | P [64][64] DT | gamma [64] f32 | dec [64] f32 | beta [64] f32
+//   T [64][64] DT | P [64][64] DT | gam [64] | dec [64] | beta [64] | gamq [64] (f32;
+//   the decay vectors of ChainSmem)
 
 template <typename DT> constexpr int ws_bytes_per_chunk() {
-    return 2 * kC * kC * (int)sizeof(DT) + 3 * kC * 4;
+    return 2 * kC * kC * (int)sizeof(DT) + 4 * kC * 4;
 }
 
 // Fragment record (bf16, read by chain_db_kernel): T and P each as the
 // kTriFrags MFMA fragments that cover their nonzero blocks, in lane order
-// (6 KiB each), then gamma [64] | dec [64] | beta [64] (f32) padded to 1 KiB.
+// (6 KiB each), then gam [64] | dec [64] | beta [64] | gamq [64] (f32, 1 KiB).
 // The chain copies it into LDS unchanged and reads one fragment per lane
 // with a single 16-byte load.
 constexpr int kFragBytes = kTriFrags * 64 * 16;
@@ -414,7 +432,7 @@ template <typename DT, int D, bool FRAG> struct PrepCfg {
     static constexpr int OFF_T = FRAG ? SZ_A : SZ_KQ;
     static constexpr int OFF_P = FRAG ? SZ_KQ : OFF_T + SZ_T;
     static constexpr int OFF_VEC = FRAG ? SZ_KQ : OFF_P + SZ_T;
-    static constexpr int LDS = OFF_VEC + 4 * kC * 4;
+    static constexpr int LDS = OFF_VEC + 8 * kC * 4;  // the eight vectors of prefill_kernel
     static_assert(LDS <= 160 * 1024, "LDS budget of a gfx950 CU");
 };
 
@@ -424,7 +442,7 @@ template <typename DT, int D, bool FRAG> struct PrepCfg {
 // other's latencies). FRAG: the fragment record instead of dense rows, with
 // T in the dead K/Q staging and P written from registers (35 KiB, at most
 // 128 registers: four workgroups per CU).
-template <typename DT, int D, bool FRAG>
+template <typename DT, int D, bool FRAG, bool RAWQK>
 __global__ __launch_bounds__(256, FRAG ? 4 : 1) void prep_kernel(PrefillParams p, unsigned char *ws,
                                                                  int remap_xcd) {
     static_assert(!FRAG || sizeof(DT) == 2, "fragment records are bf16");
@@ -442,6 +460,12 @@ __global__ __launch_bounds__(256, FRAG ? 4 : 1) void prep_kernel(PrefillParams p
     float *sGam = sG + kC;
     float *sDec = sG + 2 * kC;
     float *sBeta = sG + 3 * kC;
+    float *sGamQ = sG + 4 * kC;
+    float *sGrA = sG + 5 * kC;
+    float *sGrP = sG + 6 * kC;
+    float *sGc = sG + 7 * kC;
+    constexpr bool raw_qk = RAWQK;
+    const bool logits = p.flags & kGateLogits;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -513,23 +537,30 @@ __global__ __launch_bounds__(256, FRAG ? 4 : 1) void prep_kernel(PrefillParams p
     }
     constexpr int WSB = FRAG ? ws_bytes_frag() : ws_bytes_per_chunk<DT>();
     unsigned char *rec = ws + (slot * p.Hv + h) * (int64_t)WSB;
+    float *vec = reinterpret_cast<float *>(
+        rec + (FRAG ? 2 * kFragBytes : 2 * kC * kC * (int)sizeof(DT)));
     if (wave == 0) {
         const float a = a_t, b = b_t;
         const bool ok = lane < lenc;
-        const float x = wave_inclusive_scan(__logf(fmaxf(ok ? a : 1.f, FLT_MIN)));
+        const float la = logits ? neg_softplus(a) : __logf(fmaxf(a, FLT_MIN));
+        const float x = wave_inclusive_scan(ok ? la : 0.f);
         const float glast = __shfl(x, 63, 64);
-        const float gam = __expf(x), dec = __expf(glast - x), bet = ok ? b : 0.f;
+        const float gam = __expf(x), dec = __expf(glast - x);
+        const float bet = ok ? (logits ? sigmoid_f(b) : b) : 0.f;
         sG[lane] = x;
         sGam[lane] = gam;
         sDec[lane] = dec;
         sBeta[lane] = bet;
-        float *vec = reinterpret_cast<float *>(
-            rec + (FRAG ? 2 * kFragBytes : 2 * kC * kC * (int)sizeof(DT)));
-        vec[lane] = gam;
-        vec[kC + lane] = dec;
-        vec[2 * kC + lane] = bet;
+        if (!raw_qk) {  // otherwise written once the row norms are folded in
+            vec[lane] = gam;
+            vec[kC + lane] = dec;
+            vec[2 * kC + lane] = bet;
+            vec[3 * kC + lane] = gam;
+        }
     }
     __syncthreads();
+    if constexpr (raw_qk)  // K and Q stay live until the barrier after the Gram products
+        fold_qk_norms<DT, D, PK, 256>(sK, sQ, sG, sGam, sDec, sGamQ, sGrA, sGrP, sGc, tid);
     // Gram products of this wave's lower tile pairs (pr = wave, wave + 4, ...)
     f32x4 gk[3], gq[3];
 #pragma unroll
@@ -542,10 +573,17 @@ __global__ __launch_bounds__(256, FRAG ? 4 : 1) void prep_kernel(PrefillParams p
     for (int k = 0; k < 3; ++k) {
         const int pr = wave + 4 * k;
         if (pr < 10)
-            mask_pair<DT, PA, PT, FRAG>(gk[k], gq[k], pair_i(pr), pair_j(pr), g4, c16, sG, sBeta, sA,
-                                        sP, rec + kFragBytes);
+            mask_pair<DT, PA, PT, FRAG, raw_qk>(gk[k], gq[k], pair_i(pr), pair_j(pr), g4, c16,
+                                        raw_qk ? sGrA : sG, raw_qk ? sGrP : sG, raw_qk ? sGc : sG,
+                                        sBeta, sA, sP, rec + kFragBytes);
     }
     __syncthreads();
+    if (raw_qk && wave == 0) {  // raw_qk is a compile-time constant
+        vec[lane] = sGam[lane];
+        vec[kC + lane] = sDec[lane];
+        vec[2 * kC + lane] = sBeta[lane];
+        vec[3 * kC + lane] = sGamQ[lane];
+    }
     // E_b overwrite the diagonal blocks of A (each is read in full first)
     if (wave == 0) solve_diag_blocks<DT, PA, PT>(sA, sA, sT, g4, c16);
     __syncthreads();
@@ -598,12 +636,12 @@ template <typename DT, int D, int NC, int DVW> struct ChainCfg {
     static constexpr int OFF_T = OFF_V + SZ_V;
     static constexpr int OFF_P = OFF_T + SZ_T;
     static constexpr int OFF_VEC = OFF_P + SZ_T;  // gamma, dec, beta
-    static constexpr int LDS = OFF_VEC + 3 * kC * 4;
+    static constexpr int LDS = OFF_VEC + 4 * kC * 4;
     // T and P pieces (16 bytes) per thread, decay-vector pieces
     static constexpr int EPP = 16 / (int)sizeof(DT);
     static constexpr int TP_PIECES = kC * kC / EPP;
     static constexpr int NTP = (TP_PIECES + NTH - 1) / NTH;
-    static constexpr int VEC_PIECES = 3 * kC / 4;
+    static constexpr int VEC_PIECES = 4 * kC / 4;
     static_assert(NC >= 1 && NC <= 4 && DVW % 16 == 0, "chain waves");
     static_assert(LDS <= 160 * 1024, "LDS budget of a gfx950 CU");
 };
@@ -709,7 +747,8 @@ __global__ __launch_bounds__(256) void chain_kernel(PrefillParams p, const unsig
         __syncthreads();
 
         if (wave < NC) {
-            const ChainSmem<DT> m{sK, sQ, sKT, sV, sT, sP, sVec, sVec + kC, sVec + 2 * kC};
+            const ChainSmem<DT> m{sK,   sQ,        sKT,           sV,           sT,
+                                  sP,   sVec,      sVec + kC,     sVec + 2 * kC, sVec + 3 * kC};
             Frag<DT> sf[KS][NB];
             f32x4 racc[4][NB], oT[4][NB];
             chain_state_half<DT, D, NB, PK>(m, st, sf, racc, oT, g4, c16);
@@ -841,7 +880,7 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
                       reinterpret_cast<const DT *>(b + Cf::OFF_V),
                       reinterpret_cast<const bf16x8 *>(b + Cf::OFF_T),
                       reinterpret_cast<const bf16x8 *>(b + Cf::OFF_P),
-                      vec, vec + kC, vec + 2 * kC};
+                      vec, vec + kC, vec + 2 * kC, vec + 3 * kC};
     };
 
     if (wave < 2 * NC) {
@@ -1045,16 +1084,37 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
 // ----------------------------------------------------------------------------
 // launch
 
+template <typename DT, int D, int NW, int DVW, bool PREFIX, bool RAWQK>
+static void launch_fused_as(const PrefillParams &p, int nsplit, int64_t nblocks,
+                            hipStream_t stream) {
+    hipLaunchKernelGGL((prefill_kernel<DT, D, NW, DVW, PREFIX, RAWQK>), dim3((unsigned)nblocks),
+                       dim3(NW * 64), 0, stream, p, nsplit, nblocks % 8 == 0 ? 1 : 0);
+}
+
 template <typename DT, int D, int NW, int DVW>
 static hipError_t launch_fused(const PrefillParams &p, int nsplit, hipStream_t stream) {
     const int64_t nblocks = (int64_t)p.nseq * p.Hv * nsplit;
     if (nblocks <= 0 || nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    if (p.prefix)
-        hipLaunchKernelGGL((prefill_kernel<DT, D, NW, DVW, true>), dim3((unsigned)nblocks),
-                           dim3(NW * 64), 0, stream, p, nsplit, nblocks % 8 == 0 ? 1 : 0);
+    const bool raw = p.flags & kQkL2Norm;
+    if (p.prefix) {
+        if (raw) launch_fused_as<DT, D, NW, DVW, true, true>(p, nsplit, nblocks, stream);
+        else launch_fused_as<DT, D, NW, DVW, true, false>(p, nsplit, nblocks, stream);
+    } else {
+        if (raw) launch_fused_as<DT, D, NW, DVW, false, true>(p, nsplit, nblocks, stream);
+        else launch_fused_as<DT, D, NW, DVW, false, false>(p, nsplit, nblocks, stream);
+    }
+    return hipGetLastError();
+}
+
+template <typename DT, int D, bool FRAG>
+static hipError_t launch_prep(const PrefillParams &p, unsigned char *ws, int64_t nprep,
+                              hipStream_t stream) {
+    if (p.flags & kQkL2Norm)
+        hipLaunchKernelGGL((prep_kernel<DT, D, FRAG, true>), dim3((unsigned)nprep), dim3(256), 0,
+                           stream, p, ws, nprep % 8 == 0 ? 1 : 0);
     else
-        hipLaunchKernelGGL((prefill_kernel<DT, D, NW, DVW, false>), dim3((unsigned)nblocks),
-                           dim3(NW * 64), 0, stream, p, nsplit, nblocks % 8 == 0 ? 1 : 0);
+        hipLaunchKernelGGL((prep_kernel<DT, D, FRAG, false>), dim3((unsigned)nprep), dim3(256), 0,
+                           stream, p, ws, nprep % 8 == 0 ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -1065,9 +1125,7 @@ static hipError_t launch_split(const PrefillParams &p, unsigned char *ws, int64_
     const int64_t nchain = (int64_t)p.nseq * p.Hv * nsplit;
     if (nprep <= 0 || nprep > 0x7FFFFFFF || nchain <= 0 || nchain > 0x7FFFFFFF)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((prep_kernel<DT, D, false>), dim3((unsigned)nprep), dim3(256), 0, stream, p, ws,
-                       nprep % 8 == 0 ? 1 : 0);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_prep<DT, D, false>(p, ws, nprep, stream);
     if (e != hipSuccess) return e;
     if (p.prefix)
         hipLaunchKernelGGL((chain_kernel<DT, D, NC, DVW, true>), dim3((unsigned)nchain), dim3(256),
@@ -1088,9 +1146,7 @@ static hipError_t launch_split_db(const PrefillParams &p, unsigned char *ws, int
     if (nprep <= 0 || nprep > 0x7FFFFFFF || nchain <= 0 || nchain > 0x7FFFFFFF)
         return hipErrorInvalidValue;
     if (ChainDbCfg<D, NC, NH>::DVS * nsplit != D) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((prep_kernel<__bf16, D, true>), dim3((unsigned)nprep), dim3(256), 0, stream, p, ws,
-                       nprep % 8 == 0 ? 1 : 0);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_prep<__bf16, D, true>(p, ws, nprep, stream);
     if (e != hipSuccess) return e;
     if (p.prefix)
         hipLaunchKernelGGL((chain_db_kernel<D, NC, NH, true>), dim3((unsigned)nchain),

@@ -124,19 +124,21 @@ def _round_store(x32: np.ndarray, dtype: str) -> np.ndarray:
     return bf16_bits(x32) if dtype == "bf16" else x32.astype(np.float32)
 
 
-def _gen_block(child, n_tok, Hk, Hv, D, dtype, alpha_shift, beta_shift, out, row0):
+def _gen_block(child, n_tok, Hk, Hv, D, dtype, alpha_shift, beta_shift, out, row0, raw=False):
     rng = np.random.Generator(np.random.PCG64(child))
     for name, heads in (("q", Hk), ("k", Hk)):
         x = rng.standard_normal((n_tok, heads, D), dtype=np.float32)
-        nrm = np.sqrt(np.sum(x.astype(np.float64) ** 2, axis=-1, keepdims=True)).astype(np.float32)
-        x = x / nrm
+        if not raw:
+            nrm = np.sqrt(np.sum(x.astype(np.float64) ** 2, axis=-1,
+                                 keepdims=True)).astype(np.float32)
+            x = x / nrm
         out[name][row0:row0 + n_tok] = _round_store(x, dtype)
     v = rng.standard_normal((n_tok, Hv, D), dtype=np.float32)
     out["v"][row0:row0 + n_tok] = _round_store(v, dtype)
-    bl = rng.standard_normal((n_tok, Hv), dtype=np.float32)
-    al = rng.standard_normal((n_tok, Hv), dtype=np.float32)
-    out["beta"][row0:row0 + n_tok] = _sigmoid(bl + np.float32(beta_shift))
-    out["alpha"][row0:row0 + n_tok] = _exp_neg_softplus(al + np.float32(alpha_shift))
+    bl = rng.standard_normal((n_tok, Hv), dtype=np.float32) + np.float32(beta_shift)
+    al = rng.standard_normal((n_tok, Hv), dtype=np.float32) + np.float32(alpha_shift)
+    out["beta"][row0:row0 + n_tok] = bl if raw else _sigmoid(bl)
+    out["alpha"][row0:row0 + n_tok] = al if raw else _exp_neg_softplus(al)
 
 
 def lengths_for(w: Workload) -> np.ndarray:
@@ -153,8 +155,13 @@ def lengths_for(w: Workload) -> np.ndarray:
 
 
 def generate_packed(Hk, Hv, D, dtype, seed, lengths, alpha_shift=2.0, init_state=False,
-                    block_tokens=BLOCK_TOKENS, threads=None, beta_shift=0.0):
+                    block_tokens=BLOCK_TOKENS, threads=None, beta_shift=0.0, raw=False):
     """Packed tokens of several sequences.
+
+    raw=True draws the same numbers but stores q, k before their L2
+    normalisation and alpha, beta as their logits (the inputs of the
+    library's in-kernel preparation: alpha = exp(-softplus(a)),
+    beta = sigmoid(b)).
 
     Returns dict: q, k [total,Hk,D]; v [total,Hv,D] (uint16 bf16 bits or
     fp32); alpha, beta [total,Hv] fp32; cu_seqlens [N+1] int32; S0
@@ -188,7 +195,7 @@ def generate_packed(Hk, Hv, D, dtype, seed, lengths, alpha_shift=2.0, init_state
     nth = threads or _threads()
     with ThreadPoolExecutor(nth) as ex:
         list(ex.map(lambda j: _gen_block(j[0], j[1], Hk, Hv, D, dtype, alpha_shift, beta_shift,
-                                         out, j[2]),
+                                         out, j[2], raw),
                     jobs))
     S0 = None
     if init_state:
@@ -206,7 +213,7 @@ def generate_packed(Hk, Hv, D, dtype, seed, lengths, alpha_shift=2.0, init_state
     return out
 
 
-def generate(w: Workload, threads=None):
+def generate(w: Workload, threads=None, raw=False):
     """Inputs of a named workload.
 
     prefill: q,k [B,T,Hk,D], v [B,T,Hv,D], alpha,beta [B,T,Hv], S0 [B,Hv,D,D]|None
@@ -214,7 +221,7 @@ def generate(w: Workload, threads=None):
     varlen : packed layout of generate_packed()."""
     lengths = lengths_for(w)
     d = generate_packed(w.Hk, w.Hv, w.D, w.dtype, w.seed, lengths, w.alpha_shift,
-                        w.init_state, threads=threads)
+                        w.init_state, threads=threads, raw=raw)
     if w.kind == "prefill":
         for name in ("q", "k", "v", "alpha", "beta"):
             d[name] = d[name].reshape((w.B, w.T) + d[name].shape[1:])
@@ -222,17 +229,17 @@ def generate(w: Workload, threads=None):
 
 
 def small_prefill(B, T, Hk, Hv, D, dtype="bf16", seed=0, alpha_shift=2.0, init_state=False,
-                  beta_shift=0.0):
+                  beta_shift=0.0, raw=False):
     """Prefill inputs of arbitrary shape, same recipe as the workloads."""
     d = generate_packed(Hk, Hv, D, dtype, seed, [T] * B, alpha_shift, init_state,
-                        beta_shift=beta_shift)
+                        beta_shift=beta_shift, raw=raw)
     for name in ("q", "k", "v", "alpha", "beta"):
         d[name] = d[name].reshape((B, T) + d[name].shape[1:])
     return d
 
 
 def multi_decode(B, K, Hk, Hv, D, dtype, seed, num_slots=None, plan="permute",
-                 alpha_shift=2.0):
+                 alpha_shift=2.0, raw=False):
     """Inputs of a K-tokens-per-sequence decode against a slot pool.
 
     q, k [B,K,Hk,D]; v [B,K,Hv,D]; alpha, beta [B,K,Hv]: the token recipe of
@@ -242,7 +249,7 @@ def multi_decode(B, K, Hk, Hv, D, dtype, seed, num_slots=None, plan="permute",
       "pairs"  : sequence b reads slot 2b and writes slot 2b+1
       "inplace": src = dst = a random permutation of B slots
     num_slots defaults to 2B (B for "inplace")."""
-    d = generate_packed(Hk, Hv, D, dtype, seed, [K] * B, alpha_shift)
+    d = generate_packed(Hk, Hv, D, dtype, seed, [K] * B, alpha_shift, raw=raw)
     for name in ("q", "k", "v", "alpha", "beta"):
         d[name] = d[name].reshape((B, K) + d[name].shape[1:])
     if num_slots is None:

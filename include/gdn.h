@@ -63,6 +63,22 @@ typedef enum {
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype_t; /* type of q, k, v, out */
 
 /*
+ * Input preparation done inside the kernels: the `flags` argument of the
+ * compute calls (bitwise OR; 0 = inputs used as given). The pages name the
+ * layer but not these steps; they are the ones just before the recurrence in
+ * the published Gated DeltaNet (Yang, Kautz & Hatamizadeh, ICLR 2025): q and k
+ * L2-normalised per head, the write strength a sigmoid and the decay the
+ * exponential of a negative softplus of per-token projections.
+ *   GDN_QK_L2NORM    q and k hold raw rows; each row x is used as
+ *                    x / sqrt(sum(x^2) + 1e-6) (fp32 arithmetic)
+ *   GDN_GATE_LOGITS  alpha holds a, beta holds b (fp32 logits); the kernels
+ *                    use alpha = exp(-softplus(a)), beta = sigmoid(b), taking
+ *                    log(alpha) = -softplus(a) directly for the decay
+ * Any other bit: GDN_ERR_UNSUPPORTED.
+ */
+enum { GDN_QK_L2NORM = 1, GDN_GATE_LOGITS = 2 };
+
+/*
  * gdn_prefill_chunked -- chunked prefill of B equal-length sequences.
  *
  *   q, k          [B, T, Hk, Dk]  dtype
@@ -103,7 +119,7 @@ gdn_status_t gdn_prefill_chunked(const void *q, const void *k, const void *v,
                                  float *final_state, float *prefix_states,
                                  int32_t prefix_interval, int32_t B, int64_t T,
                                  int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
-                                 gdn_dtype_t dtype, float scale,
+                                 gdn_dtype_t dtype, float scale, uint32_t flags,
                                  void *workspace, size_t workspace_bytes,
                                  hipStream_t stream);
 
@@ -125,7 +141,7 @@ gdn_status_t gdn_decode_step(const void *q, const void *k, const void *v,
                              const float *alpha, const float *beta, float *state,
                              void *out, int32_t B, int32_t Hk, int32_t Hv,
                              int32_t Dk, int32_t Dv, gdn_dtype_t dtype,
-                             float scale, hipStream_t stream);
+                             float scale, uint32_t flags, hipStream_t stream);
 
 /*
  * gdn_decode_multi -- K new tokens per sequence against a pool of state
@@ -169,7 +185,8 @@ gdn_status_t gdn_decode_multi(const void *q, const void *k, const void *v,
                               const int32_t *src_slot, const int32_t *dst_slot,
                               void *out, float *step_states, int32_t B, int32_t K,
                               int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
-                              gdn_dtype_t dtype, float scale, hipStream_t stream);
+                              gdn_dtype_t dtype, float scale, uint32_t flags,
+                              hipStream_t stream);
 
 /*
  * gdn_varlen_prefill -- chunked prefill of N packed sequences.
@@ -202,7 +219,7 @@ gdn_status_t gdn_varlen_prefill(const void *q, const void *k, const void *v,
                                 float *prefix_states, int32_t prefix_interval,
                                 int32_t Hk,
                                 int32_t Hv, int32_t Dk, int32_t Dv,
-                                gdn_dtype_t dtype, float scale,
+                                gdn_dtype_t dtype, float scale, uint32_t flags,
                                 void *workspace, size_t workspace_bytes,
                                 hipStream_t stream);
 

@@ -36,6 +36,7 @@
 
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
+#define ORACLE_F64 2
 
 /* bf16 bit pattern -> fp64, exact: the 16 bits are the high half of a
  * binary32 with the low mantissa bits zero. */
@@ -51,6 +52,9 @@ static void oracle_load_vec(const void *base, int dtype, int64_t offset, int n,
     if (dtype == ORACLE_BF16) {
         const uint16_t *p = (const uint16_t *)base + offset;
         for (int i = 0; i < n; ++i) dst[i] = oracle_bf16_to_f64(p[i]);
+    } else if (dtype == ORACLE_F64) {
+        const double *p = (const double *)base + offset;
+        for (int i = 0; i < n; ++i) dst[i] = p[i];
     } else {
         const float *p = (const float *)base + offset;
         for (int i = 0; i < n; ++i) dst[i] = (double)p[i];
@@ -62,7 +66,8 @@ static void oracle_load_vec(const void *base, int dtype, int64_t offset, int n,
  *
  *   q, k      : q/k head of this chain at token 0 (dtype elements)
  *   v         : value head of this chain at token 0 (dtype elements)
- *   alpha,beta: this value head at token 0 (fp32)
+ *   dtype     : 0 fp32, 1 bf16 bit patterns, 2 fp64
+ *   alpha,beta: this value head at token 0 (ab_dtype elements: 0 fp32, 2 fp64)
  *   T         : number of tokens (>= 0)
  *   stride_qk : elements between consecutive tokens of q and k
  *   stride_v  : elements between consecutive tokens of v
@@ -76,16 +81,18 @@ static void oracle_load_vec(const void *base, int dtype, int64_t offset, int n,
  * Returns 0, or -1 for arguments it cannot take.
  */
 int gdn_oracle_chain(const void *q, const void *k, const void *v, int dtype,
-                     const float *alpha, const float *beta, int64_t T,
+                     const void *alpha, const void *beta, int ab_dtype, int64_t T,
                      int64_t stride_qk, int64_t stride_v, int64_t stride_ab,
                      int dk, int dv, double scale, double *S, double *o) {
     if (dk < 1 || dk > 256 || dv < 1 || dv > 256 || T < 0) return -1;
-    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16 && dtype != ORACLE_F64) return -1;
+    if (ab_dtype != ORACLE_F32 && ab_dtype != ORACLE_F64) return -1;
     double qt[256], kt[256], vt[256], u[256];
 
     for (int64_t t = 0; t < T; ++t) {
-        const double a = (double)alpha[t * stride_ab];
-        const double b = (double)beta[t * stride_ab];
+        double a, b;
+        oracle_load_vec(alpha, ab_dtype, t * stride_ab, 1, &a);
+        oracle_load_vec(beta, ab_dtype, t * stride_ab, 1, &b);
         oracle_load_vec(q, dtype, t * stride_qk, dk, qt);
         oracle_load_vec(k, dtype, t * stride_qk, dk, kt);
         oracle_load_vec(v, dtype, t * stride_v, dv, vt);
@@ -114,4 +121,4 @@ int gdn_oracle_chain(const void *q, const void *k, const void *v, int dtype,
     return 0;
 }
 
-int gdn_oracle_version(void) { return 1; }
+int gdn_oracle_version(void) { return 2; }

@@ -58,21 +58,21 @@ def P(i):
 
 
 def prefill(lib, q=P(0), k=P(1), v=P(2), a=P(3), b=P(4), s0=P(5), out=P(6), sf=P(7), pre=None,
-            every=0, B=1, T=64, Hk=2, Hv=4, Dk=64, Dv=64, dtype=BF16, ws=None, wsb=0):
+            every=0, B=1, T=64, Hk=2, Hv=4, Dk=64, Dv=64, dtype=BF16, ws=None, wsb=0, flags=0):
     return lib.gdn_prefill_chunked(q, k, v, a, b, s0, out, sf, pre, every, B, T, Hk, Hv, Dk, Dv,
-                                   dtype, 1.0, ws, wsb, None)
+                                   dtype, 1.0, flags, ws, wsb, None)
 
 
 def varlen(lib, q=P(0), k=P(1), v=P(2), a=P(3), b=P(4), cu=P(8), N=2, total=64, s0=P(5),
            out=P(6), sf=P(7), pre=None, every=0, Hk=2, Hv=4, Dk=64, Dv=64, dtype=BF16, ws=None,
-           wsb=0):
+           wsb=0, flags=0):
     return lib.gdn_varlen_prefill(q, k, v, a, b, cu, N, total, s0, out, sf, pre, every, Hk, Hv, Dk,
-                                  Dv, dtype, 1.0, ws, wsb, None)
+                                  Dv, dtype, 1.0, flags, ws, wsb, None)
 
 
 def decode(lib, q=P(0), k=P(1), v=P(2), a=P(3), b=P(4), s=P(5), out=P(6), B=4, Hk=2, Hv=4,
-           Dk=64, Dv=64, dtype=BF16):
-    return lib.gdn_decode_step(q, k, v, a, b, s, out, B, Hk, Hv, Dk, Dv, dtype, 1.0, None)
+           Dk=64, Dv=64, dtype=BF16, flags=0):
+    return lib.gdn_decode_step(q, k, v, a, b, s, out, B, Hk, Hv, Dk, Dv, dtype, 1.0, flags, None)
 
 
 def test_prefill_validation(lib):
@@ -136,9 +136,9 @@ def test_decode_validation(lib):
 
 
 def multi(lib, q=P(0), k=P(1), v=P(2), a=P(3), b=P(4), pool=P(5), ns=8, src=P(8), dst=P(9),
-          out=P(6), steps=P(7), B=4, K=3, Hk=2, Hv=4, Dk=64, Dv=64, dtype=BF16):
+          out=P(6), steps=P(7), B=4, K=3, Hk=2, Hv=4, Dk=64, Dv=64, dtype=BF16, flags=0):
     return lib.gdn_decode_multi(q, k, v, a, b, pool, ns, src, dst, out, steps, B, K, Hk, Hv, Dk,
-                                Dv, dtype, 1.0, None)
+                                Dv, dtype, 1.0, flags, None)
 
 
 def test_decode_multi_validation(lib):
@@ -165,6 +165,14 @@ def test_decode_multi_validation(lib):
     assert multi(lib, ns=1 << 30, Hv=1 << 20) == SHAPE  # pool bytes overflow
 
 
+def test_unknown_flags_are_rejected(lib):
+    for f in (4, 8, 1 << 31, 7):
+        assert prefill(lib, flags=f) == UNSUP
+        assert varlen(lib, flags=f) == UNSUP
+        assert decode(lib, flags=f) == UNSUP
+        assert multi(lib, flags=f) == UNSUP
+
+
 def test_valid_call_without_device_reports_hip_error(lib):
     torch = pytest.importorskip("torch")
     if torch.cuda.device_count() > 0:
@@ -172,6 +180,8 @@ def test_valid_call_without_device_reports_hip_error(lib):
     assert prefill(lib) == HIPERR
     assert b"HIP" in lib.gdn_status_string(HIPERR)
     assert decode(lib) == HIPERR
+    assert decode(lib, flags=3) == HIPERR
+    assert prefill(lib, flags=3) == HIPERR
     assert multi(lib) == HIPERR
     assert multi(lib, steps=None, K=0, q=None, k=None, v=None, a=None, b=None, out=None) == HIPERR
     assert lib.gdn_prefill_workspace_size(1, 4096, 16, 48, 128, 128, BF16, 0) == 0

@@ -91,10 +91,10 @@ def test_workspace_path_is_taken_for_small_batches(gdn):
     """48 chains (B=1, the layer's value heads) ask for a workspace; a batch
     with enough chains does not."""
     n = gdn.gdn_prefill_workspace_size(1, 4096, 16, 48, 128, 128, gdn.GDN_BF16, 0)
-    assert n == 64 * 48 * (2 * 64 * 64 * 2 + 3 * 64 * 4)
+    assert n == 64 * 48 * (2 * 64 * 64 * 2 + 4 * 64 * 4)  # T, P and four decay vectors
     assert gdn.gdn_prefill_workspace_size(64, 4096, 16, 48, 128, 128, gdn.GDN_BF16, 0) == 0
     assert gdn.gdn_prefill_workspace_size(2, 130, 16, 48, 128, 128, gdn.GDN_BF16, 1) == \
-        (3 + 2) * 48 * (2 * 64 * 64 * 2 + 3 * 64 * 4)
+        (3 + 2) * 48 * (2 * 64 * 64 * 2 + 4 * 64 * 4)
 
 
 def test_tiny_f32_workload(gdn):
@@ -535,6 +535,124 @@ def test_layer_prefill_4k_prefix_states(gdn):
     ref = oracle.prefix_states(flat["q"], flat["k"], flat["v"], flat["alpha"], flat["beta"],
                                [0, w.T], 1024)
     _check_prefix(from_torch(pre), ref, lambda n, i: i, "bf16", f"{w.name} prefix states")
+
+
+# ------------------------------------------------- input preparation in the kernels
+QK, GL = 1, 2   # GDN_QK_L2NORM, GDN_GATE_LOGITS
+
+
+def _prepared_inputs(gen, flags):
+    """Raw q, k (flag 1) and gate logits (flag 2) of a seed, the rest as the
+    plain recipe gives them for the same seed (the generator draws the same
+    numbers either way)."""
+    plain, raw = gen(False), gen(True)
+    d = dict(plain)
+    if flags & QK:
+        d["q"], d["k"] = raw["q"], raw["k"]
+    if flags & GL:
+        d["alpha"], d["beta"] = raw["alpha"], raw["beta"]
+    return d
+
+
+PREP_DENSE = [
+    # path, nsplit, dtype, D, flags
+    ("fused", "auto", "bf16", 128, QK | GL),
+    ("fused", "2", "bf16", 128, QK),
+    ("fused", "auto", "bf16", 128, GL),
+    ("split", "1", "bf16", 128, QK | GL),     # chain_kernel
+    ("split", "4", "bf16", 128, QK | GL),     # chain_db_kernel
+    ("split", "2", "bf16", 64, QK),
+    ("split", "2", "f32", 64, QK | GL),
+    ("fused", "auto", "f32", 128, QK | GL),
+]
+
+
+@pytest.mark.parametrize("path,nsplit,dtype,D,flags", PREP_DENSE)
+def test_prefill_prepared_inputs(gdn, monkeypatch, path, nsplit, dtype, D, flags):
+    monkeypatch.setenv("GDN_PREFILL_PATH", path)
+    if nsplit != "auto":
+        monkeypatch.setenv("GDN_PREFILL_NSPLIT", nsplit)
+    d = _prepared_inputs(lambda raw: small_prefill(2, 200, 2, 6, D, dtype, seed=130 + flags,
+                                                   init_state=True, raw=raw), flags)
+    q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
+    out, sf = gdn.gdn_prefill_chunked(q, k, v, a, b, to_torch(d["S0"], DEV), flags=flags)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"],
+                                  flags=flags)
+    check(from_torch(out), from_torch(sf), o_ref, S_ref, dtype,
+          f"prepared inputs flags={flags} {path} ns={nsplit} {dtype} D{D}")
+
+
+@pytest.mark.parametrize("path", ["fused", "split"])
+def test_varlen_prepared_inputs_and_zero_rows(gdn, monkeypatch, path):
+    """Raw rows of zeros normalise to zero (the 1e-6 under the root): such a
+    token writes nothing and reads nothing."""
+    monkeypatch.setenv("GDN_PREFILL_PATH", path)
+    lengths = [150, 1, 64, 300]
+    d = generate_packed(2, 6, 128, "bf16", 140, lengths, init_state=True, raw=True)
+    d["k"][[3, 70, 71, 400]] = 0
+    d["q"][[5, 200]] = 0
+    q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
+    pre = torch.full((gdn.prefix_state_rows(len(lengths), int(d["cu_seqlens"][-1]), 1, True), 6,
+                      128, 128), SENTINEL, dtype=torch.float32, device=DEV)
+    out, sf = gdn.gdn_varlen_prefill(q, k, v, a, b, to_torch(d["cu_seqlens"], DEV),
+                                     to_torch(d["S0"], DEV), flags=QK | GL, prefix_states=pre,
+                                     prefix_interval=1)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.varlen(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["cu_seqlens"],
+                                 d["S0"], flags=QK | GL)
+    o = from_torch(out)
+    cu = d["cu_seqlens"]
+    for n in range(len(lengths)):
+        e = max_error(o[cu[n]:cu[n + 1]][None], o_ref[cu[n]:cu[n + 1]][None], (0, 2))
+        assert e <= TOL["bf16"], (n, e)
+    check(o[:0], from_torch(sf), o_ref[:0], S_ref, "bf16", f"varlen prepared ({path}) states")
+    ref = oracle.prefix_states(d["q"], d["k"], d["v"], d["alpha"], d["beta"], cu, 64, d["S0"],
+                               flags=QK | GL)
+    _check_prefix(from_torch(pre), ref, lambda n, i: int(cu[n]) // 64 + n + i, "bf16",
+                  f"varlen prepared prefix states ({path})")
+
+
+@pytest.mark.parametrize("flags", [QK, GL, QK | GL])
+@pytest.mark.parametrize("D,dtype", [(128, "bf16"), (64, "f32")])
+def test_decode_prepared_inputs(gdn, flags, D, dtype):
+    d = _prepared_inputs(lambda raw: generate_packed(2, 6, D, dtype, 150 + flags, [1] * 5,
+                                                     init_state=True, raw=raw), flags)
+    q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
+    state = to_torch(d["S0"], DEV)
+    out = gdn.gdn_decode_step(q, k, v, a, b, state, scale=0.7, flags=flags)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.decode(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], 0.7,
+                                 flags=flags)
+    check(from_torch(out), from_torch(state), o_ref, S_ref, dtype,
+          f"decode prepared flags={flags} D{D} {dtype}", o_axes=(0, 1), s_axes=(0, 1))
+
+
+@pytest.mark.parametrize("steps", [False, True])
+def test_decode_multi_prepared_inputs(gdn, steps):
+    d = multi_decode(4, 5, 2, 6, 128, "bf16", seed=160, plan="permute", raw=True)
+    q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
+    pool = to_torch(d["pool"], DEV)
+    out, st = gdn.gdn_decode_multi(q, k, v, a, b, pool, to_torch(d["src_slot"], DEV),
+                                   to_torch(d["dst_slot"], DEV), flags=QK | GL,
+                                   want_step_states=steps)
+    torch.cuda.synchronize()
+    ref = oracle.decode_multi(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["pool"],
+                              d["src_slot"], d["dst_slot"], 1.0, steps, flags=QK | GL)
+    check_multi(d, from_torch(out), from_torch(pool), from_torch(st) if steps else None, ref,
+                "bf16", f"multi prepared steps={steps}")
+
+
+def test_layer_prefill_4k_prepared_inputs(gdn):
+    """The layer workload from raw q, k and gate logits."""
+    w = WORKLOADS["layer_prefill_4k"]
+    d = generate(w, raw=True)
+    q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
+    out, sf = gdn.gdn_prefill_chunked(q, k, v, a, b, None, flags=QK | GL)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], None,
+                                  flags=QK | GL)
+    check(from_torch(out), from_torch(sf), o_ref, S_ref, "bf16", f"{w.name} prepared inputs")
 
 
 # ----------------------------------------------------------------- full-size, sampled

@@ -461,3 +461,74 @@ def test_prefix_states_overwrite_at_block_ends():
         for h in range(Hv):
             np.testing.assert_allclose(pre[i, h] @ _f64(k[t, h // (Hv // Hk)]), _f64(v[t, h]),
                                        rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------- input preparation (flags)
+def test_raw_qk_scale_invariance():
+    """With q, k L2-normalised by the oracle, scaling any q or k row by a
+    positive constant leaves every output and state unchanged (up to the
+    1e-6 under the square root); a missing normalisation of either fails."""
+    rng = np.random.default_rng(61)
+    T, Hk, Hv, d = 30, 2, 4, 16
+    q, k, v, alpha, beta = _rand_inputs(rng, T, Hk, Hv, d, d, unit_k=False)
+    S0 = rng.standard_normal((1, Hv, d, d)).astype(np.float32)
+    o1, S1 = oracle.prefill(q[None], k[None], v[None], alpha[None], beta[None], S0,
+                            flags=oracle.QK_L2NORM)
+    cq = rng.uniform(0.2, 30.0, (T, Hk, 1)).astype(np.float32)
+    ck = rng.uniform(0.2, 30.0, (T, Hk, 1)).astype(np.float32)
+    o2, S2 = oracle.prefill((q * cq)[None], (k * ck)[None], v[None], alpha[None], beta[None],
+                            S0, flags=oracle.QK_L2NORM)
+    np.testing.assert_allclose(o2, o1, rtol=1e-5, atol=1e-7)
+    np.testing.assert_allclose(S2, S1, rtol=1e-5, atol=1e-7)
+
+
+def test_raw_qk_unit_rows_equal_plain():
+    """Rows that already have unit norm come out of the normalisation as
+    x / sqrt(1 + 1e-6): the prepared run matches the plain one to ~5e-7."""
+    rng = np.random.default_rng(62)
+    T, Hk, Hv, d = 20, 1, 2, 64
+    q, _, v, alpha, beta = _rand_inputs(rng, T, Hk, Hv, d, d)
+    k = _exact_unit_keys(rng, T, Hk, d, 16)
+    q = _exact_unit_keys(rng, T, Hk, d, 4)
+    o1, S1 = oracle.prefill(q[None], k[None], v[None], alpha[None], beta[None])
+    o2, S2 = oracle.prefill(q[None], k[None], v[None], alpha[None], beta[None],
+                            flags=oracle.QK_L2NORM)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=5e-6 * np.abs(o1).max())
+    np.testing.assert_allclose(S2, S1, rtol=0, atol=5e-6 * np.abs(S1).max())
+
+
+def test_gate_logits_closed_forms():
+    """exp(-softplus(0)) = 1/2 and sigmoid(0) = 1/2: zero logits equal the plain
+    run with alpha = beta = 1/2; large logits reach the limits e^-a and e^b."""
+    rng = np.random.default_rng(63)
+    T, Hk, Hv, d = 12, 1, 2, 8
+    q, k, v, _, _ = _rand_inputs(rng, T, Hk, Hv, d, d)
+    zero = np.zeros((T, Hv), np.float32)
+    half = np.full((T, Hv), 0.5, np.float32)
+    o1, S1 = oracle.prefill(q[None], k[None], v[None], zero[None], zero[None],
+                            flags=oracle.GATE_LOGITS)
+    o2, S2 = oracle.prefill(q[None], k[None], v[None], half[None], half[None])
+    np.testing.assert_allclose(o1, o2, rtol=1e-14, atol=1e-16)
+    np.testing.assert_allclose(S1, S2, rtol=1e-14, atol=1e-16)
+    _, _, _, a, b = oracle.prepare(q, k, v, np.array([40.0, -40.0, 3.0]),
+                                   np.array([-40.0, 40.0, -3.0]), oracle.GATE_LOGITS)
+    np.testing.assert_allclose(a[0], np.exp(-40.0), rtol=1e-12)
+    assert a[1] == 1.0 or abs(a[1] - 1.0) < 1e-15
+    np.testing.assert_allclose(a[2], 1.0 / (1.0 + np.exp(3.0)), rtol=1e-14)
+    np.testing.assert_allclose(b[0], np.exp(-40.0), rtol=1e-12)
+    np.testing.assert_allclose(b[2], 1.0 / (1.0 + np.exp(3.0)), rtol=1e-14)
+
+
+def test_prepare_matches_the_generator_recipe():
+    """The raw inputs of a seed, prepared, give the normalised rows and gates
+    the generator stores for the same seed (to its bf16 / fp32 rounding)."""
+    from gdn_synth import small_prefill
+    plain = small_prefill(1, 300, 2, 6, 128, "bf16", seed=64)
+    raw = small_prefill(1, 300, 2, 6, 128, "bf16", seed=64, raw=True)
+    q, k, v, a, b = oracle.prepare(raw["q"], raw["k"], raw["v"], raw["alpha"], raw["beta"],
+                                   oracle.QK_L2NORM | oracle.GATE_LOGITS)
+    np.testing.assert_allclose(q, bf16_to_f32(plain["q"]), rtol=0, atol=4e-3)
+    np.testing.assert_allclose(k, bf16_to_f32(plain["k"]), rtol=0, atol=4e-3)
+    np.testing.assert_array_equal(v, bf16_to_f32(raw["v"]).astype(np.float64))
+    np.testing.assert_allclose(a, plain["alpha"], rtol=2e-7)
+    np.testing.assert_allclose(b, plain["beta"], rtol=2e-7)
