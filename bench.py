@@ -15,8 +15,10 @@ decode state-update GB/s with its fraction of HBM bandwidth, both from HIP
 events on the stream the kernels run on; and the fp64 oracle timed on the
 host cores as a CPU baseline. Timed apart from the step: under
 "prefill_prefix_states" the same prefill also writing the state after every
-1024 tokens, and under "decode_multi" the K-token decode against a slot pool
-(B=256 sequences verifying K=4 tokens each), in tokens/s and HBM GB/s.
+1024 tokens; under "prepared_inputs" the prefill and decode step from raw
+q, k and gate logits (prepared inside the kernels); and under "decode_multi"
+the K-token decode against a slot pool (B=256 sequences verifying K=4 tokens
+each), in tokens/s and HBM GB/s.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3]
 """
@@ -120,6 +122,8 @@ def main():
                          "(evicts the 256 MiB Infinity Cache), reported as ms_cold")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured ceilings (library copy and bf16 GEMM)")
+    ap.add_argument("--no-prepared", action="store_true",
+                    help="skip the prefill / decode from raw inputs (in-kernel preparation)")
     ap.add_argument("--no-multi", action="store_true",
                     help="skip the K-token slot-pool decode measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -245,6 +249,57 @@ def main():
                   "overhead_vs_plain": round(float(np.median(pp_ms)) / float(np.median(pre_ms)) - 1,
                                              4)}
         del p_pre
+
+    # the same prefill and decode step from raw inputs (q, k before their L2
+    # normalisation, gate logits), prepared inside the kernels; beside them
+    # the time of a separate preparation pass (torch ops) over the same inputs
+    prepared = None
+    if not varlen and not args.no_prepared:
+        flags = gdn.GDN_QK_L2NORM | gdn.GDN_GATE_LOGITS
+        rp = generate(wp, raw=True)
+        rt = {n: to_torch(rp[n], dev) for n in ("q", "k", "v", "alpha", "beta")}
+        rd = generate(wd, raw=True)
+        rdt = {n: to_torch(rd[n], dev) for n in ("q", "k", "v", "alpha", "beta")}
+        r_state = to_torch(rd["S0"], dev)
+
+        def timed_ms(fn, reps):
+            fn()
+            torch.cuda.synchronize()
+            out_ms = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                out_ms.append(e0.elapsed_time(e1))
+            return float(np.median(out_ms))
+
+        def torch_prepare(t):
+            qf, kf = t["q"].float(), t["k"].float()
+            qn = (qf * torch.rsqrt((qf * qf).sum(-1, keepdim=True) + 1e-6)).to(t["q"].dtype)
+            kn = (kf * torch.rsqrt((kf * kf).sum(-1, keepdim=True) + 1e-6)).to(t["k"].dtype)
+            a = torch.exp(-torch.nn.functional.softplus(t["alpha"]))
+            b = torch.sigmoid(t["beta"])
+            return qn, kn, a, b
+        pre_raw = timed_ms(lambda: gdn.gdn_prefill_chunked(
+            rt["q"], rt["k"], rt["v"], rt["alpha"], rt["beta"], None, out=p_out, final_state=p_sf,
+            flags=flags, workspace=p_ws, stream=stream), K)
+        pre_plain = timed_ms(step_prefill, K)
+        pre_torch = timed_ms(lambda: torch_prepare(rt), K)
+        dec_raw = timed_ms(lambda: gdn.gdn_decode_step(
+            rdt["q"], rdt["k"], rdt["v"], rdt["alpha"], rdt["beta"], r_state, out=d_out,
+            flags=flags, stream=stream), K)
+        dec_plain = timed_ms(step_decode, K)
+        dec_torch = timed_ms(lambda: torch_prepare(rdt), K)
+        prepared = {"flags": "GDN_QK_L2NORM | GDN_GATE_LOGITS",
+                    "prefill_ms": round(pre_raw, 5), "prefill_plain_ms": round(pre_plain, 5),
+                    "prefill_separate_torch_pass_ms": round(pre_torch, 5),
+                    "decode_ms": round(dec_raw, 5), "decode_plain_ms": round(dec_plain, 5),
+                    "decode_separate_torch_pass_ms": round(dec_torch, 5),
+                    "note": "medians of back-to-back calls; the torch pass is what a caller "
+                            "without the flags would run first"}
+        del rt, rdt, rp, rd, r_state
 
     # K tokens per sequence against a slot pool (speculative verification):
     # timed on its own, after the step, on the same stream
@@ -376,6 +431,8 @@ def main():
     }
     if prefix is not None:
         res["prefill_prefix_states"] = prefix
+    if prepared is not None:
+        res["prepared_inputs"] = prepared
     if multi is not None:
         res["decode_multi"] = multi
     if ceilings is not None:
