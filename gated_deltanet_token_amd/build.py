@@ -9,7 +9,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn.so")
-SOURCES = ["gdn_api.hip", "gdn_prefill.hip", "gdn_decode.hip"]
+SOURCES = ["gdn_api.hip", "gdn_prefill.hip", "gdn_decode.hip", "gdn_segment.hip"]
 ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
 
 

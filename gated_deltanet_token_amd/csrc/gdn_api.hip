@@ -150,7 +150,12 @@ size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t tokens, int32_t Hk, 
     if (device_cus(&cus) != GDN_OK) return 0;
     if (!gdn::prefill_wants_workspace((int64_t)num_seqs * Hv, cus)) return 0;
     const int64_t slots = gdn::prefill_ws_slots(num_seqs, total, packed ? 0 : tokens, packed != 0);
-    return gdn::prefill_ws_bytes(slots, Hv, dtype == GDN_BF16 ? 1 : 0);
+    const size_t two_pass = gdn::prefill_ws_bytes(slots, Hv, dtype == GDN_BF16 ? 1 : 0);
+    // few long sequences: the segmented path, whose layout also holds the above
+    const size_t seg = packed ? 0
+                              : gdn::prefill_seg_ws_bytes(num_seqs, tokens, Hv, Dk,
+                                                          dtype == GDN_BF16 ? 1 : 0, cus);
+    return seg > two_pass ? seg : two_pass;
 }
 
 gdn_status_t gdn_prefill_chunked(const void *q, const void *k, const void *v, const float *alpha,
@@ -178,7 +183,7 @@ gdn_status_t gdn_prefill_chunked(const void *q, const void *k, const void *v, co
     gdn::PrefillParams p{q,  k,     v,     alpha,         beta,
                          initial_state, out, final_state, nullptr, T,
                          B,  Hk,    Hv,    scale,         prefix_rows ? prefix_states : nullptr,
-                         prefix_interval, flags};
+                         prefix_interval, flags, (int64_t)Hv * Dv, false, false};
     const int64_t slots = gdn::prefill_ws_slots(B, tokens, T, false);
     const hipError_t e = gdn::launch_prefill(p, dtype == GDN_BF16 ? 1 : 0, Dk, cus, workspace,
                                              workspace_bytes, slots, stream);
@@ -211,7 +216,7 @@ gdn_status_t gdn_varlen_prefill(const void *q, const void *k, const void *v, con
     if ((st = device_cus(&cus)) != GDN_OK) return st;
     gdn::PrefillParams p{q,          k,  v,  alpha, beta, initial_state, out, final_state,
                          cu_seqlens, 0,  N,  Hk,    Hv,   scale,         prefix_states,
-                         prefix_interval, flags};
+                         prefix_interval, flags, (int64_t)Hv * Dv, false, false};
     const int64_t slots = gdn::prefill_ws_slots(N, total_T, 0, true);
     const hipError_t e = gdn::launch_prefill(p, dtype == GDN_BF16 ? 1 : 0, Dk, cus, workspace,
                                              workspace_bytes, slots, stream);

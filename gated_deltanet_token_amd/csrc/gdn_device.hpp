@@ -139,6 +139,14 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
+// Four consecutive entries (row, col0 .. col0 + 3) of the identity matrix.
+__device__ __forceinline__ f32x4 eye4(int row, int col0) {
+    f32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = row == col0 + e ? 1.f : 0.f;
+    return r;
+}
+
 // Gates from logits: log(alpha) = -softplus(a) (stable for either sign of
 // a), beta = sigmoid(b).
 __device__ __forceinline__ float neg_softplus(float a) {

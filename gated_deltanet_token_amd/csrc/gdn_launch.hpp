@@ -19,6 +19,11 @@ struct PrefillParams {
     float *prefix;         // block-aligned prefix states, or nullptr
     int32_t prefix_every;  // block length in chunks (>= 1 when prefix is set)
     uint32_t flags;        // input preparation (kQkL2Norm | kGateLogits)
+    int64_t v_stride;      // elements between consecutive tokens of v (Hv * Dv; 0: one row
+                           // serves every token)
+    bool s0_identity;      // initial state I (Dv == Dk) instead of s0 / zeros
+    bool records_ready;    // two-pass: the workspace already holds this batch's per-chunk
+                           // factors (they depend on q, k, alpha, beta only)
 };
 
 // Input preparation flags (the ABI's GDN_QK_L2NORM, GDN_GATE_LOGITS).
@@ -59,6 +64,18 @@ hipError_t launch_prefill(const PrefillParams &p, int dtype, int D, int num_cus,
 int64_t prefill_ws_slots(int64_t nseq, int64_t total_tokens, int64_t seq_len, bool packed);
 size_t prefill_ws_bytes(int64_t slots, int Hv, int dtype);
 bool prefill_wants_workspace(int64_t chains, int num_cus);
+// Workspace bytes of the segmented prefill (dense bf16 batches with few
+// chains), or 0 when it does not apply to these shapes.
+size_t prefill_seg_ws_bytes(int64_t nseq, int64_t T, int Hv, int D, int dtype, int num_cus);
+
+hipError_t launch_segment_setup(int32_t *cu, int32_t B, int32_t P, int64_t T, int64_t L,
+                                __bf16 *zero_v, int32_t nzero, hipStream_t stream);
+hipError_t launch_segment_scan(const float *s0, const float *n_end, const float *m_end,
+                               float *s_start, float *s_final, int32_t B, int32_t P, int32_t Hv,
+                               int D, hipStream_t stream);
+hipError_t launch_segment_correct(__bf16 *out, const __bf16 *o_id, const float *s_start,
+                                  const int32_t *cu, int32_t B, int32_t P, int32_t Hv,
+                                  int64_t seg_len, int32_t first_seg, int D, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams &p, int dtype, int D, hipStream_t stream);
 hipError_t launch_decode_multi(const DecodeMultiParams &p, int dtype, int D, hipStream_t stream);
 

@@ -275,7 +275,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p, int n
     const int64_t sVO = (int64_t)p.Hv * D;
     const DT *qh = reinterpret_cast<const DT *>(p.q) + tok0 * sQK + (int64_t)grp * D;
     const DT *kh = reinterpret_cast<const DT *>(p.k) + tok0 * sQK + (int64_t)grp * D;
-    const DT *vh = reinterpret_cast<const DT *>(p.v) + tok0 * sVO + (int64_t)h * D + dv0;
+    const int64_t sVt = p.v_stride;
+    const DT *vh = reinterpret_cast<const DT *>(p.v) + tok0 * sVt + (int64_t)h * D + dv0;
     DT *oh = reinterpret_cast<DT *>(p.out) + tok0 * sVO + (int64_t)h * D + dv0 + wdv;
     const float *ah = p.alpha + tok0 * p.Hv + h;
     const float *bh = p.beta + tok0 * p.Hv + h;
@@ -291,9 +292,10 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p, int n
         for (int a = 0; a < NKT; ++a)
 #pragma unroll
             for (int b = 0; b < NB; ++b)
-                st[a][b] = s0 ? *reinterpret_cast<const f32x4 *>(
-                                    s0 + (int64_t)(dv0 + wdv + 16 * b + c16) * D + 16 * a + 4 * g4)
-                              : zero4();
+                st[a][b] = p.s0_identity ? eye4(dv0 + wdv + 16 * b + c16, 16 * a + 4 * g4)
+                           : s0 ? *reinterpret_cast<const f32x4 *>(
+                                      s0 + (int64_t)(dv0 + wdv + 16 * b + c16) * D + 16 * a + 4 * g4)
+                                : zero4();
     }
 
     Stager<DT, D, NTH, Cf::DVS> sg;
@@ -302,7 +304,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p, int n
     auto load_chunk = [&](int64_t c) {
         const int64_t t0 = c * kC;
         const int lenc = (int)((len - t0) < kC ? (len - t0) : kC);
-        sg.load(kh, qh, vh, t0, lenc, sQK, sVO, tid);
+        sg.load(kh, qh, vh, t0, lenc, sQK, sVt, tid);
         if (wave == 0) {
             const int rr = lane < lenc ? lane : lenc - 1;
             rAl = ah[(t0 + rr) * p.Hv];
@@ -689,7 +691,8 @@ __global__ __launch_bounds__(256) void chain_kernel(PrefillParams p, const unsig
     const int64_t sVO = (int64_t)p.Hv * D;
     const DT *qh = reinterpret_cast<const DT *>(p.q) + tok0 * sQK + (int64_t)grp * D;
     const DT *kh = reinterpret_cast<const DT *>(p.k) + tok0 * sQK + (int64_t)grp * D;
-    const DT *vh = reinterpret_cast<const DT *>(p.v) + tok0 * sVO + (int64_t)h * D + dv0;
+    const int64_t sVt = p.v_stride;
+    const DT *vh = reinterpret_cast<const DT *>(p.v) + tok0 * sVt + (int64_t)h * D + dv0;
     DT *oh = reinterpret_cast<DT *>(p.out) + tok0 * sVO + (int64_t)h * D + dv0 + wdv;
 
     f32x4 st[NKT][NB];
@@ -699,9 +702,10 @@ __global__ __launch_bounds__(256) void chain_kernel(PrefillParams p, const unsig
         for (int a = 0; a < NKT; ++a)
 #pragma unroll
             for (int b = 0; b < NB; ++b)
-                st[a][b] = s0 ? *reinterpret_cast<const f32x4 *>(
-                                    s0 + (int64_t)(dv0 + wdv + 16 * b + c16) * D + 16 * a + 4 * g4)
-                              : zero4();
+                st[a][b] = p.s0_identity ? eye4(dv0 + wdv + 16 * b + c16, 16 * a + 4 * g4)
+                           : s0 ? *reinterpret_cast<const f32x4 *>(
+                                      s0 + (int64_t)(dv0 + wdv + 16 * b + c16) * D + 16 * a + 4 * g4)
+                                : zero4();
     }
 
     Stager<DT, D, 256, Cf::DVS> sg;
@@ -710,7 +714,7 @@ __global__ __launch_bounds__(256) void chain_kernel(PrefillParams p, const unsig
     auto load_chunk = [&](int64_t c) {
         const int64_t t0 = c * kC;
         const int lenc = (int)((len - t0) < kC ? (len - t0) : kC);
-        sg.load(kh, qh, vh, t0, lenc, sQK, sVO, tid);
+        sg.load(kh, qh, vh, t0, lenc, sQK, sVt, tid);
         const unsigned char *rec = ws + ((base + c) * p.Hv + h) * (int64_t)WSB;
 #pragma unroll
         for (int i = 0; i < Cf::NTP; ++i) {
@@ -896,9 +900,10 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
             const float *s0 = p.s0 ? p.s0 + ((int64_t)n * p.Hv + h) * D * D : nullptr;
 #pragma unroll
             for (int a = 0; a < NKT; ++a)
-                st[a][0] = s0 ? *reinterpret_cast<const f32x4 *>(
-                                    s0 + (int64_t)(dv0 + wdv + c16) * D + 16 * a + 4 * g4)
-                              : zero4();
+                st[a][0] = p.s0_identity ? eye4(dv0 + wdv + c16, 16 * a + 4 * g4)
+                           : s0 ? *reinterpret_cast<const f32x4 *>(
+                                      s0 + (int64_t)(dv0 + wdv + c16) * D + 16 * a + 4 * g4)
+                                : zero4();
             if (lane == 0) *flag = 0;
             PrefixRows pre(p, n, len);
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): initial state; see prefill_kernel
@@ -969,8 +974,8 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
         const unsigned char *qb = reinterpret_cast<const unsigned char *>(p.q) +
                                   (tok0 * sQK + (int64_t)grp * D) * 2;
         const unsigned char *vhb = reinterpret_cast<const unsigned char *>(p.v) +
-                                   (tok0 * sVO + (int64_t)h * D) * 2;
-        const int64_t rowqk = sQK * 2, rowv = sVO * 2;
+                                   (tok0 * p.v_stride + (int64_t)h * D) * 2;
+        const int64_t rowqk = sQK * 2, rowv = p.v_stride * 2;
         uint32_t pend[NL], acc = 0;
 #pragma unroll
         for (int j = 0; j < NL; ++j) pend[j] = 0;
@@ -1031,8 +1036,8 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
     const unsigned char *kb = reinterpret_cast<const unsigned char *>(p.k) +
                               (tok0 * sQK + (int64_t)grp * D) * 2;
     const unsigned char *vb = reinterpret_cast<const unsigned char *>(p.v) +
-                              (tok0 * sVO + (int64_t)h * D + dv0) * 2;
-    const int64_t rowqk = sQK * 2, rowv = sVO * 2;
+                              (tok0 * p.v_stride + (int64_t)h * D + dv0) * 2;
+    const int64_t rowqk = sQK * 2, rowv = p.v_stride * 2;
     // one 1 KiB block: slots 64 b .. 64 b + 63 of a swizzled region with rows
     // of ROWB bytes; LDS slot s of row r receives data piece s ^ swz_f(r),
     // src(row, piece) gives its address
@@ -1109,6 +1114,7 @@ static hipError_t launch_fused(const PrefillParams &p, int nsplit, hipStream_t s
 template <typename DT, int D, bool FRAG>
 static hipError_t launch_prep(const PrefillParams &p, unsigned char *ws, int64_t nprep,
                               hipStream_t stream) {
+    if (p.records_ready) return hipSuccess;
     if (p.flags & kQkL2Norm)
         hipLaunchKernelGGL((prep_kernel<DT, D, FRAG, true>), dim3((unsigned)nprep), dim3(256), 0,
                            stream, p, ws, nprep % 8 == 0 ? 1 : 0);
@@ -1190,8 +1196,127 @@ static int pow2_floor(int v) {
     return r;
 }
 
+// ----------------------------------------------------------------------------
+// segmented prefill (gdn_segment.hip): few long sequences, split into P
+// segments of L tokens (L a multiple of 64) that run as a packed batch.
+
+struct SegPlan {
+    int32_t P = 0;  // segments per sequence (0: not segmented)
+    int64_t L = 0;  // tokens per segment (the last may be shorter)
+};
+
+// Segments when the plain two-pass path would leave most CUs idle: at most
+// num_cus / 8 (sequence, value head) chains and at least 4 chunks each. P is
+// chosen so that the P-fold batch about fills the chip at 4 value-column
+// slices per chain, with at least 2 chunks per segment. GDN_PREFILL_SEGMENTS
+// = 0 disables it, = P forces P segments (any dense bf16 batch, for tests).
+static SegPlan seg_plan(int64_t nseq, int64_t T, int Hv, int D, int dtype, int num_cus) {
+    SegPlan sp;
+    if (dtype != 1 || (D != 64 && D != 128) || T <= 0) return sp;
+    const int64_t chains = nseq * Hv;
+    const int64_t nchunks = (T + kC - 1) / kC;
+    const int forced = env_int("GDN_PREFILL_SEGMENTS", -1);
+    int64_t P;
+    if (forced == 0) return sp;
+    if (forced > 0) {
+        P = forced;
+    } else {
+        if (chains * 8 > num_cus || nchunks < 8) return sp;
+        P = (int64_t)num_cus / 4 / chains;
+        if (P > nchunks / 2) P = nchunks / 2;
+    }
+    if (P < 2 || P > nchunks) return sp;
+    const int64_t lc = (nchunks + P - 1) / P;  // chunks per segment
+    sp.P = (int32_t)((nchunks + lc - 1) / lc);
+    sp.L = lc * kC;
+    if (sp.P < 2 || nseq * sp.P > 0x7FFFFFFF / 8) sp.P = 0;
+    return sp;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct SegLayout {
+    size_t rec, cu, zero_v, n_end, m_end, s_start, o_id, total;
+};
+
+static SegLayout seg_layout(int64_t nseq, int64_t T, int Hv, int D, const SegPlan &sp) {
+    SegLayout l{};
+    const int64_t nsegs = nseq * sp.P;
+    const size_t states = (size_t)nsegs * Hv * D * D * 4;
+    size_t off = 0;
+    l.rec = off;
+    off += align256(prefill_ws_bytes(prefill_ws_slots(nsegs, nseq * T, 0, true), Hv, 1));
+    l.cu = off;
+    off += align256((size_t)(nsegs + 1) * 4);
+    l.zero_v = off;
+    off += align256((size_t)Hv * D * 2);
+    l.n_end = off;
+    off += align256(states);
+    l.m_end = off;
+    off += align256(states);
+    l.s_start = off;
+    off += align256(states);
+    l.o_id = off;
+    off += align256((size_t)nseq * T * Hv * D * 2);
+    l.total = off;
+    return l;
+}
+
+size_t prefill_seg_ws_bytes(int64_t nseq, int64_t T, int Hv, int D, int dtype, int num_cus) {
+    const SegPlan sp = seg_plan(nseq, T, Hv, D, dtype, num_cus);
+    return sp.P ? seg_layout(nseq, T, Hv, D, sp).total : 0;
+}
+
+static hipError_t launch_segmented(const PrefillParams &p, int D, int num_cus, unsigned char *ws,
+                                   const SegPlan &sp, hipStream_t stream) {
+    const int64_t B = p.nseq, T = p.seq_len;
+    const int32_t nsegs = (int32_t)(B * sp.P);
+    const SegLayout l = seg_layout(B, T, p.Hv, D, sp);
+    int32_t *cu = reinterpret_cast<int32_t *>(ws + l.cu);
+    __bf16 *zero_v = reinterpret_cast<__bf16 *>(ws + l.zero_v);
+    float *n_end = reinterpret_cast<float *>(ws + l.n_end);
+    float *m_end = reinterpret_cast<float *>(ws + l.m_end);
+    float *s_start = reinterpret_cast<float *>(ws + l.s_start);
+    __bf16 *o_id = reinterpret_cast<__bf16 *>(ws + l.o_id);
+    hipError_t e = launch_segment_setup(cu, (int32_t)B, sp.P, T, sp.L, zero_v, p.Hv * D, stream);
+    if (e != hipSuccess) return e;
+    const int64_t slots = prefill_ws_slots(nsegs, B * T, 0, true);
+    const size_t rec_bytes = prefill_ws_bytes(slots, p.Hv, 1);
+    // 1. every segment from a zero state: outputs o^0 (into out), end states N_j
+    PrefillParams pz = p;
+    pz.cu_seqlens = cu;
+    pz.nseq = nsegs;
+    pz.seq_len = 0;
+    pz.s0 = nullptr;
+    pz.s_final = n_end;
+    e = launch_prefill(pz, 1, D, num_cus, ws + l.rec, rec_bytes, slots, stream);
+    if (e != hipSuccess) return e;
+    // 2. every segment from the identity with v = 0: outputs M_{->t} q_t, end states M_j
+    PrefillParams pi = pz;
+    pi.v = zero_v;
+    pi.v_stride = 0;
+    pi.s0_identity = true;
+    pi.records_ready = true;  // same q, k, alpha, beta and slots as step 1
+    pi.out = o_id;
+    pi.s_final = m_end;
+    e = launch_prefill(pi, 1, D, num_cus, ws + l.rec, rec_bytes, slots, stream);
+    if (e != hipSuccess) return e;
+    // 3. the scan over segments; 4. the corrections (segment 0 only from a
+    // nonzero initial state)
+    e = launch_segment_scan(p.s0, n_end, m_end, s_start, p.s_final, (int32_t)B, sp.P, p.Hv, D,
+                            stream);
+    if (e != hipSuccess) return e;
+    return launch_segment_correct(static_cast<__bf16 *>(p.out), o_id, s_start, cu, (int32_t)B,
+                                  sp.P, p.Hv, sp.L, p.s0 ? 0 : 1, D, stream);
+}
+
 hipError_t launch_prefill(const PrefillParams &p, int dtype, int D, int num_cus, void *ws,
                           size_t ws_bytes, int64_t nslots, hipStream_t stream) {
+    if (!p.cu_seqlens && !p.prefix && !p.s0_identity && ws) {
+        const SegPlan sp = seg_plan(p.nseq, p.seq_len, p.Hv, D, dtype, num_cus);
+        if (sp.P && ws_bytes >= seg_layout(p.nseq, p.seq_len, p.Hv, D, sp).total)
+            return launch_segmented(p, D, num_cus, static_cast<unsigned char *>(ws), sp, stream);
+    }
     const int64_t chains = (int64_t)p.nseq * p.Hv;
     const bool split = ws != nullptr && nslots > 0 &&
                        ws_bytes >= prefill_ws_bytes(nslots, p.Hv, dtype) &&

@@ -1,0 +1,289 @@
+// gdn_segment.hip -- prefill of few long sequences split into segments that
+// run in parallel (gfx950).
+//
+// The state after a chunk is an affine function of the state before it:
+// S' = S M_c + N_c, with M_c in R^{Dk x Dk} (gamma_C I minus a rank-64 term
+// built from the chunk's keys) and N_c the chunk's contribution from zero.
+// Composing the chunks of a segment gives the same form, S_end = S_start M + N,
+// and every output inside the segment is o_t = S_start (M_{->t} q_t) + o^0_t,
+// where M_{->t} composes the segment up to token t and o^0_t is the output
+// the segment gives from a zero state. So a sequence of P segments runs as
+//   1. every segment from a zero state (outputs o^0, end states N_j);
+//   2. every segment from the identity state with v = 0 (outputs o'_t =
+//      M_{->t} q_t, end states M_j): the same chunked kernels, whose state
+//      then holds the composed map;
+//   3. the scan S_0 = initial state, S_{j+1} = S_j M_j + N_j, sequential over
+//      the segments only (seg_scan_kernel);
+//   4. o_t += S_j o'_t for the tokens of segment j (seg_correct_kernel).
+// Steps 1 and 2 expose P times more chains to the chip than one pass over
+// the whole sequence, at twice its chunk work. The same affine form is what
+// lets a sequence be split across GPUs (context parallelism); here the
+// segments stay on one GPU.
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+
+// Segment bounds as packed-sequence offsets: segment j of sequence b covers
+// tokens [b T + j L, min(b T + (j + 1) L, (b + 1) T)), entry b P + j; and a
+// zero row of v (Hv * D elements) for step 2.
+__global__ __launch_bounds__(256) void seg_setup_kernel(int32_t *cu, int32_t B, int32_t P,
+                                                        int64_t T, int64_t L, __bf16 *zero_v,
+                                                        int32_t nzero) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i <= B * P) {
+        const int b = i / P, j = i - b * P;
+        const int64_t start = (int64_t)b * T + (int64_t)j * L;
+        const int64_t end_b = (int64_t)(b + 1) * T;
+        cu[i] = (int32_t)(i == B * P ? (int64_t)B * T : (start < end_b ? start : end_b));
+    }
+    for (int e = i; e < nzero; e += gridDim.x * 256) zero_v[e] = (__bf16)0.f;
+}
+
+// The scan over segments for 16 state rows of one (sequence, value head):
+//   S_0 = initial state (or 0), S_{j+1} = S_j M_j + N_j, j = 0 .. P-1,
+// writing S_j (the start state of segment j) for the corrections and S_P as
+// the final state. fp32 MFMA (16x16x4): wave w forms columns
+// [w D/4, (w + 1) D/4) of the product. The k order inside each 16-deep block
+// is permuted (MFMA step 4 q + e takes k = 16 q + 4 g4 + e on lane group g4),
+// so a lane's A operands are four consecutive entries of S_j's row (one
+// 16-byte LDS read per four steps) and its B operands are the entries of
+// M_j's column at those k: each wave loads exactly its own B operands from
+// memory into registers, one segment ahead, and no copy of M_j goes through
+// LDS. Two accumulators per tile halve the dependent MFMA chain.
+template <int D>
+__global__ __launch_bounds__(256) void seg_scan_kernel(const float *s0, const float *n_end,
+                                                       const float *m_end, float *s_start,
+                                                       float *s_final, int32_t B, int32_t P,
+                                                       int32_t Hv) {
+    constexpr int RS = 16;        // rows per workgroup
+    constexpr int NT = D / 64;    // 16-column tiles per wave
+    constexpr int NQ = D / 16;    // 16-deep k blocks
+    constexpr int PS = D + 4;     // padded LDS row of S: the 16 rows of an A read differ in bank
+    __shared__ __attribute__((aligned(16))) float sS[RS * PS];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g4 = lane >> 4, c16 = lane & 15;
+    const int slices = D / RS;
+    const int bh = blockIdx.x / slices, slice = blockIdx.x - bh * slices;
+    const int b = bh / Hv, h = bh - b * Hv;
+    const size_t DD = (size_t)D * D;
+    auto state_off = [&](int seg) {  // of state (b, seg, h) in [B*P, Hv, D, D]
+        return (((size_t)b * P + seg) * Hv + h) * DD;
+    };
+    const int row0 = slice * RS;
+
+    // S_0 rows -> LDS and to the corrections (segment 0)
+    {
+        const float *src = s0 ? s0 + ((size_t)b * Hv + h) * DD : nullptr;
+        for (int i = tid; i < RS * D; i += 256) {
+            const float x = src ? src[(size_t)row0 * D + i] : 0.f;
+            sS[(i / D) * PS + i % D] = x;
+            s_start[state_off(0) + (size_t)row0 * D + i] = x;
+        }
+    }
+    // B operands of segment `seg`: breg[nt][q][e] = M[16 q + 4 g4 + e][col(nt)]
+    float breg[NT][NQ][4], nreg[NT][4];
+    auto load_ops = [&](int seg) {
+        const float *m = m_end + state_off(seg);
+        const float *n = n_end + state_off(seg) + (size_t)row0 * D;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int col = (wave * NT + nt) * 16 + c16;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    breg[nt][q][e] = m[(size_t)(16 * q + 4 * g4 + e) * D + col];
+            // N in C layout: rows 4 g4 .. 4 g4 + 3 of column col
+#pragma unroll
+            for (int i = 0; i < 4; ++i) nreg[nt][i] = n[(size_t)(4 * g4 + i) * D + col];
+        }
+    };
+    load_ops(0);
+    f32x4 acc[NT];
+    for (int j = 0; j < P; ++j) {
+        __syncthreads();  // S_j is in LDS
+        float bcur[NT][NQ][4];
+        f32x4 acc2[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            acc[nt] = f32x4{nreg[nt][0], nreg[nt][1], nreg[nt][2], nreg[nt][3]};
+            acc2[nt] = zero4();
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bcur[nt][q][e] = breg[nt][q][e];
+        }
+        if (j + 1 < P) load_ops(j + 1);  // arrive while this step computes
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(sS + c16 * PS + 16 * q + 4 * g4);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (q & 1)
+                        acc2[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], bcur[nt][q][e],
+                                                                        acc2[nt], 0, 0, 0);
+                    else
+                        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], bcur[nt][q][e],
+                                                                       acc[nt], 0, 0, 0);
+                }
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt] += acc2[nt];
+        __syncthreads();  // every wave is done reading S_j
+        // S_{j+1} -> LDS, and to the corrections of segment j + 1
+        float *dst = j + 1 < P ? s_start + state_off(j + 1) + (size_t)row0 * D : nullptr;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int col = (wave * NT + nt) * 16 + c16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sS[(4 * g4 + i) * PS + col] = acc[nt][i];
+                if (dst) dst[(size_t)(4 * g4 + i) * D + col] = acc[nt][i];
+            }
+        }
+    }
+    if (s_final) {
+        float *out = s_final + ((size_t)b * Hv + h) * DD + (size_t)row0 * D;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int col = (wave * NT + nt) * 16 + c16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) out[(size_t)(4 * g4 + i) * D + col] = acc[nt][i];
+        }
+    }
+}
+
+// o_t += S_j o'_t for the tokens of segment j (bf16 out and o', fp32 S_j):
+// one workgroup per (sequence, segment, value head, group of `tiles` 64-token
+// tiles: more when there are many, so that staging S_j is amortised).
+// S_j^T is staged in LDS as bf16 MFMA fragments once and reused for the
+// group's tiles; wave w forms rows 16 w .. 16 w + 15 of a tile,
+// all D columns: C[t][n] = sum_k o'[t][k] S_j[n][k].
+template <int D>
+__global__ __launch_bounds__(256) void seg_correct_kernel(__bf16 *out, const __bf16 *o_id,
+                                                          const float *s_start,
+                                                          const int32_t *cu, int32_t B,
+                                                          int32_t P, int32_t Hv, int32_t groups,
+                                                          int32_t first_seg, int32_t tiles) {
+    constexpr int NT = D / 16;     // 16-column tiles
+    constexpr int KS = D / 32;     // k steps of 32
+    const int GT = 64 * tiles;     // tokens per workgroup
+    __shared__ bf16x8 sB[KS * NT * 64];  // fragment (ks, nt), lane l
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g4 = lane >> 4, c16 = lane & 15;
+    int rest = blockIdx.x;
+    const int grp = rest % groups;
+    rest /= groups;
+    const int h = rest % Hv;
+    rest /= Hv;
+    const int seg = rest % (P - first_seg) + first_seg;
+    const int b = rest / (P - first_seg);
+    const int si = b * P + seg;
+    const int64_t t_lo = cu[si], t_hi = cu[si + 1];
+    const int64_t g0 = t_lo + (int64_t)grp * GT;
+    if (g0 >= t_hi) return;  // uniform over the workgroup
+    const float *S = s_start + ((size_t)si * Hv + h) * D * D;
+
+    // B fragments: B[k][n] = S[n][k]; lane (g4, c16) of fragment (ks, nt)
+    // holds n = 16 nt + c16, k = 32 ks + 8 g4 .. + 7
+    for (int f = tid; f < KS * NT * 64; f += 256) {
+        const int l = f & 63, nt = (f >> 6) % NT, ks = (f >> 6) / NT;
+        const int n = 16 * nt + (l & 15), k0 = 32 * ks + 8 * (l >> 4);
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(S + (size_t)n * D + k0);
+        const f32x4 c = *reinterpret_cast<const f32x4 *>(S + (size_t)n * D + k0 + 4);
+        bf16x8 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[e] = (__bf16)a[e];
+            v[4 + e] = (__bf16)c[e];
+        }
+        sB[f] = v;
+    }
+    __syncthreads();
+
+    const int64_t sO = (int64_t)Hv * D;
+    for (int tile = 0; tile < tiles; ++tile) {
+        const int64_t t0 = g0 + 64 * tile + 16 * wave;  // this wave's first row
+        if (t0 >= t_hi) break;                          // uniform over the wave
+        const int64_t ta = t0 + c16;                    // A row of this lane
+        const bool ok_a = ta < t_hi;
+        f32x4 acc[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            bf16x8 a;
+            if (ok_a)
+                a = *reinterpret_cast<const bf16x8 *>(o_id + ta * sO + (int64_t)h * D + 32 * ks +
+                                                      8 * g4);
+            else
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a[e] = (__bf16)0.f;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) acc[nt] = mma(a, sB[(ks * NT + nt) * 64 + lane], acc[nt]);
+        }
+        // C layout: lane holds rows 4 g4 .. 4 g4 + 3 of column c16 of each tile
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t t = t0 + 4 * g4 + i;
+            if (t < t_hi) {
+                __bf16 *o = out + t * sO + (int64_t)h * D + c16;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    o[16 * nt] = (__bf16)((float)o[16 * nt] + acc[nt][i]);
+            }
+        }
+    }
+}
+
+hipError_t launch_segment_setup(int32_t *cu, int32_t B, int32_t P, int64_t T, int64_t L,
+                                __bf16 *zero_v, int32_t nzero, hipStream_t stream) {
+    const int n = B * P + 1 > nzero ? B * P + 1 : nzero;
+    hipLaunchKernelGGL(seg_setup_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                       cu, B, P, T, L, zero_v, nzero);
+    return hipGetLastError();
+}
+
+hipError_t launch_segment_scan(const float *s0, const float *n_end, const float *m_end,
+                               float *s_start, float *s_final, int32_t B, int32_t P, int32_t Hv,
+                               int D, hipStream_t stream) {
+    const unsigned grid = (unsigned)(B * Hv * (D / 16));
+    if (D == 128)
+        hipLaunchKernelGGL(seg_scan_kernel<128>, dim3(grid), dim3(256), 0, stream, s0, n_end,
+                           m_end, s_start, s_final, B, P, Hv);
+    else if (D == 64)
+        hipLaunchKernelGGL(seg_scan_kernel<64>, dim3(grid), dim3(256), 0, stream, s0, n_end,
+                           m_end, s_start, s_final, B, P, Hv);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_segment_correct(__bf16 *out, const __bf16 *o_id, const float *s_start,
+                                  const int32_t *cu, int32_t B, int32_t P, int32_t Hv,
+                                  int64_t seg_len, int32_t first_seg, int D, hipStream_t stream) {
+    // 64-token tiles per workgroup: 1 while that leaves under ~1024
+    // workgroups, up to 8 for long segments
+    const int64_t seg_tiles = (seg_len + 63) / 64;
+    const int64_t all_tiles = (int64_t)B * (P - first_seg) * Hv * seg_tiles;
+    int32_t tiles = (int32_t)(all_tiles / 1024);
+    tiles = tiles < 1 ? 1 : tiles > 8 ? 8 : tiles;
+    const int32_t groups = (int32_t)((seg_tiles + tiles - 1) / tiles);
+    const int64_t grid = (int64_t)B * (P - first_seg) * Hv * groups;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (D == 128)
+        hipLaunchKernelGGL(seg_correct_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream,
+                           out, o_id, s_start, cu, B, P, Hv, groups, first_seg, tiles);
+    else if (D == 64)
+        hipLaunchKernelGGL(seg_correct_kernel<64>, dim3((unsigned)grid), dim3(256), 0, stream,
+                           out, o_id, s_start, cu, B, P, Hv, groups, first_seg, tiles);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -102,6 +102,13 @@ WORKLOADS = {
         len_range=(1024, 32768), init_state=True,
         description="varlen packed prefill: 64 sequences, lengths U[1024,32768], "
                     "layer head shapes, initial states 0.1*N(0,1)"),
+    "layer_prefill_4k_tp8": Workload(
+        "layer_prefill_4k_tp8", "prefill", 2, 6, 128, "bf16", 1006, B=1, T=4096,
+        description="one GPU's share of the layer prefill at 8-way head-group sharding: "
+                    "B=1, T=4096, 2 q/k heads, 6 v heads, d=128, zero initial state"),
+    "long_prefill_256k_tp8": Workload(
+        "long_prefill_256k_tp8", "prefill", 2, 6, 128, "bf16", 1007, B=1, T=262144,
+        description="the long-context prefill's share at 8-way head-group sharding"),
 }
 
 

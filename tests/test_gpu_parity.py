@@ -655,6 +655,88 @@ def test_layer_prefill_4k_prepared_inputs(gdn):
     check(from_torch(out), from_torch(sf), o_ref, S_ref, "bf16", f"{w.name} prepared inputs")
 
 
+# ------------------------------------------------- segmented prefill (few long sequences)
+SEG_CASES = [
+    # B, T, Hk, Hv, D, segments, init, flags, inner path, alpha shift
+    (1, 450, 1, 2, 128, "3", True, 0, "auto", 2.0),
+    (2, 700, 2, 4, 128, "2", True, 0, "auto", 2.0),
+    (1, 1000, 1, 3, 64, "5", False, 0, "auto", 2.0),
+    (1, 640, 2, 6, 128, "4", True, QK | GL, "auto", 2.0),
+    (1, 513, 1, 2, 128, "8", True, 0, "fused", 2.0),
+    # slow decay (alpha ~ 0.993): the state carried across segments matters,
+    # so the segment maps, their scan and the corrections carry the result
+    (1, 1300, 1, 2, 128, "6", True, 0, "auto", -5.0),
+    (2, 777, 2, 4, 128, "3", False, 0, "auto", -5.0),
+    (1, 900, 1, 3, 64, "4", True, 0, "auto", -5.0),
+    (1, 1024, 2, 6, 128, "8", True, QK | GL, "auto", -5.0),
+    (1, 700, 1, 2, 128, "5", True, 0, "fused", -5.0),
+]
+
+
+@pytest.mark.parametrize("B,T,Hk,Hv,D,segs,init,flags,inner,ashift", SEG_CASES)
+def test_segmented_prefill(gdn, monkeypatch, B, T, Hk, Hv, D, segs, init, flags, inner, ashift):
+    """Segments forced: every segment from zero and from the identity, the
+    scan of the segment maps and the corrections, against the oracle."""
+    monkeypatch.setenv("GDN_PREFILL_SEGMENTS", segs)
+    if inner != "auto":
+        monkeypatch.setenv("GDN_PREFILL_PATH", inner)
+    gen = lambda raw: small_prefill(B, T, Hk, Hv, D, "bf16", seed=170 + T, init_state=init,
+                                    raw=raw, alpha_shift=ashift)
+    d = _prepared_inputs(gen, flags) if flags else gen(False)
+    q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
+    s0 = to_torch(d["S0"], DEV) if init else None
+    n = gdn.gdn_prefill_workspace_size(B, T, Hk, Hv, D, D, gdn.GDN_BF16, 0)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
+    out, sf = gdn.gdn_prefill_chunked(q, k, v, a, b, s0, flags=flags, workspace=ws)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                  d["S0"] if init else None, flags=flags)
+    check(from_torch(out), from_torch(sf), o_ref, S_ref, "bf16",
+          f"segmented P={segs} B{B} T{T} Hv{Hv} D{D} init={init} flags={flags} ({inner}) "
+          f"alpha shift {ashift}")
+
+
+def test_layer_prefill_4k_tp8_segmented(gdn, monkeypatch):
+    """The per-GPU share of the layer at 8-way head-group sharding: few
+    enough chains that the segmented path is chosen by itself; its result
+    matches the oracle, as does the unsegmented path's."""
+    w = WORKLOADS["layer_prefill_4k_tp8"]
+    d = generate(w)
+    n_seg = gdn.gdn_prefill_workspace_size(1, w.T, w.Hk, w.Hv, w.D, w.D, gdn.GDN_BF16, 0)
+    monkeypatch.setenv("GDN_PREFILL_SEGMENTS", "0")
+    n_plain = gdn.gdn_prefill_workspace_size(1, w.T, w.Hk, w.Hv, w.D, w.D, gdn.GDN_BF16, 0)
+    assert n_seg > n_plain > 0, (n_seg, n_plain)
+    o_ref, S_ref = oracle.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], None)
+    q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
+    for label in ("unsegmented", "segmented"):
+        if label == "segmented":
+            monkeypatch.delenv("GDN_PREFILL_SEGMENTS")
+        out, sf = gdn.gdn_prefill_chunked(q, k, v, a, b, None)
+        torch.cuda.synchronize()
+        check(from_torch(out), from_torch(sf), o_ref, S_ref, "bf16", f"{w.name} {label}")
+
+
+def test_tp8_shapes_slow_decay_segmented(gdn, monkeypatch):
+    """The TP8 shapes at slow decay and with an initial state, chosen
+    segmentation against the oracle; the two paths round differently, which
+    shows that the segmented one ran."""
+    d = small_prefill(1, 4096, 2, 6, 128, "bf16", seed=180, alpha_shift=-5.0, init_state=True)
+    q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
+    s0 = to_torch(d["S0"], DEV)
+    o_ref, S_ref = oracle.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"])
+    res = {}
+    for label, env in (("unsegmented", "0"), ("segmented", None)):
+        if env is None:
+            monkeypatch.delenv("GDN_PREFILL_SEGMENTS", raising=False)
+        else:
+            monkeypatch.setenv("GDN_PREFILL_SEGMENTS", env)
+        out, sf = gdn.gdn_prefill_chunked(q, k, v, a, b, s0)
+        torch.cuda.synchronize()
+        res[label] = (from_torch(out), from_torch(sf))
+        check(*res[label], o_ref, S_ref, "bf16", f"TP8 shapes slow decay {label}")
+    assert not np.array_equal(res["segmented"][1], res["unsegmented"][1])
+
+
 # ----------------------------------------------------------------- full-size, sampled
 def _chains_check(d, out_t, sf_t, chains, cu, label):
     worst_o = worst_s = 0.0
