@@ -1206,10 +1206,12 @@ struct SegPlan {
 };
 
 // Segments when the plain two-pass path would leave most CUs idle: at most
-// num_cus / 8 (sequence, value head) chains and at least 4 chunks each. P is
-// chosen so that the P-fold batch about fills the chip at 4 value-column
-// slices per chain, with at least 2 chunks per segment. GDN_PREFILL_SEGMENTS
-// = 0 disables it, = P forces P segments (any dense bf16 batch, for tests).
+// num_cus / 8 (sequence, value head) chains and at least 8 chunks each. The
+// two passes cost about 3 us per chunk of a segment and the scan about 2.3 us
+// per segment (measured at D = 128), so P is near sqrt(1.3 * chunks), and at
+// most what fills the chip at 4 value-column slices per chain.
+// GDN_PREFILL_SEGMENTS = 0 disables it, = P forces P segments (any dense
+// bf16 batch, for tests).
 static SegPlan seg_plan(int64_t nseq, int64_t T, int Hv, int D, int dtype, int num_cus) {
     SegPlan sp;
     if (dtype != 1 || (D != 64 && D != 128) || T <= 0) return sp;
@@ -1223,6 +1225,9 @@ static SegPlan seg_plan(int64_t nseq, int64_t T, int Hv, int D, int dtype, int n
     } else {
         if (chains * 8 > num_cus || nchunks < 8) return sp;
         P = (int64_t)num_cus / 4 / chains;
+        int64_t best = 1;
+        while ((best + 1) * (best + 1) <= 13 * nchunks / 10) ++best;  // floor(sqrt(1.3 n))
+        if (P > best) P = best;
         if (P > nchunks / 2) P = nchunks / 2;
     }
     if (P < 2 || P > nchunks) return sp;

@@ -40,6 +40,57 @@ __global__ __launch_bounds__(256) void seg_setup_kernel(int32_t *cu, int32_t B, 
     for (int e = i; e < nzero; e += gridDim.x * 256) zero_v[e] = (__bf16)0.f;
 }
 
+// Operands of one scan step held in registers by a lane: B operands
+// b[nt][q][e] = M_j[16 q + 4 g4 + e][col(nt)] and N_j in C layout.
+template <int NT, int NQ> struct ScanOps {
+    float b[NT][NQ][4];
+    float n[NT][4];
+};
+
+template <int D, int NT, int NQ>
+__device__ __forceinline__ void scan_load(ScanOps<NT, NQ> &o, const float *m, const float *n,
+                                          int wave, int g4, int c16) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int col = (wave * NT + nt) * 16 + c16;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o.b[nt][q][e] = m[(size_t)(16 * q + 4 * g4 + e) * D + col];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o.n[nt][i] = n[(size_t)(4 * g4 + i) * D + col];
+    }
+}
+
+// acc = N_j + S_j M_j for this wave's columns; S_j rows in LDS (pitch PS).
+template <int D, int NT, int NQ, int PS>
+__device__ __forceinline__ void scan_product(const ScanOps<NT, NQ> &o, const float *sS,
+                                             f32x4 (&acc)[NT], int g4, int c16) {
+    f32x4 acc2[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        acc[nt] = f32x4{o.n[nt][0], o.n[nt][1], o.n[nt][2], o.n[nt][3]};
+        acc2[nt] = zero4();
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(sS + c16 * PS + 16 * q + 4 * g4);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (q & 1)
+                    acc2[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], o.b[nt][q][e], acc2[nt],
+                                                                    0, 0, 0);
+                else
+                    acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], o.b[nt][q][e], acc[nt],
+                                                                   0, 0, 0);
+            }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] += acc2[nt];
+}
+
 // The scan over segments for 16 state rows of one (sequence, value head):
 //   S_0 = initial state (or 0), S_{j+1} = S_j M_j + N_j, j = 0 .. P-1,
 // writing S_j (the start state of segment j) for the corrections and S_P as
@@ -49,8 +100,9 @@ __global__ __launch_bounds__(256) void seg_setup_kernel(int32_t *cu, int32_t B, 
 // so a lane's A operands are four consecutive entries of S_j's row (one
 // 16-byte LDS read per four steps) and its B operands are the entries of
 // M_j's column at those k: each wave loads exactly its own B operands from
-// memory into registers, one segment ahead, and no copy of M_j goes through
-// LDS. Two accumulators per tile halve the dependent MFMA chain.
+// memory into registers, two segments ahead (two register sets, used in
+// turn), and no copy of M_j goes through LDS. Two accumulators per tile
+// halve the dependent MFMA chain.
 template <int D>
 __global__ __launch_bounds__(256) void seg_scan_kernel(const float *s0, const float *n_end,
                                                        const float *m_end, float *s_start,
@@ -67,10 +119,9 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(const float *s0, const fl
     const int bh = blockIdx.x / slices, slice = blockIdx.x - bh * slices;
     const int b = bh / Hv, h = bh - b * Hv;
     const size_t DD = (size_t)D * D;
-    auto state_off = [&](int seg) {  // of state (b, seg, h) in [B*P, Hv, D, D]
-        return (((size_t)b * P + seg) * Hv + h) * DD;
-    };
     const int row0 = slice * RS;
+    const size_t base = ((size_t)b * P * Hv + h) * DD;  // state (b, 0, h); + seg * Hv * DD
+    const size_t seg_stride = (size_t)Hv * DD;
 
     // S_0 rows -> LDS and to the corrections (segment 0)
     {
@@ -78,63 +129,26 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(const float *s0, const fl
         for (int i = tid; i < RS * D; i += 256) {
             const float x = src ? src[(size_t)row0 * D + i] : 0.f;
             sS[(i / D) * PS + i % D] = x;
-            s_start[state_off(0) + (size_t)row0 * D + i] = x;
+            s_start[base + (size_t)row0 * D + i] = x;
         }
     }
-    // B operands of segment `seg`: breg[nt][q][e] = M[16 q + 4 g4 + e][col(nt)]
-    float breg[NT][NQ][4], nreg[NT][4];
-    auto load_ops = [&](int seg) {
-        const float *m = m_end + state_off(seg);
-        const float *n = n_end + state_off(seg) + (size_t)row0 * D;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const int col = (wave * NT + nt) * 16 + c16;
-#pragma unroll
-            for (int q = 0; q < NQ; ++q)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    breg[nt][q][e] = m[(size_t)(16 * q + 4 * g4 + e) * D + col];
-            // N in C layout: rows 4 g4 .. 4 g4 + 3 of column col
-#pragma unroll
-            for (int i = 0; i < 4; ++i) nreg[nt][i] = n[(size_t)(4 * g4 + i) * D + col];
-        }
+    ScanOps<NT, NQ> ops[2];
+    auto load = [&](ScanOps<NT, NQ> &o, int seg) {
+        scan_load<D>(o, m_end + base + seg * seg_stride,
+                     n_end + base + seg * seg_stride + (size_t)row0 * D, wave, g4, c16);
     };
-    load_ops(0);
+    load(ops[0], 0);
+    if (P > 1) load(ops[1], 1);
     f32x4 acc[NT];
-    for (int j = 0; j < P; ++j) {
+    // One step: S_{j+1} = N_j + S_j M_j from the operand set o, which is then
+    // refilled with segment j + 2.
+    auto step = [&](ScanOps<NT, NQ> &o, int j) {
         __syncthreads();  // S_j is in LDS
-        float bcur[NT][NQ][4];
-        f32x4 acc2[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            acc[nt] = f32x4{nreg[nt][0], nreg[nt][1], nreg[nt][2], nreg[nt][3]};
-            acc2[nt] = zero4();
-#pragma unroll
-            for (int q = 0; q < NQ; ++q)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) bcur[nt][q][e] = breg[nt][q][e];
-        }
-        if (j + 1 < P) load_ops(j + 1);  // arrive while this step computes
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            const f32x4 a = *reinterpret_cast<const f32x4 *>(sS + c16 * PS + 16 * q + 4 * g4);
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (q & 1)
-                        acc2[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], bcur[nt][q][e],
-                                                                        acc2[nt], 0, 0, 0);
-                    else
-                        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], bcur[nt][q][e],
-                                                                       acc[nt], 0, 0, 0);
-                }
-        }
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt] += acc2[nt];
+        scan_product<D, NT, NQ, PS>(o, sS, acc, g4, c16);
+        if (j + 2 < P) load(o, j + 2);
         __syncthreads();  // every wave is done reading S_j
-        // S_{j+1} -> LDS, and to the corrections of segment j + 1
-        float *dst = j + 1 < P ? s_start + state_off(j + 1) + (size_t)row0 * D : nullptr;
+        float *dst = j + 1 < P ? s_start + base + (j + 1) * seg_stride + (size_t)row0 * D
+                               : nullptr;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const int col = (wave * NT + nt) * 16 + c16;
@@ -144,6 +158,10 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(const float *s0, const fl
                 if (dst) dst[(size_t)(4 * g4 + i) * D + col] = acc[nt][i];
             }
         }
+    };
+    for (int j = 0; j < P; j += 2) {
+        step(ops[0], j);
+        if (j + 1 < P) step(ops[1], j + 1);
     }
     if (s_final) {
         float *out = s_final + ((size_t)b * Hv + h) * DD + (size_t)row0 * D;

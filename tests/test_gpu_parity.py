@@ -476,6 +476,8 @@ PREFIX_DENSE = [
 @pytest.mark.parametrize("path,nsplit,dtype,D,every", PREFIX_DENSE)
 def test_prefill_prefix_states(gdn, monkeypatch, path, nsplit, dtype, D, every):
     monkeypatch.setenv("GDN_PREFILL_PATH", path)
+    # a call with prefix states never segments: compare with the same path
+    monkeypatch.setenv("GDN_PREFILL_SEGMENTS", "0")
     if nsplit != "auto":
         monkeypatch.setenv("GDN_PREFILL_NSPLIT", nsplit)
     B, T, Hk, Hv = 2, 450, 2, 6
