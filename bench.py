@@ -16,7 +16,9 @@ events on the stream the kernels run on; and the fp64 oracle timed on the
 host cores as a CPU baseline. Timed apart from the step: under
 "prefill_prefix_states" the same prefill also writing the state after every
 1024 tokens; under "prepared_inputs" the prefill and decode step from raw
-q, k and gate logits (prepared inside the kernels); and under "decode_multi"
+q, k and gate logits (prepared inside the kernels); under "segmented_prefill"
+the per-GPU share of the layer at 8-way head-group sharding (6 value heads,
+T = 4096 and 262,144) in one pass and split into segments; and under "decode_multi"
 the K-token decode against a slot pool (B=256 sequences verifying K=4 tokens
 each), in tokens/s and HBM GB/s.
 
@@ -124,6 +126,8 @@ def main():
                     help="skip the measured ceilings (library copy and bf16 GEMM)")
     ap.add_argument("--no-prepared", action="store_true",
                     help="skip the prefill / decode from raw inputs (in-kernel preparation)")
+    ap.add_argument("--no-segmented", action="store_true",
+                    help="skip the few-long-sequence prefill (segmented vs one pass)")
     ap.add_argument("--no-multi", action="store_true",
                     help="skip the K-token slot-pool decode measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -301,6 +305,51 @@ def main():
                             "without the flags would run first"}
         del rt, rdt, rp, rd, r_state
 
+    # few long sequences: the per-GPU share of the layer at 8-way head-group
+    # sharding (6 value heads), whole sequence in one pass vs split into
+    # segments that run in parallel
+    segmented = None
+    if not args.no_segmented:
+        segmented = {}
+        for wname, reps in (("layer_prefill_4k_tp8", max(K, 5)), ("long_prefill_256k_tp8", 3)):
+            ws_ = WORKLOADS[wname]
+            dg = generate(ws_)
+            gt = {n: to_torch(dg[n], dev) for n in ("q", "k", "v", "alpha", "beta")}
+            g_out = torch.empty(gt["v"].shape, dtype=gt["q"].dtype, device=dev)
+            g_sf = torch.empty((ws_.B, ws_.Hv, ws_.D, ws_.D), dtype=torch.float32, device=dev)
+            row = {}
+            for label, env in (("unsegmented", "0"), ("segmented", None)):
+                if env is None:
+                    os.environ.pop("GDN_PREFILL_SEGMENTS", None)
+                else:
+                    os.environ["GDN_PREFILL_SEGMENTS"] = env
+                nws = gdn.gdn_prefill_workspace_size(ws_.B, ws_.T, ws_.Hk, ws_.Hv, ws_.D, ws_.D,
+                                                     gt["q"].dtype, False)
+                g_ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+                ms = []
+                for i in range(reps + 1):
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    gdn.gdn_prefill_chunked(gt["q"], gt["k"], gt["v"], gt["alpha"], gt["beta"],
+                                            None, out=g_out, final_state=g_sf, workspace=g_ws,
+                                            stream=stream)
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    if i:
+                        ms.append(e0.elapsed_time(e1))
+                med = float(np.median(ms))
+                tf = ws_.B * ws_.T * prefill_flops_per_token(ws_.Hk, ws_.Hv, ws_.D, ws_.D) / (
+                    med * 1e-3) / 1e12
+                row[label] = {"ms": round(med, 5), "workspace_bytes": nws,
+                              "tokens_per_s": round(ws_.B * ws_.T / (med * 1e-3), 1),
+                              "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+                del g_ws
+            os.environ.pop("GDN_PREFILL_SEGMENTS", None)
+            row["speedup"] = round(row["unsegmented"]["ms"] / row["segmented"]["ms"], 3)
+            segmented[wname] = row
+            del gt, dg, g_out, g_sf
+
     # K tokens per sequence against a slot pool (speculative verification):
     # timed on its own, after the step, on the same stream
     multi = None
@@ -433,6 +482,8 @@ def main():
         res["prefill_prefix_states"] = prefix
     if prepared is not None:
         res["prepared_inputs"] = prepared
+    if segmented is not None:
+        res["segmented_prefill"] = segmented
     if multi is not None:
         res["decode_multi"] = multi
     if ceilings is not None:
