@@ -126,6 +126,8 @@ def main():
                     help="skip the measured ceilings (library copy and bf16 GEMM)")
     ap.add_argument("--no-prepared", action="store_true",
                     help="skip the prefill / decode from raw inputs (in-kernel preparation)")
+    ap.add_argument("--no-prefix", action="store_true",
+                    help="skip the prefill with block-aligned prefix states")
     ap.add_argument("--no-segmented", action="store_true",
                     help="skip the few-long-sequence prefill (segmented vs one pass)")
     ap.add_argument("--no-multi", action="store_true",
@@ -228,7 +230,7 @@ def main():
     # the same prefill emitting block-aligned prefix states (one per 1024
     # tokens): what a prefix cache keeps
     prefix = None
-    if not varlen and wp.T >= 1024:
+    if not varlen and wp.T >= 1024 and not args.no_prefix:
         every = 16
         rows = gdn.prefix_state_rows(wp.B, wp.T, every, False)
         p_pre = torch.empty((rows, wp.Hv, wp.D, wp.D), dtype=torch.float32, device=dev)
