@@ -794,3 +794,53 @@ def test_slow_decay_stress_diagnostic(gdn):
     o, S = gpu_prefill(gdn, d)
     o_ref, S_ref = oracle_prefill(d)
     check(o, S, o_ref, S_ref, "bf16", "slow-decay stress T=4096")
+
+
+# ------------------------------------------------- HIP graph capture
+def test_graph_capture_replays_match_eager(gdn, monkeypatch):
+    """Decode step, K-token decode and prefill (two-pass and segmented)
+    captured in one HIP graph (the calls enqueue kernels only: no
+    allocation, copy or memset), replayed three times with eager work and
+    synchronisations between replays; every replay equals the eager calls
+    bit for bit."""
+    monkeypatch.setenv("GDN_PREFILL_SEGMENTS", "4")  # the small prefill below segments
+    dd = generate_packed(2, 6, 128, "bf16", 190, [1] * 8, init_state=True)
+    dq, dk, dv, da, db = _t(dd, ("q", "k", "v", "alpha", "beta"))
+    dm = multi_decode(4, 3, 2, 6, 128, "bf16", seed=192, plan="pairs")
+    mq, mk, mv, ma, mb = _t(dm, ("q", "k", "v", "alpha", "beta"))
+    src, dst = to_torch(dm["src_slot"], DEV), to_torch(dm["dst_slot"], DEV)
+    dp = small_prefill(1, 700, 2, 6, 128, "bf16", seed=191, init_state=True)
+    pq, pk, pv, pa, pb = _t(dp, ("q", "k", "v", "alpha", "beta"))
+    ps0 = to_torch(dp["S0"], DEV)
+    nws = gdn.gdn_prefill_workspace_size(1, 700, 2, 6, 128, 128, gdn.GDN_BF16, 0)
+
+    def buffers():
+        return dict(state=to_torch(dd["S0"], DEV),
+                    d_out=torch.empty(dv.shape, dtype=torch.bfloat16, device=DEV),
+                    pool=to_torch(dm["pool"], DEV),
+                    m_out=torch.empty(mv.shape, dtype=torch.bfloat16, device=DEV),
+                    p_out=torch.empty(pv.shape, dtype=torch.bfloat16, device=DEV),
+                    p_sf=torch.empty((1, 6, 128, 128), dtype=torch.float32, device=DEV),
+                    ws=torch.empty(nws, dtype=torch.uint8, device=DEV))
+
+    def calls(x):
+        gdn.gdn_decode_step(dq, dk, dv, da, db, x["state"], out=x["d_out"])
+        gdn.gdn_decode_multi(mq, mk, mv, ma, mb, x["pool"], src, dst, out=x["m_out"])
+        gdn.gdn_prefill_chunked(pq, pk, pv, pa, pb, ps0, out=x["p_out"], final_state=x["p_sf"],
+                                workspace=x["ws"])
+
+    xg, xe = buffers(), buffers()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls(xg)
+    torch.cuda.synchronize()
+    for r in range(3):
+        g.replay()
+        calls(xe)
+        torch.cuda.synchronize()
+        for name in ("state", "d_out", "pool", "m_out", "p_out", "p_sf"):
+            assert torch.equal(xg[name], xe[name]), (r, name)
+    o_ref, S_ref = oracle.prefill(dp["q"], dp["k"], dp["v"], dp["alpha"], dp["beta"], dp["S0"])
+    check(from_torch(xg["p_out"]), from_torch(xg["p_sf"]), o_ref, S_ref, "bf16",
+          "graph-captured segmented prefill")
