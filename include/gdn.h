@@ -54,7 +54,7 @@ typedef enum {
     GDN_OK = 0,
     GDN_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
     GDN_ERR_BAD_SHAPE = 2,    /* a size is out of range or inconsistent */
-    GDN_ERR_UNSUPPORTED = 3,  /* a valid shape this build has no kernel for */
+    GDN_ERR_UNSUPPORTED = 3,  /* a valid shape the library has no kernel for */
     GDN_ERR_MISALIGNED = 4,   /* a pointer is not 16-byte aligned */
     GDN_ERR_ALIAS = 5,        /* forbidden overlap between buffers */
     GDN_ERR_HIP = 6           /* HIP runtime error; see gdn_status_string */
