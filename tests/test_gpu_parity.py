@@ -698,6 +698,28 @@ def test_segmented_prefill(gdn, monkeypatch, B, T, Hk, Hv, D, segs, init, flags,
           f"alpha shift {ashift}")
 
 
+@pytest.mark.parametrize("segs", ["3", "4"])
+def test_segmented_prefill_without_final_state(gdn, monkeypatch, segs):
+    """Segmented with no final state asked for (the scan then writes the last
+    state to workspace scratch): outputs bit-equal to those of the same call
+    with a final state, and within tolerance of the oracle."""
+    monkeypatch.setenv("GDN_PREFILL_SEGMENTS", segs)
+    d = small_prefill(1, 900, 1, 2, 128, "bf16", seed=191, alpha_shift=-5.0, init_state=True)
+    q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
+    s0 = to_torch(d["S0"], DEV)
+    n = gdn.gdn_prefill_workspace_size(1, 900, 1, 2, 128, 128, gdn.GDN_BF16, 0)
+    ws = torch.empty(n, dtype=torch.uint8, device=DEV)
+    out_f, sf = gdn.gdn_prefill_chunked(q, k, v, a, b, s0, workspace=ws)
+    out_n, none = gdn.gdn_prefill_chunked(q, k, v, a, b, s0, workspace=ws,
+                                          want_final_state=False)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(out_f, out_n)
+    o_ref, S_ref = oracle.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"])
+    check(from_torch(out_n), from_torch(sf), o_ref, S_ref, "bf16",
+          f"segmented P={segs} without final state")
+
+
 def test_layer_prefill_4k_tp8_segmented(gdn, monkeypatch):
     """The per-GPU share of the layer at 8-way head-group sharding: few
     enough chains that the segmented path is chosen by itself; its result
