@@ -178,8 +178,12 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(const float *s0, const fl
 // one workgroup per (sequence, segment, value head, group of `tiles` 64-token
 // tiles: more when there are many, so that staging S_j is amortised).
 // S_j^T is staged in LDS as bf16 MFMA fragments once and reused for the
-// group's tiles; wave w forms rows 16 w .. 16 w + 15 of a tile,
-// all D columns: C[t][n] = sum_k o'[t][k] S_j[n][k].
+// group's tiles; wave w forms rows 16 w .. 16 w + 15 of a tile, all D
+// columns: C[t][n] = sum_k o'[t][k] S_j[n][k]. C goes through a per-wave LDS
+// block so that out is read and written as whole rows (16-byte accesses,
+// 64 contiguous bytes per row and instruction); the next tile's o' and out
+// rows are loaded before the current tile's products. Rows past the end of
+// the segment re-read its last row and are never stored.
 template <int D>
 __global__ __launch_bounds__(256) void seg_correct_kernel(__bf16 *out, const __bf16 *o_id,
                                                           const float *s_start,
@@ -188,8 +192,10 @@ __global__ __launch_bounds__(256) void seg_correct_kernel(__bf16 *out, const __b
                                                           int32_t first_seg, int32_t tiles) {
     constexpr int NT = D / 16;     // 16-column tiles
     constexpr int KS = D / 32;     // k steps of 32
-    const int GT = 64 * tiles;     // tokens per workgroup
+    constexpr int VP = D / 32;     // 16-byte pieces of a row per lane in the row pass
+    constexpr int PC = D + 4;      // fp32 pitch of the staged C rows
     __shared__ bf16x8 sB[KS * NT * 64];  // fragment (ks, nt), lane l
+    __shared__ __attribute__((aligned(16))) float sC[4 * 16 * PC];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g4 = lane >> 4, c16 = lane & 15;
     int rest = blockIdx.x;
@@ -201,7 +207,7 @@ __global__ __launch_bounds__(256) void seg_correct_kernel(__bf16 *out, const __b
     const int b = rest / (P - first_seg);
     const int si = b * P + seg;
     const int64_t t_lo = cu[si], t_hi = cu[si + 1];
-    const int64_t g0 = t_lo + (int64_t)grp * GT;
+    const int64_t g0 = t_lo + (int64_t)grp * 64 * tiles;
     if (g0 >= t_hi) return;  // uniform over the workgroup
     const float *S = s_start + ((size_t)si * Hv + h) * D * D;
 
@@ -223,37 +229,65 @@ __global__ __launch_bounds__(256) void seg_correct_kernel(__bf16 *out, const __b
     __syncthreads();
 
     const int64_t sO = (int64_t)Hv * D;
-    for (int tile = 0; tile < tiles; ++tile) {
+    const __bf16 *oi = o_id + (int64_t)h * D;
+    __bf16 *oo = out + (int64_t)h * D;
+    // row pass: lane takes row rr of the wave's 16 and the 16-byte pieces
+    // 4 v + q (v < VP) of it
+    const int rr = lane & 15, q = lane >> 4;
+    float *cw = sC + wave * 16 * PC;
+    const int ntl = (int)((t_hi - g0 + 63) / 64 < tiles ? (t_hi - g0 + 63) / 64 : tiles);
+    auto load_tile = [&](int tile, bf16x8 (&a)[KS], bf16x8 (&ov)[VP]) {
+        const int64_t t0 = g0 + 64 * tile + 16 * wave;
+        const int64_t ta = t0 + c16 < t_hi ? t0 + c16 : t_hi - 1;
+        const int64_t tr = t0 + rr < t_hi ? t0 + rr : t_hi - 1;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            a[ks] = *reinterpret_cast<const bf16x8 *>(oi + ta * sO + 32 * ks + 8 * g4);
+#pragma unroll
+        for (int v = 0; v < VP; ++v)
+            ov[v] = *reinterpret_cast<const bf16x8 *>(oo + tr * sO + 8 * (4 * v + q));
+    };
+    bf16x8 a[KS], ov[VP];
+    load_tile(0, a, ov);
+    for (int tile = 0; tile < ntl; ++tile) {
         const int64_t t0 = g0 + 64 * tile + 16 * wave;  // this wave's first row
-        if (t0 >= t_hi) break;                          // uniform over the wave
-        const int64_t ta = t0 + c16;                    // A row of this lane
-        const bool ok_a = ta < t_hi;
+        bf16x8 an[KS], on[VP];
+        load_tile(tile + 1 < ntl ? tile + 1 : tile, an, on);  // the last re-reads its own rows
         f32x4 acc[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[nt] = zero4();
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            bf16x8 a;
-            if (ok_a)
-                a = *reinterpret_cast<const bf16x8 *>(o_id + ta * sO + (int64_t)h * D + 32 * ks +
-                                                      8 * g4);
-            else
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) a[e] = (__bf16)0.f;
+            for (int nt = 0; nt < NT; ++nt) acc[nt] = mma(a[ks], sB[(ks * NT + nt) * 64 + lane], acc[nt]);
+        // C layout (rows 4 g4 + i, column 16 nt + c16) -> rows in LDS; the
+        // wave reads back only what it wrote, in order
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) acc[nt] = mma(a, sB[(ks * NT + nt) * 64 + lane], acc[nt]);
-        }
-        // C layout: lane holds rows 4 g4 .. 4 g4 + 3 of column c16 of each tile
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t t = t0 + 4 * g4 + i;
-            if (t < t_hi) {
-                __bf16 *o = out + t * sO + (int64_t)h * D + c16;
+            for (int i = 0; i < 4; ++i) cw[(4 * g4 + i) * PC + 16 * nt + c16] = acc[nt][i];
+        asm volatile("" ::: "memory");
+        const int64_t t = t0 + rr;
+        if (t < t_hi) {
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                    o[16 * nt] = (__bf16)((float)o[16 * nt] + acc[nt][i]);
+            for (int v = 0; v < VP; ++v) {
+                const int col = 8 * (4 * v + q);
+                const f32x4 c0 = *reinterpret_cast<const f32x4 *>(cw + rr * PC + col);
+                const f32x4 c1 = *reinterpret_cast<const f32x4 *>(cw + rr * PC + col + 4);
+                bf16x8 r;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    r[e] = (__bf16)((float)ov[v][e] + c0[e]);
+                    r[4 + e] = (__bf16)((float)ov[v][4 + e] + c1[e]);
+                }
+                *reinterpret_cast<bf16x8 *>(oo + t * sO + col) = r;
             }
         }
+        asm volatile("" ::: "memory");  // this tile's C rows are read before the next tile's writes
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) a[ks] = an[ks];
+#pragma unroll
+        for (int v = 0; v < VP; ++v) ov[v] = on[v];
     }
 }
 
