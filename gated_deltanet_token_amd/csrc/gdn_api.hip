@@ -150,7 +150,11 @@ size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t tokens, int32_t Hk, 
     if (device_cus(&cus) != GDN_OK) return 0;
     if (!gdn::prefill_wants_workspace((int64_t)num_seqs * Hv, cus)) return 0;
     const int64_t slots = gdn::prefill_ws_slots(num_seqs, total, packed ? 0 : tokens, packed != 0);
-    const size_t two_pass = gdn::prefill_ws_bytes(slots, Hv, dtype == GDN_BF16 ? 1 : 0);
+    const size_t recs = gdn::prefill_ws_bytes(slots, Hv, dtype == GDN_BF16 ? 1 : 0);
+    const size_t two_pass =
+        packed ? recs
+               : gdn::prefill_two_pass_ws_bytes(num_seqs, tokens, Hv, Dk,
+                                                dtype == GDN_BF16 ? 1 : 0, cus, recs);
     // few long sequences: the segmented path, whose layout also holds the above
     const size_t seg = packed ? 0
                               : gdn::prefill_seg_ws_bytes(num_seqs, tokens, Hv, Dk,

@@ -24,6 +24,8 @@ struct PrefillParams {
     bool s0_identity;      // initial state I (Dv == Dk) instead of s0 / zeros
     bool records_ready;    // two-pass: the workspace already holds this batch's per-chunk
                            // factors (they depend on q, k, alpha, beta only)
+    int64_t chunk0;        // two-pass, one dense sequence: first chunk of this launch
+    int64_t chunk_end;     // one past its last (0: to the end of the sequence)
 };
 
 // Input preparation flags (the ABI's GDN_QK_L2NORM, GDN_GATE_LOGITS).
@@ -64,6 +66,11 @@ hipError_t launch_prefill(const PrefillParams &p, int dtype, int D, int num_cus,
 int64_t prefill_ws_slots(int64_t nseq, int64_t total_tokens, int64_t seq_len, bool packed);
 size_t prefill_ws_bytes(int64_t slots, int Hv, int dtype);
 bool prefill_wants_workspace(int64_t chains, int num_cus);
+// Two-pass workspace bytes for these shapes given the records' rec_bytes:
+// rec_bytes, or more when one long sequence runs its chunks in blocks (the
+// carried state after the records).
+size_t prefill_two_pass_ws_bytes(int64_t nseq, int64_t T, int Hv, int D, int dtype, int num_cus,
+                                 size_t rec_bytes);
 // Workspace bytes of the segmented prefill (dense bf16 batches with few
 // chains), or 0 when it does not apply to these shapes.
 size_t prefill_seg_ws_bytes(int64_t nseq, int64_t T, int Hv, int D, int dtype, int num_cus);

@@ -30,6 +30,8 @@
 #include <float.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "gdn_chunk.hpp"
 #include <type_traits>
 
@@ -479,7 +481,7 @@ __global__ __launch_bounds__(256, FRAG ? 4 : 1) void prep_kernel(PrefillParams p
     // heads sharing a q/k head read K and Q through one L2
     const int wg = logical_wg(remap_xcd);
     const int h = wg % p.Hv;
-    const int64_t slot = wg / p.Hv;
+    const int64_t slot = p.chunk0 + wg / p.Hv;  // chunk0 > 0 only for one dense sequence
     // which (sequence, chunk) owns this slot
     int n;
     if (p.cu_seqlens) {
@@ -874,6 +876,11 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
     const int64_t sQK = (int64_t)p.Hk * D;
     const int64_t sVO = (int64_t)p.Hv * D;
     const int64_t nchunks = (len + kC - 1) / kC;
+    // this launch's chunks [cb, cb + npc) of the sequence; loop indices below
+    // count from cb (flags, handoff slots, LDS buffers), addresses use cb + c
+    const int64_t cb = p.chunk0;
+    const int64_t ce = p.chunk_end > 0 && p.chunk_end < nchunks ? p.chunk_end : nchunks;
+    const int64_t npc = ce > cb ? ce - cb : 0;
     int *flags = reinterpret_cast<int *>(smem + Cf::OFF_FLAG);
 
     auto smem_view = [&](int64_t c) {
@@ -908,10 +915,10 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
             PrefixRows pre(p, n, len);
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): initial state; see prefill_kernel
             __syncthreads();
-            for (int64_t c = 0; c < nchunks; ++c) {
+            for (int64_t c = 0; c < npc; ++c) {
                 chain_core_db<D, Cf::DVS, 1, (Cf::NW > 8)>(smem_view(c), st, wdv, ho, flag, (int)c,
                                                            g4, c16, lane);
-                const int64_t prow = PREFIX ? pre.take(p, c) : -1;
+                const int64_t prow = PREFIX ? pre.take(p, cb + c) : -1;
                 if (prow >= 0) {
                     float *ps = p.prefix + (prow * p.Hv + h) * D * D;
 #pragma unroll
@@ -935,15 +942,15 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
             __syncthreads();
             OutCarry<D, 1> carry;
             auto lenc_of = [&](int64_t c) { return (int)((len - c * kC) < kC ? (len - c * kC) : kC); };
-            for (int64_t c = 0; c < nchunks; ++c) {
-                const int64_t cp = c > 0 ? c - 1 : 0;
+            for (int64_t c = 0; c < npc; ++c) {
+                const int64_t cp = cb + (c > 0 ? c - 1 : 0);
                 out_step<D, 1, (Cf::NW > 8)>(smem_view(c), ho, flag, (int)c, carry, oh + cp * kC * sVO, sVO,
                                lenc_of(cp), p.scale, g4, c16, lane);
                 __syncthreads();
             }
-            if (nchunks > 0)
-                out_tail<D, 1>(ho, flag, (int)nchunks - 1, carry, oh + (nchunks - 1) * kC * sVO,
-                               sVO, lenc_of(nchunks - 1), p.scale, g4, c16, lane);
+            if (npc > 0)
+                out_tail<D, 1>(ho, flag, (int)npc - 1, carry, oh + (ce - 1) * kC * sVO,
+                               sVO, lenc_of(ce - 1), p.scale, g4, c16, lane);
         }
         return;
     }
@@ -1009,13 +1016,13 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
         // touched PF_AHEAD iterations earlier (chunks 1 + DEPTH .. LEAD - 1
         // here). The dummy line, row 0 of the sequence, exists only if the
         // sequence is not empty.
-        if (nchunks > 0) {
+        if (npc > 0) {
 #pragma unroll
-            for (int j = 1 + DEPTH; j < LEAD; ++j) touch(j);
+            for (int j = 1 + DEPTH; j < LEAD; ++j) touch(cb + j);
         }
         __syncthreads();
-        for (int64_t c = 0; c < nchunks; ++c) {
-            touch(c + LEAD);
+        for (int64_t c = 0; c < npc; ++c) {
+            touch(cb + c + LEAD);
             __syncthreads();
         }
 #pragma unroll
@@ -1050,11 +1057,11 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
     };
     using KR_c = std::integral_constant<int, Cf::KR>;
     using VR_c = std::integral_constant<int, Cf::VR>;
-    auto copy_chunk = [&](int64_t c) {
+    auto copy_chunk = [&](int64_t c) {  // c counts from cb
         unsigned char *buf = smem + (c & 1) * Cf::BUF;
-        const int64_t t0 = c * kC;
+        const int64_t t0 = (cb + c) * kC;
         const int lenc = (int)((len - t0) < kC ? (len - t0) : kC);
-        const unsigned char *rec = ws + ((base + c) * p.Hv + h) * (int64_t)WSB;
+        const unsigned char *rec = ws + ((base + cb + c) * p.Hv + h) * (int64_t)WSB;
         auto srcK = [&](int row, int pc) { return kb + (t0 + min(row, lenc - 1)) * rowqk + 16 * pc; };
         auto srcQ = [&](int row, int pc) { return qb + (t0 + min(row, lenc - 1)) * rowqk + 16 * pc; };
         auto srcV = [&](int row, int pc) { return vb + (t0 + min(row, lenc - 1)) * rowv + 16 * pc; };
@@ -1078,10 +1085,10 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
             }
         }
     };
-    if (nchunks > 0) copy_chunk(0);
+    if (npc > 0) copy_chunk(0);
     __syncthreads();  // waits for this wave's copies, then the workgroup barrier
-    for (int64_t c = 0; c < nchunks; ++c) {
-        if (c + 1 < nchunks) copy_chunk(c + 1);
+    for (int64_t c = 0; c < npc; ++c) {
+        if (c + 1 < npc) copy_chunk(c + 1);
         __syncthreads();
     }
 }
@@ -1240,6 +1247,148 @@ static SegPlan seg_plan(int64_t nseq, int64_t T, int Hv, int D, int dtype, int n
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// ----------------------------------------------------------------------------
+// blocked two-pass prefill: one long dense sequence
+//
+// The chain kernel keeps a quarter of the CUs idle at the full layer (192
+// workgroups on 256 CUs), and a prep workgroup fits beside a chain workgroup
+// in a CU's LDS. So the chunks run in blocks: the chain walks block i on the
+// caller's stream while prep forms block i + 1's records on a side stream.
+// Events order the two (prep of block i before its chain; the side stream
+// first waits for the caller's earlier work, and the last chain waits for
+// the last prep), so nothing waits inside a kernel on another kernel. The
+// state passes from block to block through a workspace buffer after the
+// records, in place (a chain workgroup reads its rows of the initial state
+// before it writes them back); the arithmetic is the one-block run's, so the
+// results are the same bits.
+
+constexpr int kMaxBlocks = 16;
+
+static int chain_slices(int64_t chains, int num_cus) {
+    int ns = env_int("GDN_PREFILL_NSPLIT", 0);
+    if (ns != 1 && ns != 2 && ns != 4 && ns != 8) {
+        const int64_t want = (int64_t)num_cus / (chains > 0 ? chains : 1);
+        ns = pow2_floor((int)(want < 4 ? (want < 1 ? 1 : want) : 4));
+    }
+    return ns;
+}
+
+// Blocks of a two-pass call: more than one only for one dense bf16 sequence
+// of at least 1,024 chunks on the double-buffered chain whose workgroups
+// leave a quarter of the CUs free; one block per 512 chunks, at most
+// kMaxBlocks (GDN_PREFILL_BLOCKS overrides).
+static int prefill_blocks(int64_t nseq, int64_t T, int Hv, int D, int dtype, int num_cus) {
+    if (nseq != 1 || dtype != 1) return 1;
+    const int64_t nchunks = (T + kC - 1) / kC;
+    const int ns = chain_slices(Hv, num_cus);
+    if (!(D == 64 || ns >= 2)) return 1;  // the single-slice D = 128 chain is another kernel
+    int64_t nb = 1;
+    if (nchunks >= 1024 && (int64_t)Hv * ns * 4 <= (int64_t)num_cus * 3)
+        nb = nchunks / 512 < kMaxBlocks ? nchunks / 512 : kMaxBlocks;
+    const int e = env_int("GDN_PREFILL_BLOCKS", 0);
+    if (e >= 1) nb = e < kMaxBlocks ? e : kMaxBlocks;
+    if (nb > nchunks) nb = nchunks > 0 ? nchunks : 1;
+    return (int)nb;
+}
+
+size_t prefill_two_pass_ws_bytes(int64_t nseq, int64_t T, int Hv, int D, int dtype, int num_cus,
+                                 size_t rec_bytes) {
+    if (prefill_blocks(nseq, T, Hv, D, dtype, num_cus) < 2) return rec_bytes;
+    return align256(rec_bytes) + (size_t)nseq * Hv * D * D * 4;
+}
+
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t ev[kMaxBlocks + 1] = {};  // per block (prep done), then the fork
+};
+static std::mutex g_side_mu;
+static SideStream g_side[64];
+
+// The calling thread's device's side stream, created on first use (default
+// priority) and kept until the process ends. Call with g_side_mu held.
+static hipError_t side_stream(SideStream **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    SideStream &ss = g_side[dev];
+    if (!ss.s) {
+        SideStream n;
+        for (auto &ev : n.ev) {
+            e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+            if (e != hipSuccess) break;
+        }
+        if (e == hipSuccess) e = hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking);
+        if (e != hipSuccess) {
+            for (auto &ev : n.ev)
+                if (ev) (void)hipEventDestroy(ev);
+            return e;
+        }
+        ss = n;
+    }
+    *out = &ss;
+    return hipSuccess;
+}
+
+template <int D, int NC, int NH>
+static hipError_t launch_db_blocks(const PrefillParams &p, unsigned char *ws, int nsplit, int nb,
+                                   float *carry, hipStream_t stream) {
+    const int64_t nchunks = (p.seq_len + kC - 1) / kC;
+    const int64_t nchain = (int64_t)p.Hv * nsplit;
+    if (ChainDbCfg<D, NC, NH>::DVS * nsplit != D) return hipErrorInvalidValue;
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream *ss = nullptr;
+    hipError_t e = side_stream(&ss);
+    if (e != hipSuccess) return e;
+    // block 0 is short (1/32 of the chunks): its prep runs alone, before any
+    // chain; the other blocks share the rest evenly
+    const int64_t first = nchunks / 32 > 0 ? nchunks / 32 : 1;
+    auto edge = [&](int i) {
+        return i == 0 ? 0 : first + (nchunks - first) * (i - 1) / (nb - 1);
+    };
+    auto prep_block = [&](int i) -> hipError_t {
+        PrefillParams pp = p;
+        pp.chunk0 = edge(i);
+        pp.chunk_end = edge(i + 1);
+        const hipError_t r =
+            launch_prep<__bf16, D, true>(pp, ws, (edge(i + 1) - edge(i)) * p.Hv, ss->s);
+        return r != hipSuccess ? r : hipEventRecord(ss->ev[i], ss->s);
+    };
+    // fork: the side stream starts after the caller's earlier work
+    e = hipEventRecord(ss->ev[kMaxBlocks], stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(ss->s, ss->ev[kMaxBlocks], 0);
+    if (e == hipSuccess) e = prep_block(0);
+    for (int i = 0; i < nb && e == hipSuccess; ++i) {
+        e = hipStreamWaitEvent(stream, ss->ev[i], 0);  // block i's records are written
+        if (e == hipSuccess && i + 1 < nb) e = prep_block(i + 1);
+        if (e != hipSuccess) break;
+        PrefillParams pc = p;
+        pc.chunk0 = edge(i);
+        pc.chunk_end = edge(i + 1);
+        pc.s0 = i == 0 ? p.s0 : carry;
+        pc.s_final = i + 1 == nb ? p.s_final : carry;
+        hipLaunchKernelGGL((chain_db_kernel<D, NC, NH, false>), dim3((unsigned)nchain),
+                           dim3(ChainDbCfg<D, NC, NH>::NW * 64), 0, stream, pc,
+                           (const unsigned char *)ws, nsplit, nchain % 8 == 0 ? 1 : 0);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+// The two-pass chain on the double-buffered kernel: blocked when planned and
+// the stream is not being captured into a graph, else one launch pair.
+template <int D, int NC, int NH>
+static hipError_t run_split_db(const PrefillParams &p, unsigned char *ws, int64_t nslots,
+                               int nsplit, int nb, float *carry, hipStream_t stream) {
+    if (nb > 1 && carry && p.nseq == 1 && !p.cu_seqlens && !p.prefix && !p.records_ready &&
+        !p.s0_identity) {
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone)
+            return launch_db_blocks<D, NC, NH>(p, ws, nsplit, nb, carry, stream);
+    }
+    return launch_split_db<D, NC, NH>(p, ws, nslots, nsplit, stream);
+}
+
 struct SegLayout {
     size_t rec, cu, zero_v, n_end, m_end, s_start, o_id, total;
 };
@@ -1329,24 +1478,27 @@ hipError_t launch_prefill(const PrefillParams &p, int dtype, int D, int num_cus,
     if (split) {
         // Value-column slices per head: about one workgroup per CU (the
         // double-buffered chain kernel fills a CU's LDS), at most four.
-        int ns = env_int("GDN_PREFILL_NSPLIT", 0);
-        if (ns != 1 && ns != 2 && ns != 4 && ns != 8) {
-            const int64_t want = (int64_t)num_cus / (chains > 0 ? chains : 1);
-            ns = pow2_floor((int)(want < 4 ? (want < 1 ? 1 : want) : 4));
-        }
+        const int ns = chain_slices(chains, num_cus);
         unsigned char *w = static_cast<unsigned char *>(ws);
+        // blocks of one long sequence, when the workspace holds the carried state
+        int nb = p.cu_seqlens ? 1 : prefill_blocks(p.nseq, p.seq_len, p.Hv, D, dtype, num_cus);
+        const size_t rec = prefill_ws_bytes(nslots, p.Hv, dtype);
+        float *carry = nullptr;
+        if (nb > 1 && ws_bytes >= align256(rec) + (size_t)p.nseq * p.Hv * D * D * 4)
+            carry = reinterpret_cast<float *>(w + align256(rec));
+        if (!carry) nb = 1;
         if (dtype == 1 && D == 128) {
             switch (ns) {
             case 1: return launch_split<__bf16, 128, 4, 32>(p, w, nslots, 1, stream);
-            case 2: return launch_split_db<128, 4, 1>(p, w, nslots, 2, stream);
-            case 4: return launch_split_db<128, 2, 1>(p, w, nslots, 4, stream);
-            default: return launch_split_db<128, 1, 1>(p, w, nslots, 8, stream);
+            case 2: return run_split_db<128, 4, 1>(p, w, nslots, 2, nb, carry, stream);
+            case 4: return run_split_db<128, 2, 1>(p, w, nslots, 4, nb, carry, stream);
+            default: return run_split_db<128, 1, 1>(p, w, nslots, 8, nb, carry, stream);
             }
         } else if (dtype == 1 && D == 64) {
             switch (ns) {
-            case 1: return launch_split_db<64, 4, 1>(p, w, nslots, 1, stream);
-            case 2: return launch_split_db<64, 2, 1>(p, w, nslots, 2, stream);
-            default: return launch_split_db<64, 1, 1>(p, w, nslots, 4, stream);
+            case 1: return run_split_db<64, 4, 1>(p, w, nslots, 1, nb, carry, stream);
+            case 2: return run_split_db<64, 2, 1>(p, w, nslots, 2, nb, carry, stream);
+            default: return run_split_db<64, 1, 1>(p, w, nslots, 4, nb, carry, stream);
             }
         } else if (dtype == 0 && D == 64) {
             switch (ns) {

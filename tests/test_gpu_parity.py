@@ -698,6 +698,31 @@ def test_segmented_prefill(gdn, monkeypatch, B, T, Hk, Hv, D, segs, init, flags,
           f"alpha shift {ashift}")
 
 
+@pytest.mark.parametrize("D,blocks,init", [(128, "2", True), (128, "3", False), (128, "8", True),
+                                           (64, "3", True)])
+def test_prefill_blocks_match_one_block(gdn, monkeypatch, D, blocks, init):
+    """One sequence run in chunk blocks (the chain of block i beside the prep
+    of block i + 1 on a side stream, the state carried through the
+    workspace): the same bits as the run in one block, and within tolerance
+    of the oracle."""
+    monkeypatch.setenv("GDN_PREFILL_SEGMENTS", "0")
+    T = 64 * 40 + 17  # 41 chunks, the last one partial
+    d = small_prefill(1, T, 2, 6, D, "bf16", seed=193 + D, init_state=init, alpha_shift=-5.0)
+    q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
+    s0 = to_torch(d["S0"], DEV) if init else None
+    res = {}
+    for nb in ("1", blocks):
+        monkeypatch.setenv("GDN_PREFILL_BLOCKS", nb)
+        res[nb] = gdn.gdn_prefill_chunked(q, k, v, a, b, s0)
+        torch.cuda.synchronize()
+    assert torch.equal(res["1"][0], res[blocks][0])
+    assert torch.equal(res["1"][1], res[blocks][1])
+    o_ref, S_ref = oracle.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                  d["S0"] if init else None)
+    check(from_torch(res[blocks][0]), from_torch(res[blocks][1]), o_ref, S_ref, "bf16",
+          f"{blocks} blocks D{D} init={init}")
+
+
 @pytest.mark.parametrize("segs", ["3", "4"])
 def test_segmented_prefill_without_final_state(gdn, monkeypatch, segs):
     """Segmented with no final state asked for (the scan then writes the last
