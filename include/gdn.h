@@ -23,8 +23,11 @@
  *    stated per call, and 16-byte aligned. q, k, v and out have the element
  *    type `dtype` (GDN_BF16 or GDN_F32); alpha, beta and states are fp32.
  *  - Ownership: the caller owns every buffer. The library allocates and
- *    frees nothing, keeps no pointer after the call returns and holds no
- *    global mutable state; calls are re-entrant and thread-safe.
+ *    frees no memory and keeps no pointer after the call returns; calls are
+ *    re-entrant and thread-safe. Its one piece of lasting state: the blocked
+ *    two-pass prefill (gdn_prefill_chunked) creates, on its first use on a
+ *    device, one side stream (default priority) and 17 events there, kept
+ *    until the process ends; a lock serialises their use.
  *  - Asynchrony: each call validates its arguments on the host, enqueues
  *    kernels on `stream` and returns without synchronising. Results are
  *    ready when the stream reaches that point.
@@ -111,7 +114,18 @@ enum { GDN_QK_L2NORM = 1, GDN_GATE_LOGITS = 2 };
  * gdn_prefill_workspace_size() bytes the call may run in two passes: the
  * state-independent per-chunk factors of all chunks first, then the
  * sequential state chain. NULL (or too small) selects the single-pass
- * kernel. Both give the same result up to rounding.
+ * kernel. Both give the same result up to rounding. With the workspace, two
+ * more arrangements may run, chosen by shape (and both disabled for a
+ * workspace smaller than the size query's answer):
+ *  - few (sequence, value head) chains, bf16, no prefix states: each
+ *    sequence is split into segments run in parallel from zero and from the
+ *    identity state, and joined by a scan of the segment maps and an output
+ *    correction (same result up to rounding);
+ *  - one long sequence (B = 1, at least 1,024 chunks, bf16): the two passes
+ *    run in blocks of chunks, the chain of block i on `stream` while the
+ *    factors of block i + 1 are formed on the library's side stream, ordered
+ *    by events only; the result is bit-identical to the run in one block. A
+ *    stream being captured into a graph gets the run in one block.
  */
 gdn_status_t gdn_prefill_chunked(const void *q, const void *k, const void *v,
                                  const float *alpha, const float *beta,
@@ -232,9 +246,12 @@ gdn_status_t gdn_varlen_prefill(const void *q, const void *k, const void *v,
  * Returns 0 when the library would not use a workspace for this shape on the
  * current device (enough (sequence, value head) pairs to fill it in one
  * pass), when an argument is invalid, or when no device is available. The
- * size is 17,152 bytes (bf16) or 33,536 bytes (fp32) per (64-token chunk,
- * value head): B * ceil(T/64) chunks, or ceil(total_T/64) + N for packed
- * batches.
+ * base size is 17,152 bytes (bf16) or 33,536 bytes (fp32) per (64-token
+ * chunk, value head): B * ceil(T/64) chunks, or ceil(total_T/64) + N for
+ * packed batches. It is larger where gdn_prefill_chunked would run
+ * segmented (the segment end states, maps, start states and the
+ * identity-start outputs) or in blocks (plus, after 256-byte alignment,
+ * Hv * Dv * Dk * 4 bytes for the state carried between blocks).
  */
 size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t tokens, int32_t Hk,
                                   int32_t Hv, int32_t Dk, int32_t Dv,
