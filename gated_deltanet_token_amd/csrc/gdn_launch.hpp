@@ -26,6 +26,13 @@ struct PrefillParams {
                            // factors (they depend on q, k, alpha, beta only)
     int64_t chunk0;        // two-pass, one dense sequence: first chunk of this launch
     int64_t chunk_end;     // one past its last (0: to the end of the sequence)
+    // Two-pass on the double-buffered chain only: with dual set, chains
+    // nseq .. 2 nseq - 1 run sequence n - nseq a second time, from the
+    // identity state with v = v2 (token stride 0), writing out2 and s_final2.
+    bool dual;
+    const void *v2;
+    void *out2;
+    float *s_final2;
 };
 
 // Input preparation flags (the ABI's GDN_QK_L2NORM, GDN_GATE_LOGITS).

@@ -867,7 +867,10 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
     const int slice = wg % nsplit;
     const int nh = wg / nsplit;
     const int h = nh % p.Hv;
-    const int n = nh / p.Hv;
+    // dual: the second half of the chains reruns the sequences from the
+    // identity state with the zero v row
+    const bool second = p.dual && nh / p.Hv >= p.nseq;
+    const int n = nh / p.Hv - (second ? p.nseq : 0);
     const int grp = h / (p.Hv / p.Hk);
     int64_t tok0, len;
     seq_bounds(p, n, tok0, len);
@@ -904,10 +907,10 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
             // (and with it LDS request) arbitration against the other waves
             __builtin_amdgcn_s_setprio(3);
             f32x4 st[NKT][1];
-            const float *s0 = p.s0 ? p.s0 + ((int64_t)n * p.Hv + h) * D * D : nullptr;
+            const float *s0 = p.s0 && !second ? p.s0 + ((int64_t)n * p.Hv + h) * D * D : nullptr;
 #pragma unroll
             for (int a = 0; a < NKT; ++a)
-                st[a][0] = p.s0_identity ? eye4(dv0 + wdv + c16, 16 * a + 4 * g4)
+                st[a][0] = p.s0_identity || second ? eye4(dv0 + wdv + c16, 16 * a + 4 * g4)
                            : s0 ? *reinterpret_cast<const f32x4 *>(
                                       s0 + (int64_t)(dv0 + wdv + c16) * D + 16 * a + 4 * g4)
                                 : zero4();
@@ -929,8 +932,9 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
                 }
                 __syncthreads();
             }
-            if (p.s_final) {
-                float *sf = p.s_final + ((int64_t)n * p.Hv + h) * D * D;
+            float *sfin = second ? p.s_final2 : p.s_final;
+            if (sfin) {
+                float *sf = sfin + ((int64_t)n * p.Hv + h) * D * D;
 #pragma unroll
                 for (int a = 0; a < NKT; ++a)
                     *reinterpret_cast<f32x4 *>(sf + (int64_t)(dv0 + wdv + c16) * D + 16 * a +
@@ -938,7 +942,8 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
             }
         } else {
             // output wave
-            DT *oh = reinterpret_cast<DT *>(p.out) + tok0 * sVO + (int64_t)h * D + dv0 + wdv;
+            DT *oh = reinterpret_cast<DT *>(second ? p.out2 : p.out) + tok0 * sVO + (int64_t)h * D +
+                     dv0 + wdv;
             __syncthreads();
             OutCarry<D, 1> carry;
             auto lenc_of = [&](int64_t c) { return (int)((len - c * kC) < kC ? (len - c * kC) : kC); };
@@ -980,9 +985,10 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
                                   (tok0 * sQK + (int64_t)grp * D) * 2;
         const unsigned char *qb = reinterpret_cast<const unsigned char *>(p.q) +
                                   (tok0 * sQK + (int64_t)grp * D) * 2;
-        const unsigned char *vhb = reinterpret_cast<const unsigned char *>(p.v) +
-                                   (tok0 * p.v_stride + (int64_t)h * D) * 2;
-        const int64_t rowqk = sQK * 2, rowv = p.v_stride * 2;
+        const int64_t vstride = second ? 0 : p.v_stride;
+        const unsigned char *vhb = reinterpret_cast<const unsigned char *>(second ? p.v2 : p.v) +
+                                   (tok0 * vstride + (int64_t)h * D) * 2;
+        const int64_t rowqk = sQK * 2, rowv = vstride * 2;
         uint32_t pend[NL], acc = 0;
 #pragma unroll
         for (int j = 0; j < NL; ++j) pend[j] = 0;
@@ -1042,9 +1048,10 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
                               (tok0 * sQK + (int64_t)grp * D) * 2;
     const unsigned char *kb = reinterpret_cast<const unsigned char *>(p.k) +
                               (tok0 * sQK + (int64_t)grp * D) * 2;
-    const unsigned char *vb = reinterpret_cast<const unsigned char *>(p.v) +
-                              (tok0 * p.v_stride + (int64_t)h * D + dv0) * 2;
-    const int64_t rowqk = sQK * 2, rowv = p.v_stride * 2;
+    const int64_t vstride = second ? 0 : p.v_stride;
+    const unsigned char *vb = reinterpret_cast<const unsigned char *>(second ? p.v2 : p.v) +
+                              (tok0 * vstride + (int64_t)h * D + dv0) * 2;
+    const int64_t rowqk = sQK * 2, rowv = vstride * 2;
     // one 1 KiB block: slots 64 b .. 64 b + 63 of a swizzled region with rows
     // of ROWB bytes; LDS slot s of row r receives data piece s ^ swz_f(r),
     // src(row, piece) gives its address
@@ -1105,6 +1112,7 @@ static void launch_fused_as(const PrefillParams &p, int nsplit, int64_t nblocks,
 
 template <typename DT, int D, int NW, int DVW>
 static hipError_t launch_fused(const PrefillParams &p, int nsplit, hipStream_t stream) {
+    if (p.dual) return hipErrorInvalidValue;  // the double-buffered chain only
     const int64_t nblocks = (int64_t)p.nseq * p.Hv * nsplit;
     if (nblocks <= 0 || nblocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     const bool raw = p.flags & kQkL2Norm;
@@ -1134,6 +1142,7 @@ static hipError_t launch_prep(const PrefillParams &p, unsigned char *ws, int64_t
 template <typename DT, int D, int NC, int DVW>
 static hipError_t launch_split(const PrefillParams &p, unsigned char *ws, int64_t nslots,
                                int nsplit, hipStream_t stream) {
+    if (p.dual) return hipErrorInvalidValue;  // the double-buffered chain only
     const int64_t nprep = nslots * p.Hv;
     const int64_t nchain = (int64_t)p.nseq * p.Hv * nsplit;
     if (nprep <= 0 || nprep > 0x7FFFFFFF || nchain <= 0 || nchain > 0x7FFFFFFF)
@@ -1155,7 +1164,7 @@ template <int D, int NC, int NH>
 static hipError_t launch_split_db(const PrefillParams &p, unsigned char *ws, int64_t nslots,
                                   int nsplit, hipStream_t stream) {
     const int64_t nprep = nslots * p.Hv;
-    const int64_t nchain = (int64_t)p.nseq * p.Hv * nsplit;
+    const int64_t nchain = (int64_t)p.nseq * p.Hv * nsplit * (p.dual ? 2 : 1);
     if (nprep <= 0 || nprep > 0x7FFFFFFF || nchain <= 0 || nchain > 0x7FFFFFFF)
         return hipErrorInvalidValue;
     if (ChainDbCfg<D, NC, NH>::DVS * nsplit != D) return hipErrorInvalidValue;
@@ -1203,6 +1212,17 @@ static int pow2_floor(int v) {
     return r;
 }
 
+// Value-column slices per head of the two-pass chain: about one workgroup
+// per CU (the double-buffered chain kernel fills a CU's LDS), at most four.
+static int chain_slices(int64_t chains, int num_cus) {
+    int ns = env_int("GDN_PREFILL_NSPLIT", 0);
+    if (ns != 1 && ns != 2 && ns != 4 && ns != 8) {
+        const int64_t want = (int64_t)num_cus / (chains > 0 ? chains : 1);
+        ns = pow2_floor((int)(want < 4 ? (want < 1 ? 1 : want) : 4));
+    }
+    return ns;
+}
+
 // ----------------------------------------------------------------------------
 // segmented prefill (gdn_segment.hip): few long sequences, split into P
 // segments of L tokens (L a multiple of 64) that run as a packed batch.
@@ -1231,11 +1251,29 @@ static SegPlan seg_plan(int64_t nseq, int64_t T, int Hv, int D, int dtype, int n
         P = forced;
     } else {
         if (chains * 8 > num_cus || nchunks < 8) return sp;
-        P = (int64_t)num_cus / 4 / chains;
-        int64_t best = 1;
-        while ((best + 1) * (best + 1) <= 13 * nchunks / 10) ++best;  // floor(sqrt(1.3 n))
-        if (P > best) P = best;
-        if (P > nchunks / 2) P = nchunks / 2;
+        // P from a cost model of the parts, measured on the MI355X: per
+        // 64-token chunk of a segment ~1.6 / 2.4 / 5.8 us on the chain at
+        // 4 / 2 / 1 value-column slices per head (twice that when the two
+        // segment passes cannot run as one launch), ~1.9 us per scan step,
+        // ~15 us of setup, scan start and corrections; against one pass.
+        auto chunk_us = [](int ns) { return ns >= 4 ? 1.6 : ns == 2 ? 2.4 : 5.8; };
+        const int64_t pmax = (int64_t)num_cus / 4 / chains < nchunks / 2
+                                 ? (int64_t)num_cus / 4 / chains
+                                 : nchunks / 2;
+        double best_t = (double)nchunks * chunk_us(chain_slices(chains, num_cus));
+        P = 0;
+        for (int64_t q = 2; q <= pmax; ++q) {
+            const int64_t lc = (nchunks + q - 1) / q;
+            const int ns2 = chain_slices(2 * q * chains, num_cus);
+            const bool merged = D == 64 || ns2 >= 2;
+            const int ns = merged ? ns2 : chain_slices(q * chains, num_cus);
+            const double t = (merged ? 1 : 2) * lc * chunk_us(ns) + 1.9 * q + 15.0;
+            if (t < best_t) {
+                best_t = t;
+                P = q;
+            }
+        }
+        if (P == 0) return sp;
     }
     if (P < 2 || P > nchunks) return sp;
     const int64_t lc = (nchunks + P - 1) / P;  // chunks per segment
@@ -1263,15 +1301,6 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // results are the same bits.
 
 constexpr int kMaxBlocks = 16;
-
-static int chain_slices(int64_t chains, int num_cus) {
-    int ns = env_int("GDN_PREFILL_NSPLIT", 0);
-    if (ns != 1 && ns != 2 && ns != 4 && ns != 8) {
-        const int64_t want = (int64_t)num_cus / (chains > 0 ? chains : 1);
-        ns = pow2_floor((int)(want < 4 ? (want < 1 ? 1 : want) : 4));
-    }
-    return ns;
-}
 
 // Blocks of a two-pass call: more than one only for one dense bf16 sequence
 // of at least 1,024 chunks on the double-buffered chain whose workgroups
@@ -1443,18 +1472,35 @@ static hipError_t launch_segmented(const PrefillParams &p, int D, int num_cus, u
     pz.seq_len = 0;
     pz.s0 = nullptr;
     pz.s_final = n_end;
+    // 2. every segment from the identity with v = 0: outputs M_{->t} q_t, end states M_j.
+    // Steps 1 and 2 share the per-chunk records and are independent, so on
+    // the double-buffered chain they run as one launch over twice the chains
+    // (half the value-column slices each, so that the launch fits the chip
+    // once); otherwise one after the other.
+    const int64_t chains2 = (int64_t)2 * nsegs * p.Hv;
+    const char *path = getenv("GDN_PREFILL_PATH");
+    const bool merge = env_int("GDN_PREFILL_SEG_MERGE", 1) != 0 && !(path && path[0] == 'f') &&
+                       prefill_wants_workspace(chains2, num_cus) &&
+                       (D == 64 || chain_slices(chains2, num_cus) >= 2);
+    if (merge) {
+        pz.dual = true;
+        pz.v2 = zero_v;
+        pz.out2 = o_id;
+        pz.s_final2 = m_end;
+    }
     e = launch_prefill(pz, 1, D, num_cus, ws + l.rec, rec_bytes, slots, stream);
     if (e != hipSuccess) return e;
-    // 2. every segment from the identity with v = 0: outputs M_{->t} q_t, end states M_j
-    PrefillParams pi = pz;
-    pi.v = zero_v;
-    pi.v_stride = 0;
-    pi.s0_identity = true;
-    pi.records_ready = true;  // same q, k, alpha, beta and slots as step 1
-    pi.out = o_id;
-    pi.s_final = m_end;
-    e = launch_prefill(pi, 1, D, num_cus, ws + l.rec, rec_bytes, slots, stream);
-    if (e != hipSuccess) return e;
+    if (!merge) {
+        PrefillParams pi = pz;
+        pi.v = zero_v;
+        pi.v_stride = 0;
+        pi.s0_identity = true;
+        pi.records_ready = true;  // same q, k, alpha, beta and slots as step 1
+        pi.out = o_id;
+        pi.s_final = m_end;
+        e = launch_prefill(pi, 1, D, num_cus, ws + l.rec, rec_bytes, slots, stream);
+        if (e != hipSuccess) return e;
+    }
     // 3. the scan over segments; 4. the corrections (segment 0 only from a
     // nonzero initial state)
     e = launch_segment_scan(p.s0, n_end, m_end, s_start, p.s_final, (int32_t)B, sp.P, p.Hv, D,
@@ -1471,7 +1517,7 @@ hipError_t launch_prefill(const PrefillParams &p, int dtype, int D, int num_cus,
         if (sp.P && ws_bytes >= seg_layout(p.nseq, p.seq_len, p.Hv, D, sp).total)
             return launch_segmented(p, D, num_cus, static_cast<unsigned char *>(ws), sp, stream);
     }
-    const int64_t chains = (int64_t)p.nseq * p.Hv;
+    const int64_t chains = (int64_t)p.nseq * p.Hv * (p.dual ? 2 : 1);
     const bool split = ws != nullptr && nslots > 0 &&
                        ws_bytes >= prefill_ws_bytes(nslots, p.Hv, dtype) &&
                        prefill_wants_workspace(chains, num_cus);

@@ -723,6 +723,28 @@ def test_prefill_blocks_match_one_block(gdn, monkeypatch, D, blocks, init):
           f"{blocks} blocks D{D} init={init}")
 
 
+@pytest.mark.parametrize("D,segs", [(128, "4"), (128, "7"), (64, "5")])
+def test_segmented_passes_merged_match_separate(gdn, monkeypatch, D, segs):
+    """The two segment passes (from zero, and from the identity with v = 0)
+    as one launch over twice the chains, against the same passes launched
+    one after the other: both within tolerance of the oracle, and the same
+    bits (each value column's arithmetic does not depend on the slicing)."""
+    monkeypatch.setenv("GDN_PREFILL_SEGMENTS", segs)
+    d = small_prefill(1, 1100, 2, 6, D, "bf16", seed=197 + D, alpha_shift=-5.0, init_state=True)
+    q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
+    s0 = to_torch(d["S0"], DEV)
+    o_ref, S_ref = oracle.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"])
+    res = {}
+    for merge in ("0", "1"):
+        monkeypatch.setenv("GDN_PREFILL_SEG_MERGE", merge)
+        res[merge] = gdn.gdn_prefill_chunked(q, k, v, a, b, s0)
+        torch.cuda.synchronize()
+        check(from_torch(res[merge][0]), from_torch(res[merge][1]), o_ref, S_ref, "bf16",
+              f"segmented P={segs} D{D} merged={merge}")
+    assert torch.equal(res["0"][0], res["1"][0])
+    assert torch.equal(res["0"][1], res["1"][1])
+
+
 @pytest.mark.parametrize("segs", ["3", "4"])
 def test_segmented_prefill_without_final_state(gdn, monkeypatch, segs):
     """Segmented with no final state asked for (the scan then writes the last
