@@ -723,6 +723,44 @@ def test_prefill_blocks_match_one_block(gdn, monkeypatch, D, blocks, init):
           f"{blocks} blocks D{D} init={init}")
 
 
+def test_prefill_blocks_in_place_and_captured(gdn, monkeypatch):
+    """Chunk blocks with the state updated in place (initial and final state
+    the same buffer), and the same call captured in a graph (which runs in
+    one block, without the side stream): both equal the one-block run bit
+    for bit, every replay included."""
+    monkeypatch.setenv("GDN_PREFILL_SEGMENTS", "0")
+    T = 64 * 24 + 9
+    d = small_prefill(1, T, 2, 6, 128, "bf16", seed=199, init_state=True, alpha_shift=-5.0)
+    q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
+    monkeypatch.setenv("GDN_PREFILL_BLOCKS", "1")
+    ref_o, ref_s = gdn.gdn_prefill_chunked(q, k, v, a, b, to_torch(d["S0"], DEV))
+    monkeypatch.setenv("GDN_PREFILL_BLOCKS", "3")
+    n = gdn.gdn_prefill_workspace_size(1, T, 2, 6, 128, 128, gdn.GDN_BF16, 0)
+    ws = torch.empty(n, dtype=torch.uint8, device=DEV)
+    st = to_torch(d["S0"], DEV)
+    out = torch.empty(v.shape, dtype=torch.bfloat16, device=DEV)
+    gdn.gdn_prefill_chunked(q, k, v, a, b, st, out=out, final_state=st, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_o)
+    assert torch.equal(st, ref_s)
+    s0_g = to_torch(d["S0"], DEV)
+    sf_g = torch.empty_like(s0_g)
+    out_g = torch.empty_like(out)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gdn.gdn_prefill_chunked(q, k, v, a, b, s0_g, out=out_g, final_state=sf_g, workspace=ws)
+    torch.cuda.synchronize()
+    for r in range(3):
+        out_g.zero_()
+        sf_g.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, ref_o), r
+        assert torch.equal(sf_g, ref_s), r
+
+
 @pytest.mark.parametrize("D,segs", [(128, "4"), (128, "7"), (64, "5")])
 def test_segmented_passes_merged_match_separate(gdn, monkeypatch, D, segs):
     """The two segment passes (from zero, and from the identity with v = 0)
