@@ -3,26 +3,30 @@
 
 One step = one pass of the whole hot path on synthetic inputs already
 resident in HBM:
-  * prefill of the layer workload (B=1, T=4096, 16 q/k heads, 48 value
-    heads, d=128, bf16 q/k/v, fp32 alpha/beta/state, zero initial state), and
+  * prefill of the long-context workload (B=1, T=262,144, 16 q/k heads, 48
+    value heads, d=128, bf16 q/k/v, fp32 alpha/beta/state, zero initial
+    state), and
   * one decode step of the batched workload (B=256, same heads, fp32 states
     updated in place).
 Shapes follow "The Hybrid Attention in Qwen3.8-27B" (section "Grouped-query
-attention multiplies on top of that").
+attention multiplies on top of that"; the 262,144-token native context from
+its section "Why 27B parameters can carry 262K tokens").
 
-Reported: prefill tokens/s (value) with its fraction of the bf16 MFMA peak,
-decode state-update GB/s with its fraction of HBM bandwidth, both from HIP
-events on the stream the kernels run on; and the fp64 oracle timed on the
-host cores as a CPU baseline. Timed apart from the step: under
-"prefill_prefix_states" the same prefill also writing the state after every
-1024 tokens; under "prepared_inputs" the prefill and decode step from raw
-q, k and gate logits (prepared inside the kernels); under "segmented_prefill"
-the per-GPU share of the layer at 8-way head-group sharding (6 value heads,
-T = 4096 and 262,144) in one pass and split into segments; and under "decode_multi"
-the K-token decode against a slot pool (B=256 sequences verifying K=4 tokens
-each), in tokens/s and HBM GB/s.
+Reported: the long prefill's tokens/s (value) with its fraction of the bf16
+MFMA peak, the decode step's state-update GB/s with its fraction of HBM
+bandwidth, both from HIP events on the stream the kernels run on; beside
+them, each with its own roofline object, the layer prefill (T=4096) and the
+packed 64-sequence prefill (1,141,939 tokens, nonzero initial states); and
+the fp64 oracle timed on the host cores as a CPU baseline. Timed apart from
+the step: under "prefill_prefix_states" the layer prefill also writing the
+state after every 1024 tokens; under "prepared_inputs" the layer prefill and
+the decode step from raw q, k and gate logits (prepared inside the kernels);
+under "segmented_prefill" the per-GPU share of the layer at 8-way head-group
+sharding (6 value heads, T = 4096 and 262,144) in one pass and split into
+segments; and under "decode_multi" the K-token decode against a slot pool
+(B=256 sequences verifying K=4 tokens each), in tokens/s and HBM GB/s.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+    python bench.py [--gpus 1] [--steps 10] [--warmup 2]
 """
 import argparse
 import hashlib
@@ -91,9 +95,9 @@ def _traffic(kernel_key, digest):
 
 
 def cpu_baseline(d, w, budget_s=20.0):
-    """Time the fp64 oracle on the prefill workload on the host cores: whole
-    passes over all 48 value heads until about budget_s seconds are spent
-    (at least one pass)."""
+    """Time the fp64 oracle on the layer prefill workload on the host cores:
+    whole passes over all 48 value heads until about budget_s seconds are
+    spent (at least one pass)."""
     import oracle
     threads = oracle.default_threads()
     tokens = 0
@@ -106,22 +110,27 @@ def cpu_baseline(d, w, budget_s=20.0):
         el = time.perf_counter() - t0
         if el >= budget_s or el * (passes + 1) / passes > 1.5 * budget_s:
             break
-    return {"value": tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": tokens / el, "unit": "tokens/s", "cores": threads,
+            "host_cpus": os.cpu_count(), "kind": "oracle",
             "sample": f"{passes} full pass(es) of the fp64 token-by-token oracle over "
-                      f"{w.name} (B={w.B}, T={w.T}, {w.Hv} value heads), {el:.1f} s"}
+                      f"{w.name} (B={w.B}, T={w.T}, {w.Hv} value heads), {el:.1f} s, on "
+                      f"{threads} threads of the {os.cpu_count()} host CPUs"}
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--prefill-workload", default="layer_prefill_4k",
-                    help="prefill workload name from gdn_synth.WORKLOADS")
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--prefill-workload", default="long_prefill_256k",
+                    help="workload of the step's prefill (gdn_synth.WORKLOADS)")
+    ap.add_argument("--legs", default="layer_prefill_4k,varlen_64seq",
+                    help="comma-separated prefill workloads timed beside the step, each with "
+                         "its own roofline object ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold-steps", type=int, default=5,
-                    help="extra prefill calls, each after overwriting a 1 GiB scratch buffer "
-                         "(evicts the 256 MiB Infinity Cache), reported as ms_cold")
+    ap.add_argument("--cold-steps", type=int, default=3,
+                    help="extra layer-prefill calls, each after overwriting a 1 GiB scratch "
+                         "buffer (evicts the 256 MiB Infinity Cache), reported as ms_cold")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured ceilings (library copy and bf16 GEMM)")
     ap.add_argument("--no-prepared", action="store_true",
@@ -132,6 +141,8 @@ def main():
                     help="skip the few-long-sequence prefill (segmented vs one pass)")
     ap.add_argument("--no-multi", action="store_true",
                     help="skip the K-token slot-pool decode measurement")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="leave the decode step out of the step (prefill-only profiles)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy three times (the "
                          "reference for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -150,6 +161,9 @@ def main():
 
     gdn.load_library()
     dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    pdig = _src_digest("gdn_prefill.hip", "gdn_chunk.hpp", "gdn_device.hpp")
+    ddig = _src_digest("gdn_decode.hip", "gdn_device.hpp")
     if args.calibrate_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -157,110 +171,190 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    wp = WORKLOADS[args.prefill_workload]
-    wd = WORKLOADS["decode_b256"]
-    dp = generate(wp)
-    dd = generate(wd)
 
-    pt = {n: to_torch(dp[n], dev) for n in ("q", "k", "v", "alpha", "beta")}
-    p_s0 = to_torch(dp["S0"], dev) if dp["S0"] is not None else None
-    p_out = torch.empty(pt["v"].shape, dtype=pt["q"].dtype, device=dev)
-    p_sf = torch.empty((wp.B, wp.Hv, wp.D, wp.D), dtype=torch.float32, device=dev)
-    varlen = wp.kind == "varlen"
-    p_cu = to_torch(dp["cu_seqlens"], dev) if varlen else None
-    # the workspace the library asks for (none: single-pass kernel), allocated once
-    ntok = int(pt["v"].shape[0]) if varlen else wp.T
-    ws_bytes = gdn.gdn_prefill_workspace_size(wp.B, ntok, wp.Hk, wp.Hv, wp.D, wp.D,
-                                              pt["q"].dtype, varlen)
-    p_ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    class Prefill:
+        """One prefill workload resident on the device, with its call."""
+
+        def __init__(self, name):
+            self.w = w = WORKLOADS[name]
+            self.d = generate(w)
+            self.t = {n: to_torch(self.d[n], dev) for n in ("q", "k", "v", "alpha", "beta")}
+            self.s0 = to_torch(self.d["S0"], dev) if self.d["S0"] is not None else None
+            self.varlen = w.kind == "varlen"
+            self.out = torch.empty(self.t["v"].shape, dtype=self.t["q"].dtype, device=dev)
+            self.sf = torch.empty((w.B, w.Hv, w.D, w.D), dtype=torch.float32, device=dev)
+            self.cu = to_torch(self.d["cu_seqlens"], dev) if self.varlen else None
+            self.tokens = int(self.t["v"].shape[0] if self.varlen else w.B * w.T)
+            ntok = self.tokens if self.varlen else w.T
+            # the workspace the library asks for (none: single-pass kernel), allocated once
+            self.ws_bytes = gdn.gdn_prefill_workspace_size(w.B, ntok, w.Hk, w.Hv, w.D, w.D,
+                                                           self.t["q"].dtype, self.varlen)
+            self.ws = (torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+                       if self.ws_bytes else None)
+
+        def __call__(self):
+            t = self.t
+            if self.varlen:
+                gdn.gdn_varlen_prefill(t["q"], t["k"], t["v"], t["alpha"], t["beta"], self.cu,
+                                       self.s0, out=self.out, final_state=self.sf,
+                                       workspace=self.ws, stream=stream)
+            else:
+                gdn.gdn_prefill_chunked(t["q"], t["k"], t["v"], t["alpha"], t["beta"], self.s0,
+                                        out=self.out, final_state=self.sf, workspace=self.ws,
+                                        stream=stream)
+
+        def kernels(self):
+            return (["prep_kernel", "chain_db_kernel"] if self.ws_bytes else ["prefill_kernel"])
+
+        def summary(self, ms_list, extra=None):
+            w = self.w
+            avg = float(np.mean(ms_list))
+            f_tok = prefill_flops_per_token(w.Hk, w.Hv, w.D, w.D)
+            tflops = self.tokens * f_tok / (avg * 1e-3) / 1e12
+            gbs = self.tokens * prefill_bytes_per_token(w.Hk, w.Hv, w.D, w.D) / (avg * 1e-3) / 1e9
+            r = {"workload": w.name, "tokens": self.tokens,
+                 "tokens_per_s": round(self.tokens / (avg * 1e-3), 1),
+                 "ms": round(avg, 5), "ms_median": round(float(np.median(ms_list)), 5),
+                 "ms_min": round(float(np.min(ms_list)), 5), "calls": len(ms_list),
+                 "path": ("two-pass (workspace %d bytes)" % self.ws_bytes if self.ws_bytes
+                          else "single-pass"),
+                 "algorithmic_tflops": round(tflops, 2),
+                 "frac_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+                 "required_io_GBps": round(gbs, 1),
+                 "roofline": {"kernels": self.kernels(), "bound": "mfma",
+                              "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                              "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                              "traffic": _traffic("prefill_" + w.name, pdig)}}
+            if extra:
+                r.update(extra)
+            return r
+
+        def free(self):
+            del self.t, self.out, self.sf, self.ws, self.s0, self.cu, self.d
+
+    def timed_calls(fn, reps, warm=1):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for i in range(reps):
+            evs[i][0].record(stream)
+            fn()
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+    # ------------------------------------------------------------ the step
+    K = args.steps
+    main_pf = Prefill(args.prefill_workload)
+    wd = WORKLOADS["decode_b256"]
+    dd = generate(wd)
     dt = {n: to_torch(dd[n], dev) for n in ("q", "k", "v", "alpha", "beta")}
     d_state = to_torch(dd["S0"], dev)
     d_out = torch.empty((wd.B, wd.Hv, wd.D), dtype=dt["q"].dtype, device=dev)
-    stream = torch.cuda.current_stream(dev)
-
-    def step_prefill():
-        if varlen:
-            gdn.gdn_varlen_prefill(pt["q"], pt["k"], pt["v"], pt["alpha"], pt["beta"], p_cu,
-                                   p_s0, out=p_out, final_state=p_sf, workspace=p_ws,
-                                   stream=stream)
-        else:
-            gdn.gdn_prefill_chunked(pt["q"], pt["k"], pt["v"], pt["alpha"], pt["beta"], p_s0,
-                                    out=p_out, final_state=p_sf, workspace=p_ws, stream=stream)
 
     def step_decode():
         gdn.gdn_decode_step(dt["q"], dt["k"], dt["v"], dt["alpha"], dt["beta"], d_state,
                             out=d_out, stream=stream)
 
     for _ in range(args.warmup):
-        step_prefill()
-        step_decode()
+        main_pf()
+        if not args.no_decode:
+            step_decode()
     torch.cuda.synchronize()
-
-    K = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     t0 = time.perf_counter()
     for i in range(K):
         ev[i][0].record(stream)
-        step_prefill()
+        main_pf()
         ev[i][1].record(stream)
-        step_decode()
+        if not args.no_decode:
+            step_decode()
         ev[i][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     pre_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
     dec_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
-    pre_avg = float(np.mean(pre_ms))
-    dec_avg = float(np.mean(dec_ms))
+    main_sum = main_pf.summary(pre_ms)
+    main_w = main_pf.w
+    main_pf.free()
+    del main_pf
 
-    # cold prefill: the inputs are evicted from the Infinity Cache first
-    cold_ms = []
-    if args.cold_steps > 0:
-        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        evc = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
-               for _ in range(args.cold_steps)]
-        for i in range(args.cold_steps):
-            scratch.fill_(i & 0xFF)
-            evc[i][0].record(stream)
-            step_prefill()
-            evc[i][1].record(stream)
-        torch.cuda.synchronize()
-        cold_ms = [e0.elapsed_time(e1) for e0, e1 in evc]
-        del scratch
+    decode = None
+    if not args.no_decode:
+        dec_avg = float(np.mean(dec_ms))
+        dec_bytes = decode_bytes_per_step(wd.B, wd.Hk, wd.Hv, wd.D, wd.D)
+        dec_gbs = dec_bytes / (dec_avg * 1e-3) / 1e9
+        decode = {"workload": wd.name, "GB_per_s": round(dec_gbs, 1), "ms": round(dec_avg, 5),
+                  "ms_median": round(float(np.median(dec_ms)), 5),
+                  "ms_min": round(float(np.min(dec_ms)), 5),
+                  "frac_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4),
+                  "tokens_per_s": round(wd.B / (dec_avg * 1e-3), 1),
+                  "roofline": {"kernel": "decode_kernel", "bound": "hbm",
+                               "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
+                               "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                               "traffic": _traffic("decode_" + wd.name, ddig)}}
 
-    # the same prefill emitting block-aligned prefix states (one per 1024
+    # ------------------------------------------------ the other prefill legs
+    legs = {}
+    c1 = None  # the layer prefill stays resident for the extra legs below
+    for name in [x for x in args.legs.split(",") if x]:
+        pf = Prefill(name)
+        reps = max(3, K // 2) if pf.tokens > 100000 else max(K, 10)
+        ms = timed_calls(pf, reps)
+        extra = None
+        if name == "layer_prefill_4k" and args.cold_steps > 0:
+            scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+            evc = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                   for _ in range(args.cold_steps)]
+            for i in range(args.cold_steps):
+                scratch.fill_(i & 0xFF)
+                evc[i][0].record(stream)
+                pf()
+                evc[i][1].record(stream)
+            torch.cuda.synchronize()
+            extra = {"ms_cold": round(float(np.median([a.elapsed_time(b) for a, b in evc])), 5)}
+            del scratch
+        legs[name] = pf.summary(ms, extra)
+        if name == "layer_prefill_4k":
+            c1 = pf
+        else:
+            pf.free()
+            del pf
+        torch.cuda.empty_cache()
+    if c1 is None and not (args.no_prefix and args.no_prepared and args.no_cpu_baseline):
+        c1 = Prefill("layer_prefill_4k")
+    wp = WORKLOADS["layer_prefill_4k"]
+
+    # the layer prefill emitting block-aligned prefix states (one per 1024
     # tokens): what a prefix cache keeps
     prefix = None
-    if not varlen and wp.T >= 1024 and not args.no_prefix:
+    if not args.no_prefix:
         every = 16
         rows = gdn.prefix_state_rows(wp.B, wp.T, every, False)
         p_pre = torch.empty((rows, wp.Hv, wp.D, wp.D), dtype=torch.float32, device=dev)
+        t = c1.t
 
         def step_prefill_prefix():
-            gdn.gdn_prefill_chunked(pt["q"], pt["k"], pt["v"], pt["alpha"], pt["beta"], p_s0,
-                                    out=p_out, final_state=p_sf, prefix_states=p_pre,
-                                    prefix_interval=every, workspace=p_ws, stream=stream)
-        step_prefill_prefix()
-        torch.cuda.synchronize()
-        evp = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
-        for i in range(K):
-            evp[i][0].record(stream)
-            step_prefill_prefix()
-            evp[i][1].record(stream)
-        torch.cuda.synchronize()
-        pp_ms = [e0.elapsed_time(e1) for e0, e1 in evp]
-        prefix = {"block_tokens": 64 * every, "states": rows * wp.Hv,
+            gdn.gdn_prefill_chunked(t["q"], t["k"], t["v"], t["alpha"], t["beta"], None,
+                                    out=c1.out, final_state=c1.sf, prefix_states=p_pre,
+                                    prefix_interval=every, workspace=c1.ws, stream=stream)
+        pp_ms = timed_calls(step_prefill_prefix, max(K, 10))
+        plain_ms = timed_calls(c1, max(K, 10))
+        prefix = {"workload": wp.name, "block_tokens": 64 * every, "states": rows * wp.Hv,
                   "bytes_written": rows * wp.Hv * wp.D * wp.D * 4,
                   "ms": round(float(np.mean(pp_ms)), 5),
                   "ms_median": round(float(np.median(pp_ms)), 5),
-                  "overhead_vs_plain": round(float(np.median(pp_ms)) / float(np.median(pre_ms)) - 1,
-                                             4)}
+                  "plain_ms_median": round(float(np.median(plain_ms)), 5),
+                  "overhead_vs_plain": round(float(np.median(pp_ms)) /
+                                             float(np.median(plain_ms)) - 1, 4)}
         del p_pre
 
-    # the same prefill and decode step from raw inputs (q, k before their L2
-    # normalisation, gate logits), prepared inside the kernels; beside them
-    # the time of a separate preparation pass (torch ops) over the same inputs
+    # the layer prefill and the decode step from raw inputs (q, k before
+    # their L2 normalisation, gate logits), prepared inside the kernels;
+    # beside them the time of a separate preparation pass (torch ops)
     prepared = None
-    if not varlen and not args.no_prepared:
+    if not args.no_prepared:
         flags = gdn.GDN_QK_L2NORM | gdn.GDN_GATE_LOGITS
         rp = generate(wp, raw=True)
         rt = {n: to_torch(rp[n], dev) for n in ("q", "k", "v", "alpha", "beta")}
@@ -268,18 +362,8 @@ def main():
         rdt = {n: to_torch(rd[n], dev) for n in ("q", "k", "v", "alpha", "beta")}
         r_state = to_torch(rd["S0"], dev)
 
-        def timed_ms(fn, reps):
-            fn()
-            torch.cuda.synchronize()
-            out_ms = []
-            for _ in range(reps):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                fn()
-                e1.record(stream)
-                torch.cuda.synchronize()
-                out_ms.append(e0.elapsed_time(e1))
-            return float(np.median(out_ms))
+        def med(fn):
+            return float(np.median(timed_calls(fn, max(K, 10))))
 
         def torch_prepare(t):
             qf, kf = t["q"].float(), t["k"].float()
@@ -288,17 +372,17 @@ def main():
             a = torch.exp(-torch.nn.functional.softplus(t["alpha"]))
             b = torch.sigmoid(t["beta"])
             return qn, kn, a, b
-        pre_raw = timed_ms(lambda: gdn.gdn_prefill_chunked(
-            rt["q"], rt["k"], rt["v"], rt["alpha"], rt["beta"], None, out=p_out, final_state=p_sf,
-            flags=flags, workspace=p_ws, stream=stream), K)
-        pre_plain = timed_ms(step_prefill, K)
-        pre_torch = timed_ms(lambda: torch_prepare(rt), K)
-        dec_raw = timed_ms(lambda: gdn.gdn_decode_step(
+        pre_raw = med(lambda: gdn.gdn_prefill_chunked(
+            rt["q"], rt["k"], rt["v"], rt["alpha"], rt["beta"], None, out=c1.out,
+            final_state=c1.sf, flags=flags, workspace=c1.ws, stream=stream))
+        pre_plain = med(c1)
+        pre_torch = med(lambda: torch_prepare(rt))
+        dec_raw = med(lambda: gdn.gdn_decode_step(
             rdt["q"], rdt["k"], rdt["v"], rdt["alpha"], rdt["beta"], r_state, out=d_out,
-            flags=flags, stream=stream), K)
-        dec_plain = timed_ms(step_decode, K)
-        dec_torch = timed_ms(lambda: torch_prepare(rdt), K)
-        prepared = {"flags": "GDN_QK_L2NORM | GDN_GATE_LOGITS",
+            flags=flags, stream=stream))
+        dec_plain = med(step_decode)
+        dec_torch = med(lambda: torch_prepare(rdt))
+        prepared = {"flags": "GDN_QK_L2NORM | GDN_GATE_LOGITS", "prefill_workload": wp.name,
                     "prefill_ms": round(pre_raw, 5), "prefill_plain_ms": round(pre_plain, 5),
                     "prefill_separate_torch_pass_ms": round(pre_torch, 5),
                     "decode_ms": round(dec_raw, 5), "decode_plain_ms": round(dec_plain, 5),
@@ -328,23 +412,14 @@ def main():
                 nws = gdn.gdn_prefill_workspace_size(ws_.B, ws_.T, ws_.Hk, ws_.Hv, ws_.D, ws_.D,
                                                      gt["q"].dtype, False)
                 g_ws = torch.empty(nws, dtype=torch.uint8, device=dev)
-                ms = []
-                for i in range(reps + 1):
-                    e0 = torch.cuda.Event(enable_timing=True)
-                    e1 = torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
-                    gdn.gdn_prefill_chunked(gt["q"], gt["k"], gt["v"], gt["alpha"], gt["beta"],
-                                            None, out=g_out, final_state=g_sf, workspace=g_ws,
-                                            stream=stream)
-                    e1.record(stream)
-                    torch.cuda.synchronize()
-                    if i:
-                        ms.append(e0.elapsed_time(e1))
-                med = float(np.median(ms))
+                ms = timed_calls(lambda: gdn.gdn_prefill_chunked(
+                    gt["q"], gt["k"], gt["v"], gt["alpha"], gt["beta"], None, out=g_out,
+                    final_state=g_sf, workspace=g_ws, stream=stream), reps)
+                med_ms = float(np.median(ms))
                 tf = ws_.B * ws_.T * prefill_flops_per_token(ws_.Hk, ws_.Hv, ws_.D, ws_.D) / (
-                    med * 1e-3) / 1e12
-                row[label] = {"ms": round(med, 5), "workspace_bytes": nws,
-                              "tokens_per_s": round(ws_.B * ws_.T / (med * 1e-3), 1),
+                    med_ms * 1e-3) / 1e12
+                row[label] = {"ms": round(med_ms, 5), "workspace_bytes": nws,
+                              "tokens_per_s": round(ws_.B * ws_.T / (med_ms * 1e-3), 1),
                               "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
                 del g_ws
             os.environ.pop("GDN_PREFILL_SEGMENTS", None)
@@ -352,8 +427,7 @@ def main():
             segmented[wname] = row
             del gt, dg, g_out, g_sf
 
-    # K tokens per sequence against a slot pool (speculative verification):
-    # timed on its own, after the step, on the same stream
+    # K tokens per sequence against a slot pool (speculative verification)
     multi = None
     if not args.no_multi:
         from gdn_synth import SPEC_DECODE, multi_decode
@@ -367,16 +441,7 @@ def main():
         def step_multi():
             gdn.gdn_decode_multi(mt["q"], mt["k"], mt["v"], mt["alpha"], mt["beta"], mt["pool"],
                                  mt["src_slot"], mt["dst_slot"], out=m_out, stream=stream)
-        for _ in range(max(args.warmup, 1)):
-            step_multi()
-        torch.cuda.synchronize()
-        evm = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
-        for i in range(K):
-            evm[i][0].record(stream)
-            step_multi()
-            evm[i][1].record(stream)
-        torch.cuda.synchronize()
-        m_ms = [e0.elapsed_time(e1) for e0, e1 in evm]
+        m_ms = timed_calls(step_multi, K, warm=max(args.warmup, 1))
         m_avg = float(np.mean(m_ms))
         m_bytes = decode_multi_bytes(wm["B"], wm["K"], wm["Hk"], wm["Hv"], wm["D"], wm["D"])
         m_gbs = m_bytes / (m_avg * 1e-3) / 1e9
@@ -390,9 +455,7 @@ def main():
                  "roofline": {"kernel": "decode_multi_kernel", "bound": "hbm",
                               "achieved": round(m_gbs, 1), "peak": PEAK_HBM_GBS,
                               "unit": "GB/s", "frac": round(m_gbs / PEAK_HBM_GBS, 4),
-                              "traffic": _traffic("decode_multi_" + wm["name"],
-                                                  _src_digest("gdn_decode.hip",
-                                                              "gdn_device.hpp"))}}
+                              "traffic": _traffic("decode_multi_" + wm["name"], ddig)}}
         del mt, dm
 
     # measured ceilings beside the spec peaks: a device-to-device copy and a
@@ -423,21 +486,9 @@ def main():
                     "bf16_gemm_tflops": round(2 * n ** 3 / t_gemm / 1e12, 1),
                     "gemm": "torch.matmul bf16 8192 x 8192 x 8192"}
 
-    tokens = int(pt["v"].shape[0] * (1 if varlen else pt["v"].shape[1]))
-    f_tok = prefill_flops_per_token(wp.Hk, wp.Hv, wp.D, wp.D)
-    pre_tflops = tokens * f_tok / (pre_avg * 1e-3) / 1e12
-    pre_tok_s = tokens / (pre_avg * 1e-3)
-    pre_gbs = tokens * prefill_bytes_per_token(wp.Hk, wp.Hv, wp.D, wp.D) / (pre_avg * 1e-3) / 1e9
-    dec_bytes = decode_bytes_per_step(wd.B, wd.Hk, wd.Hv, wd.D, wd.D)
-    dec_gbs = dec_bytes / (dec_avg * 1e-3) / 1e9
-
-    pdig = _src_digest("gdn_prefill.hip", "gdn_chunk.hpp", "gdn_device.hpp")
-    prefill_kernels = (["prep_kernel", "chain_db_kernel" if wp.D == 128 or wp.D == 64 else
-                        "chain_kernel"] if ws_bytes else ["prefill_kernel"])
-    ddig = _src_digest("gdn_decode.hip", "gdn_device.hpp")
     res = {
         "metric": METRIC,
-        "value": round(pre_tok_s, 1),
+        "value": main_sum["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
@@ -449,37 +500,24 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{wp.name} prefill + {wd.name} decode step",
-            "prefill": {"B": wp.B, "T": wp.T if not varlen else None, "tokens": tokens,
-                        "Hk": wp.Hk, "Hv": wp.Hv, "d": wp.D,
-                        "path": "two-pass (workspace %d bytes)" % ws_bytes if ws_bytes
-                        else "single-pass",
-                        "chunk": CHUNK, "io": "bf16 q/k/v/o, fp32 alpha/beta/state"},
-            "decode": {"B": wd.B, "Hk": wd.Hk, "Hv": wd.Hv, "d": wd.D,
-                       "state": "fp32, updated in place"},
+            "workload": f"{main_w.name} prefill" + ("" if args.no_decode else
+                                                    f" + {wd.name} decode step"),
+            "prefill": {"B": main_w.B, "T": main_w.T if main_w.kind == "prefill" else None,
+                        "tokens": main_sum["tokens"], "Hk": main_w.Hk, "Hv": main_w.Hv,
+                        "d": main_w.D, "path": main_sum["path"], "chunk": CHUNK,
+                        "io": "bf16 q/k/v/o, fp32 alpha/beta/state"},
+            "decode": None if args.no_decode else
+            {"B": wd.B, "Hk": wd.Hk, "Hv": wd.Hv, "d": wd.D, "state": "fp32, updated in place"},
         },
-        "prefill": {"tokens_per_s": round(pre_tok_s, 1), "ms": round(pre_avg, 5),
-                    "ms_median": round(float(np.median(pre_ms)), 5),
-                    "ms_min": round(float(np.min(pre_ms)), 5),
-                    "ms_cold": round(float(np.median(cold_ms)), 5) if cold_ms else None,
-                    "algorithmic_tflops": round(pre_tflops, 2),
-                    "frac_mfma_peak": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
-                    "required_io_GBps": round(pre_gbs, 1)},
-        "decode": {"GB_per_s": round(dec_gbs, 1), "ms": round(dec_avg, 5),
-                   "ms_median": round(float(np.median(dec_ms)), 5),
-                   "ms_min": round(float(np.min(dec_ms)), 5),
-                   "frac_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4),
-                   "tokens_per_s": round(wd.B / (dec_avg * 1e-3), 1)},
-        # the step's dominant kernel by time is the decode step
-        "roofline": {"kernel": "decode_kernel", "bound": "hbm",
-                     "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
-                     "traffic": _traffic("decode_" + wd.name, ddig)},
-        "roofline_prefill": {"kernels": prefill_kernels, "bound": "mfma",
-                             "achieved": round(pre_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                             "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
-                             "traffic": _traffic("prefill_" + wp.name, pdig)},
+        "prefill": main_sum,
+        # the step's headline: the long prefill (its kernels together)
+        "roofline": main_sum["roofline"],
     }
+    if decode is not None:
+        res["decode"] = decode
+        res["roofline_decode"] = decode["roofline"]
+    if legs:
+        res["prefill_legs"] = legs
     if prefix is not None:
         res["prefill_prefix_states"] = prefix
     if prepared is not None:
@@ -489,11 +527,15 @@ def main():
     if multi is not None:
         res["decode_multi"] = multi
     if ceilings is not None:
-        ceilings["decode_frac_of_copy"] = round(dec_gbs / ceilings["copy_GBps"], 4)
-        ceilings["prefill_frac_of_gemm"] = round(pre_tflops / ceilings["bf16_gemm_tflops"], 4)
+        if decode is not None:
+            ceilings["decode_frac_of_copy"] = round(decode["GB_per_s"] / ceilings["copy_GBps"], 4)
+        ceilings["prefill_frac_of_gemm"] = round(main_sum["algorithmic_tflops"] /
+                                                 ceilings["bf16_gemm_tflops"], 4)
         res["measured_ceilings"] = ceilings
-    if not args.no_cpu_baseline and not varlen:
-        res["cpu_baseline"] = cpu_baseline(dp, wp)
+    if not args.no_cpu_baseline:
+        if c1 is None:
+            c1 = Prefill("layer_prefill_4k")
+        res["cpu_baseline"] = cpu_baseline(c1.d, c1.w)
     print(json.dumps(res), flush=True)
 
 

@@ -9,7 +9,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn.so")
-SOURCES = ["gdn_api.hip", "gdn_prefill.hip", "gdn_decode.hip", "gdn_segment.hip"]
+SOURCES = ["gdn_api.hip", "gdn_prefill.hip", "gdn_chain4.hip", "gdn_decode.hip",
+           "gdn_segment.hip"]
 ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
 
 
@@ -19,8 +20,8 @@ def hipcc() -> str:
 
 
 def compile_flags() -> list:
-    """hipcc flags of the library (without inputs and output)."""
-    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    """hipcc flags of the library's objects (without inputs and output)."""
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
             "-Wall", "-Wno-unused-function",
             # no packed fp32 instructions (v_pk_*_f32) anywhere in device code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -30,17 +31,35 @@ def compile_flags() -> list:
             "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into one shared library; returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + compile_flags() + ["-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
+_NOISE = "'-packed-fp32-ops' is not a recognized feature for this target"
+
+
+def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "'-packed-fp32-ops' is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+    err = "\n".join(l for l in res.stderr.splitlines() if _NOISE not in l)
+    return res.returncode, err
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source (one hipcc per source, in parallel) and link
+    them into one shared library; returns its path."""
+    from concurrent.futures import ThreadPoolExecutor
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    cmds = [[hipcc()] + compile_flags() + ["-c", "-o", o, os.path.join(CSRC, s)]
+            for s, o in zip(SOURCES, objs)]
+    with ThreadPoolExecutor(len(cmds)) as ex:
+        results = list(ex.map(_run, cmds))
+    for (rc, err), s in zip(results, SOURCES):
+        if rc != 0:
+            raise RuntimeError(f"hipcc failed on {s} ({rc}):\n{err}")
+        if verbose and err.strip():
+            print(err, file=sys.stderr)
+    tmp = LIB + ".tmp"
+    rc, err = _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs)
+    if rc != 0:
+        raise RuntimeError(f"hipcc link failed ({rc}):\n{err}")
     os.replace(tmp, LIB)
     return LIB
 

@@ -5,49 +5,24 @@
 // Accepted calls enqueue their kernels on the caller's stream and return.
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
+
+#include <vector>
 
 #include "../../include/gdn.h"
 #include "gdn_launch.hpp"
+#include "gdn_validate.hpp"
 
 namespace {
+
+using namespace gdn::val;
 
 thread_local char g_detail[256];
 
 constexpr uint32_t kKnownFlags = GDN_QK_L2NORM | GDN_GATE_LOGITS;
 static_assert(GDN_QK_L2NORM == gdn::kQkL2Norm && GDN_GATE_LOGITS == gdn::kGateLogits,
               "flag values of the ABI and the kernels");
-
-struct Range {
-    uintptr_t lo, hi;  // [lo, hi); empty when lo == hi
-};
-
-Range range_of(const void *p, int64_t bytes) {
-    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-    return Range{a, bytes > 0 && p ? a + (uintptr_t)bytes : a};
-}
-
-bool overlap(const Range &a, const Range &b) {
-    if (a.lo == a.hi || b.lo == b.hi) return false;
-    return a.lo < b.hi && b.lo < a.hi;
-}
-
-bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-// a*b*c*... as int64 with overflow detection (all factors >= 0)
-bool mul_ok(int64_t &acc, int64_t f) {
-    if (f < 0) return false;
-    if (f != 0 && acc > INT64_MAX / f) return false;
-    acc *= f;
-    return true;
-}
-
-gdn_status_t check_heads(int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv) {
-    if (Hk < 1 || Hv < 1 || Dk < 1 || Dv < 1) return GDN_ERR_BAD_SHAPE;
-    if (Hv % Hk != 0) return GDN_ERR_BAD_SHAPE;
-    if (Dk != Dv || (Dk != 64 && Dk != 128)) return GDN_ERR_UNSUPPORTED;
-    return GDN_OK;
-}
 
 gdn_status_t hip_fail(hipError_t e, const char *where) {
     snprintf(g_detail, sizeof g_detail, "HIP error in %s: %s (%d)", where, hipGetErrorString(e),
@@ -64,58 +39,57 @@ gdn_status_t device_cus(int *cus) {
     return GDN_OK;
 }
 
-// Shared checks of the two prefill entry points. `tokens` is B*T or total_T,
-// `nstates` is B or N.
-gdn_status_t check_prefill(const void *q, const void *k, const void *v, const float *alpha,
-                           const float *beta, const float *s0, const void *out, const float *sf,
-                           const float *prefix, int64_t prefix_rows,
-                           const int32_t *cu, int64_t cu_count, int64_t tokens, int64_t nstates,
-                           int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv, gdn_dtype_t dtype,
-                           const void *ws, size_t ws_bytes) {
-    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
-    const int64_t es = dtype == GDN_BF16 ? 2 : 4;
-    int64_t nqk = tokens, nv = tokens, nab = tokens, nst = nstates;
-    if (!mul_ok(nqk, Hk) || !mul_ok(nqk, Dk) || !mul_ok(nqk, es)) return GDN_ERR_BAD_SHAPE;
-    if (!mul_ok(nv, Hv) || !mul_ok(nv, Dv) || !mul_ok(nv, es)) return GDN_ERR_BAD_SHAPE;
-    if (!mul_ok(nab, Hv) || !mul_ok(nab, 4)) return GDN_ERR_BAD_SHAPE;
-    if (!mul_ok(nst, Hv) || !mul_ok(nst, Dv) || !mul_ok(nst, Dk) || !mul_ok(nst, 4))
-        return GDN_ERR_BAD_SHAPE;
-    if (nstates * Hv > 0x7FFFFFFF / 8) return GDN_ERR_BAD_SHAPE;  // grid size
-    int64_t npre = prefix ? prefix_rows : 0;
-    if (!mul_ok(npre, Hv) || !mul_ok(npre, Dv) || !mul_ok(npre, Dk) || !mul_ok(npre, 4))
-        return GDN_ERR_BAD_SHAPE;
+// GDN_DEBUG=1 in the environment turns on the synchronous checks: the
+// contents of cu_seqlens before a packed prefill, and the workspace's status
+// word (set by a kernel whose bounded wait for another wave ran out) after a
+// prefill that used a workspace. They synchronise the stream, so they are
+// skipped for a stream that is being captured into a graph.
+bool debug_checks(hipStream_t stream) {
+    const char *e = getenv("GDN_DEBUG");
+    if (!e || e[0] != '1') return false;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(stream, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone;
+}
 
-    if (tokens > 0 && (!q || !k || !v || !alpha || !beta || !out)) return GDN_ERR_NULL_POINTER;
-    if (cu_count > 0 && !cu) return GDN_ERR_NULL_POINTER;
-    const void *ptrs[] = {q, k, v, alpha, beta, s0, out, sf, prefix, cu, ws};
-    for (const void *ptr : ptrs)
-        if (ptr && !aligned16(ptr)) return GDN_ERR_MISALIGNED;
-    if (ws_bytes > (size_t)INT64_MAX) return GDN_ERR_BAD_SHAPE;
+gdn_status_t debug_cu_seqlens(const int32_t *cu, int32_t N, int64_t total_T, hipStream_t stream) {
+    std::vector<int32_t> h((size_t)N + 1);
+    hipError_t e = hipMemcpyAsync(h.data(), cu, h.size() * 4, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "GDN_DEBUG copy of cu_seqlens");
+    return check_cu_seqlens(h.data(), N, total_T);
+}
 
-    const Range rq = range_of(q, nqk), rk = range_of(k, nqk), rv = range_of(v, nv);
-    const Range ra = range_of(alpha, nab), rb = range_of(beta, nab);
-    const Range rs0 = range_of(s0, nst), ro = range_of(out, nv), rsf = range_of(sf, nst);
-    const Range rcu = range_of(cu, cu_count * 4);
-    const Range inputs[] = {rq, rk, rv, ra, rb, rs0, rcu};
-    for (const Range &r : inputs)
-        if (overlap(ro, r) || overlap(ro, rsf)) return GDN_ERR_ALIAS;
-    if (sf && sf != s0) {
-        for (const Range &r : inputs)
-            if (overlap(rsf, r)) return GDN_ERR_ALIAS;
+gdn_status_t debug_clear_status(void *ws, hipStream_t stream) {
+    const hipError_t e = hipMemsetAsync(ws, 0, gdn::kWsStatusBytes, stream);
+    return e == hipSuccess ? GDN_OK : hip_fail(e, "GDN_DEBUG clear of the status word");
+}
+
+gdn_status_t debug_read_status(const void *ws, hipStream_t stream) {
+    int32_t word = 0;
+    hipError_t e = hipMemcpyAsync(&word, ws, 4, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "GDN_DEBUG read of the status word");
+    if (word != 0) {
+        snprintf(g_detail, sizeof g_detail,
+                 "a prefill kernel's bounded wait for another wave ran out (status word 0x%x); "
+                 "results of this call are invalid", (unsigned)word);
+        return GDN_ERR_HIP;
     }
-    if (sf && sf == s0) {
-        const Range others[] = {rq, rk, rv, ra, rb, rcu};
-        for (const Range &r : others)
-            if (overlap(rsf, r)) return GDN_ERR_ALIAS;
+    return GDN_OK;
+}
+
+// Launch of a prefill with the debug checks around it.
+gdn_status_t run_prefill(const gdn::PrefillParams &p, int dtype, int D, int cus, void *ws,
+                         size_t ws_bytes, int64_t slots, hipStream_t stream, bool debug,
+                         const char *where) {
+    const bool ws_used = ws && ws_bytes >= gdn::kWsStatusBytes;
+    if (debug && ws_used) {
+        const gdn_status_t st = debug_clear_status(ws, stream);
+        if (st != GDN_OK) return st;
     }
-    const Range rws = range_of(ws, (int64_t)ws_bytes);
-    const Range all[] = {rq, rk, rv, ra, rb, rs0, ro, rsf, rcu};
-    for (const Range &r : all)
-        if (overlap(rws, r)) return GDN_ERR_ALIAS;
-    const Range rpre = range_of(prefix, npre);
-    for (const Range &r : all)
-        if (overlap(rpre, r)) return GDN_ERR_ALIAS;
-    if (overlap(rpre, rws)) return GDN_ERR_ALIAS;
+    const hipError_t e = gdn::launch_prefill(p, dtype, D, cus, ws, ws_bytes, slots, stream);
+    if (e != hipSuccess) return hip_fail(e, where);
+    if (debug && ws_used) return debug_read_status(ws, stream);
     return GDN_OK;
 }
 
@@ -151,15 +125,11 @@ size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t tokens, int32_t Hk, 
     if (!gdn::prefill_wants_workspace((int64_t)num_seqs * Hv, cus)) return 0;
     const int64_t slots = gdn::prefill_ws_slots(num_seqs, total, packed ? 0 : tokens, packed != 0);
     const size_t recs = gdn::prefill_ws_bytes(slots, Hv, dtype == GDN_BF16 ? 1 : 0);
-    const size_t two_pass =
-        packed ? recs
-               : gdn::prefill_two_pass_ws_bytes(num_seqs, tokens, Hv, Dk,
-                                                dtype == GDN_BF16 ? 1 : 0, cus, recs);
     // few long sequences: the segmented path, whose layout also holds the above
     const size_t seg = packed ? 0
                               : gdn::prefill_seg_ws_bytes(num_seqs, tokens, Hv, Dk,
                                                           dtype == GDN_BF16 ? 1 : 0, cus);
-    return seg > two_pass ? seg : two_pass;
+    return gdn::kWsStatusBytes + (seg > recs ? seg : recs);
 }
 
 gdn_status_t gdn_prefill_chunked(const void *q, const void *k, const void *v, const float *alpha,
@@ -189,10 +159,8 @@ gdn_status_t gdn_prefill_chunked(const void *q, const void *k, const void *v, co
                          B,  Hk,    Hv,    scale,         prefix_rows ? prefix_states : nullptr,
                          prefix_interval, flags, (int64_t)Hv * Dv, false, false};
     const int64_t slots = gdn::prefill_ws_slots(B, tokens, T, false);
-    const hipError_t e = gdn::launch_prefill(p, dtype == GDN_BF16 ? 1 : 0, Dk, cus, workspace,
-                                             workspace_bytes, slots, stream);
-    if (e != hipSuccess) return hip_fail(e, "gdn_prefill_chunked launch");
-    return GDN_OK;
+    return run_prefill(p, dtype == GDN_BF16 ? 1 : 0, Dk, cus, workspace, workspace_bytes, slots,
+                       stream, debug_checks(stream), "gdn_prefill_chunked launch");
 }
 
 gdn_status_t gdn_varlen_prefill(const void *q, const void *k, const void *v, const float *alpha,
@@ -216,46 +184,26 @@ gdn_status_t gdn_varlen_prefill(const void *q, const void *k, const void *v, con
                        workspace, workspace_bytes);
     if (st != GDN_OK) return st;
     if (total_T == 0 && !final_state) return GDN_OK;
+    const bool debug = debug_checks(stream);
+    if (debug && (st = debug_cu_seqlens(cu_seqlens, N, total_T, stream)) != GDN_OK) return st;
     int cus = 0;
     if ((st = device_cus(&cus)) != GDN_OK) return st;
     gdn::PrefillParams p{q,          k,  v,  alpha, beta, initial_state, out, final_state,
                          cu_seqlens, 0,  N,  Hk,    Hv,   scale,         prefix_states,
                          prefix_interval, flags, (int64_t)Hv * Dv, false, false};
+    p.total_tokens = total_T;
     const int64_t slots = gdn::prefill_ws_slots(N, total_T, 0, true);
-    const hipError_t e = gdn::launch_prefill(p, dtype == GDN_BF16 ? 1 : 0, Dk, cus, workspace,
-                                             workspace_bytes, slots, stream);
-    if (e != hipSuccess) return hip_fail(e, "gdn_varlen_prefill launch");
-    return GDN_OK;
+    return run_prefill(p, dtype == GDN_BF16 ? 1 : 0, Dk, cus, workspace, workspace_bytes, slots,
+                       stream, debug, "gdn_varlen_prefill launch");
 }
 
 gdn_status_t gdn_decode_step(const void *q, const void *k, const void *v, const float *alpha,
                              const float *beta, float *state, void *out, int32_t B, int32_t Hk,
                              int32_t Hv, int32_t Dk, int32_t Dv, gdn_dtype_t dtype, float scale,
                              uint32_t flags, hipStream_t stream) {
-    gdn_status_t st = check_heads(Hk, Hv, Dk, Dv);
+    gdn_status_t st = check_decode(q, k, v, alpha, beta, state, out, B, Hk, Hv, Dk, Dv, dtype);
     if (st != GDN_OK) return st;
     if (flags & ~kKnownFlags) return GDN_ERR_UNSUPPORTED;
-    if (B < 1) return GDN_ERR_BAD_SHAPE;
-    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
-    if (!q || !k || !v || !alpha || !beta || !state || !out) return GDN_ERR_NULL_POINTER;
-    const int64_t es = dtype == GDN_BF16 ? 2 : 4;
-    int64_t nqk = B, nv = B, nab = B, nst = B;
-    if (!mul_ok(nqk, Hk) || !mul_ok(nqk, Dk) || !mul_ok(nqk, es)) return GDN_ERR_BAD_SHAPE;
-    if (!mul_ok(nv, Hv) || !mul_ok(nv, Dv) || !mul_ok(nv, es)) return GDN_ERR_BAD_SHAPE;
-    if (!mul_ok(nab, Hv) || !mul_ok(nab, 4)) return GDN_ERR_BAD_SHAPE;
-    if (!mul_ok(nst, Hv) || !mul_ok(nst, Dv) || !mul_ok(nst, Dk) || !mul_ok(nst, 4))
-        return GDN_ERR_BAD_SHAPE;
-    if ((int64_t)B * Hv > 0x7FFFFFFF) return GDN_ERR_BAD_SHAPE;
-    const void *ptrs[] = {q, k, v, alpha, beta, state, out};
-    for (const void *ptr : ptrs)
-        if (!aligned16(ptr)) return GDN_ERR_MISALIGNED;
-    const Range rq = range_of(q, nqk), rk = range_of(k, nqk), rv = range_of(v, nv);
-    const Range ra = range_of(alpha, nab), rb = range_of(beta, nab);
-    const Range rs = range_of(state, nst), ro = range_of(out, nv);
-    const Range inputs[] = {rq, rk, rv, ra, rb};
-    for (const Range &r : inputs)
-        if (overlap(ro, r) || overlap(rs, r)) return GDN_ERR_ALIAS;
-    if (overlap(ro, rs)) return GDN_ERR_ALIAS;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -271,41 +219,10 @@ gdn_status_t gdn_decode_multi(const void *q, const void *k, const void *v, const
                               float *step_states, int32_t B, int32_t K, int32_t Hk, int32_t Hv,
                               int32_t Dk, int32_t Dv, gdn_dtype_t dtype, float scale,
                               uint32_t flags, hipStream_t stream) {
-    gdn_status_t st = check_heads(Hk, Hv, Dk, Dv);
+    gdn_status_t st = check_decode_multi(q, k, v, alpha, beta, state_pool, num_slots, src_slot,
+                                         dst_slot, out, step_states, B, K, Hk, Hv, Dk, Dv, dtype);
     if (st != GDN_OK) return st;
     if (flags & ~kKnownFlags) return GDN_ERR_UNSUPPORTED;
-    if (B < 1 || K < 0 || num_slots < 1) return GDN_ERR_BAD_SHAPE;
-    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
-    if (!state_pool || !src_slot || !dst_slot) return GDN_ERR_NULL_POINTER;
-    if (K > 0 && (!q || !k || !v || !alpha || !beta || !out)) return GDN_ERR_NULL_POINTER;
-    const int64_t es = dtype == GDN_BF16 ? 2 : 4;
-    int64_t ntok = B;
-    if (!mul_ok(ntok, K)) return GDN_ERR_BAD_SHAPE;
-    int64_t nqk = ntok, nv = ntok, nab = ntok, nsteps = ntok, npool = num_slots;
-    if (!mul_ok(nqk, Hk) || !mul_ok(nqk, Dk) || !mul_ok(nqk, es)) return GDN_ERR_BAD_SHAPE;
-    if (!mul_ok(nv, Hv) || !mul_ok(nv, Dv) || !mul_ok(nv, es)) return GDN_ERR_BAD_SHAPE;
-    if (!mul_ok(nab, Hv) || !mul_ok(nab, 4)) return GDN_ERR_BAD_SHAPE;
-    if (!mul_ok(nsteps, Hv) || !mul_ok(nsteps, Dv) || !mul_ok(nsteps, Dk) || !mul_ok(nsteps, 4))
-        return GDN_ERR_BAD_SHAPE;
-    if (!mul_ok(npool, Hv) || !mul_ok(npool, Dv) || !mul_ok(npool, Dk) || !mul_ok(npool, 4))
-        return GDN_ERR_BAD_SHAPE;
-    if ((int64_t)B * Hv > 0x7FFFFFFF) return GDN_ERR_BAD_SHAPE;
-    const void *ptrs[] = {q, k, v, alpha, beta, state_pool, out, step_states};
-    for (const void *ptr : ptrs)
-        if (ptr && !aligned16(ptr)) return GDN_ERR_MISALIGNED;
-    if ((reinterpret_cast<uintptr_t>(src_slot) | reinterpret_cast<uintptr_t>(dst_slot)) & 3u)
-        return GDN_ERR_MISALIGNED;
-    const Range rq = range_of(q, nqk), rk = range_of(k, nqk), rv = range_of(v, nv);
-    const Range ra = range_of(alpha, nab), rb = range_of(beta, nab);
-    const Range rss = range_of(src_slot, (int64_t)B * 4), rds = range_of(dst_slot, (int64_t)B * 4);
-    const Range rp = range_of(state_pool, npool), ro = range_of(out, nv);
-    const Range rst = range_of(step_states, nsteps);
-    const Range reads[] = {rq, rk, rv, ra, rb, rss, rds};
-    const Range writes[] = {rp, ro, rst};
-    for (const Range &w : writes)
-        for (const Range &r : reads)
-            if (overlap(w, r)) return GDN_ERR_ALIAS;
-    if (overlap(rp, ro) || overlap(rp, rst) || overlap(ro, rst)) return GDN_ERR_ALIAS;
     gdn::DecodeMultiParams p{q,        k,        v,   alpha,       beta, state_pool,
                              src_slot, dst_slot, out, step_states, B,    K,
                              Hk,       Hv,       num_slots, scale, flags};

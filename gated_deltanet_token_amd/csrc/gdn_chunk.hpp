@@ -748,13 +748,20 @@ template <int D, int NB> struct Handoff {
 // outstanding LDS requests is needed.
 // The wait is bounded: the writer is another wave of the same workgroup,
 // which is always resident, so it ends; the bound only guarantees that a
-// wrong protocol cannot hang the device.
-__device__ __forceinline__ void wait_flag(int *flag, int target) {
+// wrong protocol cannot hang the device. When the bound runs out, the wave
+// ORs kStatusWaitBound into the caller's status word (device memory, or
+// nothing when `status` is null), which a debug check reads after the call.
+__device__ __forceinline__ void wait_flag(int *flag, int target, int *status) {
+    bool seen = false;
     for (int spin = 0; spin < (1 << 20); ++spin) {
-        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target)
+        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) {
+            seen = true;
             break;
+        }
         __builtin_amdgcn_s_sleep(1);
     }
+    if (!seen && status && (threadIdx.x & 63) == 0)
+        __hip_atomic_fetch_or(status, kStatusWaitBound, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("" ::: "memory");
 }
 __device__ __forceinline__ void set_flag(int *flag, int v) {
@@ -909,12 +916,13 @@ template <int D, int NB> struct OutCarry {
 template <int D, int NB>
 __device__ __forceinline__ void out_tail(Handoff<D, NB> ho, int *flag, int c, OutCarry<D, NB> &o,
                                          __bf16 *oc, int64_t sVO, int lenc, float scale, int g4,
-                                         int c16, int lane);
+                                         int c16, int lane, int *status);
 
 template <int D, int NB, bool EARLY_TAIL = false>
 __device__ __forceinline__ void out_step(const DbSmem &m, Handoff<D, NB> ho, int *flag, int c,
                                          OutCarry<D, NB> &o, __bf16 *oc_prev, int64_t sVO,
-                                         int lenc_prev, float scale, int g4, int c16, int lane) {
+                                         int lenc_prev, float scale, int g4, int c16, int lane,
+                                         int *status) {
     using F = bf16x8;
     constexpr int KS = D / 32;
     constexpr int KR = D * 2;
@@ -924,7 +932,7 @@ __device__ __forceinline__ void out_step(const DbSmem &m, Handoff<D, NB> ho, int
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) ld_chain_s<KR>(m.Q, 16 * mt, c16, 32 * kk + 4 * g4, fq[kk][mt]);
     if constexpr (EARLY_TAIL) {
-        if (c > 0) out_tail<D, NB>(ho, flag, c - 1, o, oc_prev, sVO, lenc_prev, scale, g4, c16, lane);
+        if (c > 0) out_tail<D, NB>(ho, flag, c - 1, o, oc_prev, sVO, lenc_prev, scale, g4, c16, lane, status);
     }
     F fp[kTriFrags];
 #pragma unroll
@@ -932,7 +940,7 @@ __device__ __forceinline__ void out_step(const DbSmem &m, Handoff<D, NB> ho, int
     float gamr[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) gamr[mt] = m.gamq[16 * mt + c16];
-    wait_flag(flag, 2 * c + 1);
+    wait_flag(flag, 2 * c + 1, status);
     F sf[KS][NB];
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
@@ -950,7 +958,7 @@ __device__ __forceinline__ void out_step(const DbSmem &m, Handoff<D, NB> ho, int
 #pragma unroll
             for (int b = 0; b < NB; ++b) acc[mt][b] = mma(sf[kk][b], fq[kk][mt], acc[mt][b]);
     if constexpr (!EARLY_TAIL) {
-        if (c > 0) out_tail<D, NB>(ho, flag, c - 1, o, oc_prev, sVO, lenc_prev, scale, g4, c16, lane);
+        if (c > 0) out_tail<D, NB>(ho, flag, c - 1, o, oc_prev, sVO, lenc_prev, scale, g4, c16, lane, status);
     }
 #pragma unroll
     for (int i = 0; i < kTriFrags; ++i) o.fp[i] = fp[i];
@@ -963,9 +971,9 @@ __device__ __forceinline__ void out_step(const DbSmem &m, Handoff<D, NB> ho, int
 template <int D, int NB>
 __device__ __forceinline__ void out_tail(Handoff<D, NB> ho, int *flag, int c, OutCarry<D, NB> &o,
                                          __bf16 *oc, int64_t sVO, int lenc, float scale, int g4,
-                                         int c16, int lane) {
+                                         int c16, int lane, int *status) {
     using F = bf16x8;
-    wait_flag(flag, 2 * c + 2);
+    wait_flag(flag, 2 * c + 2, status);
     const F *us = ho.u_slot(c);
     F fu[2][NB];
 #pragma unroll

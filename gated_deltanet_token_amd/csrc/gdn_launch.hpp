@@ -33,7 +33,15 @@ struct PrefillParams {
     const void *v2;
     void *out2;
     float *s_final2;
+    int64_t total_tokens;  // packed batches: tokens in the batch (offsets are clamped to it)
+    int *status;           // the workspace's status word (nullptr without a workspace)
 };
+
+// The prefill workspace starts with a status word (padded to 256 bytes): a
+// kernel whose bounded wait for another wave of its workgroup runs out ORs a
+// nonzero code into it. The rest of the workspace follows.
+constexpr size_t kWsStatusBytes = 256;
+constexpr int kStatusWaitBound = 1;
 
 // Input preparation flags (the ABI's GDN_QK_L2NORM, GDN_GATE_LOGITS).
 constexpr uint32_t kQkL2Norm = 1, kGateLogits = 2;
@@ -62,8 +70,9 @@ struct DecodeMultiParams {
     uint32_t flags;
 };
 
-// dtype: 0 = fp32, 1 = bf16. D: 64 or 128. Returns a hipError_t. With a
-// workspace of at least prefill_ws_bytes(nslots, ...) bytes (and when
+// dtype: 0 = fp32, 1 = bf16. D: 64 or 128. Returns a hipError_t. `ws` is
+// the caller's whole workspace (status word first). With at least
+// kWsStatusBytes + prefill_ws_bytes(nslots, ...) bytes (and when
 // prefill_wants_workspace agrees) the two-pass path runs; otherwise the
 // fused kernel.
 hipError_t launch_prefill(const PrefillParams &p, int dtype, int D, int num_cus, void *ws,
@@ -73,11 +82,6 @@ hipError_t launch_prefill(const PrefillParams &p, int dtype, int D, int num_cus,
 int64_t prefill_ws_slots(int64_t nseq, int64_t total_tokens, int64_t seq_len, bool packed);
 size_t prefill_ws_bytes(int64_t slots, int Hv, int dtype);
 bool prefill_wants_workspace(int64_t chains, int num_cus);
-// Two-pass workspace bytes for these shapes given the records' rec_bytes:
-// rec_bytes, or more when one long sequence runs its chunks in blocks (the
-// carried state after the records).
-size_t prefill_two_pass_ws_bytes(int64_t nseq, int64_t T, int Hv, int D, int dtype, int num_cus,
-                                 size_t rec_bytes);
 // Workspace bytes of the segmented prefill (dense bf16 batches with few
 // chains), or 0 when it does not apply to these shapes.
 size_t prefill_seg_ws_bytes(int64_t nseq, int64_t T, int Hv, int D, int dtype, int num_cus);
@@ -90,6 +94,11 @@ hipError_t launch_segment_scan(const float *s0, const float *n_end, const float 
 hipError_t launch_segment_correct(__bf16 *out, const __bf16 *o_id, const float *s_start,
                                   const int32_t *cu, int32_t B, int32_t P, int32_t Hv,
                                   int64_t seg_len, int32_t first_seg, int D, hipStream_t stream);
+// The two-pass chain with one wave per SIMD (gdn_chain4.hip): bf16, D = 128,
+// four value-column slices per head, plain or identity-free calls.
+bool chain4_supported(const PrefillParams &p, int D, int nsplit);
+hipError_t launch_chain4(const PrefillParams &p, const unsigned char *ws, int64_t nchain,
+                         hipStream_t stream);
 hipError_t launch_decode(const DecodeParams &p, int dtype, int D, hipStream_t stream);
 hipError_t launch_decode_multi(const DecodeMultiParams &p, int dtype, int D, hipStream_t stream);
 

@@ -30,9 +30,8 @@
 #include <float.h>
 #include <stdlib.h>
 
-#include <mutex>
-
 #include "gdn_chunk.hpp"
+#include "gdn_seq.hpp"
 #include <type_traits>
 
 #include "gdn_launch.hpp"
@@ -43,61 +42,6 @@ namespace gdn {
 // shared per-workgroup bookkeeping
 
 // Sequence bounds of sequence n.
-__device__ __forceinline__ void seq_bounds(const PrefillParams &p, int n, int64_t &tok0,
-                                           int64_t &len) {
-    if (p.cu_seqlens) {
-        tok0 = p.cu_seqlens[n];
-        len = (int64_t)p.cu_seqlens[n + 1] - tok0;
-    } else {
-        tok0 = (int64_t)n * p.seq_len;
-        len = p.seq_len;
-    }
-}
-
-// Workspace slot of chunk 0 of sequence n. Dense batches: n * ceil(T/64).
-// Packed batches: floor(cu[n] / 64) + n, which is injective over all
-// (sequence, chunk) pairs and below ceil(total/64) + N.
-__device__ __forceinline__ int64_t slot_base(const PrefillParams &p, int n) {
-    if (p.cu_seqlens) return (int64_t)(p.cu_seqlens[n] >> 6) + n;
-    return (int64_t)n * ((p.seq_len + kC - 1) / kC);
-}
-
-// Prefix states: the state after every block of 64 * prefix_every tokens of
-// a sequence (whole blocks only). Block i of sequence n goes to row
-//   dense : n * floor(T / blk) + i
-//   packed: floor(cu[n] / blk) + n + i   (injective, below floor(total/blk) + N)
-// The divisions run once per workgroup; per chunk the check is one compare
-// (this sits on the sequential path of the chain).
-struct PrefixRows {
-    int64_t next;  // chunk after which the next state is due; -1: none left
-    int64_t row;   // its row
-    int64_t left;  // states still due
-    __device__ __forceinline__ PrefixRows(const PrefillParams &p, int n, int64_t len) {
-        const int64_t every = p.prefix ? p.prefix_every : 1, blk = every * kC;
-        left = p.prefix ? len / blk : 0;
-        next = left > 0 ? every - 1 : -1;
-        row = p.cu_seqlens ? (int64_t)p.cu_seqlens[n] / blk + n : (int64_t)n * (p.seq_len / blk);
-    }
-    // Row for the state after chunk c, or -1; advances when one is due.
-    __device__ __forceinline__ int64_t take(const PrefillParams &p, int64_t c) {
-        if (c != next) return -1;
-        const int64_t r = row++;
-        next = --left > 0 ? next + p.prefix_every : -1;
-        return r;
-    }
-};
-
-// Logical workgroup id: workgroups are dispatched to the 8 XCDs round-robin;
-// give each XCD a contiguous range of logical ids so that workgroups sharing
-// a q/k head (and thus K, Q) share that XCD's L2.
-// A select, not a branch: the compiler then loads the kernel arguments in
-// one batch instead of waiting for remap_xcd before reading the grid size.
-__device__ __forceinline__ int logical_wg(int remap_xcd) {
-    const int wg = blockIdx.x;
-    const int remapped = (wg & 7) * (int)(gridDim.x >> 3) + (wg >> 3);
-    return remap_xcd ? remapped : wg;
-}
-
 // ----------------------------------------------------------------------------
 // staging of K, Q (row-major, K^T for bf16) and a V column slice (V^T for
 // bf16, row-major for fp32) through registers, one chunk ahead.
@@ -840,12 +784,6 @@ template <int D, int NC, int NH> struct ChainDbCfg {
     }
 };
 
-// LDS-DMA load of 16 bytes per lane (global -> LDS without registers): lane l
-// writes lds + 16 l, so a wave fills one contiguous KiB.
-__device__ __forceinline__ void dma16(const unsigned char *src, unsigned char *lds) {
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t *>(src), lds, 16, 0, 0);
-}
-
 // The LDS buffers allow one workgroup per CU.
 template <int D, int NC, int NH, bool PREFIX>
 __global__ __launch_bounds__((ChainDbCfg<D, NC, NH>::NW * 64)) __attribute__((amdgpu_waves_per_eu(1, 2)))
@@ -950,12 +888,12 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
             for (int64_t c = 0; c < npc; ++c) {
                 const int64_t cp = cb + (c > 0 ? c - 1 : 0);
                 out_step<D, 1, (Cf::NW > 8)>(smem_view(c), ho, flag, (int)c, carry, oh + cp * kC * sVO, sVO,
-                               lenc_of(cp), p.scale, g4, c16, lane);
+                               lenc_of(cp), p.scale, g4, c16, lane, p.status);
                 __syncthreads();
             }
             if (npc > 0)
                 out_tail<D, 1>(ho, flag, (int)npc - 1, carry, oh + (ce - 1) * kC * sVO,
-                               sVO, lenc_of(ce - 1), p.scale, g4, c16, lane);
+                               sVO, lenc_of(ce - 1), p.scale, g4, c16, lane, p.status);
         }
         return;
     }
@@ -1170,6 +1108,9 @@ static hipError_t launch_split_db(const PrefillParams &p, unsigned char *ws, int
     if (ChainDbCfg<D, NC, NH>::DVS * nsplit != D) return hipErrorInvalidValue;
     hipError_t e = launch_prep<__bf16, D, true>(p, ws, nprep, stream);
     if (e != hipSuccess) return e;
+    const char *ck = getenv("GDN_CHAIN");
+    if (ck && ck[0] == '4' && chain4_supported(p, D, nsplit))
+        return launch_chain4(p, ws, nchain, stream);
     if (p.prefix)
         hipLaunchKernelGGL((chain_db_kernel<D, NC, NH, true>), dim3((unsigned)nchain),
                            dim3(ChainDbCfg<D, NC, NH>::NW * 64), 0, stream, p,
@@ -1285,136 +1226,11 @@ static SegPlan seg_plan(int64_t nseq, int64_t T, int Hv, int D, int dtype, int n
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// ----------------------------------------------------------------------------
-// blocked two-pass prefill: one long dense sequence
-//
-// The chain kernel keeps a quarter of the CUs idle at the full layer (192
-// workgroups on 256 CUs), and a prep workgroup fits beside a chain workgroup
-// in a CU's LDS. So the chunks run in blocks: the chain walks block i on the
-// caller's stream while prep forms block i + 1's records on a side stream.
-// Events order the two (prep of block i before its chain; the side stream
-// first waits for the caller's earlier work, and the last chain waits for
-// the last prep), so nothing waits inside a kernel on another kernel. The
-// state passes from block to block through a workspace buffer after the
-// records, in place (a chain workgroup reads its rows of the initial state
-// before it writes them back); the arithmetic is the one-block run's, so the
-// results are the same bits.
-
-constexpr int kMaxBlocks = 16;
-
-// Blocks of a two-pass call: more than one only for one dense bf16 sequence
-// of at least 1,024 chunks on the double-buffered chain whose workgroups
-// leave a quarter of the CUs free; one block per 512 chunks, at most
-// kMaxBlocks (GDN_PREFILL_BLOCKS overrides).
-static int prefill_blocks(int64_t nseq, int64_t T, int Hv, int D, int dtype, int num_cus) {
-    if (nseq != 1 || dtype != 1) return 1;
-    const int64_t nchunks = (T + kC - 1) / kC;
-    const int ns = chain_slices(Hv, num_cus);
-    if (!(D == 64 || ns >= 2)) return 1;  // the single-slice D = 128 chain is another kernel
-    int64_t nb = 1;
-    if (nchunks >= 1024 && (int64_t)Hv * ns * 4 <= (int64_t)num_cus * 3)
-        nb = nchunks / 512 < kMaxBlocks ? nchunks / 512 : kMaxBlocks;
-    const int e = env_int("GDN_PREFILL_BLOCKS", 0);
-    if (e >= 1) nb = e < kMaxBlocks ? e : kMaxBlocks;
-    if (nb > nchunks) nb = nchunks > 0 ? nchunks : 1;
-    return (int)nb;
-}
-
-size_t prefill_two_pass_ws_bytes(int64_t nseq, int64_t T, int Hv, int D, int dtype, int num_cus,
-                                 size_t rec_bytes) {
-    if (prefill_blocks(nseq, T, Hv, D, dtype, num_cus) < 2) return rec_bytes;
-    return align256(rec_bytes) + (size_t)nseq * Hv * D * D * 4;
-}
-
-struct SideStream {
-    hipStream_t s = nullptr;
-    hipEvent_t ev[kMaxBlocks + 1] = {};  // per block (prep done), then the fork
-};
-static std::mutex g_side_mu;
-static SideStream g_side[64];
-
-// The calling thread's device's side stream, created on first use (default
-// priority) and kept until the process ends. Call with g_side_mu held.
-static hipError_t side_stream(SideStream **out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    SideStream &ss = g_side[dev];
-    if (!ss.s) {
-        SideStream n;
-        for (auto &ev : n.ev) {
-            e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
-            if (e != hipSuccess) break;
-        }
-        if (e == hipSuccess) e = hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking);
-        if (e != hipSuccess) {
-            for (auto &ev : n.ev)
-                if (ev) (void)hipEventDestroy(ev);
-            return e;
-        }
-        ss = n;
-    }
-    *out = &ss;
-    return hipSuccess;
-}
-
-template <int D, int NC, int NH>
-static hipError_t launch_db_blocks(const PrefillParams &p, unsigned char *ws, int nsplit, int nb,
-                                   float *carry, hipStream_t stream) {
-    const int64_t nchunks = (p.seq_len + kC - 1) / kC;
-    const int64_t nchain = (int64_t)p.Hv * nsplit;
-    if (ChainDbCfg<D, NC, NH>::DVS * nsplit != D) return hipErrorInvalidValue;
-    std::lock_guard<std::mutex> lock(g_side_mu);
-    SideStream *ss = nullptr;
-    hipError_t e = side_stream(&ss);
-    if (e != hipSuccess) return e;
-    // block 0 is short (1/32 of the chunks): its prep runs alone, before any
-    // chain; the other blocks share the rest evenly
-    const int64_t first = nchunks / 32 > 0 ? nchunks / 32 : 1;
-    auto edge = [&](int i) {
-        return i == 0 ? 0 : first + (nchunks - first) * (i - 1) / (nb - 1);
-    };
-    auto prep_block = [&](int i) -> hipError_t {
-        PrefillParams pp = p;
-        pp.chunk0 = edge(i);
-        pp.chunk_end = edge(i + 1);
-        const hipError_t r =
-            launch_prep<__bf16, D, true>(pp, ws, (edge(i + 1) - edge(i)) * p.Hv, ss->s);
-        return r != hipSuccess ? r : hipEventRecord(ss->ev[i], ss->s);
-    };
-    // fork: the side stream starts after the caller's earlier work
-    e = hipEventRecord(ss->ev[kMaxBlocks], stream);
-    if (e == hipSuccess) e = hipStreamWaitEvent(ss->s, ss->ev[kMaxBlocks], 0);
-    if (e == hipSuccess) e = prep_block(0);
-    for (int i = 0; i < nb && e == hipSuccess; ++i) {
-        e = hipStreamWaitEvent(stream, ss->ev[i], 0);  // block i's records are written
-        if (e == hipSuccess && i + 1 < nb) e = prep_block(i + 1);
-        if (e != hipSuccess) break;
-        PrefillParams pc = p;
-        pc.chunk0 = edge(i);
-        pc.chunk_end = edge(i + 1);
-        pc.s0 = i == 0 ? p.s0 : carry;
-        pc.s_final = i + 1 == nb ? p.s_final : carry;
-        hipLaunchKernelGGL((chain_db_kernel<D, NC, NH, false>), dim3((unsigned)nchain),
-                           dim3(ChainDbCfg<D, NC, NH>::NW * 64), 0, stream, pc,
-                           (const unsigned char *)ws, nsplit, nchain % 8 == 0 ? 1 : 0);
-        e = hipGetLastError();
-    }
-    return e;
-}
-
-// The two-pass chain on the double-buffered kernel: blocked when planned and
-// the stream is not being captured into a graph, else one launch pair.
+// The two-pass chain on the double-buffered kernel: one prep launch over all
+// chunks, then one chain launch.
 template <int D, int NC, int NH>
 static hipError_t run_split_db(const PrefillParams &p, unsigned char *ws, int64_t nslots,
-                               int nsplit, int nb, float *carry, hipStream_t stream) {
-    if (nb > 1 && carry && p.nseq == 1 && !p.cu_seqlens && !p.prefix && !p.records_ready &&
-        !p.s0_identity) {
-        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-        if (hipStreamIsCapturing(stream, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone)
-            return launch_db_blocks<D, NC, NH>(p, ws, nsplit, nb, carry, stream);
-    }
+                               int nsplit, hipStream_t stream) {
     return launch_split_db<D, NC, NH>(p, ws, nslots, nsplit, stream);
 }
 
@@ -1450,6 +1266,9 @@ size_t prefill_seg_ws_bytes(int64_t nseq, int64_t T, int Hv, int D, int dtype, i
     return sp.P ? seg_layout(nseq, T, Hv, D, sp).total : 0;
 }
 
+static hipError_t launch_prefill_ws(const PrefillParams &p, int dtype, int D, int num_cus,
+                                   void *ws, size_t ws_bytes, int64_t nslots, hipStream_t stream);
+
 static hipError_t launch_segmented(const PrefillParams &p, int D, int num_cus, unsigned char *ws,
                                    const SegPlan &sp, hipStream_t stream) {
     const int64_t B = p.nseq, T = p.seq_len;
@@ -1468,6 +1287,7 @@ static hipError_t launch_segmented(const PrefillParams &p, int D, int num_cus, u
     // 1. every segment from a zero state: outputs o^0 (into out), end states N_j
     PrefillParams pz = p;
     pz.cu_seqlens = cu;
+    pz.total_tokens = B * T;
     pz.nseq = nsegs;
     pz.seq_len = 0;
     pz.s0 = nullptr;
@@ -1488,7 +1308,7 @@ static hipError_t launch_segmented(const PrefillParams &p, int D, int num_cus, u
         pz.out2 = o_id;
         pz.s_final2 = m_end;
     }
-    e = launch_prefill(pz, 1, D, num_cus, ws + l.rec, rec_bytes, slots, stream);
+    e = launch_prefill_ws(pz, 1, D, num_cus, ws + l.rec, rec_bytes, slots, stream);
     if (e != hipSuccess) return e;
     if (!merge) {
         PrefillParams pi = pz;
@@ -1498,7 +1318,7 @@ static hipError_t launch_segmented(const PrefillParams &p, int D, int num_cus, u
         pi.records_ready = true;  // same q, k, alpha, beta and slots as step 1
         pi.out = o_id;
         pi.s_final = m_end;
-        e = launch_prefill(pi, 1, D, num_cus, ws + l.rec, rec_bytes, slots, stream);
+        e = launch_prefill_ws(pi, 1, D, num_cus, ws + l.rec, rec_bytes, slots, stream);
         if (e != hipSuccess) return e;
     }
     // 3. the scan over segments; 4. the corrections (segment 0 only from a
@@ -1510,8 +1330,8 @@ static hipError_t launch_segmented(const PrefillParams &p, int D, int num_cus, u
                                   sp.P, p.Hv, sp.L, p.s0 ? 0 : 1, D, stream);
 }
 
-hipError_t launch_prefill(const PrefillParams &p, int dtype, int D, int num_cus, void *ws,
-                          size_t ws_bytes, int64_t nslots, hipStream_t stream) {
+static hipError_t launch_prefill_ws(const PrefillParams &p, int dtype, int D, int num_cus,
+                                   void *ws, size_t ws_bytes, int64_t nslots, hipStream_t stream) {
     if (!p.cu_seqlens && !p.prefix && !p.s0_identity && ws) {
         const SegPlan sp = seg_plan(p.nseq, p.seq_len, p.Hv, D, dtype, num_cus);
         if (sp.P && ws_bytes >= seg_layout(p.nseq, p.seq_len, p.Hv, D, sp).total)
@@ -1526,25 +1346,18 @@ hipError_t launch_prefill(const PrefillParams &p, int dtype, int D, int num_cus,
         // double-buffered chain kernel fills a CU's LDS), at most four.
         const int ns = chain_slices(chains, num_cus);
         unsigned char *w = static_cast<unsigned char *>(ws);
-        // blocks of one long sequence, when the workspace holds the carried state
-        int nb = p.cu_seqlens ? 1 : prefill_blocks(p.nseq, p.seq_len, p.Hv, D, dtype, num_cus);
-        const size_t rec = prefill_ws_bytes(nslots, p.Hv, dtype);
-        float *carry = nullptr;
-        if (nb > 1 && ws_bytes >= align256(rec) + (size_t)p.nseq * p.Hv * D * D * 4)
-            carry = reinterpret_cast<float *>(w + align256(rec));
-        if (!carry) nb = 1;
         if (dtype == 1 && D == 128) {
             switch (ns) {
             case 1: return launch_split<__bf16, 128, 4, 32>(p, w, nslots, 1, stream);
-            case 2: return run_split_db<128, 4, 1>(p, w, nslots, 2, nb, carry, stream);
-            case 4: return run_split_db<128, 2, 1>(p, w, nslots, 4, nb, carry, stream);
-            default: return run_split_db<128, 1, 1>(p, w, nslots, 8, nb, carry, stream);
+            case 2: return run_split_db<128, 4, 1>(p, w, nslots, 2, stream);
+            case 4: return run_split_db<128, 2, 1>(p, w, nslots, 4, stream);
+            default: return run_split_db<128, 1, 1>(p, w, nslots, 8, stream);
             }
         } else if (dtype == 1 && D == 64) {
             switch (ns) {
-            case 1: return run_split_db<64, 4, 1>(p, w, nslots, 1, nb, carry, stream);
-            case 2: return run_split_db<64, 2, 1>(p, w, nslots, 2, nb, carry, stream);
-            default: return run_split_db<64, 1, 1>(p, w, nslots, 4, nb, carry, stream);
+            case 1: return run_split_db<64, 4, 1>(p, w, nslots, 1, stream);
+            case 2: return run_split_db<64, 2, 1>(p, w, nslots, 2, stream);
+            default: return run_split_db<64, 1, 1>(p, w, nslots, 4, stream);
             }
         } else if (dtype == 0 && D == 64) {
             switch (ns) {
@@ -1602,6 +1415,16 @@ hipError_t launch_prefill(const PrefillParams &p, int dtype, int D, int num_cus,
         }
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill(const PrefillParams &p, int dtype, int D, int num_cus, void *ws,
+                          size_t ws_bytes, int64_t nslots, hipStream_t stream) {
+    if (!ws || ws_bytes < kWsStatusBytes) return launch_prefill_ws(p, dtype, D, num_cus, nullptr, 0,
+                                                                   nslots, stream);
+    PrefillParams pw = p;
+    pw.status = static_cast<int *>(ws);
+    return launch_prefill_ws(pw, dtype, D, num_cus, static_cast<unsigned char *>(ws) + kWsStatusBytes,
+                             ws_bytes - kWsStatusBytes, nslots, stream);
 }
 
 }  // namespace gdn

@@ -23,11 +23,10 @@
  *    stated per call, and 16-byte aligned. q, k, v and out have the element
  *    type `dtype` (GDN_BF16 or GDN_F32); alpha, beta and states are fp32.
  *  - Ownership: the caller owns every buffer. The library allocates and
- *    frees no memory and keeps no pointer after the call returns; calls are
- *    re-entrant and thread-safe. Its one piece of lasting state: the blocked
- *    two-pass prefill (gdn_prefill_chunked) creates, on its first use on a
- *    device, one side stream (default priority) and 17 events there, kept
- *    until the process ends; a lock serialises their use.
+ *    frees no memory, creates no stream or event, keeps no pointer after the
+ *    call returns and holds no mutable global state; calls are re-entrant
+ *    and thread-safe (two calls that share a workspace must not overlap in
+ *    time on the device, like any two users of one buffer).
  *  - Asynchrony: each call validates its arguments on the host, enqueues
  *    kernels on `stream` and returns without synchronising. Results are
  *    ready when the stream reaches that point.
@@ -38,6 +37,13 @@
  *  - Values are not validated: NaN or Inf inputs propagate. alpha and beta
  *    are meant to lie in [0, 1]; alpha is clamped to >= FLT_MIN before its
  *    logarithm is taken.
+ *  - Debug checks: with GDN_DEBUG=1 in the environment, the prefill calls
+ *    also run synchronous checks (they synchronise `stream`, and are skipped
+ *    while the stream is being captured into a graph): the contents of
+ *    cu_seqlens (GDN_ERR_BAD_SHAPE before any launch when malformed), and,
+ *    after a call that used a workspace, its status word (GDN_ERR_HIP when a
+ *    kernel's bounded wait for another wave of its workgroup ran out, which
+ *    a correct run never does).
  *  - `out` must not overlap any input. `final_state` must either be the same
  *    pointer as `initial_state` (in-place update) or not overlap it, and it
  *    must not overlap any other argument.
@@ -110,22 +116,17 @@ enum { GDN_QK_L2NORM = 1, GDN_GATE_LOGITS = 2 };
  *
  * workspace: optional device scratch of workspace_bytes bytes (16-byte
  * aligned, disjoint from every other argument, contents ignored and
- * overwritten; the caller keeps ownership). When it holds at least
+ * overwritten; the caller keeps ownership). Its first 256 bytes hold a status
+ * word (see "Debug checks" above). When it holds at least
  * gdn_prefill_workspace_size() bytes the call may run in two passes: the
  * state-independent per-chunk factors of all chunks first, then the
  * sequential state chain. NULL (or too small) selects the single-pass
- * kernel. Both give the same result up to rounding. With the workspace, two
- * more arrangements may run, chosen by shape (and both disabled for a
- * workspace smaller than the size query's answer):
- *  - few (sequence, value head) chains, bf16, no prefix states: each
- *    sequence is split into segments run in parallel from zero and from the
- *    identity state, and joined by a scan of the segment maps and an output
- *    correction (same result up to rounding);
- *  - one long sequence (B = 1, at least 1,024 chunks, bf16): the two passes
- *    run in blocks of chunks, the chain of block i on `stream` while the
- *    factors of block i + 1 are formed on the library's side stream, ordered
- *    by events only; the result is bit-identical to the run in one block. A
- *    stream being captured into a graph gets the run in one block.
+ * kernel. Both give the same result up to rounding. With few (sequence,
+ * value head) chains, bf16 and no prefix states, a workspace of the size
+ * query's answer also allows the segmented arrangement: each sequence is
+ * split into segments run in parallel from zero and from the identity
+ * state, joined by a scan of the segment maps and an output correction
+ * (same result up to rounding).
  */
 gdn_status_t gdn_prefill_chunked(const void *q, const void *k, const void *v,
                                  const float *alpha, const float *beta,
@@ -211,7 +212,10 @@ gdn_status_t gdn_decode_multi(const void *q, const void *k, const void *v,
  *   cu_seqlens    [N + 1] int32, DEVICE memory: sequence n spans tokens
  *                 cu_seqlens[n] .. cu_seqlens[n+1]-1; cu_seqlens[0] = 0,
  *                 non-decreasing, cu_seqlens[N] = total_T. Its contents are
- *                 not checked (malformed offsets are undefined behaviour).
+ *                 checked only under GDN_DEBUG=1. Otherwise the kernels clamp
+ *                 each sequence's start and end into [0, total_T] (end >=
+ *                 start), so malformed offsets give meaningless results but
+ *                 no access outside the caller's buffers.
  *   initial_state [N, Hv, Dv, Dk] fp32 or NULL (zero states)
  *   final_state   [N, Hv, Dv, Dk] fp32 or NULL; may equal initial_state
  *   prefix_states [floor(total_T / L) + N, Hv, Dv, Dk] fp32 or NULL, with
@@ -246,12 +250,11 @@ gdn_status_t gdn_varlen_prefill(const void *q, const void *k, const void *v,
  * Returns 0 when the library would not use a workspace for this shape on the
  * current device (enough (sequence, value head) pairs to fill it in one
  * pass), when an argument is invalid, or when no device is available. The
- * base size is 17,152 bytes (bf16) or 33,536 bytes (fp32) per (64-token
- * chunk, value head): B * ceil(T/64) chunks, or ceil(total_T/64) + N for
- * packed batches. It is larger where gdn_prefill_chunked would run
- * segmented (the segment end states, maps, start states and the
- * identity-start outputs) or in blocks (plus, after 256-byte alignment,
- * Hv * Dv * Dk * 4 bytes for the state carried between blocks).
+ * size is 256 bytes (the status word) plus 17,152 bytes (bf16) or 33,536
+ * bytes (fp32) per (64-token chunk, value head): B * ceil(T/64) chunks, or
+ * ceil(total_T/64) + N for packed batches. It is larger where
+ * gdn_prefill_chunked would run segmented (the segment end states, maps,
+ * start states and the identity-start outputs).
  */
 size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t tokens, int32_t Hk,
                                   int32_t Hv, int32_t Dk, int32_t Dv,

@@ -3,10 +3,10 @@
 Every case draws seeded synthetic inputs, runs the library on cuda:0 and
 compares with the oracle on the same bits. Metric (per (sequence, value
 head) slice, max |x - r| / max |r|) and tolerances (2e-2 for bf16 inputs,
-1e-4 for fp32) are in tests/parity.py. Full-size workloads that the oracle
-cannot redo whole (the 262,144-token prefill and the 64-sequence varlen
-batch) are checked on sampled (sequence, head) chains, each run by the oracle
-over its full length.
+1e-4 for fp32) are in tests/parity.py. The full-size workloads (the
+262,144-token prefill and the 64-sequence varlen batch) are checked chain by
+chain over every (sequence, value head) pair, each chain run by the oracle
+over its full length on host threads and compared as it finishes.
 """
 import os
 
@@ -91,10 +91,11 @@ def test_workspace_path_is_taken_for_small_batches(gdn):
     """48 chains (B=1, the layer's value heads) ask for a workspace; a batch
     with enough chains does not."""
     n = gdn.gdn_prefill_workspace_size(1, 4096, 16, 48, 128, 128, gdn.GDN_BF16, 0)
-    assert n == 64 * 48 * (2 * 64 * 64 * 2 + 4 * 64 * 4)  # T, P and four decay vectors
+    # the status word (256 bytes), then T, P and four decay vectors per (chunk, value head)
+    assert n == 256 + 64 * 48 * (2 * 64 * 64 * 2 + 4 * 64 * 4)
     assert gdn.gdn_prefill_workspace_size(64, 4096, 16, 48, 128, 128, gdn.GDN_BF16, 0) == 0
     assert gdn.gdn_prefill_workspace_size(2, 130, 16, 48, 128, 128, gdn.GDN_BF16, 1) == \
-        (3 + 2) * 48 * (2 * 64 * 64 * 2 + 4 * 64 * 4)
+        256 + (3 + 2) * 48 * (2 * 64 * 64 * 2 + 4 * 64 * 4)
 
 
 def test_tiny_f32_workload(gdn):
@@ -698,51 +699,27 @@ def test_segmented_prefill(gdn, monkeypatch, B, T, Hk, Hv, D, segs, init, flags,
           f"alpha shift {ashift}")
 
 
-@pytest.mark.parametrize("D,blocks,init", [(128, "2", True), (128, "3", False), (128, "8", True),
-                                           (64, "3", True)])
-def test_prefill_blocks_match_one_block(gdn, monkeypatch, D, blocks, init):
-    """One sequence run in chunk blocks (the chain of block i beside the prep
-    of block i + 1 on a side stream, the state carried through the
-    workspace): the same bits as the run in one block, and within tolerance
-    of the oracle."""
-    monkeypatch.setenv("GDN_PREFILL_SEGMENTS", "0")
-    T = 64 * 40 + 17  # 41 chunks, the last one partial
-    d = small_prefill(1, T, 2, 6, D, "bf16", seed=193 + D, init_state=init, alpha_shift=-5.0)
-    q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
-    s0 = to_torch(d["S0"], DEV) if init else None
-    res = {}
-    for nb in ("1", blocks):
-        monkeypatch.setenv("GDN_PREFILL_BLOCKS", nb)
-        res[nb] = gdn.gdn_prefill_chunked(q, k, v, a, b, s0)
-        torch.cuda.synchronize()
-    assert torch.equal(res["1"][0], res[blocks][0])
-    assert torch.equal(res["1"][1], res[blocks][1])
-    o_ref, S_ref = oracle.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"],
-                                  d["S0"] if init else None)
-    check(from_torch(res[blocks][0]), from_torch(res[blocks][1]), o_ref, S_ref, "bf16",
-          f"{blocks} blocks D{D} init={init}")
-
-
-def test_prefill_blocks_in_place_and_captured(gdn, monkeypatch):
-    """Chunk blocks with the state updated in place (initial and final state
-    the same buffer), and the same call captured in a graph (which runs in
-    one block, without the side stream): both equal the one-block run bit
-    for bit, every replay included."""
+def test_prefill_two_pass_in_place_and_captured(gdn, monkeypatch):
+    """The two-pass run of one sequence with the state updated in place
+    (initial and final state the same buffer), and the same call captured in
+    a graph and replayed: both equal the plain call bit for bit, every
+    replay included."""
     monkeypatch.setenv("GDN_PREFILL_SEGMENTS", "0")
     T = 64 * 24 + 9
     d = small_prefill(1, T, 2, 6, 128, "bf16", seed=199, init_state=True, alpha_shift=-5.0)
     q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
-    monkeypatch.setenv("GDN_PREFILL_BLOCKS", "1")
-    ref_o, ref_s = gdn.gdn_prefill_chunked(q, k, v, a, b, to_torch(d["S0"], DEV))
-    monkeypatch.setenv("GDN_PREFILL_BLOCKS", "3")
     n = gdn.gdn_prefill_workspace_size(1, T, 2, 6, 128, 128, gdn.GDN_BF16, 0)
+    assert n > 0
     ws = torch.empty(n, dtype=torch.uint8, device=DEV)
+    ref_o, ref_s = gdn.gdn_prefill_chunked(q, k, v, a, b, to_torch(d["S0"], DEV), workspace=ws)
     st = to_torch(d["S0"], DEV)
     out = torch.empty(v.shape, dtype=torch.bfloat16, device=DEV)
     gdn.gdn_prefill_chunked(q, k, v, a, b, st, out=out, final_state=st, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(out, ref_o)
     assert torch.equal(st, ref_s)
+    o_ref, S_ref = oracle.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"])
+    check(from_torch(out), from_torch(st), o_ref, S_ref, "bf16", "two-pass in place")
     s0_g = to_torch(d["S0"], DEV)
     sf_g = torch.empty_like(s0_g)
     out_g = torch.empty_like(out)
@@ -759,6 +736,33 @@ def test_prefill_blocks_in_place_and_captured(gdn, monkeypatch):
         torch.cuda.synchronize()
         assert torch.equal(out_g, ref_o), r
         assert torch.equal(sf_g, ref_s), r
+
+
+def test_debug_checks_reject_bad_offsets(gdn, monkeypatch):
+    """GDN_DEBUG=1: malformed cu_seqlens (not starting at 0, decreasing, not
+    ending at total_T) are refused with GDN_ERR_BAD_SHAPE before any kernel
+    runs; well-formed ones pass, and the workspace status word reads clean
+    after a two-pass call."""
+    monkeypatch.setenv("GDN_DEBUG", "1")
+    d = generate_packed(2, 6, 128, "bf16", 77, [100, 50, 170], init_state=True)
+    q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
+    total = int(d["cu_seqlens"][-1])
+    for bad in ([5, 100, 150, 320], [0, 150, 100, 320], [0, 100, 150, 300]):
+        cu = torch.tensor(bad, dtype=torch.int32, device=DEV)
+        with pytest.raises(gdn.GDNError) as ei:
+            gdn.gdn_varlen_prefill(q, k, v, a, b, cu, None)
+        assert ei.value.status == 2, bad
+    assert total == 320
+    cu = to_torch(d["cu_seqlens"], DEV)
+    out, sf = gdn.gdn_varlen_prefill(q, k, v, a, b, cu, to_torch(d["S0"], DEV))
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.varlen(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["cu_seqlens"],
+                                 d["S0"])
+    o, c = from_torch(out), d["cu_seqlens"]
+    for n in range(3):
+        e = max_error(o[c[n]:c[n + 1]][None], o_ref[c[n]:c[n + 1]][None], (0, 2))
+        assert e <= TOL["bf16"], (n, e)
+    check(o[:0], from_torch(sf), o_ref[:0], S_ref, "bf16", "GDN_DEBUG varlen states")
 
 
 @pytest.mark.parametrize("D,segs", [(128, "4"), (128, "7"), (64, "5")])
@@ -846,24 +850,44 @@ def test_tp8_shapes_slow_decay_segmented(gdn, monkeypatch):
     assert not np.array_equal(res["segmented"][1], res["unsegmented"][1])
 
 
-# ----------------------------------------------------------------- full-size, sampled
-def _chains_check(d, out_t, sf_t, chains, cu, label):
-    worst_o = worst_s = 0.0
-    for (n, h) in chains:
+# ----------------------------------------------------------------- full-size, every chain
+def _all_chains_check(d, results, cu, Hv, label):
+    """Every (sequence, value head) chain of a packed batch against the fp64
+    oracle, on host threads; each chain is compared as soon as it is done, so
+    the fp64 outputs are never held whole. `results` maps a path label to the
+    GPU's (out [total, Hv, D] as host bf16 bits, final states [N, Hv, D, D])."""
+    from concurrent.futures import ThreadPoolExecutor
+    N = len(cu) - 1
+    worst = {name: [0.0, 0.0] for name in results}
+
+    def work(nh):
+        n, h = nh
         s0 = d["S0"][n, h] if d.get("S0") is not None else None
         o_ref, S_ref = oracle.chain(d["q"], d["k"], d["v"], d["alpha"], d["beta"], int(cu[n]),
                                     int(cu[n + 1]), h, s0)
-        o = from_torch(out_t[int(cu[n]):int(cu[n + 1]), h])
-        S = from_torch(sf_t[n, h])
-        worst_o = max(worst_o, slice_error(o, o_ref))
-        worst_s = max(worst_s, slice_error(S, S_ref))
-    print(f"[parity] {label}: {len(chains)} sampled chains: out {worst_o:.3e} "
-          f"state {worst_s:.3e}", flush=True)
-    assert worst_o <= TOL["bf16"] and worst_s <= TOL["bf16"]
+        errs = {}
+        for name, (o, S) in results.items():
+            errs[name] = (slice_error(o[int(cu[n]):int(cu[n + 1]), h], o_ref),
+                          slice_error(S[n, h], S_ref))
+        return errs
+
+    chains = [(n, h) for n in range(N) for h in range(Hv)]
+    with ThreadPoolExecutor(oracle.default_threads()) as ex:
+        for errs in ex.map(work, chains):
+            for name, (eo, es) in errs.items():
+                worst[name][0] = max(worst[name][0], eo)
+                worst[name][1] = max(worst[name][1], es)
+    for name, (eo, es) in worst.items():
+        print(f"[parity] {label} ({name}): all {len(chains)} chains: out {eo:.3e} "
+              f"state {es:.3e}", flush=True)
+        assert eo <= TOL["bf16"] and es <= TOL["bf16"], (name, eo, es)
 
 
 @pytest.mark.slow
-def test_long_prefill_256k_workload_sampled(gdn):
+@pytest.mark.timeout(900)
+def test_long_prefill_256k_workload_all_chains(gdn):
+    """The 262,144-token layer prefill: all 48 value-head chains against the
+    oracle over their full length."""
     w = WORKLOADS["long_prefill_256k"]
     d = generate(w)
     flat = {n: d[n].reshape((-1,) + d[n].shape[2:]) for n in ("q", "k", "v", "alpha", "beta")}
@@ -871,26 +895,49 @@ def test_long_prefill_256k_workload_sampled(gdn):
     q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
     out, sf = gdn.gdn_prefill_chunked(q, k, v, a, b, None)
     torch.cuda.synchronize()
-    assert torch.isfinite(out.float()).all()
-    out = out.reshape(-1, w.Hv, w.D)
-    cu = np.array([0, w.T])
-    _chains_check(flat, out, sf, [(0, 0), (0, 25), (0, 47)], cu, w.name)
+    res = {"default": (from_torch(out.reshape(-1, w.Hv, w.D)), from_torch(sf))}
+    del q, k, v, a, b, out, sf
+    _all_chains_check(flat, res, np.array([0, w.T]), w.Hv, w.name)
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("path", ["auto", "split"])
-def test_varlen_64seq_workload_sampled(gdn, monkeypatch, path):
-    if path != "auto":
-        monkeypatch.setenv("GDN_PREFILL_PATH", path)
+@pytest.mark.timeout(900)
+def test_varlen_64seq_workload_all_chains(gdn, monkeypatch):
+    """The 64-sequence packed batch (nonzero initial states): all 3,072
+    chains against the oracle, for the default path (one pass: the chains
+    fill the chip) and for the two-pass path."""
     w = WORKLOADS["varlen_64seq"]
     d = generate(w)
-    out, sf = gpu_varlen(gdn, d)
-    assert torch.isfinite(out.float()).all()
-    L = lengths_for(w)
-    order = np.argsort(L)
-    chains = [(int(order[-1]), 0), (int(order[0]), 47), (int(order[len(L) // 2]), 17),
-              (5, 30)]
-    _chains_check(d, out, sf, chains, d["cu_seqlens"], f"{w.name} ({path})")
+    res = {}
+    for path in ("default", "split"):
+        if path == "split":
+            monkeypatch.setenv("GDN_PREFILL_PATH", "split")
+        out, sf = gpu_varlen(gdn, d)
+        res[path] = (from_torch(out), from_torch(sf))
+        del out, sf
+        torch.cuda.empty_cache()
+    monkeypatch.delenv("GDN_PREFILL_PATH", raising=False)
+    _all_chains_check(d, res, d["cu_seqlens"], w.Hv, w.name)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("T,alpha", [(4096, "slow"), (4096, "one"), (65536, "slow")])
+def test_layer_shapes_slow_decay_all_chains(gdn, T, alpha):
+    """Slow decay at the layer's shapes (16 q/k heads, 48 value heads, d=128)
+    on the default path: alpha = exp(-softplus(N(0,1) - 5)) (median ~0.993)
+    or alpha = 1, beta = sigmoid(N(0,1) - 2), initial states 0.1 N(0,1). Here
+    the state carried across chunks dominates the outputs (at the
+    workloads' decay a chunk scales it by ~1e-61), so a wrong carry fails."""
+    d = small_prefill(1, T, 16, 48, 128, "bf16", seed=300 + T // 4096 + (alpha == "one"),
+                      alpha_shift=-5.0, beta_shift=-2.0, init_state=True)
+    if alpha == "one":
+        d["alpha"][:] = 1.0
+    flat = {n: d[n].reshape((-1,) + d[n].shape[2:]) for n in ("q", "k", "v", "alpha", "beta")}
+    flat["S0"] = d["S0"]
+    out, sf = gpu_prefill(gdn, d)
+    res = {"default": (out.reshape(-1, 48, 128), sf)}
+    _all_chains_check(flat, res, np.array([0, T]), 48, f"layer shapes T={T} alpha {alpha}")
 
 
 def test_slow_decay_stress_diagnostic(gdn):
