@@ -1108,8 +1108,10 @@ static hipError_t launch_split_db(const PrefillParams &p, unsigned char *ws, int
     if (ChainDbCfg<D, NC, NH>::DVS * nsplit != D) return hipErrorInvalidValue;
     hipError_t e = launch_prep<__bf16, D, true>(p, ws, nprep, stream);
     if (e != hipSuccess) return e;
+    // the one-wave-per-SIMD chain where it applies; GDN_CHAIN=db keeps this
+    // kernel (for comparisons and the tests that cover both)
     const char *ck = getenv("GDN_CHAIN");
-    if (ck && ck[0] == '4' && chain4_supported(p, D, nsplit))
+    if (!(ck && ck[0] == 'd') && chain4_supported(p, D, nsplit))
         return launch_chain4(p, ws, nchain, stream);
     if (p.prefix)
         hipLaunchKernelGGL((chain_db_kernel<D, NC, NH, true>), dim3((unsigned)nchain),
