@@ -31,7 +31,8 @@ _STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL_POINTER", 2: "GDN_ERR_BAD_SHAPE",
            3: "GDN_ERR_UNSUPPORTED", 4: "GDN_ERR_MISALIGNED", 5: "GDN_ERR_ALIAS",
            6: "GDN_ERR_HIP"}
 EXPORTS = ("gdn_prefill_chunked", "gdn_decode_step", "gdn_varlen_prefill", "gdn_decode_multi",
-           "gdn_prefill_workspace_size", "gdn_status_string", "gdn_version")
+           "gdn_prefill_workspace_size", "gdn_status_string", "gdn_version",
+           "gdn_prefill_chunked_noalloc")
 
 _lib = None
 
@@ -57,6 +58,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_prefill_chunked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i64, i32,
                                         i32, i32, i32, ctypes.c_int, f32, u32, vp, sz, vp]
     lib.gdn_prefill_chunked.restype = ctypes.c_int
+    lib.gdn_prefill_chunked_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i64,
+                                                i32, i32, i32, i32, ctypes.c_int, f32, u32, vp]
+    lib.gdn_prefill_chunked_noalloc.restype = ctypes.c_int
     lib.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                     ctypes.c_int, f32, u32, vp]
     lib.gdn_decode_step.restype = ctypes.c_int
@@ -189,6 +193,42 @@ def gdn_prefill_chunked(q, k, v, alpha, beta, initial_state=None, *, out=None,
         _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state), _ptr(out),
         _ptr(final_state), _ptr(pre), pint, B, T, Hk, Hv, Dk, Dv, _dtype_code(q), float(scale),
         int(flags), wp, wb, st.cuda_stream))
+    return out, final_state
+
+
+def gdn_prefill_chunked_noalloc(q, k, v, alpha, beta, initial_state=None, *, out=None,
+                                final_state=None, scale: float = 1.0,
+                                want_final_state: bool = True, prefix_states=None,
+                                prefix_interval: int = 0, flags: int = 0, stream=None):
+    """gdn_prefill_chunked on the library's static device scratch (no
+    workspace argument, nothing allocated by the library; outputs the caller
+    does not pass are allocated here by torch, as for the other calls).
+    Calls that overlap in time on one device race on that scratch."""
+    lib = load_library()
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    dev = q.device
+    _need(q, "q", device=dev)
+    _need(k, "k", q.dtype, q.shape, dev)
+    _need(v, "v", q.dtype, (B, T, Hv, Dv), dev)
+    _need(alpha, "alpha", torch.float32, (B, T, Hv), dev)
+    _need(beta, "beta", torch.float32, (B, T, Hv), dev)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (B, Hv, Dv, Dk), dev)
+    if out is None:
+        out = torch.empty((B, T, Hv, Dv), dtype=q.dtype, device=dev)
+    _need(out, "out", q.dtype, (B, T, Hv, Dv), dev)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((B, Hv, Dv, Dk), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, (B, Hv, Dv, Dk), dev)
+    pre, pint = _prefix(prefix_states, prefix_interval,
+                        prefix_state_rows(B, T, max(int(prefix_interval), 1), False), Hv, Dv, Dk,
+                        dev)
+    _check(lib.gdn_prefill_chunked_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state), _ptr(out),
+        _ptr(final_state), _ptr(pre), pint, B, T, Hk, Hv, Dk, Dv, _dtype_code(q), float(scale),
+        int(flags), _stream(dev, stream).cuda_stream))
     return out, final_state
 
 

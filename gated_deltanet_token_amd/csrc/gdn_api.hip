@@ -8,6 +8,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <vector>
 
 #include "../../include/gdn.h"
@@ -93,6 +94,34 @@ gdn_status_t run_prefill(const gdn::PrefillParams &p, int dtype, int D, int cus,
     return GDN_OK;
 }
 
+// Device scratch of gdn_prefill_chunked_noalloc: the workspace of callers
+// that cannot allocate. Each device holds its own copy for the life of the
+// process. In host code the array's name is only a stand-in; its device
+// address on the current device comes from hipGetSymbolAddress, taken once
+// per device and kept in scratch_ptr.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<uintptr_t> g_scratch_ptr[kMaxDevices];
+
+gdn_status_t scratch_ptr(void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return hip_fail(hipErrorInvalidDevice, "scratch device index");
+    uintptr_t a = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (a == 0) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        a = reinterpret_cast<uintptr_t>(p);
+        g_scratch_ptr[dev].store(a, std::memory_order_release);  // the same value from any thread
+    }
+    *ptr = reinterpret_cast<void *>(a);
+    return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -102,7 +131,9 @@ const char *gdn_status_string(gdn_status_t s) {
     case GDN_OK: return "ok";
     case GDN_ERR_NULL_POINTER: return "a required pointer is NULL";
     case GDN_ERR_BAD_SHAPE: return "a size is out of range or inconsistent";
-    case GDN_ERR_UNSUPPORTED: return "unsupported dtype or head dimension (Dk == Dv in {64, 128})";
+    case GDN_ERR_UNSUPPORTED:
+        return "unsupported dtype or head dimension (Dk == Dv in {64, 128}), or a shape whose "
+               "scratch exceeds the static 64 MiB of gdn_prefill_chunked_noalloc";
     case GDN_ERR_MISALIGNED: return "a pointer is not 16-byte aligned";
     case GDN_ERR_ALIAS: return "forbidden overlap between buffers";
     case GDN_ERR_HIP: return g_detail[0] ? g_detail : "HIP runtime error";
@@ -161,6 +192,32 @@ gdn_status_t gdn_prefill_chunked(const void *q, const void *k, const void *v, co
     const int64_t slots = gdn::prefill_ws_slots(B, tokens, T, false);
     return run_prefill(p, dtype == GDN_BF16 ? 1 : 0, Dk, cus, workspace, workspace_bytes, slots,
                        stream, debug_checks(stream), "gdn_prefill_chunked launch");
+}
+
+gdn_status_t gdn_prefill_chunked_noalloc(const void *q, const void *k, const void *v,
+                                         const float *alpha, const float *beta,
+                                         const float *initial_state, void *out,
+                                         float *final_state, float *prefix_states,
+                                         int32_t prefix_interval, int32_t B, int64_t T, int32_t Hk,
+                                         int32_t Hv, int32_t Dk, int32_t Dv, gdn_dtype_t dtype,
+                                         float scale, uint32_t flags, hipStream_t stream) {
+    gdn_status_t st = check_heads(Hk, Hv, Dk, Dv);
+    if (st != GDN_OK) return st;
+    if (!known_dtype(dtype)) return GDN_ERR_UNSUPPORTED;
+    if (B < 1 || T < 0) return GDN_ERR_BAD_SHAPE;
+    const size_t want = gdn_prefill_workspace_size(B, T, Hk, Hv, Dk, Dv, dtype, 0);
+    if (want > kNoAllocScratchBytes) {
+        snprintf(g_detail, sizeof g_detail,
+                 "gdn_prefill_chunked_noalloc: this shape needs %zu bytes of scratch, the "
+                 "library's static scratch holds %zu",
+                 want, kNoAllocScratchBytes);
+        return GDN_ERR_UNSUPPORTED;
+    }
+    void *ws = nullptr;
+    if (want > 0 && (st = scratch_ptr(&ws)) != GDN_OK) return st;
+    return gdn_prefill_chunked(q, k, v, alpha, beta, initial_state, out, final_state,
+                               prefix_states, prefix_interval, B, T, Hk, Hv, Dk, Dv, dtype, scale,
+                               flags, want > 0 ? ws : nullptr, want, stream);
 }
 
 gdn_status_t gdn_varlen_prefill(const void *q, const void *k, const void *v, const float *alpha,

@@ -17,39 +17,39 @@ struct Range {
     uintptr_t lo, hi;  // [lo, hi); empty when lo == hi
 };
 
-inline Range range_of(const void *p, int64_t bytes) {
+static inline Range range_of(const void *p, int64_t bytes) {
     const uintptr_t a = reinterpret_cast<uintptr_t>(p);
     return Range{a, bytes > 0 && p ? a + (uintptr_t)bytes : a};
 }
 
-inline bool overlap(const Range &a, const Range &b) {
+static inline bool overlap(const Range &a, const Range &b) {
     if (a.lo == a.hi || b.lo == b.hi) return false;
     return a.lo < b.hi && b.lo < a.hi;
 }
 
-inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+static inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // acc *= f with overflow detection (all factors >= 0).
-inline bool mul_ok(int64_t &acc, int64_t f) {
+static inline bool mul_ok(int64_t &acc, int64_t f) {
     if (f < 0 || acc < 0) return false;
     if (f != 0 && acc > INT64_MAX / f) return false;
     acc *= f;
     return true;
 }
 
-inline gdn_status_t check_heads(int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv) {
+static inline gdn_status_t check_heads(int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv) {
     if (Hk < 1 || Hv < 1 || Dk < 1 || Dv < 1) return GDN_ERR_BAD_SHAPE;
     if (Hv % Hk != 0) return GDN_ERR_BAD_SHAPE;
     if (Dk != Dv || (Dk != 64 && Dk != 128)) return GDN_ERR_UNSUPPORTED;
     return GDN_OK;
 }
 
-inline bool known_dtype(gdn_dtype_t d) { return d == GDN_F32 || d == GDN_BF16; }
+static inline bool known_dtype(gdn_dtype_t d) { return d == GDN_F32 || d == GDN_BF16; }
 
 // Shared checks of the two prefill entry points. `tokens` is B*T or total_T,
 // `nstates` is B or N, `cu_count` the number of cu_seqlens entries (0 for a
 // dense batch).
-inline gdn_status_t check_prefill(const void *q, const void *k, const void *v, const float *alpha,
+static inline gdn_status_t check_prefill(const void *q, const void *k, const void *v, const float *alpha,
                                   const float *beta, const float *s0, const void *out,
                                   const float *sf, const float *prefix, int64_t prefix_rows,
                                   const int32_t *cu, int64_t cu_count, int64_t tokens,
@@ -103,7 +103,7 @@ inline gdn_status_t check_prefill(const void *q, const void *k, const void *v, c
     return GDN_OK;
 }
 
-inline gdn_status_t check_decode(const void *q, const void *k, const void *v, const float *alpha,
+static inline gdn_status_t check_decode(const void *q, const void *k, const void *v, const float *alpha,
                                  const float *beta, const float *state, const void *out,
                                  int32_t B, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
                                  gdn_dtype_t dtype) {
@@ -133,7 +133,7 @@ inline gdn_status_t check_decode(const void *q, const void *k, const void *v, co
     return GDN_OK;
 }
 
-inline gdn_status_t check_decode_multi(const void *q, const void *k, const void *v,
+static inline gdn_status_t check_decode_multi(const void *q, const void *k, const void *v,
                                        const float *alpha, const float *beta,
                                        const float *state_pool, int32_t num_slots,
                                        const int32_t *src_slot, const int32_t *dst_slot,
@@ -180,7 +180,7 @@ inline gdn_status_t check_decode_multi(const void *q, const void *k, const void 
 // Contents of cu_seqlens (a host copy of its N + 1 entries): starts at 0,
 // never decreases, ends at total_T. The library runs this only when the
 // environment sets GDN_DEBUG=1 (it needs a synchronous device-to-host copy).
-inline gdn_status_t check_cu_seqlens(const int32_t *cu, int32_t N, int64_t total_T) {
+static inline gdn_status_t check_cu_seqlens(const int32_t *cu, int32_t N, int64_t total_T) {
     if (!cu) return GDN_ERR_NULL_POINTER;
     if (N < 1) return GDN_ERR_BAD_SHAPE;
     if (cu[0] != 0) return GDN_ERR_BAD_SHAPE;

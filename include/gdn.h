@@ -139,6 +139,31 @@ gdn_status_t gdn_prefill_chunked(const void *q, const void *k, const void *v,
                                  hipStream_t stream);
 
 /*
+ * gdn_prefill_chunked_noalloc -- gdn_prefill_chunked for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same arguments and results as
+ * gdn_prefill_chunked without the workspace pair: the call uses the
+ * library's own static device scratch of 64 MiB per device (allocated when
+ * the library's code is loaded on that device, held until the process ends)
+ * as the workspace that gdn_prefill_workspace_size() names, and calls no
+ * allocating routine. Shapes that need more scratch than 64 MiB are
+ * rejected with GDN_ERR_UNSUPPORTED and no side effects (the scratch covers,
+ * for example, one 4,096-token sequence at 16 q/k and 48 value heads of
+ * dimension 128). Every call on a device shares that device's scratch, which
+ * keeps the last call's contents: calls that may overlap in time on one
+ * device (different streams, or threads) race and must be serialised by the
+ * caller.
+ */
+gdn_status_t gdn_prefill_chunked_noalloc(const void *q, const void *k, const void *v,
+                                         const float *alpha, const float *beta,
+                                         const float *initial_state, void *out,
+                                         float *final_state, float *prefix_states,
+                                         int32_t prefix_interval, int32_t B, int64_t T,
+                                         int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
+                                         gdn_dtype_t dtype, float scale, uint32_t flags,
+                                         hipStream_t stream);
+
+/*
  * gdn_decode_step -- one new token per sequence, state updated in place.
  *
  *   q, k         [B, Hk, Dk]     dtype
