@@ -9,8 +9,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn.so")
-SOURCES = ["gdn_api.hip", "gdn_prefill.hip", "gdn_chain4.hip", "gdn_decode.hip",
-           "gdn_segment.hip"]
+SOURCES = ["gdn_api.hip", "gdn_prefill.hip", "gdn_chain4.hip", "gdn_fused2.hip",
+           "gdn_decode.hip", "gdn_segment.hip"]
 ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
 
 

@@ -96,6 +96,10 @@ hipError_t launch_segment_correct(__bf16 *out, const __bf16 *o_id, const float *
                                   int64_t seg_len, int32_t first_seg, int D, hipStream_t stream);
 // The two-pass chain with one wave per SIMD (gdn_chain4.hip): bf16, D = 128,
 // four value-column slices per head, plain or identity-free calls.
+// Single-pass prefill with one workgroup per (sequence, value head) chain and
+// two workgroups per CU (gdn_fused2.hip): bf16, head dimension 128.
+bool fused2_supported(const PrefillParams &p, int dtype, int D);
+hipError_t launch_fused2(const PrefillParams &p, hipStream_t stream);
 bool chain4_supported(const PrefillParams &p, int D, int nsplit);
 hipError_t launch_chain4(const PrefillParams &p, const unsigned char *ws, int64_t nchain,
                          hipStream_t stream);

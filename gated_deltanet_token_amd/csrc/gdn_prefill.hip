@@ -1387,7 +1387,12 @@ static hipError_t launch_prefill_ws(const PrefillParams &p, int dtype, int D, in
     if (dtype == 1) {
         if (D == 128) {
             switch (ns) {
-            case 1: return launch_fused<__bf16, 128, 8, 16>(p, 1, stream);
+            case 1: {
+                // GDN_FUSED=old keeps the eight-wave kernel (for comparison)
+                const char *fe = getenv("GDN_FUSED");
+                if (!(fe && fe[0] == 'o') && fused2_supported(p, dtype, D)) return launch_fused2(p, stream);
+                return launch_fused<__bf16, 128, 8, 16>(p, 1, stream);
+            }
             case 2: return launch_fused<__bf16, 128, 4, 16>(p, 2, stream);
             case 4: return launch_fused<__bf16, 128, 2, 16>(p, 4, stream);
             default: return launch_fused<__bf16, 128, 1, 16>(p, 8, stream);

@@ -34,6 +34,17 @@ def _t(d, names):
     return [to_torch(d[n], DEV) for n in names]
 
 
+def _set_path(monkeypatch, path):
+    """Prefill path for a test: "fused" or "split" as given; "fused1" is the
+    one-pass path with one workgroup per (sequence, value head) chain (the
+    path a batch with many chains takes by default)."""
+    if path == "fused1":
+        monkeypatch.setenv("GDN_PREFILL_PATH", "fused")
+        monkeypatch.setenv("GDN_PREFILL_NSPLIT", "1")
+    else:
+        monkeypatch.setenv("GDN_PREFILL_PATH", path)
+
+
 def gpu_prefill(gdn, d, use_init=True, scale=1.0, stream=None):
     q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
     s0 = to_torch(d["S0"], DEV) if use_init and d.get("S0") is not None else None
@@ -204,9 +215,9 @@ def _edge_gates(d, case):
 
 
 @pytest.mark.parametrize("case", ["beta0", "alpha1_beta1", "alpha0"])
-@pytest.mark.parametrize("path", ["fused", "split"])
+@pytest.mark.parametrize("path", ["fused", "fused1", "split"])
 def test_prefill_edge_gates(gdn, monkeypatch, case, path):
-    monkeypatch.setenv("GDN_PREFILL_PATH", path)
+    _set_path(monkeypatch, path)
     d = _edge_gates(small_prefill(1, 200, 2, 6, 128, "bf16", seed=71, alpha_shift=-5.0,
                                   init_state=True), case)
     o, S = gpu_prefill(gdn, d)
@@ -406,9 +417,9 @@ def gpu_varlen(gdn, d, use_init=True):
 
 
 @pytest.mark.parametrize("D,dtype", [(128, "bf16"), (64, "bf16"), (64, "f32")])
-@pytest.mark.parametrize("path", ["fused", "split"])
+@pytest.mark.parametrize("path", ["fused", "fused1", "split"])
 def test_varlen_small(gdn, monkeypatch, D, dtype, path):
-    monkeypatch.setenv("GDN_PREFILL_PATH", path)
+    _set_path(monkeypatch, path)
     lengths = [5, 1, 70, 0, 129, 64, 200]
     d = generate_packed(2, 6, D, dtype, 40 + D, lengths, init_state=True)
     out, sf = gpu_varlen(gdn, d)
@@ -466,6 +477,8 @@ PREFIX_DENSE = [
     # path, nsplit, dtype, D, every  (kernel reached)
     ("fused", "auto", "bf16", 128, 1),   # prefill_kernel
     ("fused", "8", "bf16", 128, 3),
+    ("fused", "1", "bf16", 128, 1),      # fused2_kernel
+    ("fused", "1", "bf16", 128, 3),
     ("split", "1", "bf16", 128, 2),      # chain_kernel
     ("split", "4", "bf16", 128, 1),      # chain_db_kernel
     ("split", "2", "bf16", 64, 3),       # chain_db_kernel, D = 64
@@ -501,9 +514,9 @@ def test_prefill_prefix_states(gdn, monkeypatch, path, nsplit, dtype, D, every):
                   f"prefix states {path} ns={nsplit} {dtype} D{D} L={L}")
 
 
-@pytest.mark.parametrize("path", ["fused", "split"])
+@pytest.mark.parametrize("path", ["fused", "fused1", "split"])
 def test_varlen_prefix_states(gdn, monkeypatch, path):
-    monkeypatch.setenv("GDN_PREFILL_PATH", path)
+    _set_path(monkeypatch, path)
     lengths = [300, 64, 1, 640, 127, 128, 0, 257]
     every = 2
     L = 64 * every
@@ -561,6 +574,8 @@ PREP_DENSE = [
     # path, nsplit, dtype, D, flags
     ("fused", "auto", "bf16", 128, QK | GL),
     ("fused", "2", "bf16", 128, QK),
+    ("fused", "1", "bf16", 128, QK | GL),   # fused2_kernel
+    ("fused", "1", "bf16", 128, QK),
     ("fused", "auto", "bf16", 128, GL),
     ("split", "1", "bf16", 128, QK | GL),     # chain_kernel
     ("split", "4", "bf16", 128, QK | GL),     # chain_db_kernel
@@ -586,11 +601,11 @@ def test_prefill_prepared_inputs(gdn, monkeypatch, path, nsplit, dtype, D, flags
           f"prepared inputs flags={flags} {path} ns={nsplit} {dtype} D{D}")
 
 
-@pytest.mark.parametrize("path", ["fused", "split"])
+@pytest.mark.parametrize("path", ["fused", "fused1", "split"])
 def test_varlen_prepared_inputs_and_zero_rows(gdn, monkeypatch, path):
     """Raw rows of zeros normalise to zero (the 1e-6 under the root): such a
     token writes nothing and reads nothing."""
-    monkeypatch.setenv("GDN_PREFILL_PATH", path)
+    _set_path(monkeypatch, path)
     lengths = [150, 1, 64, 300]
     d = generate_packed(2, 6, 128, "bf16", 140, lengths, init_state=True, raw=True)
     d["k"][[3, 70, 71, 400]] = 0
@@ -673,6 +688,10 @@ SEG_CASES = [
     (1, 900, 1, 3, 64, "4", True, 0, "auto", -5.0),
     (1, 1024, 2, 6, 128, "8", True, QK | GL, "auto", -5.0),
     (1, 700, 1, 2, 128, "5", True, 0, "fused", -5.0),
+    # one-pass segment passes with one workgroup per chain (identity start,
+    # token stride 0 for v)
+    (1, 700, 1, 2, 128, "5", True, 0, "fused1", -5.0),
+    (1, 640, 2, 6, 128, "4", True, QK | GL, "fused1", 2.0),
 ]
 
 
@@ -682,7 +701,7 @@ def test_segmented_prefill(gdn, monkeypatch, B, T, Hk, Hv, D, segs, init, flags,
     scan of the segment maps and the corrections, against the oracle."""
     monkeypatch.setenv("GDN_PREFILL_SEGMENTS", segs)
     if inner != "auto":
-        monkeypatch.setenv("GDN_PREFILL_PATH", inner)
+        _set_path(monkeypatch, inner)
     gen = lambda raw: small_prefill(B, T, Hk, Hv, D, "bf16", seed=170 + T, init_state=init,
                                     raw=raw, alpha_shift=ashift)
     d = _prepared_inputs(gen, flags) if flags else gen(False)
