@@ -14,16 +14,16 @@
 //   | wave 0: the chunk-local decay (scan of ln alpha)
 //   | Gram tiles K K^T, Q K^T on MFMA and the decay masks: A (fp32), P as
 //     MFMA fragments
-//   | wave 0: the diagonal 16x16 blocks of T by forward substitution
+//   | wave 0: the diagonal 16x16 blocks of T by forward substitution, while
+//     waves 1..3 form K S^T and S Q^T for their columns
 //   | waves 1..3: the blocks below the diagonal, one block column each, on
-//     MFMA; T as fragments
-//   | every wave: K S^T and S Q^T; the next chunk's K starts to load
-//   | the next chunk's Q starts to load; every wave: R, U = T R, the output
-//     O and the state update for its 32 columns; after R it starts to load
-//     its 32 columns of the next chunk's V.
+//     MFMA (T as fragments), while wave 0 forms its K S^T and S Q^T
+//   | the next chunk's K and Q start to load; every wave: R, U = T R, the
+//     output O and the state update for its 32 columns; after R it starts
+//     to load its 32 columns of the next chunk's V.
 // K, Q and V move by LDS-DMA (global_load_lds: no registers) into their LDS
 // areas as soon as the current chunk is done with them: Q after the state
-// products, V (per wave: its own column block) after R. K is needed until the
+// products and the solve, V (per wave: its own column block) after R. K is needed until the
 // state update, so K and A share two areas that swap roles every chunk: the
 // next chunk's K lands in the area that held this chunk's A. No LDS read
 // waits on the copies in flight; they are waited for once, at the barrier
@@ -140,6 +140,48 @@ __device__ __forceinline__ void mask_pair_f2(const f32x4 &gk, const f32x4 &gq, i
     unsigned char *f = pfr + (tri_frag(ti, tj >> 1) * 64 + 16 * g4 + c16) * 16;
     *reinterpret_cast<bf16x4 *>(f + (tj & 1) * 8) = pb;
     if (ti == tj && (tj & 1) == 0) *reinterpret_cast<uint2 *>(f + 8) = uint2{0u, 0u};
+}
+
+// Gram products and decay masks of this wave's lower tile pairs
+// pr = wave + 4 k (three pairs on waves 0 and 1, two on waves 2 and 3). The
+// twelve fragments of a pair (K rows of tile tj, K and Q rows of tile ti, four
+// k steps each) are read one pair ahead, so that the MFMAs of a pair do not
+// wait on LDS.
+template <bool NORMS>
+__device__ __forceinline__ void gram_masks_f2(const __bf16 *sK, const __bf16 *sQ, int wave, int g4,
+                                              int c16, const float *sGrA, const float *sGrP,
+                                              const float *sGc, const float *sBeta,
+                                              unsigned char *A, unsigned char *pfr) {
+    using F = bf16x8;
+    F fr[2][3][kF2D / 32];
+    auto load = [&](int k, F (&f)[3][kF2D / 32]) {
+        const int pr = wave + 4 * k;
+        const int ti = pair_i(pr), tj = pair_j(pr);
+#pragma unroll
+        for (int kk = 0; kk < kF2D / 32; ++kk) {
+            f[0][kk] = *reinterpret_cast<const F *>(swz_at<kF2Row>(sK, 16 * tj, c16, 32 * kk + 8 * g4));
+            f[1][kk] = *reinterpret_cast<const F *>(swz_at<kF2Row>(sK, 16 * ti, c16, 32 * kk + 8 * g4));
+            f[2][kk] = *reinterpret_cast<const F *>(swz_at<kF2Row>(sQ, 16 * ti, c16, 32 * kk + 8 * g4));
+        }
+    };
+    const int np = wave < 2 ? 3 : 2;
+    load(0, fr[0]);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        if (k < np) {
+            if (k + 1 < np) load(k + 1, fr[(k + 1) & 1]);
+            phase_fence();
+            const int pr = wave + 4 * k;
+            const int ti = pair_i(pr), tj = pair_j(pr);
+            f32x4 gk = zero4(), gq = zero4();
+#pragma unroll
+            for (int kk = 0; kk < kF2D / 32; ++kk) {
+                gk = mma(fr[k & 1][0][kk], fr[k & 1][1][kk], gk);
+                gq = mma(fr[k & 1][0][kk], fr[k & 1][2][kk], gq);
+            }
+            mask_pair_f2<NORMS>(gk, gq, ti, tj, g4, c16, sGrA, sGrP, sGc, sBeta, A, pfr);
+        }
+    }
 }
 
 // Diagonal blocks E_b = (I + A_bb)^{-1} of T (one wave; lane = 16 b + column)
@@ -381,20 +423,23 @@ __global__ __launch_bounds__(kF2Waves * 64, 2) void fused2_kernel(PrefillParams 
     {
         const int g4 = lane >> 4, c16 = lane & 15;
         const float *s0 = p.s0 ? p.s0 + ((int64_t)n * p.Hv + h) * D * D : nullptr;
+        if (s0 && !p.s0_identity) {
 #pragma unroll
-        for (int a = 0; a < NKT; ++a)
+            for (int a = 0; a < NKT; ++a)
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const int dv = wdv + 16 * b + c16;
-                f32x4 e = zero4();
-                if (p.s0_identity) {
+                for (int b = 0; b < NB; ++b)
+                    st[a][b] = *reinterpret_cast<const f32x4 *>(
+                        s0 + (int64_t)(wdv + 16 * b + c16) * D + st_key(a, g4));
+        } else {
+            const float one = p.s0_identity ? 1.f : 0.f;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) e[r] = dv == st_key(a, g4) + r ? 1.f : 0.f;
-                } else if (s0) {
-                    e = *reinterpret_cast<const f32x4 *>(s0 + (int64_t)dv * D + st_key(a, g4));
-                }
-                st[a][b] = e;
-            }
+            for (int a = 0; a < NKT; ++a)
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        st[a][b][r] = wdv + 16 * b + c16 == st_key(a, g4) + r ? one : 0.f;
+        }
     }
 
     const int64_t nchunks = (len + kC - 1) / kC;
@@ -481,44 +526,37 @@ __global__ __launch_bounds__(kF2Waves * 64, 2) void fused2_kernel(PrefillParams 
         }
 
         int g4 = fresh_lane(lane) >> 4, c16 = fresh_lane(lane) & 15;
-        // Gram tiles of this wave's lower tile pairs (wave, wave + 4, ...),
-        // transposed (X[s][t], s in tile tj, t in tile ti), and their masks
-#pragma unroll
-        for (int k = 0; k < 3; ++k) {
-            const int pr = wave + 4 * k;
-            if (pr >= 10) continue;
-            const int ti = pair_i(pr), tj = pair_j(pr);
-            f32x4 gk = zero4(), gq = zero4();
-#pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) {
-                const F fks = *reinterpret_cast<const F *>(swz_at<kF2Row>(sK, 16 * tj, c16, 32 * kk + 8 * g4));
-                const F fkt = *reinterpret_cast<const F *>(swz_at<kF2Row>(sK, 16 * ti, c16, 32 * kk + 8 * g4));
-                const F fqt = *reinterpret_cast<const F *>(swz_at<kF2Row>(sQ, 16 * ti, c16, 32 * kk + 8 * g4));
-                gk = mma(fks, fkt, gk);
-                gq = mma(fks, fqt, gq);
-            }
-            mask_pair_f2<RAWQK>(gk, gq, ti, tj, g4, c16, RAWQK ? sGrA : sG, RAWQK ? sGrP : sG,
-                                RAWQK ? sGc : sG, sBeta, Ac, Ps);
-        }
+        gram_masks_f2<RAWQK>(sK, sQ, wave, g4, c16, RAWQK ? sGrA : sG, RAWQK ? sGrP : sG,
+                             RAWQK ? sGc : sG, sBeta, Ac, Ps);
         __syncthreads();
-        g4 = fresh_lane(lane) >> 4;
-        c16 = fresh_lane(lane) & 15;
-        if (wave == 0) solve_diag_f2(Ac, Ts, g4, c16);
-        __syncthreads();
-        g4 = fresh_lane(lane) >> 4;
-        c16 = fresh_lane(lane) & 15;
-        if (wave != 0) solve_column_f2(Ac, Ts, wave - 1, g4, c16);
-        __syncthreads();
-        // A is done with: the next chunk's K goes to its area
-        if (more) copy_rows(kb, Ac, c + 1);
-
-        g4 = fresh_lane(lane) >> 4;
-        c16 = fresh_lane(lane) & 15;
+        // the diagonal blocks of T on wave 0 while waves 1..3 form their
+        // state products; then the blocks below the diagonal on waves 1..3
+        // while wave 0 forms its own
+        // (the accumulators start defined on every path: the register
+        // allocator then keeps one set of them across both phases)
         f32x4 racc[4][NB], oT[4][NB];
-        state_products_f2(sK, sQ, st, racc, oT, g4, c16);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) racc[mt][b] = oT[mt][b] = zero4();
+        g4 = fresh_lane(lane) >> 4;
+        c16 = fresh_lane(lane) & 15;
+        if (wave == 0)
+            solve_diag_f2(Ac, Ts, g4, c16);
+        else
+            state_products_f2(sK, sQ, st, racc, oT, g4, c16);
         __syncthreads();
-        // Q is done with
+        g4 = fresh_lane(lane) >> 4;
+        c16 = fresh_lane(lane) & 15;
+        if (wave == 0)
+            state_products_f2(sK, sQ, st, racc, oT, g4, c16);
+        else
+            solve_column_f2(Ac, Ts, wave - 1, g4, c16);
+        __syncthreads();
+        // A and Q are done with: the next chunk's K goes to A's area, its Q
+        // to Q's
         if (more) {
+            copy_rows(kb, Ac, c + 1);
             copy_rows(qb, Qs, c + 1);
             load_gates(c + 1);
         }
@@ -636,27 +674,30 @@ __global__ __launch_bounds__(kF2Waves * 64, 2) void fused2_kernel(PrefillParams 
         // unless the row norms are folded in)
         const float gC = sGam[kC - 1] * __builtin_amdgcn_rcpf(sDec[kC - 1]);
         const int rl = 4 * g4 + (c16 >> 2);
+        // all of K^T's fragments first (64 registers), then the MFMAs
+        F fkt[NKT][2];
 #pragma unroll
         for (int a = 0; a < NKT; ++a) {
             const int col = st_key(a, c16 & 3);
-            F fkt[2];
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
                 const bf16x4 lo = ld_tr(swz_at<kF2Row>(sK, 32 * k2, rl, col));
                 const bf16x4 hi = ld_tr(swz_at<kF2Row>(sK, 32 * k2 + 16, rl, col));
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    fkt[k2][e] = lo[e];
-                    fkt[k2][e + 4] = hi[e];
+                    fkt[a][k2][e] = lo[e];
+                    fkt[a][k2][e + 4] = hi[e];
                 }
             }
+        }
+#pragma unroll
+        for (int a = 0; a < NKT; ++a)
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 st[a][b] *= gC;
 #pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2) st[a][b] = mma(fkt[k2], fd[k2][b], st[a][b]);
+                for (int k2 = 0; k2 < 2; ++k2) st[a][b] = mma(fkt[a][k2], fd[k2][b], st[a][b]);
             }
-        }
         const int64_t prow = PREFIX ? pre.take(p, c) : -1;
         if (prow >= 0) {
             float *ps = p.prefix + (prow * p.Hv + h) * D * D;
