@@ -162,7 +162,8 @@ def main():
     gdn.load_library()
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
-    pdig = _src_digest("gdn_prefill.hip", "gdn_chunk.hpp", "gdn_device.hpp")
+    pdig = _src_digest("gdn_prefill.hip", "gdn_chain4.hip", "gdn_fused2.hip", "gdn_segment.hip",
+                       "gdn_chunk.hpp", "gdn_device.hpp", "gdn_seq.hpp", "gdn_launch.hpp")
     ddig = _src_digest("gdn_decode.hip", "gdn_device.hpp")
     if args.calibrate_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -204,7 +205,15 @@ def main():
                                         stream=stream)
 
         def kernels(self):
-            return (["prep_kernel", "chain_db_kernel"] if self.ws_bytes else ["prefill_kernel"])
+            # the library's choice for these shapes (bf16, d = 128): with few
+            # (sequence, value head) chains the two-pass path (per-chunk
+            # factors, then the chain at four value-column slices per head);
+            # with at least one chain per CU the single-pass kernel, one
+            # workgroup per chain
+            w = self.w
+            if self.ws_bytes:
+                return ["prep_kernel", "chain4_kernel" if w.D == 128 else "chain_db_kernel"]
+            return ["fused2_kernel" if w.D == 128 else "prefill_kernel"]
 
         def summary(self, ms_list, extra=None):
             w = self.w
