@@ -184,11 +184,13 @@ __device__ __forceinline__ void mask_pair(const f32x4 &gk, const f32x4 &gq, int 
 // likewise, and g, gamma = e^g, dec as the scan left them:
 //   gam_t = gamma_t ik_t, dec_t *= ik_t, gamq_t = gamma_t iq_t,
 //   grA_t = g_t + ln ik_t, grP_t = g_t + ln iq_t, gc_t = g_t - ln ik_t.
-// One thread per row (K rows first: a wave never holds both kinds).
+// One thread per row (K rows first: a wave never holds both kinds). qscale
+// multiplies gamq (a kernel that puts the output scale there passes it).
 template <typename DT, int D, int PK, int NTH>
 __device__ __forceinline__ void fold_qk_norms(const DT *sK, const DT *sQ, const float *sG,
                                               float *sGam, float *sDec, float *sGamQ,
-                                              float *sGrA, float *sGrP, float *sGc, int tid) {
+                                              float *sGrA, float *sGrP, float *sGc, int tid,
+                                              float qscale = 1.f) {
     constexpr int EPP = 16 / (int)sizeof(DT);
     for (int r = tid; r < 2 * kC; r += NTH) {
         const int t = r & (kC - 1);
@@ -212,7 +214,7 @@ __device__ __forceinline__ void fold_qk_norms(const DT *sK, const DT *sQ, const 
         const float g = sG[t];
         if (isq) {
             sGrP[t] = g + li;
-            sGamQ[t] = __expf(g) * inv;
+            sGamQ[t] = qscale * __expf(g) * inv;
         } else {
             sGrA[t] = g + li;
             sGc[t] = g - li;

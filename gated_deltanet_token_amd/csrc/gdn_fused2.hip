@@ -77,14 +77,17 @@ __device__ __forceinline__ int fresh_lane(int lane) {
 // LDS reads it cannot tell apart from the copy's target, and every workgroup
 // barrier, wait for all copies in flight. The kernel waits for its copies
 // itself (vmcnt(0) before the barrier that publishes them) and reads or
-// writes no target area before then. M0 holds the LDS address; one wait state
-// separates its write from the load that reads it.
-__device__ __forceinline__ void dma16_async(const unsigned char *src, unsigned char *lds) {
+// writes no target area before then. The source is base + off (base
+// workgroup-uniform, off a 32-bit lane offset: no 64-bit address arithmetic
+// per lane). M0 holds the LDS address; one wait state separates its write from
+// the load that reads it.
+__device__ __forceinline__ void dma16_async(const unsigned char *base, uint32_t off,
+                                            unsigned char *lds) {
     typedef __attribute__((address_space(3))) unsigned char lds_u8;
     const uint32_t m0 = (uint32_t)(uintptr_t)(lds_u8 *)lds;
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "v"(src), "s"(m0)
+                 : "v"(off), "s"(base), "s"(m0)
                  : "memory", "m0");
 }
 
@@ -110,7 +113,8 @@ __device__ __forceinline__ int tfrag_off(int row, int col) {
 
 // Decay masks of one transposed Gram pair (accumulators X[s][t], s in tile
 // tj, t in tile ti): A_ts = beta_t e^{grA_t - gc_s} k_t.k_s (s < t) into the
-// A area, P_ts = e^{grP_t - gc_s} q_t.k_s (s <= t) into P's fragments (this
+// A area, P_ts = scale e^{grP_t - gc_s} q_t.k_s (s <= t; the output scale
+// rides on P and on gamq) into P's fragments (this
 // lane's four values are one half of fragment (ti, tj / 2); pairs on even
 // diagonal tiles also clear the other half). With q and k used as given the
 // three exponent vectors are the log decay g; with raw rows (NORMS) they
@@ -119,10 +123,10 @@ template <bool NORMS>
 __device__ __forceinline__ void mask_pair_f2(const f32x4 &gk, const f32x4 &gq, int ti, int tj, int g4,
                                              int c16, const float *sGrA, const float *sGrP,
                                              const float *sGc, const float *sBeta, unsigned char *A,
-                                             unsigned char *pfr) {
+                                             unsigned char *pfr, float scale) {
     const int t = 16 * ti + c16;
     const float gt = sGrA[t];
-    const float rt = NORMS ? __expf(sGrP[t] - gt) : 1.f;
+    const float rt = NORMS ? __expf(sGrP[t] - gt) * scale : scale;
     const float bt = sBeta[t];
     const f32x4 gs = *reinterpret_cast<const f32x4 *>(sGc + 16 * tj + 4 * g4);
     f32x4 av;
@@ -151,7 +155,7 @@ template <bool NORMS>
 __device__ __forceinline__ void gram_masks_f2(const __bf16 *sK, const __bf16 *sQ, int wave, int g4,
                                               int c16, const float *sGrA, const float *sGrP,
                                               const float *sGc, const float *sBeta,
-                                              unsigned char *A, unsigned char *pfr) {
+                                              unsigned char *A, unsigned char *pfr, float scale) {
     using F = bf16x8;
     F fr[2][3][kF2D / 32];
     auto load = [&](int k, F (&f)[3][kF2D / 32]) {
@@ -179,7 +183,7 @@ __device__ __forceinline__ void gram_masks_f2(const __bf16 *sK, const __bf16 *sQ
                 gk = mma(fr[k & 1][0][kk], fr[k & 1][1][kk], gk);
                 gq = mma(fr[k & 1][0][kk], fr[k & 1][2][kk], gq);
             }
-            mask_pair_f2<NORMS>(gk, gq, ti, tj, g4, c16, sGrA, sGrP, sGc, sBeta, A, pfr);
+            mask_pair_f2<NORMS>(gk, gq, ti, tj, g4, c16, sGrA, sGrP, sGc, sBeta, A, pfr, scale);
         }
     }
 }
@@ -448,15 +452,17 @@ __global__ __launch_bounds__(kF2Waves * 64, 2) void fused2_kernel(PrefillParams 
     // wave): instruction j fills rows 4 j' .. 4 j' + 3 (j' = 4 wave + j), lane l
     // piece (l % 16) ^ swz_f(row) of row 4 j' + l / 16. Rows past the end of the
     // sequence repeat its last row (finite values, weighted zero by beta = 0).
+    const uint32_t rowQK = (uint32_t)(sQK * 2), rowV = (uint32_t)(sVt * 2);  // bytes per token
     auto copy_rows = [&](const unsigned char *src, unsigned char *dst, int64_t c) {
         const int ln = fresh_lane(lane);
         const int lc = chunk_len(c);
+        const unsigned char *base = src + c * kC * (int64_t)rowQK;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int row = 16 * wave + 4 * j + (ln >> 4);
             const int piece = (ln & 15) ^ swz_f<kF2Row>(row & 15);
-            const int64_t r = c * kC + (row < lc ? row : lc - 1);
-            dma16_async(src + r * sQK * 2 + 16 * piece, dst + (16 * wave + 4 * j) * kF2Row);
+            const uint32_t off = (uint32_t)(row < lc ? row : lc - 1) * rowQK + 16 * piece;
+            dma16_async(base, off, dst + (16 * wave + 4 * j) * kF2Row);
         }
     };
     // LDS-DMA of this wave's 32 value columns of a chunk's V: a block of 64
@@ -465,13 +471,14 @@ __global__ __launch_bounds__(kF2Waves * 64, 2) void fused2_kernel(PrefillParams 
         const int ln = fresh_lane(lane);
         const int lc = chunk_len(c);
         unsigned char *dst = Vs + wave * (kC * kF2VRow);
+        const unsigned char *base = vb + c * kC * (int64_t)rowV;
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of the block are done
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int row = 16 * j + (ln >> 2);
             const int piece = (ln & 3) ^ swz_f<kF2VRow>(row & 15);
-            const int64_t r = c * kC + (row < lc ? row : lc - 1);
-            dma16_async(vb + r * sVt * 2 + 16 * piece, dst + j * 1024);
+            const uint32_t off = (uint32_t)(row < lc ? row : lc - 1) * rowV + 16 * piece;
+            dma16_async(base, off, dst + j * 1024);
         }
     };
     float rAl = 1.f, rBe = 0.f;  // wave 0: alpha, beta of token `lane` of the next chunk
@@ -514,20 +521,21 @@ __global__ __launch_bounds__(kF2Waves * 64, 2) void fused2_kernel(PrefillParams 
             sGam[lane] = __expf(x);
             sDec[lane] = __expf(glast - x);
             sBeta[lane] = ok ? (logits ? sigmoid_f(rBe) : rBe) : 0.f;
-            if (!RAWQK) sGamQ[lane] = __expf(x);
+            if (!RAWQK) sGamQ[lane] = p.scale * __expf(x);  // the output scale rides on gamq and P
         }
         // this chunk's K, Q and V have landed (each wave waits for its own
         // copies; the barrier publishes them)
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
         if constexpr (RAWQK) {
-            fold_qk_norms<DT, D, D, NTH>(sK, sQ, sG, sGam, sDec, sGamQ, sGrA, sGrP, sGc, tid);
+            fold_qk_norms<DT, D, D, NTH>(sK, sQ, sG, sGam, sDec, sGamQ, sGrA, sGrP, sGc, tid,
+                                         p.scale);
             __syncthreads();
         }
 
         int g4 = fresh_lane(lane) >> 4, c16 = fresh_lane(lane) & 15;
         gram_masks_f2<RAWQK>(sK, sQ, wave, g4, c16, RAWQK ? sGrA : sG, RAWQK ? sGrP : sG,
-                             RAWQK ? sGc : sG, sBeta, Ac, Ps);
+                             RAWQK ? sGc : sG, sBeta, Ac, Ps, p.scale);
         __syncthreads();
         // the diagonal blocks of T on wave 0 while waves 1..3 form their
         // state products; then the blocks below the diagonal on waves 1..3
@@ -628,7 +636,8 @@ __global__ __launch_bounds__(kF2Waves * 64, 2) void fused2_kernel(PrefillParams 
                 c_to_frag(dl, dh, fd[k2][b]);
             }
         }
-        // O^T = (S Q^T) diag(gamma_q) + U^T P^T, stored for rows t < lenc
+        // O^T = (S Q^T) diag(gamq) + U^T P^T (the scale is in gamq and P),
+        // stored for rows t < lenc
         const F *Pf = reinterpret_cast<const F *>(Ps) + lane;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
@@ -661,7 +670,7 @@ __global__ __launch_bounds__(kF2Waves * 64, 2) void fused2_kernel(PrefillParams 
                     for (int b = 0; b < NB; ++b) {
                         bf16x4 ob;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) ob[r] = (__bf16)(p.scale * oT[mt][b][r]);
+                        for (int r = 0; r < 4; ++r) ob[r] = (__bf16)oT[mt][b][r];
                         *reinterpret_cast<bf16x4 *>(o0 + (int64_t)(16 * mt) * sVO + 16 * b) = ob;
                     }
                 }
@@ -726,7 +735,10 @@ __global__ __launch_bounds__(kF2Waves * 64, 2) void fused2_kernel(PrefillParams 
 }  // namespace
 
 bool fused2_supported(const PrefillParams &p, int dtype, int D) {
-    return dtype == 1 && D == kF2D && !p.dual;
+    // the copies' lane offsets are 32-bit: a chunk's 64 rows of q, k or v must
+    // span less than 4 GiB
+    return dtype == 1 && D == kF2D && !p.dual && (int64_t)p.Hk * D * 2 * kC < ((int64_t)1 << 32) &&
+           p.v_stride * 2 * kC < ((int64_t)1 << 32);
 }
 
 hipError_t launch_fused2(const PrefillParams &p, hipStream_t stream) {

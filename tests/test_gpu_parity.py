@@ -963,6 +963,22 @@ def test_layer_shapes_slow_decay_all_chains(gdn, T, alpha):
     _all_chains_check(flat, res, np.array([0, T]), 48, f"layer shapes T={T} alpha {alpha}")
 
 
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+def test_varlen_layer_shapes_slow_decay_all_chains(gdn):
+    """A packed batch at the layer's shapes with slow decay and nonzero
+    initial states on the default path: 12 sequences x 48 value heads fill the
+    chip, so the single-pass kernel with its longest-first, XCD-balanced order
+    runs (ragged and one-token sequences included). Every chain against the
+    oracle; the state carried across chunks dominates the outputs."""
+    lengths = [4096, 1, 3000, 64, 2500, 700, 130, 1900, 65, 1200, 3333, 10]
+    d = generate_packed(16, 48, 128, "bf16", 310, lengths, alpha_shift=-5.0, beta_shift=-2.0,
+                        init_state=True)
+    out, sf = gpu_varlen(gdn, d)
+    res = {"default": (from_torch(out), from_torch(sf))}
+    _all_chains_check(d, res, d["cu_seqlens"], 48, "packed layer shapes, slow decay")
+
+
 def test_slow_decay_stress_diagnostic(gdn):
     """Slow decay (alpha ~ 0.99, small beta) exercises the carried state across
     many chunks, which the workloads' fast decay hides. Diagnostic bound."""
