@@ -91,6 +91,13 @@ __device__ __forceinline__ void dma16_async(const unsigned char *base, uint32_t 
                  : "memory", "m0");
 }
 
+__device__ __forceinline__ bf16x4 to_bf4(const f32x4 &x) {
+    bf16x4 y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = (__bf16)x[e];
+    return y;
+}
+
 // Byte offset of A[row][col] (fp32) in its area.
 __device__ __forceinline__ int a_off(int row, int col) {
     return row * 256 + ((((col >> 2) ^ (row & 15))) << 4) + ((col & 3) << 2);
@@ -279,10 +286,9 @@ __device__ __forceinline__ void solve_column_f2(const unsigned char *A, unsigned
     }
 }
 
-// K S^T (C layout [t][dv]) and then S Q^T (C layout [dv][t]) for one wave's
-// value tiles, each with the k steps as the outer loop (8 independent
-// accumulators). The state's keys 32 kk + 8 g4 .. +7 are one 16-byte piece
-// of a K or Q row.
+// K S^T (C layout [t][dv]) and S Q^T (C layout [dv][t]) for one wave's
+// value tiles, the k steps as the outer loop (16 independent accumulators).
+// The state's keys 32 kk + 8 g4 .. +7 are one 16-byte piece of a K or Q row.
 __device__ __forceinline__ void state_products_f2(const __bf16 *sK, const __bf16 *sQ,
                                                   const f32x4 (&st)[kF2D / 16][kF2NB],
                                                   f32x4 (&racc)[4][kF2NB], f32x4 (&oT)[4][kF2NB],
@@ -296,27 +302,23 @@ __device__ __forceinline__ void state_products_f2(const __bf16 *sK, const __bf16
             oT[mt][b] = zero4();
         }
 #pragma unroll
-    for (int side = 0; side < 2; ++side) {
-        const __bf16 *src = side ? sQ : sK;
+    for (int kk = 0; kk < kF2D / 32; ++kk) {
+        // the state's bf16 fragments once per k step, for both products
+        F sf[kF2NB], fk[4], fq[4];
 #pragma unroll
-        for (int kk = 0; kk < kF2D / 32; ++kk) {
-            F sf[kF2NB], fx[4];
+        for (int b = 0; b < kF2NB; ++b) c_to_frag(st[2 * kk][b], st[2 * kk + 1][b], sf[b]);
 #pragma unroll
-            for (int b = 0; b < kF2NB; ++b) c_to_frag(st[2 * kk][b], st[2 * kk + 1][b], sf[b]);
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-                fx[mt] = *reinterpret_cast<const F *>(
-                    swz_at<kF2Row>(src, 16 * mt, c16, 32 * kk + 8 * g4));
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int b = 0; b < kF2NB; ++b) {
-                    if (side == 0)
-                        racc[mt][b] = mma(fx[mt], sf[b], racc[mt][b]);
-                    else
-                        oT[mt][b] = mma(sf[b], fx[mt], oT[mt][b]);
-                }
+        for (int mt = 0; mt < 4; ++mt) {
+            fk[mt] = *reinterpret_cast<const F *>(swz_at<kF2Row>(sK, 16 * mt, c16, 32 * kk + 8 * g4));
+            fq[mt] = *reinterpret_cast<const F *>(swz_at<kF2Row>(sQ, 16 * mt, c16, 32 * kk + 8 * g4));
         }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int b = 0; b < kF2NB; ++b) {
+                racc[mt][b] = mma(fk[mt], sf[b], racc[mt][b]);
+                oT[mt][b] = mma(sf[b], fq[mt], oT[mt][b]);
+            }
     }
 }
 
@@ -662,18 +664,23 @@ __global__ __launch_bounds__(kF2Waves * 64, 2) void fused2_kernel(PrefillParams 
             }
         }
         {
-            DT *o0 = oh + (c * kC + c16) * sVO + 4 * g4;
+            // Lane (g4, c16) holds columns 4 g4 .. + 3 of both tiles (b = 0, 1)
+            // for token 16 mt + c16. One exchange between lane rows (row g4 odd
+            // <-> row g4 - 1, v_permlane16_swap) gives each lane 8 consecutive
+            // columns of one tile -- rows 0, 1, 2, 3: columns 0, 16, 8, 24 .. + 7
+            // -- so each token's 64 bytes go out as four 16-byte stores, not
+            // eight 8-byte ones.
+            const int dvo = 8 * (g4 >> 1) + 16 * (g4 & 1);
+            DT *o0 = oh + (c * kC + c16) * sVO + dvo;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                if (16 * mt + c16 < lenc) {
-#pragma unroll
-                    for (int b = 0; b < NB; ++b) {
-                        bf16x4 ob;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) ob[r] = (__bf16)oT[mt][b][r];
-                        *reinterpret_cast<bf16x4 *>(o0 + (int64_t)(16 * mt) * sVO + 16 * b) = ob;
-                    }
-                }
+                const u32x2 x = __builtin_bit_cast(u32x2, to_bf4(oT[mt][0]));
+                const u32x2 y = __builtin_bit_cast(u32x2, to_bf4(oT[mt][1]));
+                const auto s0 = __builtin_amdgcn_permlane16_swap(x[0], y[0], false, false);
+                const auto s1 = __builtin_amdgcn_permlane16_swap(x[1], y[1], false, false);
+                if (16 * mt + c16 < lenc)
+                    *reinterpret_cast<u32x4 *>(o0 + (int64_t)(16 * mt) * sVO) =
+                        u32x4{s0[0], s1[0], s0[1], s1[1]};
             }
         }
         g4 = fresh_lane(lane) >> 4;
