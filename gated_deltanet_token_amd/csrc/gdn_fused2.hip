@@ -57,8 +57,8 @@ constexpr int kF2Row = 2 * kF2D;      // bytes per K / Q row
 constexpr int kF2VRow = 64;           // bytes per row of a wave's V block
 constexpr int kF2Area = kC * kF2Row;  // 16 KiB: K, Q, V, or A (fp32 64 x 64)
 static_assert(kF2Area == kC * kC * 4, "K and A share an area");
-constexpr int kF2MaxRankedSeqs = 1024;  // packed batches up to this size run longest first
-static_assert(kF2MaxRankedSeqs * 4 <= kF2Area, "sequence lengths fit an area");
+constexpr int kF2MaxRankedSeqs = 2048;  // packed batches up to this size run longest first
+static_assert(kF2MaxRankedSeqs * 8 <= kF2Area, "the sort keys fit an area");
 
 __device__ __forceinline__ int st_key(int a, int g) { return 32 * (a >> 1) + 8 * g + 4 * (a & 1); }
 
@@ -324,29 +324,45 @@ __device__ __forceinline__ void state_products_f2(const __bf16 *sK, const __bf16
 
 // Sequence processed by ranked workgroup slot r of a packed batch: the r-th
 // longest (ties by index), so that the longest chains start first and the
-// tail of the launch is short. All threads of the workgroup call this; the
-// sequence lengths are staged in `lens` (LDS, nseq ints, at most
-// kF2MaxRankedSeqs), then each thread counts the rank of its sequences.
-__device__ __forceinline__ int ranked_seq(const PrefillParams &p, int r, int *lens, int *slot) {
+// tail of the launch is short. All threads of the workgroup call this. The
+// keys (length << 32 | ~index, sorted descending) go to `keys` (LDS, room
+// for kF2MaxRankedSeqs), padded with zeros to a power of two, and are sorted
+// by a bitonic network (log2(n) (log2(n) + 1) / 2 barrier-separated stages):
+// a few microseconds even at the largest batch, where counting each
+// sequence's rank would take O(N^2 / threads) steps.
+__device__ __forceinline__ int ranked_seq(const PrefillParams &p, int r, uint64_t *keys) {
     const int N = p.nseq;
-    for (int m = threadIdx.x; m < N; m += blockDim.x) {
-        int64_t t0, lm;
-        seq_bounds(p, m, t0, lm);
-        lens[m] = (int)(lm < 0x7FFFFFFF ? lm : 0x7FFFFFFF);
-    }
-    if (threadIdx.x == 0) *slot = r;
-    __syncthreads();
-    for (int n = threadIdx.x; n < N; n += blockDim.x) {
-        const int ln = lens[n];
-        int rank = 0;
-        for (int m = 0; m < N; ++m) {
-            const int lm = lens[m];
-            rank += (lm > ln || (lm == ln && m < n)) ? 1 : 0;
+    int n2 = 1;
+    while (n2 < N) n2 <<= 1;
+    for (int m = threadIdx.x; m < n2; m += blockDim.x) {
+        uint64_t key = 0;
+        if (m < N) {
+            int64_t t0, lm;
+            seq_bounds(p, m, t0, lm);
+            key = ((uint64_t)(lm < 0x7FFFFFFF ? lm : 0x7FFFFFFF) << 32) | (uint32_t)~(uint32_t)m;
         }
-        if (rank == r) *slot = n;
+        keys[m] = key;
     }
     __syncthreads();
-    return *slot;
+    // ascending sort of ~key, i.e. descending by length, then ascending index
+    for (int k = 2; k <= n2; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = threadIdx.x; i < n2; i += blockDim.x) {
+                const int ixj = i ^ j;
+                if (ixj > i) {
+                    const uint64_t a = ~keys[i], b = ~keys[ixj];
+                    if (((i & k) == 0) == (a > b)) {
+                        keys[i] = ~b;
+                        keys[ixj] = ~a;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    const int n = (int)~(uint32_t)keys[r];
+    __syncthreads();  // every thread has read its slot before the area is reused
+    return n;
 }
 
 template <bool PREFIX, bool RAWQK>
@@ -367,7 +383,6 @@ __global__ __launch_bounds__(kF2Waves * 64, 2) void fused2_kernel(PrefillParams 
     __shared__ __attribute__((aligned(16))) float Vg[4 * kC];
     __shared__ __attribute__((aligned(16))) float Vf0[4 * kC];
     __shared__ __attribute__((aligned(16))) float Vf1[4 * kC];
-    __shared__ int seq_slot;
 
     const bool logits = p.flags & kGateLogits;
     const int tid = threadIdx.x;
@@ -395,8 +410,8 @@ __global__ __launch_bounds__(kF2Waves * 64, 2) void fused2_kernel(PrefillParams 
             j = b % G3;
         }
         h = (u % p.Hk) * G3 + j;
-        // (the lengths go to X1, which the first chunk uses only after its first barrier)
-        n = ranked_seq(p, u / p.Hk, reinterpret_cast<int *>(X1), &seq_slot);
+        // (the keys go to X1, which the first chunk uses only after its first barrier)
+        n = ranked_seq(p, u / p.Hk, reinterpret_cast<uint64_t *>(X1));
     } else {
         const int wg = logical_wg(remap_xcd);
         h = wg % p.Hv;

@@ -435,6 +435,34 @@ def test_varlen_small(gdn, monkeypatch, D, dtype, path):
     check(o[:0], from_torch(sf), o_ref[:0], S_ref, dtype, f"varlen {path} D{D} {dtype} states")
 
 
+@pytest.mark.parametrize("nseq,Hk", [(300, 2), (37, 3)])
+@pytest.mark.parametrize("path", ["default", "fused1"])
+def test_varlen_many_sequences(gdn, monkeypatch, nseq, Hk, path):
+    """Many short packed sequences (0 to 200 tokens, slow decay, nonzero
+    initial states): the one-pass kernel ranks them by length in each
+    workgroup (a sort over more keys than threads; a unit count that is, and
+    one that is not, a multiple of 8), every chain against the oracle."""
+    if path != "default":
+        _set_path(monkeypatch, path)
+    rng = np.random.default_rng(400 + nseq)
+    lengths = [int(x) for x in rng.integers(0, 201, nseq)]
+    d = generate_packed(Hk, 3 * Hk, 128, "bf16", 401 + nseq, lengths, alpha_shift=-5.0,
+                        init_state=True)
+    out, sf = gpu_varlen(gdn, d)
+    o_ref, S_ref = oracle.varlen(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["cu_seqlens"],
+                                 d["S0"])
+    o = from_torch(out)
+    cu = d["cu_seqlens"]
+    worst = 0.0
+    for n in range(nseq):
+        if lengths[n]:
+            worst = max(worst, max_error(o[cu[n]:cu[n + 1]][None], o_ref[cu[n]:cu[n + 1]][None],
+                                         (0, 2)))
+    assert worst <= TOL["bf16"], worst
+    check(o[:0], from_torch(sf), o_ref[:0], S_ref, "bf16",
+          f"varlen {nseq} sequences Hk={Hk} ({path}), outputs {worst:.3e}")
+
+
 def test_varlen_matches_per_sequence_prefill(gdn):
     lengths = [77, 300, 64]
     d = generate_packed(2, 6, 128, "bf16", 50, lengths, init_state=True)
