@@ -15,12 +15,12 @@
 //   | Gram tiles K K^T, Q K^T on MFMA and the decay masks: A (fp32), P as
 //     MFMA fragments
 //   | wave 0: the diagonal 16x16 blocks of T by forward substitution, while
-//     waves 1..3 form K S^T and S Q^T for their columns
+//     waves 1..3 form K S^T, S Q^T and R for their columns (then start to
+//     load their 32 columns of the next chunk's V)
 //   | waves 1..3: the blocks below the diagonal, one block column each, on
-//     MFMA (T as fragments), while wave 0 forms its K S^T and S Q^T
-//   | the next chunk's K and Q start to load; every wave: R, U = T R, the
-//     output O and the state update for its 32 columns; after R it starts
-//     to load its 32 columns of the next chunk's V.
+//     MFMA (T as fragments), while wave 0 forms its K S^T, S Q^T and R
+//   | the next chunk's K and Q start to load; every wave: U = T R, the
+//     output O and the state update for its 32 columns.
 // K, Q and V move by LDS-DMA (global_load_lds: no registers) into their LDS
 // areas as soon as the current chunk is done with them: Q after the state
 // products and the solve, V (per wave: its own column block) after R. K is needed until the
@@ -564,19 +564,46 @@ __global__ __launch_bounds__(kF2Waves * 64, 2) void fused2_kernel(PrefillParams 
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int b = 0; b < NB; ++b) racc[mt][b] = oT[mt][b] = zero4();
+        // R = beta (V - gamma K S^T) from this wave's V block, right after
+        // the wave's state products (it needs no T); then the block is done
+        // with and the next chunk's V block starts to load
+        auto form_r = [&]() {
+            const int g4r = fresh_lane(lane) >> 4, c16r = fresh_lane(lane) & 15;
+            const DT *sVw = reinterpret_cast<const DT *>(Vs + wave * (kC * kF2VRow));
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const int tb = 16 * mt + 4 * g4r;
+                const f32x4 bet = *reinterpret_cast<const f32x4 *>(sBeta + tb);
+                const f32x4 gam = *reinterpret_cast<const f32x4 *>(sGam + tb);
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const bf16x4 v4 = ld_tr(
+                        swz_at<kF2VRow>(sVw, 16 * mt, 4 * g4r + (c16r >> 2), 16 * b + 4 * (c16r & 3)));
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        racc[mt][b][r] = bet[r] * ((float)v4[r] - gam[r] * racc[mt][b][r]);
+                }
+            }
+            // (its reads have returned: R used them)
+            if (more) copy_v(c + 1);
+        };
         g4 = fresh_lane(lane) >> 4;
         c16 = fresh_lane(lane) & 15;
-        if (wave == 0)
+        if (wave == 0) {
             solve_diag_f2(Ac, Ts, g4, c16);
-        else
+        } else {
             state_products_f2(sK, sQ, st, racc, oT, g4, c16);
+            form_r();
+        }
         __syncthreads();
         g4 = fresh_lane(lane) >> 4;
         c16 = fresh_lane(lane) & 15;
-        if (wave == 0)
+        if (wave == 0) {
             state_products_f2(sK, sQ, st, racc, oT, g4, c16);
-        else
+            form_r();
+        } else {
             solve_column_f2(Ac, Ts, wave - 1, g4, c16);
+        }
         __syncthreads();
         // A and Q are done with: the next chunk's K goes to A's area, its Q
         // to Q's
@@ -588,27 +615,6 @@ __global__ __launch_bounds__(kF2Waves * 64, 2) void fused2_kernel(PrefillParams 
 
         g4 = fresh_lane(lane) >> 4;
         c16 = fresh_lane(lane) & 15;
-        // R = beta (V - gamma K S^T) from this wave's V block
-        {
-            const DT *sVw = reinterpret_cast<const DT *>(Vs + wave * (kC * kF2VRow));
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const int tb = 16 * mt + 4 * g4;
-                const f32x4 bet = *reinterpret_cast<const f32x4 *>(sBeta + tb);
-                const f32x4 gam = *reinterpret_cast<const f32x4 *>(sGam + tb);
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    const bf16x4 v4 =
-                        ld_tr(swz_at<kF2VRow>(sVw, 16 * mt, 4 * g4 + (c16 >> 2), 16 * b + 4 * (c16 & 3)));
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        racc[mt][b][r] = bet[r] * ((float)v4[r] - gam[r] * racc[mt][b][r]);
-                }
-            }
-        }
-        // the V block is done with (its reads have returned: R used them)
-        if (more) copy_v(c + 1);
-
         // U = T R (T's fragments read as they are used)
         const F *Tf = reinterpret_cast<const F *>(Ts) + lane;
         F fr[2][NB];
