@@ -24,7 +24,11 @@
 //              larger part has two steps to land. (Measured on the MI355X:
 //              one CU's LDS-DMA copies move ~16 bytes per cycle when each
 //              chunk must land within the step that issues it, ~25 with two
-//              in flight.)
+//              in flight.) It also touches the lines of chunk c + 4 so that
+//              those copies find them in L2: a CU takes in data at a rate set
+//              by the latency of its requests, and the shared K, Q and record
+//              lines otherwise make every workgroup that shares them wait for
+//              the same HBM misses.
 // One barrier per chunk. The state's rows (the key dimension dk) are held
 // in a permuted order: state tile a, lane group g, element r is key column
 // 32 (a >> 1) + 8 g + 4 (a & 1) + r. With it the eight keys that a lane
@@ -68,11 +72,14 @@ struct C4 {
     static constexpr int HO_U = 2 * 1024;         // U fragments of one chain wave
     static constexpr int HO = HO_S + HO_U;
     static constexpr int OFF_HO = OFF_VRR + NVR * SZ_VR;  // [slot][chain wave]
-    static constexpr int LDS = OFF_HO + 2 * NC * HO;
+    static constexpr int OFF_JUNK = OFF_HO + 2 * NC * HO;  // target of the L2 touches
+    static constexpr int LDS = OFF_JUNK + 1024;
+    static constexpr int PF_AHEAD = 4;  // chunks between an L2 touch and its copy
+    static constexpr int NPF = 4;       // touch instructions per step
     static constexpr int BLK_KQ = SZ_KQ / 1024, BLK_V = SZ_V / 1024, BLK_R = WSB / 1024;
     static constexpr int BLK_VR = BLK_V + BLK_R;
     static_assert(SZ_K % 1024 == 0 && SZ_V % 1024 == 0 && WSB % 1024 == 0, "whole DMA blocks");
-    static_assert(BLK_KQ + BLK_VR < 64, "a step's copies fit the vmcnt counter");
+    static_assert(BLK_KQ + BLK_VR + NPF < 64, "a step's copies fit the vmcnt counter");
     static_assert(LDS <= 160 * 1024, "LDS budget of a gfx950 CU");
 };
 
@@ -395,6 +402,31 @@ void chain4_kernel(PrefillParams p, const unsigned char *ws, int remap_xcd) {
     // are zero there, and P masks those columns). Only the last chunk of a
     // sequence can be partial; its offsets are recomputed with the clamp.
     auto lenc_of = [&](int64_t c) { return (int)((len - c * kC) < kC ? (len - c * kC) : kC); };
+    // NPF touches of the lines of chunk c (16-byte LDS-DMA loads into a
+    // scratch KiB that nothing reads), so that its copies PF_AHEAD steps later
+    // hit L2. Each K and Q line is touched by one of the workgroups that share
+    // it (the value heads of this q/k head times the column slices), each
+    // record line by one of the slices, the V rows by their own workgroup;
+    // the lanes beyond the lines repeat the first one. (Every workgroup
+    // touching every line instead took longer than no touches at all: the
+    // extra requests queue behind the same per-CU limit as the copies.)
+    const int share = (h % (p.Hv / p.Hk)) * NSPLIT + slice;
+    const int nshare = (p.Hv / p.Hk) * NSPLIT;
+    auto touch = [&](int64_t c) {
+        unsigned char *junk = smem + Cf::OFF_JUNK;
+        const int lenc = lenc_of(c);
+        int j = share + nshare * lane;  // line j of the chunk's K rows, and of its Q rows
+        if (j >= 2 * kC) j = share;
+        const int64_t okq = (int64_t)min(j >> 1, lenc - 1) * rowqk + 128 * (j & 1);
+        dma16(kb + c * kC * rowqk + okq, junk);
+        dma16(qb + c * kC * rowqk + okq, junk);
+        int jr = slice + NSPLIT * lane;  // line of the record
+        if (jr >= Cf::WSB / 128) jr = slice;
+        dma16(record(c) + 128 * jr, junk);
+        dma16(vb + c * kC * rowv + (int64_t)min(lane, lenc - 1) * rowv, junk);
+    };
+    static_assert(Cf::NPF == 4 && kC * KR / 128 == 2 * kC, "four touch instructions: K, Q, record, V");
+    static_assert(Cf::WSB / 128 <= NSPLIT * 64, "the slices' lanes cover the record's lines");
     auto copy_kq = [&](int64_t c) {  // BLK_KQ copies
         unsigned char *dst = kslot(c);
         const unsigned char *k0 = kb + c * kC * rowqk, *q0 = qb + c * kC * rowqk;
@@ -420,11 +452,14 @@ void chain4_kernel(PrefillParams p, const unsigned char *ws, int remap_xcd) {
     };
     // Before step 0: V and the record of chunk 0, then K, Q of chunks 0 and 1;
     // step 0 needs all but chunk 1's K, Q. In step c: V and the record of
-    // chunk c + 1, then K, Q of chunk c + 2; at its end everything but the
-    // latter has landed. The barrier carries no fence (a fence would make the
-    // compiler wait for every outstanding copy): the explicit counts order
-    // this wave's copies before it, and the other waves read after their own
-    // barriers.
+    // chunk c + 1, then K, Q of chunk c + 2 and the touches of chunk c + 4
+    // (clamped to the last chunk); at its end everything but the last two
+    // groups has landed (loads complete in issue order). The barrier carries
+    // no fence (a fence would make the compiler wait for every outstanding
+    // copy): the explicit counts order this wave's copies before it, and the
+    // other waves read after their own barriers. The last steps wait for
+    // everything, so that no copy is in flight when the workgroup ends.
+    for (int64_t c = 1; c < min<int64_t>(npc, 1 + Cf::PF_AHEAD); ++c) touch(c);
     if (npc > 0) {
         copy_vr(0);
         copy_kq(0);
@@ -440,7 +475,8 @@ void chain4_kernel(PrefillParams p, const unsigned char *ws, int remap_xcd) {
         if (c + 1 < npc) copy_vr(c + 1);
         if (c + 2 < npc) {
             copy_kq(c + 2);
-            wait_vm<Cf::BLK_KQ>();
+            touch(c + Cf::PF_AHEAD < npc ? c + Cf::PF_AHEAD : npc - 1);
+            wait_vm<Cf::BLK_KQ + Cf::NPF>();
         } else {
             wait_vm<0>();
         }
