@@ -128,7 +128,8 @@ __device__ __forceinline__ void gram_pair(const DT *sK, const DT *sQ, int ti, in
 // straight to its fragments at pfr (kTriFrags x 64 lanes x 16 bytes): this
 // lane's four values are one half of its fragment (rb, k2) = (ti, tj / 2);
 // the pairs on even diagonal blocks also zero the half above the diagonal.
-template <typename DT, int PA, int PT, bool PFRAG = false, bool NORMS = false>
+// PARTS selects what is formed: 1 A, 2 P, 3 both.
+template <typename DT, int PA, int PT, bool PFRAG = false, bool NORMS = false, int PARTS = 3>
 __device__ __forceinline__ void mask_pair(const f32x4 &gk, const f32x4 &gq, int ti, int tj, int g4,
                                           int c16, const float *sGrA, const float *sGrP,
                                           const float *sGc, const float *sBeta, float *sA,
@@ -159,8 +160,9 @@ __device__ __forceinline__ void mask_pair(const f32x4 &gk, const f32x4 &gq, int 
             pv[r] = pp;
         }
     }
-    *reinterpret_cast<f32x4 *>(sA + t * PA + 16 * tj + 4 * g4) = av;
-    if constexpr (PFRAG) {
+    if constexpr ((PARTS & 1) != 0) *reinterpret_cast<f32x4 *>(sA + t * PA + 16 * tj + 4 * g4) = av;
+    if constexpr ((PARTS & 2) == 0) {
+    } else if constexpr (PFRAG) {
         static_assert(sizeof(DT) == 2, "fragments are bf16");
         bf16x4 pb;
 #pragma unroll
@@ -221,6 +223,33 @@ __device__ __forceinline__ void fold_qk_norms(const DT *sK, const DT *sQ, const 
             sGam[t] = __expf(g) * inv;
             sDec[t] *= inv;
         }
+    }
+}
+
+// The inverse norms 1 / sqrt(|row|^2 + eps) of the chunk's 64 K rows (to
+// ik) and 64 Q rows (to iq), one thread per row: what fold_qk_norms folds
+// into one head's vectors, for a workgroup that folds them into several.
+template <typename DT, int D, int PK, int NTH>
+__device__ __forceinline__ void qk_inv_norms(const DT *sK, const DT *sQ, float *ik, float *iq, int tid) {
+    constexpr int EPP = 16 / (int)sizeof(DT);
+    for (int r = tid; r < 2 * kC; r += NTH) {
+        const int t = r & (kC - 1);
+        const bool isq = r >= kC;
+        const DT *row = (isq ? sQ : sK) + t * PK;
+        float ss = 0.f;
+#pragma unroll
+        for (int c = 0; c < D; c += EPP) {
+            if constexpr (sizeof(DT) == 2) {
+                const bf16x8 x = *reinterpret_cast<const bf16x8 *>(row + c);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss += (float)x[e] * (float)x[e];
+            } else {
+                const f32x4 x = *reinterpret_cast<const f32x4 *>(row + c);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ss += x[e] * x[e];
+            }
+        }
+        (isq ? iq : ik)[t] = inv_norm(ss, kL2Eps);
     }
 }
 

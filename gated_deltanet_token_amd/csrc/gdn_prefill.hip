@@ -365,6 +365,9 @@ constexpr int kFragBytes = kTriFrags * 64 * 16;
 constexpr int ws_bytes_frag() { return 2 * kFragBytes + 1024; }
 static_assert(ws_bytes_frag() <= ws_bytes_per_chunk<__bf16>(), "fragment record fits the query");
 
+// value heads per q/k head that one prep workgroup serves at most
+constexpr int kPrepGrpMax = 3;
+
 template <typename DT, int D, bool FRAG> struct PrepCfg {
     using P = ChunkPitch<DT, D>;
     static constexpr int SZ_K = kC * P::PK * (int)sizeof(DT);
@@ -381,164 +384,20 @@ template <typename DT, int D, bool FRAG> struct PrepCfg {
     static constexpr int OFF_P = FRAG ? SZ_KQ : OFF_T + SZ_T;
     static constexpr int OFF_VEC = FRAG ? SZ_KQ : OFF_P + SZ_T;
     static constexpr int LDS = OFF_VEC + 8 * kC * 4;  // the eight vectors of prefill_kernel
+    // a workgroup for all value heads of a q/k head: their vectors and the
+    // inverse K, Q row norms
+    static constexpr int LDS_GRP = OFF_VEC + kPrepGrpMax * 7 * kC * 4 + 2 * kC * 4;
     static_assert(LDS <= 160 * 1024, "LDS budget of a gfx950 CU");
 };
 
-// One workgroup (4 waves) per (chunk slot, value head): Gram products, decay,
-// T = (I + A)^{-1}; writes T, P, gamma, dec, beta to the workspace (52 KiB
-// of LDS for bf16, D = 128: three workgroups share a CU and hide each
-// other's latencies). FRAG: the fragment record instead of dense rows, with
-// T in the dead K/Q staging and P written from registers (35 KiB, at most
-// 128 registers: four workgroups per CU).
-template <typename DT, int D, bool FRAG, bool RAWQK>
-__global__ __launch_bounds__(256, FRAG ? 4 : 1) void prep_kernel(PrefillParams p, unsigned char *ws,
-                                                                 int remap_xcd) {
-    static_assert(!FRAG || sizeof(DT) == 2, "fragment records are bf16");
-    using Cf = PrepCfg<DT, D, FRAG>;
+// T, P of one chunk and value head -> its workspace record: as fragments
+// (FRAG) or as dense [64][64] rows; blocks above the diagonal (never written
+// in LDS) are stored as zeros.
+template <typename DT, int D, bool FRAG>
+__device__ __forceinline__ void write_tp_record(unsigned char *rec, const DT *sT, const DT *sP, int tid) {
     using Pi = ChunkPitch<DT, D>;
-    constexpr int PK = Pi::PK, PT = Pi::PT, PA = Pi::PA;
+    constexpr int PT = Pi::PT;
     constexpr int EPP = 16 / (int)sizeof(DT);
-    __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::LDS];
-    DT *sK = reinterpret_cast<DT *>(smem + Cf::OFF_K);
-    DT *sQ = reinterpret_cast<DT *>(smem + Cf::OFF_Q);
-    float *sA = reinterpret_cast<float *>(smem + Cf::OFF_A);
-    DT *sT = reinterpret_cast<DT *>(smem + Cf::OFF_T);
-    DT *sP = reinterpret_cast<DT *>(smem + Cf::OFF_P);
-    float *sG = reinterpret_cast<float *>(smem + Cf::OFF_VEC);
-    float *sGam = sG + kC;
-    float *sDec = sG + 2 * kC;
-    float *sBeta = sG + 3 * kC;
-    float *sGamQ = sG + 4 * kC;
-    float *sGrA = sG + 5 * kC;
-    float *sGrP = sG + 6 * kC;
-    float *sGc = sG + 7 * kC;
-    constexpr bool raw_qk = RAWQK;
-    const bool logits = p.flags & kGateLogits;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g4 = lane >> 4;
-    const int c16 = lane & 15;
-
-    // value heads of one chunk are consecutive logical ids: same XCD, so the
-    // heads sharing a q/k head read K and Q through one L2
-    const int wg = logical_wg(remap_xcd);
-    const int h = wg % p.Hv;
-    const int64_t slot = p.chunk0 + wg / p.Hv;  // chunk0 > 0 only for one dense sequence
-    // which (sequence, chunk) owns this slot
-    int n;
-    if (p.cu_seqlens) {
-        int lo = 0, hi = p.nseq - 1;  // largest n with slot_base(n) <= slot
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (slot_base(p, mid) <= slot)
-                lo = mid;
-            else
-                hi = mid - 1;
-        }
-        n = lo;
-    } else {
-        // chunks per sequence and slots both fit 32 bits (the ABI bounds them)
-        const uint32_t per = (uint32_t)((p.seq_len + kC - 1) / kC);
-        n = (int)((uint32_t)slot / per);
-    }
-    int64_t tok0, len;
-    seq_bounds(p, n, tok0, len);
-    const int64_t c = slot - slot_base(p, n);
-    if (c < 0 || c * kC >= len) return;  // unused slot (uniform over the workgroup)
-    const int lenc = (int)((len - c * kC) < kC ? (len - c * kC) : kC);
-    const int64_t t0 = tok0 + c * kC;
-    const int grp = h / (p.Hv / p.Hk);
-    const int64_t sQK = (int64_t)p.Hk * D;
-    const DT *kh = reinterpret_cast<const DT *>(p.k) + t0 * sQK + (int64_t)grp * D;
-    const DT *qh = reinterpret_cast<const DT *>(p.q) + t0 * sQK + (int64_t)grp * D;
-
-    // alpha, beta (wave 0) and the K, Q rows are all requested before any
-    // of them is used, so their latencies overlap
-    float a_t = 1.f, b_t = 0.f;
-    if (wave == 0) {
-        const int rr = lane < lenc ? lane : lenc - 1;
-        a_t = p.alpha[(t0 + rr) * p.Hv + h];
-        b_t = p.beta[(t0 + rr) * p.Hv + h];
-    }
-    // K, Q rows -> LDS (rows past the end of the sequence are zero)
-    {
-        constexpr int PPR = D / EPP;
-        constexpr int NPC = kC * PPR / 256;  // pieces per thread
-        static_assert(kC * PPR % 256 == 0, "whole pieces per thread");
-        const u32x4 z4 = {0u, 0u, 0u, 0u};
-        u32x4 kv[NPC], qv[NPC];
-#pragma unroll
-        for (int j = 0; j < NPC; ++j) {
-            const int i = tid + 256 * j, r = i / PPR, pc = i % PPR;
-            const int rr = r < lenc ? r : lenc - 1;
-            kv[j] = *reinterpret_cast<const u32x4 *>(kh + (int64_t)rr * sQK + pc * EPP);
-            qv[j] = *reinterpret_cast<const u32x4 *>(qh + (int64_t)rr * sQK + pc * EPP);
-        }
-#pragma unroll
-        for (int j = 0; j < NPC; ++j) {
-            const int i = tid + 256 * j, r = i / PPR, pc = i % PPR;
-            *reinterpret_cast<u32x4 *>(sK + r * PK + pc * EPP) = r < lenc ? kv[j] : z4;
-            *reinterpret_cast<u32x4 *>(sQ + r * PK + pc * EPP) = r < lenc ? qv[j] : z4;
-        }
-    }
-    constexpr int WSB = FRAG ? ws_bytes_frag() : ws_bytes_per_chunk<DT>();
-    unsigned char *rec = ws + (slot * p.Hv + h) * (int64_t)WSB;
-    float *vec = reinterpret_cast<float *>(
-        rec + (FRAG ? 2 * kFragBytes : 2 * kC * kC * (int)sizeof(DT)));
-    if (wave == 0) {
-        const float a = a_t, b = b_t;
-        const bool ok = lane < lenc;
-        const float la = logits ? neg_softplus(a) : __logf(fmaxf(a, FLT_MIN));
-        const float x = wave_inclusive_scan(ok ? la : 0.f);
-        const float glast = __shfl(x, 63, 64);
-        const float gam = __expf(x), dec = __expf(glast - x);
-        const float bet = ok ? (logits ? sigmoid_f(b) : b) : 0.f;
-        sG[lane] = x;
-        sGam[lane] = gam;
-        sDec[lane] = dec;
-        sBeta[lane] = bet;
-        if (!raw_qk) {  // otherwise written once the row norms are folded in
-            vec[lane] = gam;
-            vec[kC + lane] = dec;
-            vec[2 * kC + lane] = bet;
-            vec[3 * kC + lane] = gam;
-        }
-    }
-    __syncthreads();
-    if constexpr (raw_qk)  // K and Q stay live until the barrier after the Gram products
-        fold_qk_norms<DT, D, PK, 256>(sK, sQ, sG, sGam, sDec, sGamQ, sGrA, sGrP, sGc, tid);
-    // Gram products of this wave's lower tile pairs (pr = wave, wave + 4, ...)
-    f32x4 gk[3], gq[3];
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-        const int pr = wave + 4 * k;
-        if (pr < 10) gram_pair<DT, D, PK>(sK, sQ, pair_i(pr), pair_j(pr), g4, c16, gk[k], gq[k]);
-    }
-    __syncthreads();  // K and Q are dead from here on: A overlays them
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-        const int pr = wave + 4 * k;
-        if (pr < 10)
-            mask_pair<DT, PA, PT, FRAG, raw_qk>(gk[k], gq[k], pair_i(pr), pair_j(pr), g4, c16,
-                                        raw_qk ? sGrA : sG, raw_qk ? sGrP : sG, raw_qk ? sGc : sG,
-                                        sBeta, sA, sP, rec + kFragBytes);
-    }
-    __syncthreads();
-    if (raw_qk && wave == 0) {  // raw_qk is a compile-time constant
-        vec[lane] = sGam[lane];
-        vec[kC + lane] = sDec[lane];
-        vec[2 * kC + lane] = sBeta[lane];
-        vec[3 * kC + lane] = sGamQ[lane];
-    }
-    // E_b overwrite the diagonal blocks of A (each is read in full first)
-    if (wave == 0) solve_diag_blocks<DT, PA, PT>(sA, sA, sT, g4, c16);
-    __syncthreads();
-    if (wave < 3) solve_column<DT, PA, PT>(sA, sA, sT, wave, g4, c16);
-    __syncthreads();
-    // T, P -> workspace as dense [64][64] rows; blocks above the diagonal
-    // (never written in LDS) are stored as zeros
     if constexpr (FRAG) {
         // T (P is written by mask_pair): piece q is fragment i, lane l; its
         // halves are columns 32 k2 + 4 g4 .. +3 and 16 further of row
@@ -565,6 +424,223 @@ __global__ __launch_bounds__(256, FRAG ? 4 : 1) void prep_kernel(PrefillParams p
             *reinterpret_cast<u32x4 *>(gP + r * kC + pc * EPP) =
                 upper ? z4 : *reinterpret_cast<const u32x4 *>(sP + r * PT + pc * EPP);
         }
+    }
+}
+
+// One workgroup (4 waves) per (chunk slot, value head): Gram products, decay,
+// T = (I + A)^{-1}; writes T, P, gamma, dec, beta to the workspace (52 KiB
+// of LDS for bf16, D = 128: three workgroups share a CU and hide each
+// other's latencies). FRAG: the fragment record instead of dense rows, with
+// T in the dead K/Q staging and P written from registers (35 KiB, at most
+// 128 registers: four workgroups per CU). GRP (with FRAG): one workgroup per
+// (chunk slot, q/k head) for its R = Hv / Hk <= kPrepGrpMax value heads: the
+// K, Q staging, their row norms and the Gram products K K^T, Q K^T (which no
+// gate enters) are formed once, the scans run on waves 0 .. R - 1 at once,
+// and the masks, the solve and the record follow head by head.
+template <typename DT, int D, bool FRAG, bool RAWQK, bool GRP>
+__global__ __launch_bounds__(256, FRAG ? 4 : 1) void prep_kernel(PrefillParams p, unsigned char *ws,
+                                                                 int remap_xcd) {
+    static_assert(!FRAG || sizeof(DT) == 2, "fragment records are bf16");
+    static_assert(!GRP || FRAG, "the grouped prep writes fragment records");
+    using Cf = PrepCfg<DT, D, FRAG>;
+    using Pi = ChunkPitch<DT, D>;
+    constexpr int PK = Pi::PK, PT = Pi::PT, PA = Pi::PA;
+    constexpr int EPP = 16 / (int)sizeof(DT);
+    __shared__ __attribute__((aligned(16))) unsigned char smem[GRP ? Cf::LDS_GRP : Cf::LDS];
+    DT *sK = reinterpret_cast<DT *>(smem + Cf::OFF_K);
+    DT *sQ = reinterpret_cast<DT *>(smem + Cf::OFF_Q);
+    float *sA = reinterpret_cast<float *>(smem + Cf::OFF_A);
+    DT *sT = reinterpret_cast<DT *>(smem + Cf::OFF_T);
+    DT *sP = reinterpret_cast<DT *>(smem + Cf::OFF_P);
+    // the vectors of value head r of the group at sG0 + VS r: g, gamma, dec,
+    // beta, gamq, grA, grP, gc; the grouped kernel keeps seven (gc takes
+    // g's place once the norms are folded in), so that four workgroups fit a
+    // CU's LDS
+    constexpr int VS = (GRP ? 7 : 8) * kC;
+    float *sG0 = reinterpret_cast<float *>(smem + Cf::OFF_VEC);
+    float *sIK = sG0 + kPrepGrpMax * 7 * kC;  // GRP: inverse K row norms, then Q's
+    float *sIQ = sIK + kC;
+    static_assert(!GRP || !FRAG || 4 * Cf::LDS_GRP <= 160 * 1024, "four grouped workgroups per CU");
+    constexpr bool raw_qk = RAWQK;
+    const bool logits = p.flags & kGateLogits;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g4 = lane >> 4;
+    const int c16 = lane & 15;
+
+    // value heads of one chunk are consecutive logical ids: same XCD, so the
+    // heads sharing a q/k head read K and Q through one L2
+    const int wg = logical_wg(remap_xcd);
+    const int nhg = GRP ? p.Hk : p.Hv;  // workgroups per chunk slot
+    const int hw = wg % nhg;
+    const int64_t slot = p.chunk0 + wg / nhg;  // chunk0 > 0 only for one dense sequence
+    // which (sequence, chunk) owns this slot
+    int n;
+    if (p.cu_seqlens) {
+        int lo = 0, hi = p.nseq - 1;  // largest n with slot_base(n) <= slot
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (slot_base(p, mid) <= slot)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        n = lo;
+    } else {
+        // chunks per sequence and slots both fit 32 bits (the ABI bounds them)
+        const uint32_t per = (uint32_t)((p.seq_len + kC - 1) / kC);
+        n = (int)((uint32_t)slot / per);
+    }
+    int64_t tok0, len;
+    seq_bounds(p, n, tok0, len);
+    const int64_t c = slot - slot_base(p, n);
+    if (c < 0 || c * kC >= len) return;  // unused slot (uniform over the workgroup)
+    const int lenc = (int)((len - c * kC) < kC ? (len - c * kC) : kC);
+    const int64_t t0 = tok0 + c * kC;
+    const int R = GRP ? p.Hv / p.Hk : 1;  // value heads of this workgroup: h0 .. h0 + R - 1
+    const int grp = GRP ? hw : hw / (p.Hv / p.Hk);
+    const int h0 = GRP ? hw * R : hw;
+    const int64_t sQK = (int64_t)p.Hk * D;
+    const DT *kh = reinterpret_cast<const DT *>(p.k) + t0 * sQK + (int64_t)grp * D;
+    const DT *qh = reinterpret_cast<const DT *>(p.q) + t0 * sQK + (int64_t)grp * D;
+
+    // alpha, beta (wave r: head h0 + r) and the K, Q rows are all requested
+    // before any of them is used, so their latencies overlap
+    float a_t = 1.f, b_t = 0.f;
+    if (wave < R) {
+        const int rr = lane < lenc ? lane : lenc - 1;
+        a_t = p.alpha[(t0 + rr) * p.Hv + h0 + wave];
+        b_t = p.beta[(t0 + rr) * p.Hv + h0 + wave];
+    }
+    // K, Q rows -> LDS (rows past the end of the sequence are zero)
+    {
+        constexpr int PPR = D / EPP;
+        constexpr int NPC = kC * PPR / 256;  // pieces per thread
+        static_assert(kC * PPR % 256 == 0, "whole pieces per thread");
+        const u32x4 z4 = {0u, 0u, 0u, 0u};
+        u32x4 kv[NPC], qv[NPC];
+#pragma unroll
+        for (int j = 0; j < NPC; ++j) {
+            const int i = tid + 256 * j, r = i / PPR, pc = i % PPR;
+            const int rr = r < lenc ? r : lenc - 1;
+            kv[j] = *reinterpret_cast<const u32x4 *>(kh + (int64_t)rr * sQK + pc * EPP);
+            qv[j] = *reinterpret_cast<const u32x4 *>(qh + (int64_t)rr * sQK + pc * EPP);
+        }
+#pragma unroll
+        for (int j = 0; j < NPC; ++j) {
+            const int i = tid + 256 * j, r = i / PPR, pc = i % PPR;
+            *reinterpret_cast<u32x4 *>(sK + r * PK + pc * EPP) = r < lenc ? kv[j] : z4;
+            *reinterpret_cast<u32x4 *>(sQ + r * PK + pc * EPP) = r < lenc ? qv[j] : z4;
+        }
+    }
+    constexpr int WSB = FRAG ? ws_bytes_frag() : ws_bytes_per_chunk<DT>();
+    auto rec_of = [&](int r) { return ws + (slot * p.Hv + h0 + r) * (int64_t)WSB; };
+    auto vec_of = [&](int r) {
+        return reinterpret_cast<float *>(rec_of(r) + (FRAG ? 2 * kFragBytes : 2 * kC * kC * (int)sizeof(DT)));
+    };
+    if (wave < R) {
+        float *sG = sG0 + VS * wave, *sGam = sG + kC, *sDec = sG + 2 * kC, *sBeta = sG + 3 * kC;
+        float *vec = vec_of(wave);
+        const float a = a_t, b = b_t;
+        const bool ok = lane < lenc;
+        const float la = logits ? neg_softplus(a) : __logf(fmaxf(a, FLT_MIN));
+        const float x = wave_inclusive_scan(ok ? la : 0.f);
+        const float glast = __shfl(x, 63, 64);
+        const float gam = __expf(x), dec = __expf(glast - x);
+        const float bet = ok ? (logits ? sigmoid_f(b) : b) : 0.f;
+        sG[lane] = x;
+        sGam[lane] = gam;
+        sDec[lane] = dec;
+        sBeta[lane] = bet;
+        if (!raw_qk) {  // otherwise written once the row norms are folded in
+            vec[lane] = gam;
+            vec[kC + lane] = dec;
+            vec[2 * kC + lane] = bet;
+            vec[3 * kC + lane] = gam;
+        }
+    }
+    __syncthreads();
+    if constexpr (raw_qk) {  // K and Q stay live until the barrier after the Gram products
+        if constexpr (GRP) {
+            qk_inv_norms<DT, D, PK, 256>(sK, sQ, sIK, sIQ, tid);
+        } else {
+            float *sG = sG0;
+            fold_qk_norms<DT, D, PK, 256>(sK, sQ, sG, sG + kC, sG + 2 * kC, sG + 4 * kC, sG + 5 * kC,
+                                          sG + 6 * kC, sG + 7 * kC, tid);
+        }
+    }
+    // Gram products of this wave's lower tile pairs (pr = wave, wave + 4, ...)
+    f32x4 gk[3], gq[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const int pr = wave + 4 * k;
+        if (pr < 10) gram_pair<DT, D, PK>(sK, sQ, pair_i(pr), pair_j(pr), g4, c16, gk[k], gq[k]);
+    }
+    __syncthreads();  // K and Q are dead from here on: A overlays them
+    if constexpr (raw_qk && GRP) {
+        // the row norms folded into each head's vectors (as fold_qk_norms)
+        for (int i = tid; i < R * kC; i += 256) {
+            float *sG = sG0 + VS * (i / kC);
+            const int t = i % kC;
+            const float g = sG[t], ik = sIK[t], iq = sIQ[t];
+            const float lk = logf(ik), lq = logf(iq), eg = __expf(g);
+            sG[6 * kC + t] = g + lq;  // grP
+            sG[4 * kC + t] = eg * iq; // gamq
+            sG[5 * kC + t] = g + lk;  // grA
+            sG[t] = g - lk;           // gc, in g's place
+            sG[kC + t] = eg * ik;     // gamma
+            sG[2 * kC + t] *= ik;     // dec
+        }
+        __syncthreads();
+    }
+    if constexpr (GRP) {
+        // every head's P first (straight to its record), so that only the
+        // K Gram products stay live through the solves
+        for (int r = 0; r < R; ++r) {
+            float *sG = sG0 + VS * r;  // gc in g's place
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                const int pr = wave + 4 * k;
+                if (pr < 10)
+                    mask_pair<DT, PA, PT, FRAG, raw_qk, 2>(gk[k], gq[k], pair_i(pr), pair_j(pr), g4, c16,
+                                                   raw_qk ? sG + 5 * kC : sG, raw_qk ? sG + 6 * kC : sG,
+                                                   sG, sG + 3 * kC, sA, sP, rec_of(r) + kFragBytes);
+            }
+        }
+    }
+    for (int r = 0; r < R; ++r) {
+        float *sG = sG0 + VS * r;
+        float *sGam = sG + kC, *sDec = sG + 2 * kC, *sBeta = sG + 3 * kC, *sGamQ = sG + 4 * kC;
+        float *sGrA = sG + 5 * kC, *sGrP = sG + 6 * kC, *sGc = GRP ? sG : sG + 7 * kC;
+        unsigned char *rec = rec_of(r);
+        float *vec = vec_of(r);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const int pr = wave + 4 * k;
+            if (pr < 10)
+                mask_pair<DT, PA, PT, FRAG, raw_qk, GRP ? 1 : 3>(gk[k], gq[k], pair_i(pr), pair_j(pr), g4, c16,
+                                                         raw_qk ? sGrA : sG, raw_qk ? sGrP : sG,
+                                                         raw_qk ? sGc : sG, sBeta, sA, sP, rec + kFragBytes);
+        }
+        __syncthreads();
+        if (raw_qk && wave == 0) {  // raw_qk is a compile-time constant
+            vec[lane] = sGam[lane];
+            vec[kC + lane] = sDec[lane];
+            vec[2 * kC + lane] = sBeta[lane];
+            vec[3 * kC + lane] = sGamQ[lane];
+        }
+        // E_b overwrite the diagonal blocks of A (each is read in full first);
+        // the grouped kernel reads each batch's rows when it needs them (the
+        // K Gram products hold registers across its loop)
+        if (wave == 0) solve_diag_blocks<DT, PA, PT, !GRP>(sA, sA, sT, g4, c16);
+        __syncthreads();
+        if (wave < 3) solve_column<DT, PA, PT>(sA, sA, sT, wave, g4, c16);
+        __syncthreads();
+        // T, P -> workspace (the next head's masks write only A; its solve
+        // writes T after the barrier that follows them)
+        write_tp_record<DT, D, FRAG>(rec, sT, sP, tid);
     }
 }
 
@@ -1064,16 +1140,35 @@ static hipError_t launch_fused(const PrefillParams &p, int nsplit, hipStream_t s
     return hipGetLastError();
 }
 
+// The records of nslots chunk slots. Fragment records for 2 .. kPrepGrpMax
+// value heads per q/k head take one workgroup per (slot, q/k head), which
+// shares the K, Q staging and Gram products among those heads (GDN_PREP=1:
+// one workgroup per value head, as for every other case).
 template <typename DT, int D, bool FRAG>
-static hipError_t launch_prep(const PrefillParams &p, unsigned char *ws, int64_t nprep,
+static hipError_t launch_prep(const PrefillParams &p, unsigned char *ws, int64_t nslots,
                               hipStream_t stream) {
     if (p.records_ready) return hipSuccess;
-    if (p.flags & kQkL2Norm)
-        hipLaunchKernelGGL((prep_kernel<DT, D, FRAG, true>), dim3((unsigned)nprep), dim3(256), 0,
-                           stream, p, ws, nprep % 8 == 0 ? 1 : 0);
+    const int R = p.Hv / p.Hk;
+    const char *pe = getenv("GDN_PREP");
+    const bool grp = FRAG && R >= 2 && R <= kPrepGrpMax && !(pe && pe[0] == '1');
+    const int64_t nprep = nslots * (grp ? p.Hk : p.Hv);
+    if (nprep <= 0 || nprep > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const dim3 g((unsigned)nprep), b(256);
+    const int remap = nprep % 8 == 0 ? 1 : 0;
+    const bool raw = p.flags & kQkL2Norm;
+    if constexpr (FRAG) {
+        if (grp) {
+            if (raw)
+                hipLaunchKernelGGL((prep_kernel<DT, D, FRAG, true, true>), g, b, 0, stream, p, ws, remap);
+            else
+                hipLaunchKernelGGL((prep_kernel<DT, D, FRAG, false, true>), g, b, 0, stream, p, ws, remap);
+            return hipGetLastError();
+        }
+    }
+    if (raw)
+        hipLaunchKernelGGL((prep_kernel<DT, D, FRAG, true, false>), g, b, 0, stream, p, ws, remap);
     else
-        hipLaunchKernelGGL((prep_kernel<DT, D, FRAG, false>), dim3((unsigned)nprep), dim3(256), 0,
-                           stream, p, ws, nprep % 8 == 0 ? 1 : 0);
+        hipLaunchKernelGGL((prep_kernel<DT, D, FRAG, false, false>), g, b, 0, stream, p, ws, remap);
     return hipGetLastError();
 }
 
@@ -1085,7 +1180,7 @@ static hipError_t launch_split(const PrefillParams &p, unsigned char *ws, int64_
     const int64_t nchain = (int64_t)p.nseq * p.Hv * nsplit;
     if (nprep <= 0 || nprep > 0x7FFFFFFF || nchain <= 0 || nchain > 0x7FFFFFFF)
         return hipErrorInvalidValue;
-    hipError_t e = launch_prep<DT, D, false>(p, ws, nprep, stream);
+    hipError_t e = launch_prep<DT, D, false>(p, ws, nslots, stream);
     if (e != hipSuccess) return e;
     if (p.prefix)
         hipLaunchKernelGGL((chain_kernel<DT, D, NC, DVW, true>), dim3((unsigned)nchain), dim3(256),
@@ -1106,7 +1201,7 @@ static hipError_t launch_split_db(const PrefillParams &p, unsigned char *ws, int
     if (nprep <= 0 || nprep > 0x7FFFFFFF || nchain <= 0 || nchain > 0x7FFFFFFF)
         return hipErrorInvalidValue;
     if (ChainDbCfg<D, NC, NH>::DVS * nsplit != D) return hipErrorInvalidValue;
-    hipError_t e = launch_prep<__bf16, D, true>(p, ws, nprep, stream);
+    hipError_t e = launch_prep<__bf16, D, true>(p, ws, nslots, stream);
     if (e != hipSuccess) return e;
     // the one-wave-per-SIMD chain where it applies; GDN_CHAIN=db keeps this
     // kernel (for comparisons and the tests that cover both)

@@ -629,6 +629,29 @@ def test_prefill_prepared_inputs(gdn, monkeypatch, path, nsplit, dtype, D, flags
           f"prepared inputs flags={flags} {path} ns={nsplit} {dtype} D{D}")
 
 
+@pytest.mark.parametrize("Hk,Hv", [(2, 2), (2, 4), (2, 6), (1, 4)])
+@pytest.mark.parametrize("flags", [0, QK | GL])
+@pytest.mark.parametrize("prep", ["grouped", "per_head"])
+def test_two_pass_prep_head_groups(gdn, monkeypatch, Hk, Hv, flags, prep):
+    """The two-pass prefill (bf16, d = 128, four column slices) with 1 .. 4
+    value heads per q/k head: one prep workgroup per q/k head for 2 or 3 of
+    them (sharing the K, Q staging and Gram products), one per value head
+    otherwise or with GDN_PREP=1."""
+    monkeypatch.setenv("GDN_PREFILL_PATH", "split")
+    monkeypatch.setenv("GDN_PREFILL_NSPLIT", "4")
+    if prep == "per_head":
+        monkeypatch.setenv("GDN_PREP", "1")
+    d = _prepared_inputs(lambda raw: small_prefill(1, 200, Hk, Hv, 128, "bf16", seed=150 + Hv + flags,
+                                                   init_state=True, raw=raw), flags)
+    q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
+    out, sf = gdn.gdn_prefill_chunked(q, k, v, a, b, to_torch(d["S0"], DEV), flags=flags)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"],
+                                  flags=flags)
+    check(from_torch(out), from_torch(sf), o_ref, S_ref, "bf16",
+          f"two-pass prep {prep} Hk{Hk} Hv{Hv} flags={flags}")
+
+
 @pytest.mark.parametrize("path", ["fused", "fused1", "split"])
 def test_varlen_prepared_inputs_and_zero_rows(gdn, monkeypatch, path):
     """Raw rows of zeros normalise to zero (the 1e-6 under the root): such a
