@@ -156,17 +156,11 @@ size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t tokens, int32_t Hk, 
     if (!gdn::prefill_wants_workspace((int64_t)num_seqs * Hv, cus)) return 0;
     const int64_t slots = gdn::prefill_ws_slots(num_seqs, total, packed ? 0 : tokens, packed != 0);
     const size_t recs = gdn::prefill_ws_bytes(slots, Hv, dtype == GDN_BF16 ? 1 : 0);
-    // few long sequences: the segmented path, whose layout also holds the above;
-    // one long sequence: the pipelined two-pass path (the records, then two states)
+    // few long sequences: the segmented path, whose layout also holds the above
     const size_t seg = packed ? 0
                               : gdn::prefill_seg_ws_bytes(num_seqs, tokens, Hv, Dk,
                                                           dtype == GDN_BF16 ? 1 : 0, cus);
-    const size_t pipe = packed ? 0
-                               : gdn::prefill_pipe_ws_bytes(num_seqs, tokens, Hv, Dk,
-                                                            dtype == GDN_BF16 ? 1 : 0, cus);
-    size_t need = seg > recs ? seg : recs;
-    if (pipe > need) need = pipe;
-    return gdn::kWsStatusBytes + need;
+    return gdn::kWsStatusBytes + (seg > recs ? seg : recs);
 }
 
 gdn_status_t gdn_prefill_chunked(const void *q, const void *k, const void *v, const float *alpha,

@@ -120,12 +120,7 @@ void chain4_kernel(PrefillParams p, const unsigned char *ws, int remap_xcd) {
     const int64_t base = slot_base(p, n);
     const int64_t sQK = (int64_t)p.Hk * D;
     const int64_t sVO = (int64_t)p.Hv * D;
-    // chunks cb .. ce - 1 of the sequence: all of them, or the piece one
-    // launch covers (one dense sequence; p.s0 then holds the state at chunk
-    // cb and p.s_final receives the state at chunk ce)
     const int64_t npc = (len + kC - 1) / kC;
-    const int64_t cb = p.chunk0 < npc ? p.chunk0 : npc;
-    const int64_t ce = p.chunk_end > cb && p.chunk_end < npc ? p.chunk_end : npc;
     auto kslot = [&](int64_t c) { return smem + Cf::OFF_KQR + (int)(c % Cf::NKQ) * Cf::SZ_KQ; };
     auto vslot = [&](int64_t c) { return smem + Cf::OFF_VRR + (int)(c & 1) * Cf::SZ_VR; };
     auto hslot = [&](int64_t c, int j) { return smem + Cf::OFF_HO + ((int)(c & 1) * Cf::NC + j) * Cf::HO; };
@@ -155,7 +150,7 @@ void chain4_kernel(PrefillParams p, const unsigned char *ws, int remap_xcd) {
                 for (int mt = 0; mt < 4; ++mt)
                     fk[kk][mt] = *reinterpret_cast<const F *>(swz_at<KR>(K, 16 * mt, c16, 32 * kk + 8 * g4));
         };
-        for (int64_t c = cb; c < ce; ++c) {
+        for (int64_t c = 0; c < npc; ++c) {
             const DT *K = reinterpret_cast<const DT *>(kslot(c) + Cf::OFF_K);
             const unsigned char *vt = vslot(c);
             const DT *V = reinterpret_cast<const DT *>(vt + Cf::OFF_V);
@@ -356,21 +351,21 @@ void chain4_kernel(PrefillParams p, const unsigned char *ws, int remap_xcd) {
         // step c: chunk c's operands into set c & 1, O of chunk c - 1 from set
         // (c - 1) & 1; two steps per iteration so that the sets are fixed
         // registers
-        for (int64_t c = cb; c < ce; c += 2) {
+        for (int64_t c = 0; c < npc; c += 2) {
             load_ops(c, ops[0]);
-            if (c > cb) out_chunk(c - 1, ops[1]);
+            if (c > 0) out_chunk(c - 1, ops[1]);
             __syncthreads();
-            if (c + 1 < ce) {
+            if (c + 1 < npc) {
                 load_ops(c + 1, ops[1]);
                 out_chunk(c, ops[0]);
                 __syncthreads();
             }
         }
-        if (ce > cb) {
-            if ((ce - 1 - cb) & 1)
-                out_chunk(ce - 1, ops[1]);
+        if (npc > 0) {
+            if ((npc - 1) & 1)
+                out_chunk(npc - 1, ops[1]);
             else
-                out_chunk(ce - 1, ops[0]);
+                out_chunk(npc - 1, ops[0]);
         }
         return;
     }
@@ -455,32 +450,32 @@ void chain4_kernel(PrefillParams p, const unsigned char *ws, int remap_xcd) {
 #pragma unroll
         for (int j = 0; j < Cf::BLK_R; ++j) dma16(rec + 1024 * j + 16 * lane, dst + Cf::OFF_REC + 1024 * j);
     };
-    // Chunk numbers below count from cb. Before step 0: V and the record of
-    // chunk 0, then K, Q of chunks 0 and 1; step 0 needs all but chunk 1's
-    // K, Q. In step c: V and the record of chunk c + 1, then K, Q of chunk
-    // c + 2 and the touches of chunk c + 4 (clamped to the last chunk); at its end everything but the last two
+    // Before step 0: V and the record of chunk 0, then K, Q of chunks 0 and 1;
+    // step 0 needs all but chunk 1's K, Q. In step c: V and the record of
+    // chunk c + 1, then K, Q of chunk c + 2 and the touches of chunk c + 4
+    // (clamped to the last chunk); at its end everything but the last two
     // groups has landed (loads complete in issue order). The barrier carries
     // no fence (a fence would make the compiler wait for every outstanding
     // copy): the explicit counts order this wave's copies before it, and the
     // other waves read after their own barriers. The last steps wait for
     // everything, so that no copy is in flight when the workgroup ends.
-    for (int64_t c = cb + 1; c < min<int64_t>(ce, cb + 1 + Cf::PF_AHEAD); ++c) touch(c);
-    if (ce > cb) {
-        copy_vr(cb);
-        copy_kq(cb);
+    for (int64_t c = 1; c < min<int64_t>(npc, 1 + Cf::PF_AHEAD); ++c) touch(c);
+    if (npc > 0) {
+        copy_vr(0);
+        copy_kq(0);
     }
-    if (ce > cb + 1) {
-        copy_kq(cb + 1);
+    if (npc > 1) {
+        copy_kq(1);
         wait_vm<Cf::BLK_KQ>();
     } else {
         wait_vm<0>();
     }
     __builtin_amdgcn_s_barrier();
-    for (int64_t c = cb; c < ce; ++c) {
-        if (c + 1 < ce) copy_vr(c + 1);
-        if (c + 2 < ce) {
+    for (int64_t c = 0; c < npc; ++c) {
+        if (c + 1 < npc) copy_vr(c + 1);
+        if (c + 2 < npc) {
             copy_kq(c + 2);
-            touch(c + Cf::PF_AHEAD < ce ? c + Cf::PF_AHEAD : ce - 1);
+            touch(c + Cf::PF_AHEAD < npc ? c + Cf::PF_AHEAD : npc - 1);
             wait_vm<Cf::BLK_KQ + Cf::NPF>();
         } else {
             wait_vm<0>();

@@ -85,9 +85,6 @@ bool prefill_wants_workspace(int64_t chains, int num_cus);
 // Workspace bytes of the segmented prefill (dense bf16 batches with few
 // chains), or 0 when it does not apply to these shapes.
 size_t prefill_seg_ws_bytes(int64_t nseq, int64_t T, int Hv, int D, int dtype, int num_cus);
-// Workspace bytes of the pipelined two-pass prefill (one long dense sequence
-// in pieces: the records, then two states), or 0 where it does not apply.
-size_t prefill_pipe_ws_bytes(int64_t nseq, int64_t T, int Hv, int D, int dtype, int num_cus);
 
 hipError_t launch_segment_setup(int32_t *cu, int32_t B, int32_t P, int64_t T, int64_t L,
                                 __bf16 *zero_v, int32_t nzero, hipStream_t stream);

@@ -30,8 +30,6 @@
 #include <float.h>
 #include <stdlib.h>
 
-#include <mutex>
-
 #include "gdn_chunk.hpp"
 #include "gdn_seq.hpp"
 #include <type_traits>
@@ -1368,111 +1366,6 @@ size_t prefill_seg_ws_bytes(int64_t nseq, int64_t T, int Hv, int D, int dtype, i
 static hipError_t launch_prefill_ws(const PrefillParams &p, int dtype, int D, int num_cus,
                                    void *ws, size_t ws_bytes, int64_t nslots, hipStream_t stream);
 
-// ----------------------------------------------------------------------------
-// pipelined two-pass prefill: one long dense sequence on chain4 in pieces of
-// chunks. chain4 takes one CU per workgroup and leaves a quarter of the CUs
-// idle (48 heads x 4 slices = 192 workgroups), and its LDS and registers
-// admit no prep workgroup beside it; so the prep of piece i + 1 runs on a
-// side stream, on those idle CUs, while the chain walks piece i. Events order
-// each chain piece after its prep; the state passes between pieces through
-// two buffers after the records.
-
-constexpr int kPipeMaxPieces = 16;
-constexpr int64_t kPipeMinChunks = 512;
-
-// pieces for a dense batch (0: no pipeline). GDN_PIPE=0 turns it off,
-// GDN_PIPE=n forces n pieces (n >= 2) whenever the pieces' chain would be
-// chain4 (for tests at small sizes).
-static int pipe_pieces(int64_t nseq, int64_t T, int Hv, int D, int dtype, int num_cus) {
-    if (nseq != 1 || dtype != 1 || D != 128 || T <= 0) return 0;
-    if (!prefill_wants_workspace(nseq * Hv, num_cus) || chain_slices(nseq * Hv, num_cus) != 4) return 0;
-    const int64_t nchunks = (T + kC - 1) / kC;
-    const int forced = env_int("GDN_PIPE", -1);
-    if (forced == 0) return 0;
-    int n;
-    if (forced > 0) {
-        n = forced;
-    } else {
-        if (nchunks < kPipeMinChunks) return 0;
-        n = 8;
-    }
-    if (n < 2) return 0;
-    if (n > kPipeMaxPieces) n = kPipeMaxPieces;
-    if (n > nchunks) n = (int)nchunks;
-    return n >= 2 ? n : 0;
-}
-
-static size_t pipe_states_off(int64_t nslots, int Hv) { return align256(prefill_ws_bytes(nslots, Hv, 1)); }
-
-size_t prefill_pipe_ws_bytes(int64_t nseq, int64_t T, int Hv, int D, int dtype, int num_cus) {
-    if (!pipe_pieces(nseq, T, Hv, D, dtype, num_cus)) return 0;
-    return pipe_states_off(prefill_ws_slots(nseq, nseq * T, T, false), Hv) + 2 * (size_t)Hv * D * D * 4;
-}
-
-// the side stream and the events of one device, created once (default
-// priority) and kept until the process ends
-struct PipeRes {
-    bool ok = false;
-    hipStream_t side = nullptr;
-    hipEvent_t start = nullptr;
-    hipEvent_t done[kPipeMaxPieces] = {};
-};
-constexpr int kPipeMaxDevices = 64;
-static PipeRes g_pipe[kPipeMaxDevices];
-static std::mutex g_pipe_mu;
-
-static PipeRes *pipe_res_locked() {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kPipeMaxDevices) return nullptr;
-    PipeRes &r = g_pipe[dev];
-    if (!r.ok) {
-        if (hipStreamCreateWithFlags(&r.side, hipStreamNonBlocking) != hipSuccess) return nullptr;
-        if (hipEventCreateWithFlags(&r.start, hipEventDisableTiming) != hipSuccess) return nullptr;
-        for (int i = 0; i < kPipeMaxPieces; ++i)
-            if (hipEventCreateWithFlags(&r.done[i], hipEventDisableTiming) != hipSuccess) return nullptr;
-        r.ok = true;
-    }
-    return &r;
-}
-
-// The prep of every piece on the side stream (after the caller's earlier
-// work), the chain of each piece on the caller's stream after its prep.
-// Calls that overlap from several host threads take turns on a mutex while
-// they enqueue.
-static hipError_t launch_pipelined(const PrefillParams &p, unsigned char *ws, int64_t nslots, int npieces,
-                                   hipStream_t stream) {
-    const int64_t nchunks = nslots;  // one dense sequence
-    const int64_t lc = (nchunks + npieces - 1) / npieces;
-    float *tmp = reinterpret_cast<float *>(ws + pipe_states_off(nslots, p.Hv));
-    const size_t st_elems = (size_t)p.Hv * 128 * 128;
-    const int64_t nchain = (int64_t)p.Hv * 4;
-    std::lock_guard<std::mutex> lock(g_pipe_mu);
-    PipeRes *r = pipe_res_locked();
-    if (!r) return hipErrorNotReady;
-    hipError_t e = hipEventRecord(r->start, stream);
-    if (e == hipSuccess) e = hipStreamWaitEvent(r->side, r->start, 0);
-    int n = 0;
-    for (int64_t cb = 0; e == hipSuccess && cb < nchunks; cb += lc, ++n) {
-        const int64_t ce = cb + lc < nchunks ? cb + lc : nchunks;
-        PrefillParams pp = p;
-        pp.chunk0 = cb;
-        e = launch_prep<__bf16, 128, true>(pp, ws, ce - cb, r->side);
-        if (e == hipSuccess) e = hipEventRecord(r->done[n], r->side);
-    }
-    int i = 0;
-    for (int64_t cb = 0; e == hipSuccess && cb < nchunks; cb += lc, ++i) {
-        const int64_t ce = cb + lc < nchunks ? cb + lc : nchunks;
-        PrefillParams pc = p;
-        pc.chunk0 = cb;
-        pc.chunk_end = ce;
-        pc.s0 = i == 0 ? p.s0 : tmp + (size_t)((i - 1) & 1) * st_elems;
-        pc.s_final = ce == nchunks ? p.s_final : tmp + (size_t)(i & 1) * st_elems;
-        e = hipStreamWaitEvent(stream, r->done[i], 0);
-        if (e == hipSuccess) e = launch_chain4(pc, ws, nchain, stream);
-    }
-    return e;
-}
-
 static hipError_t launch_segmented(const PrefillParams &p, int D, int num_cus, unsigned char *ws,
                                    const SegPlan &sp, hipStream_t stream) {
     const int64_t B = p.nseq, T = p.seq_len;
@@ -1550,15 +1443,6 @@ static hipError_t launch_prefill_ws(const PrefillParams &p, int dtype, int D, in
         // double-buffered chain kernel fills a CU's LDS), at most four.
         const int ns = chain_slices(chains, num_cus);
         unsigned char *w = static_cast<unsigned char *>(ws);
-        if (!p.cu_seqlens && !p.prefix && !p.dual && !p.records_ready && !p.s0_identity) {
-            const int np = pipe_pieces(p.nseq, p.seq_len, p.Hv, D, dtype, num_cus);
-            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-            const char *ck = getenv("GDN_CHAIN");
-            if (np && ws_bytes >= prefill_pipe_ws_bytes(p.nseq, p.seq_len, p.Hv, D, dtype, num_cus) &&
-                chain4_supported(p, D, 4) && !(ck && ck[0] == 'd') &&
-                hipStreamIsCapturing(stream, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone)
-                return launch_pipelined(p, w, nslots, np, stream);
-        }
         if (dtype == 1 && D == 128) {
             switch (ns) {
             case 1: return launch_split<__bf16, 128, 4, 32>(p, w, nslots, 1, stream);

@@ -652,35 +652,6 @@ def test_two_pass_prep_head_groups(gdn, monkeypatch, Hk, Hv, flags, prep):
           f"two-pass prep {prep} Hk{Hk} Hv{Hv} flags={flags}")
 
 
-@pytest.mark.parametrize("T,pieces,init,flags", [
-    (64 * 20 + 17, "3", True, 0),
-    (64 * 20 + 17, "5", False, QK | GL),
-    (64 * 7, "7", True, QK),
-    (64 * 33, "16", True, GL),
-])
-def test_two_pass_pipelined_pieces(gdn, monkeypatch, T, pieces, init, flags):
-    """One long dense sequence in pieces (forced here at small sizes): each
-    piece's prep on a side stream, its chain after it on the caller's stream,
-    the state passed between pieces through the workspace. Equal bit for bit
-    to the unpipelined two-pass call, and to the oracle within tolerance."""
-    monkeypatch.setenv("GDN_PREFILL_PATH", "split")
-    monkeypatch.setenv("GDN_PREFILL_SEGMENTS", "0")
-    d = _prepared_inputs(lambda raw: small_prefill(1, T, 2, 6, 128, "bf16", seed=170 + T + int(pieces),
-                                                   init_state=init, raw=raw), flags)
-    q, k, v, a, b = _t(d, ("q", "k", "v", "alpha", "beta"))
-    s0 = to_torch(d["S0"], DEV) if init else None
-    monkeypatch.setenv("GDN_PIPE", "0")
-    out0, sf0 = gdn.gdn_prefill_chunked(q, k, v, a, b, s0, flags=flags)
-    monkeypatch.setenv("GDN_PIPE", pieces)
-    out1, sf1 = gdn.gdn_prefill_chunked(q, k, v, a, b, s0, flags=flags)
-    torch.cuda.synchronize()
-    assert torch.equal(out0, out1) and torch.equal(sf0, sf1), "pipelined differs from one launch"
-    o_ref, S_ref = oracle.prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"],
-                                  d["S0"] if init else None, flags=flags)
-    check(from_torch(out1), from_torch(sf1), o_ref, S_ref, "bf16",
-          f"pipelined T{T} pieces={pieces} flags={flags}")
-
-
 @pytest.mark.parametrize("path", ["fused", "fused1", "split"])
 def test_varlen_prepared_inputs_and_zero_rows(gdn, monkeypatch, path):
     """Raw rows of zeros normalise to zero (the 1e-6 under the root): such a
