@@ -296,7 +296,6 @@ void chain4_kernel(PrefillParams p, const unsigned char *ws, int remap_xcd) {
         // O of chunk c from its operands and the S, U its chain waves left in LDS
         auto out_chunk = [&](int64_t c, const Ops &o) {
             const int lenc = (int)((len - c * kC) < kC ? (len - c * kC) : kC);
-            __bf16 *oc = oh + c * kC * sVO + (int64_t)c16 * sVO + 4 * g4;
             f32x4 acc[Cf::NC][4];
 #pragma unroll
             for (int j = 0; j < Cf::NC; ++j) {
@@ -334,17 +333,28 @@ void chain4_kernel(PrefillParams p, const unsigned char *ws, int remap_xcd) {
                 acc[j][2] = mma(fu[j][1], o.fp[3], acc[j][2]);
                 acc[j][3] = mma(fu[j][1], o.fp[5], acc[j][3]);
             }
+            // Lane (g4, c16) holds columns 4 g4 .. + 3 of both chain waves' tiles
+            // (j = 0, 1) for token 16 mt + c16. One exchange between lane rows
+            // (row g4 odd <-> row g4 - 1, v_permlane16_swap) gives each lane 8
+            // consecutive columns of one tile -- rows 0, 1, 2, 3: columns 0, 16,
+            // 8, 24 .. + 7 -- so a token's 64 bytes leave as four 16-byte stores
+            // instead of eight 8-byte ones: half the write requests, which
+            // share the CU's memory path with the copies.
+            static_assert(Cf::NC == 2, "two 16-column tiles per token row");
+            __bf16 *o0 = oh + (c * kC + c16) * sVO + 8 * (g4 >> 1) + 16 * (g4 & 1);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                if (16 * mt + c16 < lenc) {
+                bf16x4 xb, yb;
 #pragma unroll
-                    for (int j = 0; j < Cf::NC; ++j) {
-                        bf16x4 ob;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) ob[r] = (__bf16)(p.scale * acc[j][mt][r]);
-                        *reinterpret_cast<bf16x4 *>(oc + (int64_t)(16 * mt) * sVO + 16 * j) = ob;
-                    }
+                for (int r = 0; r < 4; ++r) {
+                    xb[r] = (__bf16)(p.scale * acc[0][mt][r]);
+                    yb[r] = (__bf16)(p.scale * acc[1][mt][r]);
                 }
+                const u32x2 x = __builtin_bit_cast(u32x2, xb), y = __builtin_bit_cast(u32x2, yb);
+                const auto s0 = __builtin_amdgcn_permlane16_swap(x[0], y[0], false, false);
+                const auto s1 = __builtin_amdgcn_permlane16_swap(x[1], y[1], false, false);
+                if (16 * mt + c16 < lenc)
+                    *reinterpret_cast<u32x4 *>(o0 + (int64_t)(16 * mt) * sVO) = u32x4{s0[0], s1[0], s0[1], s1[1]};
             }
         };
         __syncthreads();
