@@ -416,8 +416,8 @@ void chain4_kernel(PrefillParams p, const unsigned char *ws, int remap_xcd) {
     // scratch KiB that nothing reads), so that its copies PF_AHEAD steps later
     // hit L2. Each K and Q line is touched by one of the workgroups that share
     // it (the value heads of this q/k head times the column slices), each
-    // record line by one of the slices, the V rows by their own workgroup;
-    // the lanes beyond the lines repeat the first one. (Every workgroup
+    // record line and each V line by one of the slices that share it; the
+    // lanes beyond the lines repeat the first one. (Every workgroup
     // touching every line instead took longer than no touches at all: the
     // extra requests queue behind the same per-CU limit as the copies.)
     const int share = (h % (p.Hv / p.Hk)) * NSPLIT + slice;
@@ -433,10 +433,14 @@ void chain4_kernel(PrefillParams p, const unsigned char *ws, int remap_xcd) {
         int jr = slice + NSPLIT * lane;  // line of the record
         if (jr >= Cf::WSB / 128) jr = slice;
         dma16(record(c) + 128 * jr, junk);
-        dma16(vb + c * kC * rowv + (int64_t)min(lane, lenc - 1) * rowv, junk);
+        // V: a 128-byte line holds the columns of slices 2 i and 2 i + 1; each of
+        // the two touches half of its rows (lanes 32 .. 63 repeat 0 .. 31)
+        const int vrow = 32 * (slice & 1) + (lane & 31);
+        dma16(vb - 2 * dv0 + 128 * (slice >> 1) + c * kC * rowv + (int64_t)min(vrow, lenc - 1) * rowv, junk);
     };
     static_assert(Cf::NPF == 4 && kC * KR / 128 == 2 * kC, "four touch instructions: K, Q, record, V");
     static_assert(Cf::WSB / 128 <= NSPLIT * 64, "the slices' lanes cover the record's lines");
+    static_assert(NSPLIT == 4 && Cf::VR == 64, "two slices share each 128-byte V line");
     auto copy_kq = [&](int64_t c) {  // BLK_KQ copies
         unsigned char *dst = kslot(c);
         const unsigned char *k0 = kb + c * kC * rowqk, *q0 = qb + c * kC * rowqk;
