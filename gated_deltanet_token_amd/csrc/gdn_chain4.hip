@@ -56,8 +56,8 @@ struct C4 {
     static constexpr int NSPLIT = D / DVS;
     static constexpr int KR = D * 2;     // K, Q row bytes
     static constexpr int VR = DVS * 2;   // V row bytes
-    static constexpr int FRAG = kTriFrags * 64 * 16;  // T or P as MFMA fragments
-    static constexpr int WSB = 2 * FRAG + 1024;       // record: T, P, 4 vectors
+    static constexpr int FRAG = kTriFragBytes;  // T or P as (compact) MFMA fragments
+    static constexpr int WSB = 2 * FRAG + 1024; // record: T, P, 4 vectors
     // K and Q are copied two chunks ahead (ring of 3: in use, landing,
     // issued); V and the record one chunk ahead (ring of 2: in use, issued)
     static constexpr int NKQ = 3, NVR = 2;
@@ -154,7 +154,7 @@ void chain4_kernel(PrefillParams p, const unsigned char *ws, int remap_xcd) {
             const DT *K = reinterpret_cast<const DT *>(kslot(c) + Cf::OFF_K);
             const unsigned char *vt = vslot(c);
             const DT *V = reinterpret_cast<const DT *>(vt + Cf::OFF_V);
-            const F *T = reinterpret_cast<const F *>(vt + Cf::OFF_T);
+            const unsigned char *T = vt + Cf::OFF_T;
             const float *vec = reinterpret_cast<const float *>(vt + Cf::OFF_VEC);
             bf16x8 *ho_s = reinterpret_cast<bf16x8 *>(hslot(c, wave));
             bf16x8 *ho_u = ho_s + (D / 32) * 64;
@@ -170,7 +170,7 @@ void chain4_kernel(PrefillParams p, const unsigned char *ws, int remap_xcd) {
             // operands of R, U = T R and the state update (this chunk)
             F ft[kTriFrags];
 #pragma unroll
-            for (int i = 0; i < kTriFrags; ++i) ft[i] = T[i * 64 + lane];
+            for (int i = 0; i < kTriFrags; ++i) ft[i] = ld_tri_frag(T, i, lane);
             bf16x4 v4[4];
             f32x4 bet[4], gam[4], dec[4];
 #pragma unroll
@@ -286,9 +286,8 @@ void chain4_kernel(PrefillParams p, const unsigned char *ws, int remap_xcd) {
                 for (int mt = 0; mt < 4; ++mt)
                     o.fq[kk][mt] = *reinterpret_cast<const F *>(swz_at<KR>(Q, 16 * mt, c16, 32 * kk + 8 * g4));
             const unsigned char *vr = vslot(c);
-            const F *P = reinterpret_cast<const F *>(vr + Cf::OFF_P);
 #pragma unroll
-            for (int i = 0; i < kTriFrags; ++i) o.fp[i] = P[i * 64 + lane];
+            for (int i = 0; i < kTriFrags; ++i) o.fp[i] = ld_tri_frag(vr + Cf::OFF_P, i, lane);
             const float *gamq = reinterpret_cast<const float *>(vr + Cf::OFF_VEC + 3 * kC * 4);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) o.gq[mt] = gamq[16 * mt + c16];

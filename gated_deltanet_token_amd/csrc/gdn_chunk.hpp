@@ -70,6 +70,38 @@ __host__ __device__ constexpr int tri_rb(int i) { return i < 2 ? i : 2 + (i - 2)
 __host__ __device__ constexpr int tri_k2(int i) { return (i == 3 || i == 5) ? 1 : 0; }
 __host__ __device__ constexpr int tri_frag(int rb, int k2) { return rb < 2 ? rb : 2 * rb - 2 + k2; }
 
+// Compact fragment storage (the workspace record and the LDS that it is
+// copied into unchanged). Fragments (0,0) and (2,1) sit on the diagonal with
+// their columns 16..31 of the block above it: elements 4..7 of every lane are
+// zero, so they are stored as 8 bytes per lane (512 B) and the other four as
+// 16 (1 KiB): 5 KiB per matrix instead of 6. The MFMA operand is rebuilt
+// with zeros in the upper half.
+constexpr int kTriFragBytes = (kTriFrags - 1) * 1024;
+__host__ __device__ constexpr bool tri_frag_half(int i) { return i == 0 || i == 3; }
+__host__ __device__ constexpr int tri_frag_off(int i) {
+    return i == 0 ? 0 : i <= 3 ? 1024 * i - 512 : 1024 * i - 1024;
+}
+static_assert(tri_frag_off(kTriFrags - 1) + 1024 == kTriFragBytes, "compact fragments tile 5 KiB");
+// Byte offset of lane l's bytes [8 h, 8 h + 8) of fragment i (h = 0 for the
+// compact fragments).
+__host__ __device__ constexpr int tri_frag_at(int i, int l, int h) {
+    return tri_frag_off(i) + (tri_frag_half(i) ? 8 * l : 16 * l + 8 * h);
+}
+// Fragment i of a compact set as an MFMA operand, for this lane.
+__device__ __forceinline__ bf16x8 ld_tri_frag(const unsigned char *base, int i, int lane) {
+    if (tri_frag_half(i)) {
+        const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(base + tri_frag_off(i) + 8 * lane);
+        bf16x8 f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f[e] = lo[e];
+            f[e + 4] = (__bf16)0.f;
+        }
+        return f;
+    }
+    return *reinterpret_cast<const bf16x8 *>(base + tri_frag_off(i) + 16 * lane);
+}
+
 // Lower 16x16 tile pairs (ti, tj), tj <= ti, of a 64x64 chunk matrix.
 __device__ __forceinline__ constexpr int pair_i(int pr) {
     return pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3;
@@ -125,9 +157,9 @@ __device__ __forceinline__ void gram_pair(const DT *sK, const DT *sQ, int ti, in
 // Apply the decay masks to a transposed Gram pair and write rows of A
 // (fp32, pitch PA) and P (operand type, pitch PT): row t gets columns
 // s = 16 tj + 4 g4 .. +3 from this lane. PFRAG (bf16): P goes instead
-// straight to its fragments at pfr (kTriFrags x 64 lanes x 16 bytes): this
-// lane's four values are one half of its fragment (rb, k2) = (ti, tj / 2);
-// the pairs on even diagonal blocks also zero the half above the diagonal.
+// straight to its fragments at pfr (the compact set of tri_frag_off): this
+// lane's four values are one half of its fragment (rb, k2) = (ti, tj / 2)
+// (all of it for the compact fragments, whose other half is zero).
 // PARTS selects what is formed: 1 A, 2 P, 3 both.
 template <typename DT, int PA, int PT, bool PFRAG = false, bool NORMS = false, int PARTS = 3>
 __device__ __forceinline__ void mask_pair(const f32x4 &gk, const f32x4 &gq, int ti, int tj, int g4,
@@ -167,9 +199,8 @@ __device__ __forceinline__ void mask_pair(const f32x4 &gk, const f32x4 &gq, int 
         bf16x4 pb;
 #pragma unroll
         for (int r = 0; r < 4; ++r) pb[r] = (__bf16)pv[r];
-        unsigned char *f = pfr + (tri_frag(ti, tj >> 1) * 64 + 16 * g4 + c16) * 16;
-        *reinterpret_cast<bf16x4 *>(f + (tj & 1) * 8) = pb;
-        if (ti == tj && (tj & 1) == 0) *reinterpret_cast<uint2 *>(f + 8) = uint2{0u, 0u};
+        // (the pairs on even diagonal tiles fill the compact fragments whole)
+        *reinterpret_cast<bf16x4 *>(pfr + tri_frag_at(tri_frag(ti, tj >> 1), 16 * g4 + c16, tj & 1)) = pb;
     } else if constexpr (sizeof(DT) == 2) {
         bf16x4 pb;
 #pragma unroll
@@ -753,7 +784,7 @@ __device__ __forceinline__ void ld_kt_frag_s(const __bf16 *K, int a, int k2, int
 // kTriFrags fragments x 64 lanes x 16 bytes; decay vectors gamma, dec, beta.
 struct DbSmem {
     const __bf16 *K, *Q, *V;
-    const bf16x8 *T, *P;
+    const unsigned char *T, *P;            // compact fragment sets (tri_frag_off)
     const float *gam, *dec, *beta, *gamq;  // as in ChainSmem
 };
 
@@ -833,7 +864,7 @@ __device__ __forceinline__ void chain_core_db(const DbSmem &m, f32x4 (&st)[D / 1
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) ld_chain_s<KR>(m.K, 16 * mt, c16, 32 * kk + 4 * g4, fk[kk][mt]);
 #pragma unroll
-    for (int i = 0; i < kTriFrags; ++i) ft[i] = m.T[i * 64 + lane];
+    for (int i = 0; i < kTriFrags; ++i) ft[i] = ld_tri_frag(m.T, i, lane);
     phase_fence();
     // K S^T; meanwhile the operands of R and of the state update are read
     f32x4 racc[4][NB];
@@ -967,7 +998,7 @@ __device__ __forceinline__ void out_step(const DbSmem &m, Handoff<D, NB> ho, int
     }
     F fp[kTriFrags];
 #pragma unroll
-    for (int i = 0; i < kTriFrags; ++i) fp[i] = m.P[i * 64 + lane];
+    for (int i = 0; i < kTriFrags; ++i) fp[i] = ld_tri_frag(m.P, i, lane);
     float gamr[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) gamr[mt] = m.gamq[16 * mt + c16];

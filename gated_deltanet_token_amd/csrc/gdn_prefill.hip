@@ -356,12 +356,13 @@ template <typename DT> constexpr int ws_bytes_per_chunk() {
     return 2 * kC * kC * (int)sizeof(DT) + 4 * kC * 4;
 }
 
-// Fragment record (bf16, read by chain_db_kernel): T and P each as the
-// kTriFrags MFMA fragments that cover their nonzero blocks, in lane order
-// (6 KiB each), then gam [64] | dec [64] | beta [64] | gamq [64] (f32, 1 KiB).
-// The chain copies it into LDS unchanged and reads one fragment per lane
-// with a single 16-byte load.
-constexpr int kFragBytes = kTriFrags * 64 * 16;
+// Fragment record (bf16, read by chain4_kernel and chain_db_kernel): T and P
+// each as the kTriFrags MFMA fragments that cover their nonzero blocks, in
+// lane order, the two with a zero half stored compact (5 KiB each), then
+// gam [64] | dec [64] | beta [64] | gamq [64] (f32, 1 KiB): 11 KiB. The chain
+// copies it into LDS unchanged and reads one fragment per lane with a single
+// 16-byte (compact: 8-byte) load.
+constexpr int kFragBytes = kTriFragBytes;
 constexpr int ws_bytes_frag() { return 2 * kFragBytes + 1024; }
 static_assert(ws_bytes_frag() <= ws_bytes_per_chunk<__bf16>(), "fragment record fits the query");
 
@@ -401,15 +402,19 @@ __device__ __forceinline__ void write_tp_record(unsigned char *rec, const DT *sT
     if constexpr (FRAG) {
         // T (P is written by mask_pair): piece q is fragment i, lane l; its
         // halves are columns 32 k2 + 4 g4 .. +3 and 16 further of row
-        // 16 rb + c16, zero where the column block lies above the diagonal
-        const u32x2 z2 = {0u, 0u};
+        // 16 rb + c16. The upper half lies above the diagonal (zero) exactly
+        // for the compact fragments, which store the lower half alone.
         for (int q = tid; q < kTriFrags * 64; q += 256) {
             const int i = q / 64, l = q % 64, lg4 = l >> 4, lc16 = l & 15;
             const int rb = tri_rb(i), k2 = tri_k2(i);
             const DT *src = sT + (16 * rb + lc16) * PT + 32 * k2 + 4 * lg4;
-            const u32x2 lo = 2 * k2 > rb ? z2 : *reinterpret_cast<const u32x2 *>(src);
-            const u32x2 hi = 2 * k2 + 1 > rb ? z2 : *reinterpret_cast<const u32x2 *>(src + 16);
-            *reinterpret_cast<u32x4 *>(rec + (int64_t)q * 16) = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            const u32x2 lo = *reinterpret_cast<const u32x2 *>(src);
+            if (tri_frag_half(i)) {
+                *reinterpret_cast<u32x2 *>(rec + tri_frag_at(i, l, 0)) = lo;
+            } else {
+                const u32x2 hi = *reinterpret_cast<const u32x2 *>(src + 16);
+                *reinterpret_cast<u32x4 *>(rec + tri_frag_at(i, l, 0)) = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
         }
     } else {
         constexpr int PPR = kC / EPP;
@@ -906,8 +911,7 @@ void chain_db_kernel(PrefillParams p, const unsigned char *ws, int nsplit, int r
         return DbSmem{reinterpret_cast<const DT *>(b + Cf::OFF_K),
                       reinterpret_cast<const DT *>(b + Cf::OFF_Q),
                       reinterpret_cast<const DT *>(b + Cf::OFF_V),
-                      reinterpret_cast<const bf16x8 *>(b + Cf::OFF_T),
-                      reinterpret_cast<const bf16x8 *>(b + Cf::OFF_P),
+                      b + Cf::OFF_T, b + Cf::OFF_P,
                       vec, vec + kC, vec + 2 * kC, vec + 3 * kC};
     };
 

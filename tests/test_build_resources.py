@@ -17,7 +17,8 @@ CSRC = gbuild.CSRC
 
 @pytest.mark.skipif(shutil.which(gbuild.hipcc()) is None and not os.path.exists(gbuild.hipcc()),
                     reason="hipcc not available")
-@pytest.mark.parametrize("src", ["gdn_prefill.hip", "gdn_decode.hip"])
+@pytest.mark.parametrize("src", ["gdn_prefill.hip", "gdn_chain4.hip", "gdn_fused2.hip",
+                                 "gdn_segment.hip", "gdn_decode.hip"])
 def test_no_kernel_spills_registers(tmp_path, src):
     flags = [f for f in gbuild.compile_flags() if f not in ("-shared",)]
     cmd = [gbuild.hipcc()] + flags + ["-c", os.path.join(CSRC, src), "-o", str(tmp_path / "k.o"),
