@@ -727,14 +727,20 @@ __global__ __launch_bounds__(kF2Waves * 64, 2) void fused2_kernel(PrefillParams 
                 }
             }
         }
+        // the decay in place first, then the 32 MFMAs with consecutive ones
+        // independent (scaled as it goes, each tile went through one
+        // temporary, and every product waited for the one before)
 #pragma unroll
         for (int a = 0; a < NKT; ++a)
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                st[a][b] *= gC;
+            for (int b = 0; b < NB; ++b) st[a][b] *= gC;
+        phase_fence();
 #pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2) st[a][b] = mma(fkt[a][k2], fd[k2][b], st[a][b]);
-            }
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+            for (int a = 0; a < NKT; ++a)
+#pragma unroll
+                for (int b = 0; b < NB; ++b) st[a][b] = mma(fkt[a][k2], fd[k2][b], st[a][b]);
         const int64_t prow = PREFIX ? pre.take(p, c) : -1;
         if (prow >= 0) {
             float *ps = p.prefix + (prow * p.Hv + h) * D * D;
