@@ -435,13 +435,14 @@ def test_varlen_small(gdn, monkeypatch, D, dtype, path):
     check(o[:0], from_torch(sf), o_ref[:0], S_ref, dtype, f"varlen {path} D{D} {dtype} states")
 
 
-@pytest.mark.parametrize("nseq,Hk", [(300, 2), (37, 3)])
+@pytest.mark.parametrize("nseq,Hk", [(300, 2), (37, 3), (2100, 1)])
 @pytest.mark.parametrize("path", ["default", "fused1"])
 def test_varlen_many_sequences(gdn, monkeypatch, nseq, Hk, path):
     """Many short packed sequences (0 to 200 tokens, slow decay, nonzero
     initial states): the one-pass kernel ranks them by length in each
     workgroup (a sort over more keys than threads; a unit count that is, and
-    one that is not, a multiple of 8), every chain against the oracle."""
+    one that is not, a multiple of 8); past 2,048 sequences it keeps the
+    index order. Every chain against the oracle."""
     if path != "default":
         _set_path(monkeypatch, path)
     rng = np.random.default_rng(400 + nseq)
